@@ -1,0 +1,438 @@
+/*
+ * bg_oracle.c -- plain CPU oracle for the W4A16 / W8A8 quantized linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or constant with the
+ * HIP kernels.
+ *
+ * Everything here is written as the plain definition of what the pages state,
+ * step by step, with no blocking, fusion or reordering:
+ *
+ *   [LPI]  "Low-precision LLM inference: FP8/INT8/INT4/FP4 kernels and
+ *          calibration (8/10)", blog.ruahverce.com
+ *   [AIB]  "Quantization throughput by method: why W4A16 is overtaken by W8A8
+ *          as batch grows", hrletsgo.me
+ *
+ * Floating-point discipline: build with -O2 -ffp-contract=off and without any
+ * fast-math flag, on an SSE2 target (FLT_EVAL_METHOD == 0), so that every
+ * float expression below is one IEEE-754 binary32 operation, correctly
+ * rounded, and every double expression one binary64 operation.
+ *
+ * Readings of points the pages leave open (each is listed in the design notes):
+ *  - round() is round-half-to-even (rintf in the default rounding mode);
+ *  - x/s is an IEEE correctly rounded binary32 division;
+ *  - the INT4 codes are computed with the *stored* FP16-rounded group scale;
+ *  - symmetric qmax is 7 (INT4) / 127 (INT8) / 448 (FP8 E4M3);
+ *  - asymmetric INT4: range widened to include 0, s=(max-min)/15,
+ *    z=clamp(round(-min/s),0,15);
+ *  - an all-zero unit gets scale 1; an FP16 scale that would round to 0 or
+ *    overflow is clamped to [2^-24, 65504];
+ *  - FP8 is OCP E4M3 "FN" (bias 7, max 448, no Inf, S.1111.111 = NaN), cast
+ *    with round-to-nearest-even and saturation to +-448; NaN maps to NaN.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if defined(__FAST_MATH__)
+#error "the oracle must not be built with fast-math"
+#endif
+
+/* granularity codes: same numbering as the public header, restated here */
+enum { ORC_GRAN_TENSOR = 0, ORC_GRAN_ROW = 1, ORC_GRAN_ROW_G128 = 2, ORC_GRAN_BLOCK128 = 3 };
+
+/* ------------------------------------------------------------------------ */
+/* IEEE binary16 and bfloat16 codecs, from the format definitions.           */
+/* ------------------------------------------------------------------------ */
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+float orc_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0x1F) {
+        v = m ? NAN : INFINITY;
+    } else if (e == 0) {
+        v = ldexp((double)m, -24);                  /* subnormal: m * 2^-24 */
+    } else {
+        v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* Round a binary32 value to the nearest binary16, ties to even.
+ * The value is exact in double; within its binade the binary16 quantum is
+ * 2^(e-10) (e clamped to >= -14 for subnormals), so the rounded magnitude is
+ * rint(|f| / quantum) * quantum.  Magnitudes that round to >= 2^16 overflow. */
+uint16_t orc_f32_to_f16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000 : 0;
+    if (isnan(f)) return sign | 0x7E00;
+    double a = fabs((double)f);
+    if (isinf(f)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);          /* a = fr * 2^e, fr in [0.5,1): binade exponent e-1 */
+    e -= 1;
+    if (e < -14) e = -14;
+    double quantum = ldexp(1.0, e - 10);
+    double r = rint(a / quantum) * quantum;       /* RNE in double: exact */
+    if (r >= 65536.0) return sign | 0x7C00;       /* overflow to infinity */
+    if (r < ldexp(1.0, -14)) {                    /* subnormal or zero */
+        return sign | (uint16_t)(r / ldexp(1.0, -24));
+    }
+    int er;
+    frexp(r, &er);
+    er -= 1;
+    uint16_t frac = (uint16_t)((r / ldexp(1.0, er) - 1.0) * 1024.0);
+    return sign | (uint16_t)((er + 15) << 10) | frac;
+}
+
+/* bfloat16 is the upper half of a binary32. */
+float orc_bf16_to_f32(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3 ("FN"): 1 sign, 4 exponent (bias 7), 3 mantissa bits.        */
+/* Normal: 2^(e-7) * (1 + m/8), e = 1..15, except S.1111.111 which is NaN.   */
+/* Subnormal: 2^-6 * m/8.  Largest finite 448.  No infinities.              */
+/* [LPI] §7 "FP8 is a small floating point" (E4M3 = 1/4/3 bits; the variant */
+/* must be pinned), Micikevicius et al. as cited there.                      */
+/* ------------------------------------------------------------------------ */
+
+double orc_e4m3_decode(uint8_t c) {
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xF;
+    int m = c & 7;
+    double v;
+    if (e == 0xF && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Saturating round-to-nearest-even cast.  NaN -> 0x7F|sign; |v| >= 448
+ * (including infinity) -> 448 with sign.  Otherwise the quantum of the
+ * binade is 2^(e-3) with e clamped to >= -6 (the subnormal quantum is
+ * 2^-9), and the magnitude is rint(|v| / quantum) * quantum.  Anything that
+ * would round above 448 saturates to 448. */
+uint8_t orc_e4m3_encode(float v) {
+    uint8_t sign = signbit(v) ? 0x80 : 0;
+    if (isnan(v)) return sign | 0x7F;
+    double a = fabs((double)v);
+    if (a >= 448.0) return sign | 0x7E;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    e -= 1;
+    if (e < -6) e = -6;
+    double quantum = ldexp(1.0, e - 3);
+    double r = rint(a / quantum) * quantum;
+    if (r > 448.0) r = 448.0;
+    if (r == 0.0) return sign;
+    if (r < ldexp(1.0, -6)) return sign | (uint8_t)(r / ldexp(1.0, -9));
+    int er;
+    frexp(r, &er);
+    er -= 1;
+    uint8_t mant = (uint8_t)((r / ldexp(1.0, er) - 1.0) * 8.0);
+    return sign | (uint8_t)((er + 7) << 3) | mant;
+}
+
+/* ------------------------------------------------------------------------ */
+/* INT4 weight quantization, group size G along K, FP16 scales.              */
+/* [LPI] §2 eq. (1) q = clamp(round(x/s) + z, qmin, qmax), eq. (2)          */
+/* x^ = s(q - z); §3 symmetric s = max|x| / qmax (eq. 3) and asymmetric      */
+/* (observed min/max); §4 per-group scales; §5 one FP16 scale per 128.      */
+/* ------------------------------------------------------------------------ */
+
+/* The FP16 scale of one group: value v (binary32) rounded to binary16; an
+ * all-zero group gets 1; results outside [2^-24, 65504] are clamped. */
+static uint16_t group_scale_f16(float v, int all_zero) {
+    if (all_zero) return 0x3C00;                  /* 1.0 */
+    uint16_t h = orc_f32_to_f16(v);
+    if (h == 0x0000) h = 0x0001;                  /* 2^-24 */
+    if (h == 0x7C00) h = 0x7BFF;                  /* 65504 */
+    return h;
+}
+
+/* Quantize W [N][K] (binary32) into unsigned 4-bit codes u [N][K] (0..15),
+ * FP16 scale bits s16 [N][K/G] and zero-points z [N][K/G].
+ * Symmetric: z = 8 is implied (u = q + 8); asymmetric: z explicit. */
+void orc_w4_quantize(const float* w, int64_t N, int64_t K, int G, int asym,
+                     uint8_t* u, uint16_t* s16, uint8_t* z) {
+    int64_t ng = K / G;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const float* wg = w + n * K + g * G;
+            uint8_t* ug = u + n * K + g * G;
+            if (!asym) {
+                float amax = 0.0f;
+                for (int i = 0; i < G; ++i) {
+                    float a = fabsf(wg[i]);
+                    if (a > amax) amax = a;
+                }
+                uint16_t sh = group_scale_f16(amax / 7.0f, amax == 0.0f);
+                float s = orc_f16_to_f32(sh);
+                s16[n * ng + g] = sh;
+                z[n * ng + g] = 8;
+                for (int i = 0; i < G; ++i) {
+                    float q = rintf(wg[i] / s);
+                    if (q < -8.0f) q = -8.0f;
+                    if (q > 7.0f) q = 7.0f;
+                    ug[i] = (uint8_t)((int)q + 8);
+                }
+            } else {
+                float mn = 0.0f, mx = 0.0f;               /* range includes 0 */
+                for (int i = 0; i < G; ++i) {
+                    if (wg[i] < mn) mn = wg[i];
+                    if (wg[i] > mx) mx = wg[i];
+                }
+                float range = mx - mn;
+                uint16_t sh = group_scale_f16(range / 15.0f, range == 0.0f);
+                float s = orc_f16_to_f32(sh);
+                float zf = rintf(-mn / s);
+                if (zf < 0.0f) zf = 0.0f;
+                if (zf > 15.0f) zf = 15.0f;
+                s16[n * ng + g] = sh;
+                z[n * ng + g] = (uint8_t)zf;
+                for (int i = 0; i < G; ++i) {
+                    float q = rintf(wg[i] / s) + zf;
+                    if (q < 0.0f) q = 0.0f;
+                    if (q > 15.0f) q = 15.0f;
+                    ug[i] = (uint8_t)q;
+                }
+            }
+        }
+    }
+}
+
+/* Pack codes into the kernel layout:
+ *   qweight [N][K/8] u32: nibble i (bits 4i..4i+3) of word j holds u[n][8j+i];
+ *   zeros   [N][K/(2G)] u8: low nibble = z of even group, high = odd group. */
+void orc_w4_pack(const uint8_t* u, const uint8_t* z, int64_t N, int64_t K, int G,
+                 int asym, uint32_t* qweight, uint8_t* zeros) {
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < K / 8; ++j) {
+            uint32_t word = 0;
+            for (int i = 0; i < 8; ++i)
+                word |= (uint32_t)(u[n * K + 8 * j + i] & 0xF) << (4 * i);
+            qweight[n * (K / 8) + j] = word;
+        }
+        if (asym) {
+            int64_t ng = K / G;
+            for (int64_t h = 0; h < ng / 2; ++h)
+                zeros[n * (ng / 2) + h] =
+                    (uint8_t)((z[n * ng + 2 * h] & 0xF) | ((z[n * ng + 2 * h + 1] & 0xF) << 4));
+        }
+    }
+}
+
+/* Dequantized weight from the packed form: w^[n,k] = s16 * (u - z), exact
+ * in double.  z = 8 when zeros == NULL (symmetric). */
+void orc_w4_dequant(const uint32_t* qweight, const uint16_t* s16, const uint8_t* zeros,
+                    int64_t N, int64_t K, int G, double* what) {
+    int64_t ng = K / G;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t g = k / G;
+            int uu = (qweight[n * (K / 8) + k / 8] >> (4 * (k % 8))) & 0xF;
+            int zz = 8;
+            if (zeros) zz = (zeros[n * (ng / 2) + g / 2] >> (4 * (g % 2))) & 0xF;
+            what[n * K + k] = (double)orc_f16_to_f32(s16[n * ng + g]) * (double)(uu - zz);
+        }
+    }
+}
+
+/* W4A16 linear: Y[m,n] = sum_k x[m,k] * w^[n,k], in double, where x is the
+ * exact value of the FP16 or BF16 activation.  [AIB] "W4A16" section (INT4
+ * storage, dequantized just before a 16-bit GEMM); [LPI] §11 weight-only
+ * INT4.  Y = X W^T with W stored [N][K]. */
+void orc_gemm_w4a16(const uint16_t* x_bits, int x_is_bf16, int64_t M, int64_t K,
+                    const uint32_t* qweight, const uint16_t* s16, const uint8_t* zeros,
+                    int64_t N, int G, double* y) {
+    double* what = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    orc_w4_dequant(qweight, s16, zeros, N, K, G, what);
+    for (int64_t i = 0; i < M * K; ++i)
+        xd[i] = x_is_bf16 ? (double)orc_bf16_to_f32(x_bits[i]) : (double)orc_f16_to_f32(x_bits[i]);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += xd[m * K + k] * what[n * K + k];
+            y[m * N + n] = acc;
+        }
+    }
+    free(what);
+    free(xd);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dynamic activation / weight quantizers for W8A8.                          */
+/* Scale per unit: s = amax / qmax in binary32 (qmax 127 for INT8, 448 for  */
+/* E4M3); an all-zero unit gets s = 1.  INT8: q = clamp(round(x/s),-128,127)*/
+/* ([LPI] §2 eq. 1 with z = 0, §3 eq. 3).  FP8: q = e4m3_sat_rne(x/s)       */
+/* ([LPI] §8 "Current scaling" and "Block scaling": scale = amax / max_fp8). */
+/* Units ([LPI] §4): TENSOR = whole [R][C]; ROW = one row (per token, or per */
+/* output channel of a weight); ROW_G128 = 1x128 along a row; BLOCK128 =    */
+/* 128x128 tiles.  Scale layouts: TENSOR -> s[0] = scale, s[1] = amax;      */
+/* ROW -> s[R]; ROW_G128 -> s[R][C/128]; BLOCK128 -> s[R/128][C/128].        */
+/* ------------------------------------------------------------------------ */
+
+static int64_t unit_of(int gran, int64_t r, int64_t c, int64_t C) {
+    switch (gran) {
+        case ORC_GRAN_TENSOR: return 0;
+        case ORC_GRAN_ROW: return r;
+        case ORC_GRAN_ROW_G128: return r * (C / 128) + c / 128;
+        default: return (r / 128) * (C / 128) + c / 128;
+    }
+}
+
+static int64_t n_units(int gran, int64_t R, int64_t C) {
+    switch (gran) {
+        case ORC_GRAN_TENSOR: return 1;
+        case ORC_GRAN_ROW: return R;
+        case ORC_GRAN_ROW_G128: return R * (C / 128);
+        default: return (R / 128) * (C / 128);
+    }
+}
+
+/* amax per unit, then scale per unit.  Returns a malloc'd array of the
+ * binary32 scales (one per unit); writes them in the public layout. */
+static float* unit_scales(const float* x, int64_t R, int64_t C, int gran, float qmax, float* s_out) {
+    int64_t nu = n_units(gran, R, C);
+    float* amax = (float*)calloc((size_t)nu, sizeof(float));
+    float* s = (float*)malloc(sizeof(float) * (size_t)nu);
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            float a = fabsf(x[r * C + c]);
+            int64_t uidx = unit_of(gran, r, c, C);
+            if (a > amax[uidx]) amax[uidx] = a;
+        }
+    for (int64_t i = 0; i < nu; ++i) s[i] = (amax[i] == 0.0f) ? 1.0f : amax[i] / qmax;
+    if (gran == ORC_GRAN_TENSOR) {
+        s_out[0] = s[0];
+        s_out[1] = amax[0];
+    } else {
+        for (int64_t i = 0; i < nu; ++i) s_out[i] = s[i];
+    }
+    free(amax);
+    return s;
+}
+
+void orc_quant_int8(const float* x, int64_t R, int64_t C, int gran, int8_t* q, float* s_out) {
+    float* s = unit_scales(x, R, C, gran, 127.0f, s_out);
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c) {
+            float v = rintf(x[r * C + c] / s[unit_of(gran, r, c, C)]);
+            if (v < -128.0f) v = -128.0f;
+            if (v > 127.0f) v = 127.0f;
+            q[r * C + c] = (int8_t)v;
+        }
+    free(s);
+}
+
+void orc_quant_fp8(const float* x, int64_t R, int64_t C, int gran, uint8_t* q, float* s_out) {
+    float* s = unit_scales(x, R, C, gran, 448.0f, s_out);
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; ++c)
+            q[r * C + c] = orc_e4m3_encode(x[r * C + c] / s[unit_of(gran, r, c, C)]);
+    free(s);
+}
+
+/* ------------------------------------------------------------------------ */
+/* W8A8 GEMMs.  [AIB] "W8A8 / FP8" section (native INT8/FP8 GEMM, no upcast)*/
+/* and [LPI] §22 (INT32 / FP32 accumulators).  A [M][K], W [N][K], Y=A W^T. */
+/* ------------------------------------------------------------------------ */
+
+/* Exact integer accumulators.  Returns 0 on success, 1 if some accumulator
+ * does not fit in int32 (then acc holds the low 32 bits). */
+int orc_gemm_i8_acc(const int8_t* a, const int8_t* w, int64_t M, int64_t N, int64_t K, int32_t* acc) {
+    int overflow = 0;
+#pragma omp parallel for schedule(static) reduction(| : overflow)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t t = 0;
+            for (int64_t k = 0; k < K; ++k) t += (int64_t)a[m * K + k] * (int64_t)w[n * K + k];
+            if (t > INT32_MAX || t < INT32_MIN) overflow = 1;
+            acc[m * N + n] = (int32_t)t;
+        }
+    }
+    return overflow;
+}
+
+/* The scale that applies to element (r, kidx) of an operand quantized with
+ * granularity gran (the public scale layout). */
+static double scale_at(const float* s, int gran, int64_t r, int64_t kidx, int64_t C) {
+    switch (gran) {
+        case ORC_GRAN_TENSOR: return (double)s[0];
+        case ORC_GRAN_ROW: return (double)s[r];
+        case ORC_GRAN_ROW_G128: return (double)s[r * (C / 128) + kidx / 128];
+        default: return (double)s[(r / 128) * (C / 128) + kidx / 128];
+    }
+}
+
+/* Y[m,n] = sum_k (dec(a[m,k]) * s_a) * (dec(w[n,k]) * s_w) in double, where
+ * dec is the integer value (INT8) or the E4M3 value (FP8), and each scale is
+ * the one the granularity assigns to that element.  This is the exact
+ * dequantized GEMM; for per-row/per-tensor scales it equals
+ * acc * s_a[m] * s_w[n], and for block scales it equals the sum over 128-wide
+ * K blocks of the block partial sum times s_a[m,kb] * s_w[n/128,kb]. */
+void orc_gemm_w8a8(const void* a, const float* a_s, int a_gran,
+                   const void* w, const float* w_s, int w_gran,
+                   int is_fp8, int64_t M, int64_t N, int64_t K, double* y) {
+    double* ad = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double v = is_fp8 ? orc_e4m3_decode(((const uint8_t*)a)[m * K + k])
+                              : (double)((const int8_t*)a)[m * K + k];
+            ad[m * K + k] = v * scale_at(a_s, a_gran, m, k, K);
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double v = is_fp8 ? orc_e4m3_decode(((const uint8_t*)w)[n * K + k])
+                              : (double)((const int8_t*)w)[n * K + k];
+            wd[n * K + k] = v * scale_at(w_s, w_gran, n, k, K);
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += ad[m * K + k] * wd[n * K + k];
+            y[m * N + n] = acc;
+        }
+    free(ad);
+    free(wd);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Element-wise array helpers for the Python wrapper.                        */
+/* ------------------------------------------------------------------------ */
+
+void orc_f32_to_f16_n(const float* x, int64_t n, uint16_t* h) {
+    for (int64_t i = 0; i < n; ++i) h[i] = orc_f32_to_f16(x[i]);
+}
+
+void orc_f16_to_f32_n(const uint16_t* h, int64_t n, float* x) {
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_f16_to_f32(h[i]);
+}
+
+void orc_bf16_to_f32_n(const uint16_t* b, int64_t n, float* x) {
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_bf16_to_f32(b[i]);
+}
+
+void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* c) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) c[i] = orc_e4m3_encode(x[i]);
+}
+
+void orc_e4m3_decode_n(const uint8_t* c, int64_t n, double* x) {
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_e4m3_decode(c[i]);
+}
