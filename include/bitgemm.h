@@ -1,0 +1,189 @@
+/*
+ * bitgemm.h -- C ABI of the MI355X (gfx950) W4A16 / W8A8 quantized linear layer.
+ *
+ * Sources (cited by title and section):
+ *   [LPI] "Low-precision LLM inference: FP8/INT8/INT4/FP4 kernels and
+ *         calibration (8/10)", blog.ruahverce.com
+ *   [AIB] "Quantization throughput by method: why W4A16 is overtaken by W8A8
+ *         as batch grows", hrletsgo.me
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major buffers,
+ *    aligned to 16 bytes.  The caller allocates and frees them.
+ *  - Activations X are [M][K]; weights W are [N][K] (output channel major,
+ *    K contiguous); the output is Y = X W^T, [M][N].
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    validate arguments on the host and enqueue kernels: they never allocate,
+ *    free, synchronize, or read device memory on the host, so every call may
+ *    be captured into a HIP graph ([LPI] §28: device-side scales, no host
+ *    amax).
+ *  - Validation is fail-closed ([LPI] §24 kernel eligibility, §31
+ *    fallback_policy fail-closed): an ineligible call returns a BG_ERR_* code
+ *    before anything is launched and never falls back to another kernel.
+ *    bg_last_error() then returns a message naming the failed condition.
+ *  - A launch failure returns BG_ERR_HIP.
+ *  - Calls that write overlapping outputs on concurrent streams race.
+ */
+#ifndef BITGEMM_H
+#define BITGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BG_PACK_FORMAT_VERSION 1
+
+typedef enum bg_status {
+    BG_OK = 0,
+    BG_ERR_NULL = 1,         /* a required pointer is NULL                       */
+    BG_ERR_SHAPE = 2,        /* a size is out of range or not a tile multiple    */
+    BG_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned                 */
+    BG_ERR_DTYPE = 4,        /* dtype not accepted by this entry point           */
+    BG_ERR_UNSUPPORTED = 5,  /* granularity / dtype combination not implemented  */
+    BG_ERR_HIP = 6           /* the HIP runtime rejected a launch                */
+} bg_status;
+
+typedef enum bg_dtype {
+    BG_F32 = 0, BG_F16 = 1, BG_BF16 = 2, BG_I8 = 3, BG_FP8_E4M3 = 4, BG_I32 = 5
+} bg_dtype;
+
+/* Scale granularity ([LPI] §4 "Scale granularity is the key"). */
+typedef enum bg_gran {
+    BG_GRAN_TENSOR = 0,    /* one scale for the whole tensor                       */
+    BG_GRAN_ROW = 1,       /* one per row: per token (X) or per output channel (W) */
+    BG_GRAN_ROW_G128 = 2,  /* one per 1x128 group along a row                      */
+    BG_GRAN_BLOCK128 = 3   /* one per 128x128 block                                */
+} bg_gran;
+
+/* Kernel choice for the *_ex entry points (the plain ones use BG_ALGO_AUTO). */
+typedef enum bg_algo {
+    BG_ALGO_AUTO = 0,
+    BG_ALGO_GEMV = 1,      /* W4A16 small-M: VALU dot products, wave reductions    */
+    BG_ALGO_SKINNY = 2,    /* small-M on MFMA (M padded to the MFMA tile)          */
+    BG_ALGO_TILED = 3      /* large-M LDS-tiled MFMA GEMM                          */
+} bg_algo;
+
+/*
+ * w4_pack -- quantize W [N][K] to 4-bit codes with one FP16 scale (and, if
+ * asymmetric, one 4-bit zero-point) per group of `group` consecutive K.
+ *
+ * Defined by [LPI] §2 eq. (1) q = clamp(round(x/s) + z, qmin, qmax) and
+ * eq. (2) x^ = s(q - z); §3 symmetric s = max|x|/qmax (eq. 3) and asymmetric
+ * (observed min/max); §4 per-group scales; §5 FP16 scale per 128 weights.
+ * Readings: round = round-half-to-even; x/s is an IEEE binary32 division by
+ * the stored FP16 scale; symmetric s = fp16(amax/7), codes u = q + 8 in
+ * 1..15; asymmetric: mn = min(0, min w), mx = max(0, max w),
+ * s = fp16((mx - mn)/15), z = clamp(round(-mn/s), 0, 15), u in 0..15; an
+ * all-zero group has s = 1; FP16 scales are clamped to [2^-24, 65504].
+ *
+ *   w        [N][K] of w_dtype (BG_F32, BG_F16 or BG_BF16), finite values
+ *   group    must be 128
+ *   qweight  out [N][K/8] uint32; nibble i (bits 4i..4i+3) of word j holds
+ *            the code of k = 8j + i
+ *   scales   out [N][K/group] FP16 bit patterns
+ *   zeros    out [N][K/(2*group)] uint8 (low nibble: even group, high: odd
+ *            group) when asymmetric != 0; must be NULL when symmetric
+ * Requires N >= 1, K % 256 == 0 (two groups per zeros byte, 16-byte rows).
+ */
+bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, int asymmetric,
+                  uint32_t* qweight, uint16_t* scales, uint8_t* zeros, void* stream);
+
+/*
+ * gemm_w4a16 -- Y = X W^T with W in the w4_pack format, dequantized on chip
+ * (never materialized in HBM: [LPI] §23 fused fast path; [AIB] W4A16
+ * section).  Y[m,n] = sum_g s[n,g] * sum_{k in g} x[m,k] * (u[n,k] - z[n,g]),
+ * z = 8 when zeros == NULL; FP32 accumulation ([LPI] §22), output rounded to
+ * the activation dtype (round-to-nearest-even).
+ *
+ *   x        [M][K] of x_dtype (BG_F16 or BG_BF16)
+ *   qweight, scales, zeros   as produced by w4_pack (zeros NULL = symmetric)
+ *   y        out [M][N] of x_dtype
+ * Requires M >= 1, N >= 1, N % 16 == 0, K % 256 == 0, group == 128.
+ * Small M runs the bandwidth-bound decode kernels, large M the LDS-tiled
+ * MFMA kernel ([LPI] §24: small batch and large prefill use different kernels).
+ */
+bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
+                     const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                     int64_t N, int group, void* y, void* stream);
+
+/* Same as gemm_w4a16 with an explicit kernel choice (BG_ALGO_*). */
+bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        int64_t N, int group, void* y, int algo, void* stream);
+
+/*
+ * act_quant_int8 -- dynamic symmetric INT8 quantization of a [rows][cols]
+ * tensor: per unit of granularity `gran`, s = amax/127 (binary32; s = 1 for an
+ * all-zero unit) and q = clamp(round(x/s), -128, 127), round half to even.
+ * [LPI] §2 eq. (1) with z = 0, §3 eq. (3), §4 per-token / per-channel
+ * scales; §14 (W8A8 activations).  Weights for W8A8 are quantized with this
+ * same call (BG_GRAN_ROW on W gives per-output-channel scales).
+ *
+ *   x       [rows][cols] of x_dtype (BG_F32, BG_F16 or BG_BF16), finite values
+ *   gran    BG_GRAN_TENSOR: scales[0] = s, scales[1] = tensor amax (2 floats)
+ *           BG_GRAN_ROW: scales[rows]
+ *           BG_GRAN_ROW_G128: scales[rows][cols/128]
+ *           BG_GRAN_BLOCK128: scales[rows/128][cols/128] (rows % 128 == 0)
+ *   q       out [rows][cols] int8
+ * Requires rows >= 1, cols % 128 == 0.
+ */
+bg_status act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                         int8_t* q, float* scales, void* stream);
+
+/*
+ * act_quant_fp8 -- dynamic OCP FP8 E4M3 quantization: per unit, s = amax/448
+ * and q = e4m3(x/s) with round-to-nearest-even and saturation to +-448.
+ * [LPI] §7 (E4M3 = 1/4/3 bits; the variant pinned here is OCP E4M3FN: bias
+ * 7, max 448, no infinities, S.1111.111 = NaN), §8 current scaling and block
+ * scaling (scale_block = amax_block / max_representable_fp8).
+ * Arguments and scale layouts as act_quant_int8; q holds E4M3 bytes.
+ */
+bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                        uint8_t* q, float* scales, void* stream);
+
+/*
+ * gemm_w8a8 -- native INT8 or FP8 GEMM of quantized activations A [M][K] and
+ * weights W [N][K] ([AIB] W8A8/FP8 section: no upcast, low-precision matrix
+ * cores; [LPI] §9 FP8 GEMM contract, §22 INT32 / FP32 accumulators).
+ *
+ *   in_dtype BG_I8: INT32 accumulation, acc exact; Y = acc * s_a * s_w in FP32
+ *            BG_FP8_E4M3: FP32 accumulation of exact E4M3 products
+ *   a_gran / w_gran, scales laid out as produced by act_quant_*:
+ *            TENSOR or ROW for either operand (scales applied in the
+ *            epilogue), or, for FP8 only, a_gran = ROW_G128 with
+ *            w_gran = BLOCK128: every 128-wide K block's partial sum is
+ *            scaled by s_a[m][kb] * s_w[n/128][kb] ([LPI] §8 block scaling)
+ *   out_dtype BG_BF16, BG_F16 or BG_F32 (round-to-nearest-even); BG_I32
+ *            (in_dtype BG_I8 only) writes the raw INT32 accumulators
+ *   y        out [M][N] of out_dtype
+ * Requires M >= 1, N % 16 == 0, K % 128 == 0, K <= 131072 for BG_I8
+ * (so |acc| <= K * 128 * 128 < 2^31); BLOCK128 needs N % 128 == 0.
+ */
+bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran,
+                    const void* w, const float* w_scales, int w_gran,
+                    int in_dtype, int64_t M, int64_t N, int64_t K,
+                    void* y, int out_dtype, void* stream);
+
+/* Same as gemm_w8a8 with an explicit kernel choice (BG_ALGO_SKINNY / TILED). */
+bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran,
+                       const void* w, const float* w_scales, int w_gran,
+                       int in_dtype, int64_t M, int64_t N, int64_t K,
+                       void* y, int out_dtype, int algo, void* stream);
+
+/* The kernel BG_ALGO_AUTO selects for a call of this shape (a BG_ALGO_* value). */
+int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype);
+int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype);
+
+/* Static description of a status code. */
+const char* bg_status_string(int status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* bg_last_error(void);
+/* BG_PACK_FORMAT_VERSION of the library (layout of qweight/scales/zeros). */
+int bg_pack_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BITGEMM_H */

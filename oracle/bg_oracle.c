@@ -26,8 +26,9 @@
  *  - symmetric qmax is 7 (INT4) / 127 (INT8) / 448 (FP8 E4M3);
  *  - asymmetric INT4: range widened to include 0, s=(max-min)/15,
  *    z=clamp(round(-min/s),0,15);
- *  - an all-zero unit gets scale 1; an FP16 scale that would round to 0 or
- *    overflow is clamped to [2^-24, 65504];
+ *  - an all-zero unit gets scale 1 (for the binary32 W8A8 scales: any scale
+ *    that comes out 0, which also covers amax/qmax underflowing); an FP16
+ *    scale that would round to 0 or overflow is clamped to [2^-24, 65504];
  *  - FP8 is OCP E4M3 "FN" (bias 7, max 448, no Inf, S.1111.111 = NaN), cast
  *    with round-to-nearest-even and saturation to +-448; NaN maps to NaN.
  */
@@ -276,7 +277,7 @@ void orc_gemm_w4a16(const uint16_t* x_bits, int x_is_bf16, int64_t M, int64_t K,
 /* ------------------------------------------------------------------------ */
 /* Dynamic activation / weight quantizers for W8A8.                          */
 /* Scale per unit: s = amax / qmax in binary32 (qmax 127 for INT8, 448 for  */
-/* E4M3); an all-zero unit gets s = 1.  INT8: q = clamp(round(x/s),-128,127)*/
+/* E4M3); a zero scale (all-zero unit, or amax/qmax underflow) becomes 1.  INT8: q = clamp(round(x/s),-128,127)*/
 /* ([LPI] §2 eq. 1 with z = 0, §3 eq. 3).  FP8: q = e4m3_sat_rne(x/s)       */
 /* ([LPI] §8 "Current scaling" and "Block scaling": scale = amax / max_fp8). */
 /* Units ([LPI] §4): TENSOR = whole [R][C]; ROW = one row (per token, or per */
@@ -315,7 +316,10 @@ static float* unit_scales(const float* x, int64_t R, int64_t C, int gran, float 
             int64_t uidx = unit_of(gran, r, c, C);
             if (a > amax[uidx]) amax[uidx] = a;
         }
-    for (int64_t i = 0; i < nu; ++i) s[i] = (amax[i] == 0.0f) ? 1.0f : amax[i] / qmax;
+    for (int64_t i = 0; i < nu; ++i) {
+        s[i] = amax[i] / qmax;
+        if (s[i] == 0.0f) s[i] = 1.0f;     /* all-zero unit (or amax/qmax underflows) */
+    }
     if (gran == ORC_GRAN_TENSOR) {
         s_out[0] = s[0];
         s_out[1] = amax[0];

@@ -273,3 +273,17 @@ def test_quant_scale_layouts(orc):
     assert s[5, 2] == np.float32(np.abs(x[5, 256:384]).max()) / np.float32(448)
     _, s = orc.act_quant_fp8(x, 3)
     assert s[1, 0] == np.float32(np.abs(x[128:256, 0:128]).max()) / np.float32(448)
+
+
+def test_quant_underflowing_scale(orc):
+    """Reading for a unit whose amax/qmax underflows binary32 to zero: like an
+    all-zero unit it gets scale 1 (all codes 0), so no division by zero occurs."""
+    x = np.zeros((2, 128), np.float32)
+    x[0, 3] = np.float32(1e-44)                   # subnormal; 1e-44/127 == 0
+    x[1, 3] = np.float32(1e-40)                   # subnormal; scale stays subnormal, > 0
+    q, s = orc.act_quant_int8(x, 1)
+    assert s[0] == 1.0 and np.all(q[0] == 0)
+    assert 0 < s[1] < 1e-38 and q[1, 3] == 127
+    q, s = orc.act_quant_fp8(x, 1)
+    assert s[0] == 1.0 and np.all((q[0] & 0x7F) == 0)
+    assert q[1, 3] == 0x7E
