@@ -1,0 +1,202 @@
+// capi.hip -- the exported C ABI (include/bitgemm.h): argument validation
+// (fail-closed, "Low-precision LLM inference" §24 eligibility checklist and
+// §31 fallback_policy) and kernel dispatch by M ("small batch and large
+// prefill get different kernels", §24).  Validation touches no HIP API, so
+// a rejected call never reaches the device.
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/bitgemm.h"
+#include "bg_internal.h"
+
+#define BG_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bg_status fail(bg_status st, const char* fmt, long long a = 0, long long b = 0) {
+    std::snprintf(g_last_error, sizeof(g_last_error), fmt, a, b);
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bg_status launched(const char* what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        std::snprintf(g_last_error, sizeof(g_last_error), "%s: launch failed: %s", what, hipGetErrorString(e));
+        return BG_ERR_HIP;
+    }
+    g_last_error[0] = '\0';
+    return BG_OK;
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;   // N, act_quant rows
+constexpr int64_t kMaxDim = int64_t(1) << 20;    // K, cols
+constexpr int64_t kMaxM = int64_t(65535) * 16;   // GEMM M: grid.y stays below 65536
+constexpr int64_t kMaxGemvM = 256;               // explicit GEMV requests
+
+// Decode kernels up to this batch; MFMA skinny kernel up to kSkinnyMax; tiled beyond.
+constexpr int64_t kW4GemvMax = 4;
+constexpr int64_t kW4SkinnyMax = 32;
+constexpr int64_t kW8SkinnyMax = 32;
+
+int w4_auto_algo(int64_t M) {
+    if (M <= kW4GemvMax) return BG_ALGO_GEMV;
+    if (M <= kW4SkinnyMax) return BG_ALGO_SKINNY;
+    return BG_ALGO_TILED;
+}
+
+int w8_auto_algo(int64_t M) { return M <= kW8SkinnyMax ? BG_ALGO_SKINNY : BG_ALGO_TILED; }
+
+}  // namespace
+
+BG_EXPORT bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, int asymmetric,
+                            uint32_t* qweight, uint16_t* scales, uint8_t* zeros, void* stream) {
+    if (!w || !qweight || !scales) return fail(BG_ERR_NULL, "w4_pack: w, qweight and scales must be non-NULL");
+    if (asymmetric && !zeros) return fail(BG_ERR_NULL, "w4_pack: asymmetric packing needs a zeros buffer");
+    if (!asymmetric && zeros) return fail(BG_ERR_UNSUPPORTED, "w4_pack: zeros must be NULL when symmetric");
+    if (w_dtype != BG_F32 && w_dtype != BG_F16 && w_dtype != BG_BF16)
+        return fail(BG_ERR_DTYPE, "w4_pack: w_dtype %lld is not F32/F16/BF16", w_dtype);
+    if (group != 128) return fail(BG_ERR_UNSUPPORTED, "w4_pack: group %lld (only 128 is supported)", group);
+    if (N < 1 || N > kMaxRows) return fail(BG_ERR_SHAPE, "w4_pack: N=%lld out of range", N);
+    if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "w4_pack: K=%lld must be a multiple of 256", K);
+    if (N * (K / 8) / 256 >= (int64_t(1) << 31)) return fail(BG_ERR_SHAPE, "w4_pack: N*K=%lld too large", N * K);
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zeros && !aligned16(zeros)))
+        return fail(BG_ERR_ALIGN, "w4_pack: pointers must be 16-byte aligned");
+    bg::launch_w4_pack(w, w_dtype, N, K, asymmetric != 0, qweight, scales, zeros,
+                       static_cast<hipStream_t>(stream));
+    return launched("w4_pack");
+}
+
+BG_EXPORT int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype) {
+    (void)N; (void)K; (void)x_dtype;
+    return w4_auto_algo(M);
+}
+
+BG_EXPORT bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                                  const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                                  int algo, void* stream) {
+    if (!x || !qweight || !scales || !y) return fail(BG_ERR_NULL, "gemm_w4a16: x, qweight, scales and y must be non-NULL");
+    if (x_dtype != BG_F16 && x_dtype != BG_BF16)
+        return fail(BG_ERR_DTYPE, "gemm_w4a16: x_dtype %lld is not F16/BF16", x_dtype);
+    if (group != 128) return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16: group %lld (only 128 is supported)", group);
+    if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w4a16: M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w4a16: N=%lld must be a multiple of 16", N);
+    if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a16: K=%lld must be a multiple of 256", K);
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || (zeros && !aligned16(zeros)))
+        return fail(BG_ERR_ALIGN, "gemm_w4a16: pointers must be 16-byte aligned");
+    if (algo == BG_ALGO_AUTO) algo = w4_auto_algo(M);
+    if (algo == BG_ALGO_GEMV && M > kMaxGemvM)
+        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 (M=%lld)", M);
+    const bool bf16 = x_dtype == BG_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (algo) {
+        case BG_ALGO_GEMV: bg::launch_w4a16_gemv(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
+        case BG_ALGO_SKINNY: bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
+        case BG_ALGO_TILED: bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
+        default: return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16: unknown algo %lld", algo);
+    }
+    return launched("gemm_w4a16");
+}
+
+BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                               const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                               void* stream) {
+    return gemm_w4a16_ex(x, x_dtype, M, K, qweight, scales, zeros, N, group, y, BG_ALGO_AUTO, stream);
+}
+
+static bg_status act_quant(const char* name, bool fp8, const void* x, int x_dtype, int64_t rows, int64_t cols,
+                           int gran, void* q, float* scales, void* stream) {
+    if (!x || !q || !scales) return fail(BG_ERR_NULL, "act_quant: x, q and scales must be non-NULL");
+    if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
+        return fail(BG_ERR_DTYPE, "act_quant: x_dtype %lld is not F32/F16/BF16", x_dtype);
+    if (gran < BG_GRAN_TENSOR || gran > BG_GRAN_BLOCK128)
+        return fail(BG_ERR_UNSUPPORTED, "act_quant: unknown granularity %lld", gran);
+    if (rows < 1 || rows > kMaxRows) return fail(BG_ERR_SHAPE, "act_quant: rows=%lld out of range", rows);
+    if (cols < 128 || cols > kMaxDim || cols % 128)
+        return fail(BG_ERR_SHAPE, "act_quant: cols=%lld must be a multiple of 128", cols);
+    if (gran == BG_GRAN_BLOCK128 && rows % 128)
+        return fail(BG_ERR_SHAPE, "act_quant: BLOCK128 needs rows %% 128 == 0 (rows=%lld)", rows);
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
+        return fail(BG_ERR_ALIGN, "act_quant: pointers must be 16-byte aligned");
+    bg::launch_act_quant(x, x_dtype, rows, cols, gran, fp8, q, scales, static_cast<hipStream_t>(stream));
+    return launched(name);
+}
+
+BG_EXPORT bg_status act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran, int8_t* q,
+                                   float* scales, void* stream) {
+    return act_quant("act_quant_int8", false, x, x_dtype, rows, cols, gran, q, scales, stream);
+}
+
+BG_EXPORT bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran, uint8_t* q,
+                                  float* scales, void* stream) {
+    return act_quant("act_quant_fp8", true, x, x_dtype, rows, cols, gran, q, scales, stream);
+}
+
+BG_EXPORT int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype) {
+    (void)N; (void)K; (void)in_dtype;
+    return w8_auto_algo(M);
+}
+
+BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran, const void* w,
+                                 const float* w_scales, int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K,
+                                 void* y, int out_dtype, int algo, void* stream) {
+    if (!a || !w || !y) return fail(BG_ERR_NULL, "gemm_w8a8: a, w and y must be non-NULL");
+    if (in_dtype != BG_I8 && in_dtype != BG_FP8_E4M3)
+        return fail(BG_ERR_DTYPE, "gemm_w8a8: in_dtype %lld is not I8/FP8_E4M3", in_dtype);
+    const bool raw = out_dtype == BG_I32;
+    if (raw && in_dtype != BG_I8) return fail(BG_ERR_DTYPE, "gemm_w8a8: I32 output needs I8 inputs");
+    if (!raw && out_dtype != BG_BF16 && out_dtype != BG_F16 && out_dtype != BG_F32)
+        return fail(BG_ERR_DTYPE, "gemm_w8a8: out_dtype %lld is not BF16/F16/F32/I32", out_dtype);
+    if (!raw && (!a_scales || !w_scales)) return fail(BG_ERR_NULL, "gemm_w8a8: scales must be non-NULL");
+    const bool per = (a_gran == BG_GRAN_TENSOR || a_gran == BG_GRAN_ROW) &&
+                     (w_gran == BG_GRAN_TENSOR || w_gran == BG_GRAN_ROW);
+    const bool block = a_gran == BG_GRAN_ROW_G128 && w_gran == BG_GRAN_BLOCK128;
+    if (!raw && !per && !(block && in_dtype == BG_FP8_E4M3))
+        return fail(BG_ERR_UNSUPPORTED, "gemm_w8a8: granularity pair (%lld, %lld) not supported", a_gran, w_gran);
+    if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w8a8: M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w8a8: N=%lld must be a multiple of 16", N);
+    if (K < 128 || K > kMaxDim || K % 128) return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld must be a multiple of 128", K);
+    if (in_dtype == BG_I8 && K > 131072)
+        return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld too long for exact INT32 accumulation", K);
+    if (block && N % 128) return fail(BG_ERR_SHAPE, "gemm_w8a8: BLOCK128 weights need N %% 128 == 0 (N=%lld)", N);
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y) || (a_scales && !aligned16(a_scales)) ||
+        (w_scales && !aligned16(w_scales)))
+        return fail(BG_ERR_ALIGN, "gemm_w8a8: pointers must be 16-byte aligned");
+    if (algo == BG_ALGO_AUTO) algo = w8_auto_algo(M);
+    bg::W8A8Args g{a, a_scales, raw ? BG_GRAN_ROW : a_gran, w, w_scales, raw ? BG_GRAN_ROW : w_gran,
+                   in_dtype == BG_FP8_E4M3, M, N, K, y, out_dtype};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    switch (algo) {
+        case BG_ALGO_SKINNY: bg::launch_w8a8_skinny(g, s); break;
+        case BG_ALGO_TILED: bg::launch_w8a8_tiled(g, s); break;
+        default: return fail(BG_ERR_UNSUPPORTED, "gemm_w8a8: unknown algo %lld", algo);
+    }
+    return launched("gemm_w8a8");
+}
+
+BG_EXPORT bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran, const void* w,
+                              const float* w_scales, int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K,
+                              void* y, int out_dtype, void* stream) {
+    return gemm_w8a8_ex(a, a_scales, a_gran, w, w_scales, w_gran, in_dtype, M, N, K, y, out_dtype, BG_ALGO_AUTO,
+                        stream);
+}
+
+BG_EXPORT const char* bg_status_string(int status) {
+    switch (status) {
+        case BG_OK: return "ok";
+        case BG_ERR_NULL: return "null pointer";
+        case BG_ERR_SHAPE: return "unsupported shape";
+        case BG_ERR_ALIGN: return "misaligned pointer";
+        case BG_ERR_DTYPE: return "unsupported dtype";
+        case BG_ERR_UNSUPPORTED: return "unsupported combination";
+        case BG_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+BG_EXPORT const char* bg_last_error(void) { return g_last_error; }
+
+BG_EXPORT int bg_pack_format_version(void) { return BG_PACK_FORMAT_VERSION; }

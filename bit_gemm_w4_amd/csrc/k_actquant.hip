@@ -1,0 +1,240 @@
+// k_actquant.hip -- dynamic INT8 / FP8-E4M3 quantizers (act_quant_int8/fp8).
+//
+// "Low-precision LLM inference": §2 eq. (1) with z = 0 and §3 eq. (3)
+// (s = amax / qmax); §4 granularities (per tensor, per token/row, per group,
+// per block); §8 current scaling (amax of the tensor being quantized) and
+// block scaling (scale_block = amax_block / max_fp8).  qmax is 127 (INT8) or
+// 448 (E4M3); a scale that comes out 0 (all-zero unit) is replaced by 1.
+//
+// Every kernel keeps its unit in registers between the amax reduction and
+// the quantization, so HBM is read once and written once (2 B in, 1 B out per
+// element for BF16): these kernels are bandwidth-bound, and the per-token
+// amax is the reduction the page warns can sit on the critical path (§4).
+// Per-tensor scaling needs a grid-wide amax: a one-thread fill kernel clears
+// the amax slot (no hipMemset, so the sequence is graph-capturable), the amax
+// kernel combines block maxima with an integer atomic max on the float bits
+// (valid because amax >= 0), and the quantize kernel reads the slot.
+#include "bg_device.h"
+#include "bg_internal.h"
+
+namespace bg {
+
+#pragma clang fp contract(off)
+
+enum { G_TENSOR = 0, G_ROW = 1, G_ROW_G128 = 2, G_BLOCK128 = 3 };
+
+template <bool FP8>
+__device__ __forceinline__ float unit_scale(float amax) {
+    float s = amax / (FP8 ? 448.0f : 127.0f);
+    return s == 0.0f ? 1.0f : s;
+}
+
+// Quantize 8 values with scale s and store 8 bytes at q[idx].
+template <bool FP8>
+__device__ __forceinline__ void quant_store8(const float v[8], float s, void* q, int64_t idx) {
+    uint32_t lo = 0, hi = 0;
+    if constexpr (FP8) {
+        lo = e4m3x2(v[0] / s, v[1] / s) | (e4m3x2(v[2] / s, v[3] / s) << 16);
+        hi = e4m3x2(v[4] / s, v[5] / s) | (e4m3x2(v[6] / s, v[7] / s) << 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float r = __builtin_rintf(v[i] / s);
+            r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
+            const uint32_t b = (uint32_t)((int)r & 0xFF);
+            if (i < 4) lo |= b << (8 * i);
+            else hi |= b << (8 * (i - 4));
+        }
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(q) + idx) = make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ float amax8(const float v[8]) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = __builtin_fmaxf(a, __builtin_fabsf(v[i]));
+    return a;
+}
+
+// Max over a 256-thread block; every thread gets the result.
+__device__ __forceinline__ float block_max256(float a, float* red) {
+    a = wave_max<64>(a);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = a;
+    __syncthreads();
+    a = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    return a;
+}
+
+// ---- per row (token / output channel), rows up to 256 * 8 * MAXIT long ----
+constexpr int ROW_MAXIT = 8;
+
+template <int DT, bool FP8>
+__global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, int64_t C,
+                                                   void* __restrict__ q, float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const int64_t nchunk = C >> 3;
+    float v[ROW_MAXIT][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int it = 0; it < ROW_MAXIT; ++it) {
+        const int64_t c = (int64_t)it * 256 + threadIdx.x;
+        if (c < nchunk) {
+            load8_f32<DT>(x, r * C + c * 8, v[it]);
+            a = __builtin_fmaxf(a, amax8(v[it]));
+        }
+    }
+    const float s = unit_scale<FP8>(block_max256(a, red));
+#pragma unroll
+    for (int it = 0; it < ROW_MAXIT; ++it) {
+        const int64_t c = (int64_t)it * 256 + threadIdx.x;
+        if (c < nchunk) quant_store8<FP8>(v[it], s, q, r * C + c * 8);
+    }
+    if (threadIdx.x == 0) scales[r] = s;
+}
+
+// Rows longer than 256 * 8 * ROW_MAXIT: amax pass, then a second read.
+template <int DT, bool FP8>
+__global__ __launch_bounds__(256) void k_quant_row_2pass(const void* __restrict__ x, int64_t C,
+                                                         void* __restrict__ q,
+                                                         float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const int64_t nchunk = C >> 3;
+    float v[8];
+    float a = 0.0f;
+    for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
+        load8_f32<DT>(x, r * C + c * 8, v);
+        a = __builtin_fmaxf(a, amax8(v));
+    }
+    const float s = unit_scale<FP8>(block_max256(a, red));
+    for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
+        load8_f32<DT>(x, r * C + c * 8, v);
+        quant_store8<FP8>(v, s, q, r * C + c * 8);
+    }
+    if (threadIdx.x == 0) scales[r] = s;
+}
+
+// ---- 1 x 128 groups: 16 consecutive lanes per group ----
+template <int DT, bool FP8>
+__global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, int64_t total_chunks,
+                                                    void* __restrict__ q, float* __restrict__ scales) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total_chunks) return;          // total_chunks is a multiple of 16
+    float v[8];
+    load8_f32<DT>(x, t * 8, v);
+    const float s = unit_scale<FP8>(wave_max<16>(amax8(v)));
+    quant_store8<FP8>(v, s, q, t * 8);
+    if ((t & 15) == 0) scales[t >> 4] = s;
+}
+
+// ---- 128 x 128 blocks: one workgroup per block ----
+template <int DT, bool FP8>
+__global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__ x, int64_t C,
+                                                        void* __restrict__ q,
+                                                        float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t nb_c = C >> 7;
+    const int64_t rb = blockIdx.x / nb_c, cb = blockIdx.x - rb * nb_c;
+    const int lane_c = threadIdx.x & 15, lane_r = threadIdx.x >> 4;   // 16 x 16 threads
+    float v[8][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int64_t row = rb * 128 + it * 16 + lane_r;
+        load8_f32<DT>(x, row * C + cb * 128 + lane_c * 8, v[it]);
+        a = __builtin_fmaxf(a, amax8(v[it]));
+    }
+    const float s = unit_scale<FP8>(block_max256(a, red));
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int64_t row = rb * 128 + it * 16 + lane_r;
+        quant_store8<FP8>(v[it], s, q, row * C + cb * 128 + lane_c * 8);
+    }
+    if (threadIdx.x == 0) scales[blockIdx.x] = s;
+}
+
+// ---- whole tensor ----
+__global__ void k_clear_amax(float* __restrict__ scales) { scales[1] = 0.0f; }
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x, int64_t nchunk,
+                                                     float* __restrict__ scales) {
+    __shared__ float red[4];
+    float v[8];
+    float a = 0.0f;
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk;
+         c += (int64_t)gridDim.x * 256) {
+        load8_f32<DT>(x, c * 8, v);
+        a = __builtin_fmaxf(a, amax8(v));
+    }
+    a = block_max256(a, red);
+    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(scales + 1), __float_as_uint(a));
+}
+
+template <int DT, bool FP8>
+__global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x, int64_t nchunk,
+                                                      void* __restrict__ q,
+                                                      float* __restrict__ scales) {
+    const float s = unit_scale<FP8>(scales[1]);
+    float v[8];
+    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk;
+         c += (int64_t)gridDim.x * 256) {
+        load8_f32<DT>(x, c * 8, v);
+        quant_store8<FP8>(v, s, q, c * 8);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
+}
+
+static unsigned grid_for(int64_t nchunk) {
+    int64_t b = (nchunk + 255) / 256;
+    if (b > 256 * 16) b = 256 * 16;        // grid-stride beyond 16 blocks per CU
+    return (unsigned)(b < 1 ? 1 : b);
+}
+
+template <int DT, bool FP8>
+static void launch_typed(const void* x, int64_t R, int64_t C, int gran, void* q, float* sc,
+                         hipStream_t s) {
+    switch (gran) {
+        case G_ROW:
+            if (C <= 256 * 8 * ROW_MAXIT)
+                hipLaunchKernelGGL((k_quant_row<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+            else
+                hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+            break;
+        case G_ROW_G128: {
+            const int64_t chunks = R * (C >> 3);
+            hipLaunchKernelGGL((k_quant_g128<DT, FP8>), dim3((unsigned)((chunks + 255) / 256)), dim3(256),
+                               0, s, x, chunks, q, sc);
+            break;
+        }
+        case G_BLOCK128:
+            hipLaunchKernelGGL((k_quant_block128<DT, FP8>), dim3((unsigned)((R >> 7) * (C >> 7))), dim3(256),
+                               0, s, x, C, q, sc);
+            break;
+        default: {
+            const int64_t chunks = R * (C >> 3);
+            hipLaunchKernelGGL(k_clear_amax, dim3(1), dim3(1), 0, s, sc);
+            hipLaunchKernelGGL((k_amax_tensor<DT>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks, sc);
+            hipLaunchKernelGGL((k_quant_tensor<DT, FP8>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks,
+                               q, sc);
+            break;
+        }
+    }
+}
+
+void launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8, void* q,
+                      float* scales, hipStream_t s) {
+    if (out_fp8) {
+        if (dt == DT_F32) launch_typed<DT_F32, true>(x, R, C, gran, q, scales, s);
+        else if (dt == DT_F16) launch_typed<DT_F16, true>(x, R, C, gran, q, scales, s);
+        else launch_typed<DT_BF16, true>(x, R, C, gran, q, scales, s);
+    } else {
+        if (dt == DT_F32) launch_typed<DT_F32, false>(x, R, C, gran, q, scales, s);
+        else if (dt == DT_F16) launch_typed<DT_F16, false>(x, R, C, gran, q, scales, s);
+        else launch_typed<DT_BF16, false>(x, R, C, gran, q, scales, s);
+    }
+}
+
+}  // namespace bg

@@ -1,0 +1,198 @@
+"""Thin Python binding of ``libbitgemm.so`` (the C ABI in ``include/bitgemm.h``).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI.  Torch tensors supply device memory and the current HIP stream; the
+functions here check dtypes/devices, allocate outputs with torch, pass raw
+pointers and raise :class:`BitGemmError` on a non-zero status.  There is no
+CPU fallback: if the library is missing, :func:`lib` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbitgemm.so")
+
+# enums of include/bitgemm.h
+F32, F16, BF16, I8, FP8_E4M3, I32 = 0, 1, 2, 3, 4, 5
+GRAN_TENSOR, GRAN_ROW, GRAN_ROW_G128, GRAN_BLOCK128 = 0, 1, 2, 3
+ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED = 0, 1, 2, 3
+PACK_FORMAT_VERSION = 1
+
+EXPORTS = (
+    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
+    "gemm_w8a8_ex", "gemm_w4a16_algo", "gemm_w8a8_algo", "bg_status_string", "bg_last_error",
+    "bg_pack_format_version",
+)
+
+_TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+
+class BitGemmError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        L = lib()
+        self.status = status
+        msg = L.bg_last_error().decode() or L.bg_status_string(status).decode()
+        super().__init__(f"{fn}: status {status} ({L.bg_status_string(status).decode()}): {msg}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbitgemm.so (built in-tree by ``bit_gemm_w4_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_gemm_w4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        sig = {
+            "w4_pack": [P, I, I64, I64, I, I, P, P, P, P],
+            "gemm_w4a16": [P, I, I64, I64, P, P, P, I64, I, P, P],
+            "gemm_w4a16_ex": [P, I, I64, I64, P, P, P, I64, I, P, I, P],
+            "act_quant_int8": [P, I, I64, I64, I, P, P, P],
+            "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
+            "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
+            "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
+            "gemm_w4a16_algo": [I64, I64, I64, I],
+            "gemm_w8a8_algo": [I64, I64, I64, I],
+            "bg_status_string": [I],
+            "bg_last_error": [],
+            "bg_pack_format_version": [],
+        }
+        for name, argtypes in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name in ("bg_status_string", "bg_last_error") else ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("bitgemm operands must be device tensors")
+    if not t.is_contiguous():
+        raise ValueError("bitgemm operands must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise BitGemmError(status, fn)
+
+
+# --------------------------------------------------------------------- W4 ----
+
+@dataclass
+class PackedW4:
+    """INT4 weights in the w4_pack layout (BG_PACK_FORMAT_VERSION 1)."""
+    qweight: torch.Tensor        # int32 [N][K/8], nibble i of word j = k 8j+i
+    scales: torch.Tensor         # float16 [N][K/128]
+    zeros: torch.Tensor | None   # uint8 [N][K/256] (two 4-bit zero-points) or None
+    N: int
+    K: int
+    group: int = 128
+
+    @property
+    def nbytes(self) -> int:
+        z = 0 if self.zeros is None else self.zeros.numel()
+        return self.qweight.numel() * 4 + self.scales.numel() * 2 + z
+
+
+def w4_pack(w: torch.Tensor, group: int = 128, asymmetric: bool = False, stream=None) -> PackedW4:
+    N, K = w.shape
+    dt = _TORCH_DT.get(w.dtype)
+    if dt is None:
+        raise ValueError(f"w4_pack: unsupported dtype {w.dtype}")
+    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
+    scales = torch.empty((N, K // group), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((N, K // (2 * group)), dtype=torch.uint8, device=w.device) if asymmetric else None
+    _check(lib().w4_pack(_ptr(w), dt, N, K, group, int(asymmetric), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                         _stream(stream)), "w4_pack")
+    return PackedW4(qweight, scales, zeros, N, K, group)
+
+
+def gemm_w4a16(x: torch.Tensor, packed: PackedW4, out: torch.Tensor | None = None, algo: int = ALGO_AUTO,
+               stream=None) -> torch.Tensor:
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"gemm_w4a16: x has K={K}, weights K={packed.K}")
+    dt = _TORCH_DT.get(x.dtype)
+    if dt not in (F16, BF16):
+        raise ValueError(f"gemm_w4a16: activations must be float16/bfloat16, got {x.dtype}")
+    if out is None:
+        out = torch.empty((M, packed.N), dtype=x.dtype, device=x.device)
+    _check(lib().gemm_w4a16_ex(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales), _ptr(packed.zeros),
+                               packed.N, packed.group, _ptr(out), algo, _stream(stream)), "gemm_w4a16")
+    return out
+
+
+def gemm_w4a16_algo(M: int, N: int, K: int, x_dtype: torch.dtype = torch.bfloat16) -> int:
+    return lib().gemm_w4a16_algo(M, N, K, _TORCH_DT[x_dtype])
+
+
+# ------------------------------------------------------------------- W8A8 ----
+
+def scale_shape(gran: int, rows: int, cols: int):
+    return {GRAN_TENSOR: (2,), GRAN_ROW: (rows,), GRAN_ROW_G128: (rows, cols // 128),
+            GRAN_BLOCK128: (rows // 128, cols // 128)}[gran]
+
+
+def _act_quant(fn: str, x: torch.Tensor, gran: int, out_dtype: torch.dtype, stream=None):
+    R, C = x.shape
+    dt = _TORCH_DT.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"{fn}: unsupported dtype {x.dtype}")
+    q = torch.empty((R, C), dtype=out_dtype, device=x.device)
+    s = torch.empty(scale_shape(gran, R, C), dtype=torch.float32, device=x.device)
+    _check(getattr(lib(), fn)(_ptr(x), dt, R, C, gran, _ptr(q), _ptr(s), _stream(stream)), fn)
+    return q, s
+
+
+def act_quant_int8(x: torch.Tensor, gran: int = GRAN_ROW, stream=None):
+    """-> (int8 codes [R][C], float32 scales in the layout of `gran`)."""
+    return _act_quant("act_quant_int8", x, gran, torch.int8, stream)
+
+
+def act_quant_fp8(x: torch.Tensor, gran: int = GRAN_ROW, stream=None):
+    """-> (E4M3 bytes as uint8 [R][C], float32 scales in the layout of `gran`)."""
+    return _act_quant("act_quant_fp8", x, gran, torch.uint8, stream)
+
+
+_OUT_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32}
+
+
+def gemm_w8a8(a: torch.Tensor, a_scales: torch.Tensor | None, a_gran: int, w: torch.Tensor,
+              w_scales: torch.Tensor | None, w_gran: int, out_dtype: torch.dtype = torch.bfloat16,
+              out: torch.Tensor | None = None, algo: int = ALGO_AUTO, stream=None) -> torch.Tensor:
+    M, K = a.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError(f"gemm_w8a8: K mismatch {K} vs {K2}")
+    if a.dtype == torch.int8 and w.dtype == torch.int8:
+        in_dt = I8
+    elif a.dtype == torch.uint8 and w.dtype == torch.uint8:
+        in_dt = FP8_E4M3
+    else:
+        raise ValueError("gemm_w8a8: operands must both be int8 or both E4M3 bytes (uint8)")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(lib().gemm_w8a8_ex(_ptr(a), _ptr(a_scales), a_gran, _ptr(w), _ptr(w_scales), w_gran, in_dt, M, N, K,
+                              _ptr(out), _OUT_DT[out.dtype], algo, _stream(stream)), "gemm_w8a8")
+    return out
+
+
+def gemm_w8a8_algo(M: int, N: int, K: int, fp8: bool = False) -> int:
+    return lib().gemm_w8a8_algo(M, N, K, FP8_E4M3 if fp8 else I8)

@@ -100,8 +100,8 @@ bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, i
  *   x        [M][K] of x_dtype (BG_F16 or BG_BF16)
  *   qweight, scales, zeros   as produced by w4_pack (zeros NULL = symmetric)
  *   y        out [M][N] of x_dtype
- * Requires M >= 1, N >= 1, N % 16 == 0, K % 256 == 0, group == 128.
- * Small M runs the bandwidth-bound decode kernels, large M the LDS-tiled
+ * Requires 1 <= M <= 1048560, N % 16 == 0, K % 256 == 0, group == 128
+ * (BG_ALGO_GEMV: M <= 256).  Small M runs the bandwidth-bound decode kernels, large M the LDS-tiled
  * MFMA kernel ([LPI] §24: small batch and large prefill use different kernels).
  */
 bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
@@ -158,7 +158,7 @@ bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, 
  *   out_dtype BG_BF16, BG_F16 or BG_F32 (round-to-nearest-even); BG_I32
  *            (in_dtype BG_I8 only) writes the raw INT32 accumulators
  *   y        out [M][N] of out_dtype
- * Requires M >= 1, N % 16 == 0, K % 128 == 0, K <= 131072 for BG_I8
+ * Requires 1 <= M <= 1048560, N % 16 == 0, K % 128 == 0, K <= 131072 for BG_I8
  * (so |acc| <= K * 128 * 128 < 2^31); BLOCK128 needs N % 128 == 0.
  */
 bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran,

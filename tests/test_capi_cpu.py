@@ -1,0 +1,129 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function that include/bitgemm.h declares;
+* every entry point rejects ineligible calls with the documented status code
+  before touching the device (fail-closed, "Low-precision LLM inference" §24
+  eligibility checklist and §31 fallback_policy).  The pointers passed here
+  are fake, 16-byte aligned addresses: a call that got past validation would
+  fail in the HIP runtime, so a BG_ERR_* other than BG_ERR_HIP proves the
+  check happened on the host first.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitgemm.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_UNSUP, E_HIP = range(7)
+F32, F16, BF16, I8, FP8, I32 = range(6)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_gemm_w4_amd import build, ops
+    if not os.path.exists(ops.LIB_PATH):
+        build.build()
+    return ops.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(L):
+    from bit_gemm_w4_amd import ops
+    names = _declared_functions()
+    assert set(names) >= {"w4_pack", "gemm_w4a16", "act_quant_int8", "act_quant_fp8", "gemm_w8a8"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(ops.EXPORTS)
+
+
+def test_internal_symbols_hidden():
+    out = os.popen(f"nm -D --defined-only {os.path.join(ROOT, 'bit_gemm_w4_amd', 'libbitgemm.so')}").read()
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(_declared_functions())
+
+
+def test_status_strings_and_version(L):
+    assert L.bg_status_string(0) == b"ok"
+    assert L.bg_status_string(2) == b"unsupported shape"
+    assert L.bg_status_string(99) == b"unknown status"
+    assert L.bg_pack_format_version() == 1
+
+
+P = 0x10000          # fake, 16-byte aligned device addresses
+Q = 0x20000
+
+
+def _last(L):
+    return L.bg_last_error().decode()
+
+
+def test_w4_pack_validation(L):
+    f = L.w4_pack
+    assert f(None, F32, 16, 256, 128, 0, P, Q, None, None) == E_NULL
+    assert f(P, F32, 16, 256, 128, 1, P, Q, None, None) == E_NULL          # asym without zeros
+    assert f(P, F32, 16, 256, 128, 0, P, Q, P, None) == E_UNSUP            # sym with zeros
+    assert f(P, I8, 16, 256, 128, 0, P, Q, None, None) == E_DTYPE
+    assert f(P, F32, 16, 256, 64, 0, P, Q, None, None) == E_UNSUP          # group != 128
+    assert f(P, F32, 0, 256, 128, 0, P, Q, None, None) == E_SHAPE
+    assert f(P, F32, 16, 384, 128, 0, P, Q, None, None) == E_SHAPE         # K % 256
+    assert "K=384" in _last(L)
+    assert f(P + 4, F32, 16, 256, 128, 0, P, Q, None, None) == E_ALIGN
+
+
+def test_gemm_w4a16_validation(L):
+    f = L.gemm_w4a16_ex
+    assert f(None, BF16, 1, 256, P, Q, None, 16, 128, P, 0, None) == E_NULL
+    assert f(P, F32, 1, 256, P, Q, None, 16, 128, P, 0, None) == E_DTYPE
+    assert f(P, BF16, 0, 256, P, Q, None, 16, 128, P, 0, None) == E_SHAPE
+    assert f(P, BF16, 1, 256, P, Q, None, 24, 128, P, 0, None) == E_SHAPE   # N % 16
+    assert f(P, BF16, 1, 128, P, Q, None, 16, 128, P, 0, None) == E_SHAPE   # K % 256
+    assert f(P, BF16, 1, 256, P, Q, None, 16, 256, P, 0, None) == E_UNSUP   # group
+    assert f(P, BF16, 1, 256, P, Q + 2, None, 16, 128, P, 0, None) == E_ALIGN
+    assert f(P, BF16, 1, 256, P, Q, None, 16, 128, P, 9, None) == E_UNSUP   # algo
+
+
+def test_act_quant_validation(L):
+    for f in (L.act_quant_int8, L.act_quant_fp8):
+        assert f(P, BF16, 4, 128, 1, None, Q, None) == E_NULL
+        assert f(P, I8, 4, 128, 1, P, Q, None) == E_DTYPE
+        assert f(P, BF16, 4, 128, 7, P, Q, None) == E_UNSUP
+        assert f(P, BF16, 0, 128, 1, P, Q, None) == E_SHAPE
+        assert f(P, BF16, 4, 192, 1, P, Q, None) == E_SHAPE                 # cols % 128
+        assert f(P, BF16, 100, 128, 3, P, Q, None) == E_SHAPE               # BLOCK128 rows % 128
+        assert f(P, BF16, 4, 128, 1, P, Q + 8, None) == E_ALIGN
+
+
+def test_gemm_w8a8_validation(L):
+    f = L.gemm_w8a8_ex
+    T, R, G, B = 0, 1, 2, 3
+    assert f(None, P, R, P, Q, R, I8, 4, 16, 128, P, BF16, 0, None) == E_NULL
+    assert f(P, None, R, P, Q, R, I8, 4, 16, 128, P, BF16, 0, None) == E_NULL   # scales needed
+    assert f(P, P, R, P, Q, R, BF16, 4, 16, 128, P, BF16, 0, None) == E_DTYPE
+    assert f(P, P, R, P, Q, R, FP8, 4, 16, 128, P, I32, 0, None) == E_DTYPE     # I32 needs I8
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 128, P, I8, 0, None) == E_DTYPE
+    assert f(P, P, G, P, Q, B, I8, 4, 128, 128, P, BF16, 0, None) == E_UNSUP    # block needs FP8
+    assert f(P, P, G, P, Q, R, FP8, 4, 128, 128, P, BF16, 0, None) == E_UNSUP   # mixed
+    assert f(P, P, R, P, Q, B, FP8, 4, 128, 128, P, BF16, 0, None) == E_UNSUP
+    assert f(P, P, G, P, Q, B, FP8, 4, 144, 128, P, BF16, 0, None) == E_SHAPE   # BLOCK128 N % 128
+    assert f(P, P, R, P, Q, R, I8, 4, 24, 128, P, BF16, 0, None) == E_SHAPE     # N % 16
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 192, P, BF16, 0, None) == E_SHAPE     # K % 128
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 131072 + 128, P, BF16, 0, None) == E_SHAPE
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 128, P + 1, BF16, 0, None) == E_ALIGN
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 128, P, BF16, 5, None) == E_UNSUP     # algo
+
+
+def test_auto_dispatch_thresholds(L):
+    GEMV, SKINNY, TILED = 1, 2, 3
+    assert L.gemm_w4a16_algo(1, 4096, 4096, BF16) == GEMV
+    assert L.gemm_w4a16_algo(4096, 4096, 4096, BF16) == TILED
+    assert L.gemm_w8a8_algo(2048, 4096, 4096, I8) == TILED
+    seen = {L.gemm_w4a16_algo(m, 4096, 4096, BF16) for m in range(1, 300)}
+    assert seen == {GEMV, SKINNY, TILED}
