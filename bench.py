@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 / W8A8 quantized linear layer on one MI355X.
+
+One step = the W4A16 decode linears of a Llama-3-8B-shaped decoder layer
+(qkv 4096->6144, o 4096->4096, gate_up 4096->28672, down 14336->4096) at
+batch B = 1, 4 and 16, on asymmetric INT4 weights (G=128, FP16 scales, 4-bit
+zero-points), BF16 activations: 12 gemm_w4a16 calls.  `value` is the
+algorithmic HBM bytes of a step (packed weights + scales + zeros +
+activations + outputs) divided by the step time, in GB/s.
+
+Inputs are resident in HBM before timing.  Each layer has R packed copies and
+every call reads a different copy, so a weight copy is read again only after
+~0.9 GB of other traffic: MI355X's 256 MB Infinity Cache cannot serve it.
+Steps are captured into HIP graphs (one per rotation phase) and replayed, so
+host launch overhead stays out of the timed region.
+
+Also reported (one JSON line, rank 0): the roofline of the dominant kernel
+(HIP-event timing of that kernel alone), the oracle timed on the host cores
+on a bounded sample, and secondary results: W8A8 INT8 / FP8 TFLOP/s at
+M=2048 and the W4A16 large-batch points.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BATCHES = (1, 4, 16)
+LAYERS = ("qkv", "o", "gate_up", "down")
+R_COPIES = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    return ap.parse_args()
+
+
+def graph_of(fn, torch):
+    """Capture fn() into a CUDA/HIP graph on a side stream (after a warm call)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, reps, torch):
+    """Average milliseconds per replay of g, HIP events on the replay stream."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every GPU box here has one, so --gpus must be 1 "
+              "(the path shards column-parallel across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_gemm_w4_amd import ops, roofline, synth
+    if not os.path.exists(ops.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ inputs ----
+    t0 = time.time()
+    packs, xs, ys, w_host = {}, {}, {}, {}
+    for name in LAYERS:
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        w, x = synth.decode_layer(max(BATCHES), N, K, seed=0)
+        w_host[name] = w
+        wd = torch.from_numpy(w).to(dev)
+        p0 = ops.w4_pack(wd, 128, True)
+        del wd
+        copies = [p0]
+        for _ in range(R_COPIES - 1):
+            copies.append(ops.PackedW4(p0.qweight.clone(), p0.scales.clone(), p0.zeros.clone(), N, K))
+        packs[name] = copies
+        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        for B in BATCHES:
+            xs[(name, B)] = xt[:B].contiguous()
+            ys[(name, B)] = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.time() - t0:.1f}s; {R_COPIES} copies/layer, "
+        f"{sum(p.nbytes for c in packs.values() for p in c) / 1e9:.2f} GB of packed weights")
+
+    calls = [(name, B) for B in BATCHES for name in LAYERS]
+    call_bytes = {c: roofline.w4a16_bytes(c[1], *reversed(synth.LLAMA3_8B_SHAPES[c[0]])) for c in calls}
+    step_bytes = sum(call_bytes.values())
+    uses_per_step = len(BATCHES)                       # each layer is read once per batch size
+    n_phases = R_COPIES // np.gcd(R_COPIES, uses_per_step)
+
+    def step(phase):
+        for i, (name, B) in enumerate(calls):
+            b_idx = BATCHES.index(B)
+            copy = (phase * uses_per_step + b_idx) % R_COPIES
+            ops.gemm_w4a16(xs[(name, B)], packs[name][copy], out=ys[(name, B)])
+
+    graphs = [graph_of(lambda ph=ph: step(ph), torch) for ph in range(n_phases)]
+
+    # ------------------------------------------------------- timed steps ----
+    for s in range(args.warmup):
+        graphs[s % n_phases].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for s in range(args.steps):
+        graphs[s % n_phases].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"step: {ms_per_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB algorithmic -> {value:.0f} GB/s")
+
+    # ------------------------------------------- per-call / per-kernel timing ----
+    per_call = {}
+    kernel_of = {}
+    for name, B in calls:
+        def one(name=name, B=B):
+            for c in range(R_COPIES):
+                ops.gemm_w4a16(xs[(name, B)], packs[name][c], out=ys[(name, B)])
+        ops.gemm_w4a16(xs[(name, B)], packs[name][0], out=ys[(name, B)])
+        kernel_of[(name, B)] = ops.last_kernel()
+        g = graph_of(one, torch)
+        ms = time_graph(g, 20, torch) / R_COPIES
+        per_call[(name, B)] = ms
+        log(f"  {name:8s} B={B:3d} {ms * 1e3:8.2f} us {call_bytes[(name, B)] / ms / 1e6:8.0f} GB/s  "
+            f"{kernel_of[(name, B)]}")
+    by_kernel = {}
+    for c, k in kernel_of.items():
+        t, b, n = by_kernel.get(k, (0.0, 0, 0))
+        by_kernel[k] = (t + per_call[c], b + call_bytes[c], n + 1)
+    dom = max(by_kernel, key=lambda k: by_kernel[k][0])
+    t_dom, b_dom, n_dom = by_kernel[dom]
+    achieved = b_dom / (t_dom * 1e-3) / 1e9
+    roof = {"bound": "hbm", "kernel": dom, "launches_per_step": n_dom,
+            "bytes_per_launch": b_dom / n_dom, "avg_launch_us": t_dom / n_dom * 1e3,
+            "achieved": round(achieved, 1), "peak": roofline.HBM_GBPS, "unit": "GB/s",
+            "frac": round(achieved / roofline.HBM_GBPS, 4), "traffic": None}
+
+    out = {
+        "metric": "W4A16/W8A8 linear: HBM GB/s at B=1..16, TFLOPS at M=2048; % of roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int4-weights x bf16 (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": "W4A16 decode, Llama-3-8B layer shapes (qkv, o, gate_up, down), "
+                               "B in {1,4,16}, asymmetric INT4 G=128 + FP16 scales + 4-bit zeros, "
+                               "BF16 activations, 1% input channels x20",
+                   "calls_per_step": len(calls), "bytes_per_step": step_bytes,
+                   "weight_copies_rotated": R_COPIES, "timing": "HIP graph replay"},
+        "roofline": roof,
+        "per_call_gbps": {f"{n}@B{B}": round(call_bytes[(n, B)] / per_call[(n, B)] / 1e6, 1) for n, B in calls},
+    }
+
+    # -------------------------------------------------------- secondary ----
+    if not args.no_secondary:
+        out["secondary"] = secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
+
+    # ----------------------------------------------------- cpu baseline ----
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w_host, xs, calls, args.cpu_seconds, np, synth, roofline)
+
+    print(json.dumps(out), flush=True)
+
+
+def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph):
+    """W8A8 at M=2048 (INT8 per-token x per-channel; FP8 per-tensor and
+    128x128 / 1x128 blocks) and W4A16 at B=74/256, each timed alone."""
+    res = {"w8a8_m2048": {}, "w4a16_large_batch": {}}
+    M = 2048
+    for name in LAYERS:
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        w, x = synth.prefill_layer(M, N, K, seed=0)
+        xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        wt = torch.from_numpy(w).to(dev)
+        variants = [("int8_row", False, 1, 1)]
+        if name in ("gate_up", "down"):
+            variants += [("fp8_tensor", True, 0, 0), ("fp8_block", True, 2, 3)]
+        for tag, fp8, ag, wg in variants:
+            quant = ops.act_quant_fp8 if fp8 else ops.act_quant_int8
+            a, a_s = quant(xt, ag)
+            wq, w_s = quant(wt, wg)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            g = graph_of(lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y), torch)
+            ms = time_graph(g, 10, torch)
+            kname = ops.last_kernel()
+            gq = graph_of(lambda: quant(xt, ag), torch)
+            ms_q = time_graph(gq, 10, torch)
+            tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+            peak = roofline.PEAK_TFLOPS["fp8" if fp8 else "i8"]
+            res["w8a8_m2048"][f"{name}/{tag}"] = {
+                "gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac": round(tf / peak, 4),
+                "act_quant_us": round(ms_q * 1e3, 1),
+                "act_quant_gbps": round(roofline.act_quant_bytes(M, K) / (ms_q * 1e-3) / 1e9, 1),
+                "kernel": kname}
+            log(f"  w8a8 {name:8s} {tag:10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
+                f"act_quant {ms_q * 1e3:6.1f} us")
+        del wt
+    for name in LAYERS:
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        for B in (74, 256):
+            x = synth.activations(B, K, "bf16", seed=1)
+            xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+            y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+            p = packs[name][0]
+            g = graph_of(lambda: ops.gemm_w4a16(xt, p, out=y), torch)
+            ms = time_graph(g, 10, torch)
+            tf = roofline.gemm_flops(B, N, K) / (ms * 1e-3) / 1e12
+            res["w4a16_large_batch"][f"{name}@B{B}"] = {
+                "us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4),
+                "kernel": ops.last_kernel()}
+            log(f"  w4a16 {name:8s} B={B:3d} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s")
+    return res
+
+
+def cpu_baseline(w_host, xs, calls, target_s, np, synth, roofline):
+    """The oracle's W4A16 GEMM (binary64, OpenMP) on the same step, restricted
+    to a sample of output channels (rows are independent), sized for ~target_s."""
+    import oracle
+    sample = 128
+    done_bytes, done_s = 0, 0.0
+    packed = {}
+    t_start = time.time()
+    while True:
+        b_round, s_round = 0, 0.0
+        for name, B in calls:
+            K, N = synth.LLAMA3_8B_SHAPES[name]
+            n = min(sample, N)
+            key = (name, n)
+            if key not in packed:
+                packed[key] = oracle.w4_pack(w_host[name][:n], 128, True)
+            qw, s, z = packed[key]
+            x = xs[(name, B)].cpu().view(__import__("torch").int16).numpy().view(np.uint16)
+            t = time.perf_counter()
+            oracle.gemm_w4a16(x, "bf16", qw, s, z)
+            s_round += time.perf_counter() - t
+            b_round += roofline.w4a16_bytes(B, n, K)
+        done_bytes += b_round
+        done_s += s_round
+        if done_s >= target_s or time.time() - t_start > 3 * target_s or sample >= 28672:
+            break
+        sample = min(28672, int(sample * max(2.0, min(8.0, target_s / max(s_round, 1e-3)))))
+    return {"value": round(done_bytes / done_s / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"same 12 W4A16 decode calls restricted to the first <= {sample} output channels "
+                      f"of each layer; {done_s:.1f} s of oracle time (binary64 dequantized GEMM)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,26 +1,51 @@
 // bg_internal.h -- host-side launchers behind the C ABI (not exported).
-// Every launcher assumes its arguments were validated by the C-ABI layer
+// Every launcher returns the name of the kernel it enqueued (the template
+// instance, as profilers print it) and assumes its arguments were validated by the C-ABI layer
 // (shapes, alignment, dtypes) and only enqueues kernels on `stream`.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
+#include <type_traits>
+
 namespace bg {
 
+// "base<a, b, ...>" for a kernel template instance (bools print as true/false,
+// as demangled names do).  Returns a thread-local buffer overwritten by the
+// next call on the same thread.
+template <typename... A>
+const char* kname(const char* base, A... a) {
+    thread_local char buf[160];
+    int n = std::snprintf(buf, sizeof buf, "%s<", base);
+    bool first = true;
+    auto put = [&](auto v) {
+        const char* sep = first ? "" : ", ";
+        first = false;
+        if constexpr (std::is_same_v<decltype(v), bool>)
+            n += std::snprintf(buf + n, sizeof buf - n, "%s%s", sep, v ? "true" : "false");
+        else
+            n += std::snprintf(buf + n, sizeof buf - n, "%s%d", sep, (int)v);
+    };
+    (put(a), ...);
+    std::snprintf(buf + n, sizeof buf - n, ">");
+    return buf;
+}
+
 // w4_pack: N x K weights of dtype dt (0 f32, 1 f16, 2 bf16).
-void launch_w4_pack(const void* w, int dt, int64_t N, int64_t K, bool asym,
+const char* launch_w4_pack(const void* w, int dt, int64_t N, int64_t K, bool asym,
                     uint32_t* qweight, uint16_t* scales, uint8_t* zeros, hipStream_t s);
 
 // act_quant: out_fp8 selects E4M3 (else INT8); gran = bg_gran value.
-void launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8,
+const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8,
                       void* q, float* scales, hipStream_t s);
 
 // W4A16 kernels (x_bf16: activations/output are BF16, else FP16).
-void launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                        const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
-void launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                          const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
-void launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                         const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
 
 // W8A8: in_fp8 selects E4M3 x E4M3 (else INT8 x INT8); out_dt: 0 f32, 1 f16, 2 bf16, 5 i32.
@@ -37,7 +62,7 @@ struct W8A8Args {
     void* y;
     int out_dt;
 };
-void launch_w8a8_tiled(const W8A8Args& args, hipStream_t s);
-void launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
+const char* launch_w8a8_tiled(const W8A8Args& args, hipStream_t s);
+const char* launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
 
 }  // namespace bg

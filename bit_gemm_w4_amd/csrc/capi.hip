@@ -14,6 +14,11 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+thread_local char g_last_kernel[160] = "";
+
+void note_kernel(const char* name) {
+    std::snprintf(g_last_kernel, sizeof(g_last_kernel), "%s", name ? name : "");
+}
 
 bg_status fail(bg_status st, const char* fmt, long long a = 0, long long b = 0) {
     std::snprintf(g_last_error, sizeof(g_last_error), fmt, a, b);
@@ -65,8 +70,8 @@ BG_EXPORT bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, in
     if (N * (K / 8) / 256 >= (int64_t(1) << 31)) return fail(BG_ERR_SHAPE, "w4_pack: N*K=%lld too large", N * K);
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zeros && !aligned16(zeros)))
         return fail(BG_ERR_ALIGN, "w4_pack: pointers must be 16-byte aligned");
-    bg::launch_w4_pack(w, w_dtype, N, K, asymmetric != 0, qweight, scales, zeros,
-                       static_cast<hipStream_t>(stream));
+    note_kernel(bg::launch_w4_pack(w, w_dtype, N, K, asymmetric != 0, qweight, scales, zeros,
+                       static_cast<hipStream_t>(stream)));
     return launched("w4_pack");
 }
 
@@ -93,9 +98,9 @@ BG_EXPORT bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t
     const bool bf16 = x_dtype == BG_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (algo) {
-        case BG_ALGO_GEMV: bg::launch_w4a16_gemv(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
-        case BG_ALGO_SKINNY: bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
-        case BG_ALGO_TILED: bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s); break;
+        case BG_ALGO_GEMV: note_kernel(bg::launch_w4a16_gemv(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
+        case BG_ALGO_SKINNY: note_kernel(bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
+        case BG_ALGO_TILED: note_kernel(bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         default: return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16: unknown algo %lld", algo);
     }
     return launched("gemm_w4a16");
@@ -121,7 +126,7 @@ static bg_status act_quant(const char* name, bool fp8, const void* x, int x_dtyp
         return fail(BG_ERR_SHAPE, "act_quant: BLOCK128 needs rows %% 128 == 0 (rows=%lld)", rows);
     if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
         return fail(BG_ERR_ALIGN, "act_quant: pointers must be 16-byte aligned");
-    bg::launch_act_quant(x, x_dtype, rows, cols, gran, fp8, q, scales, static_cast<hipStream_t>(stream));
+    note_kernel(bg::launch_act_quant(x, x_dtype, rows, cols, gran, fp8, q, scales, static_cast<hipStream_t>(stream)));
     return launched(name);
 }
 
@@ -170,8 +175,8 @@ BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gra
                    in_dtype == BG_FP8_E4M3, M, N, K, y, out_dtype};
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (algo) {
-        case BG_ALGO_SKINNY: bg::launch_w8a8_skinny(g, s); break;
-        case BG_ALGO_TILED: bg::launch_w8a8_tiled(g, s); break;
+        case BG_ALGO_SKINNY: note_kernel(bg::launch_w8a8_skinny(g, s)); break;
+        case BG_ALGO_TILED: note_kernel(bg::launch_w8a8_tiled(g, s)); break;
         default: return fail(BG_ERR_UNSUPPORTED, "gemm_w8a8: unknown algo %lld", algo);
     }
     return launched("gemm_w8a8");
@@ -200,3 +205,5 @@ BG_EXPORT const char* bg_status_string(int status) {
 BG_EXPORT const char* bg_last_error(void) { return g_last_error; }
 
 BG_EXPORT int bg_pack_format_version(void) { return BG_PACK_FORMAT_VERSION; }
+
+BG_EXPORT const char* bg_last_kernel(void) { return g_last_kernel; }

@@ -194,47 +194,48 @@ static unsigned grid_for(int64_t nchunk) {
 }
 
 template <int DT, bool FP8>
-static void launch_typed(const void* x, int64_t R, int64_t C, int gran, void* q, float* sc,
+static const char* launch_typed(const void* x, int64_t R, int64_t C, int gran, void* q, float* sc,
                          hipStream_t s) {
     switch (gran) {
         case G_ROW:
             if (C <= 256 * 8 * ROW_MAXIT)
+            {
                 hipLaunchKernelGGL((k_quant_row<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
-            else
-                hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
-            break;
+                return kname("k_quant_row", DT, FP8);
+            }
+            hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+            return kname("k_quant_row_2pass", DT, FP8);
         case G_ROW_G128: {
             const int64_t chunks = R * (C >> 3);
             hipLaunchKernelGGL((k_quant_g128<DT, FP8>), dim3((unsigned)((chunks + 255) / 256)), dim3(256),
                                0, s, x, chunks, q, sc);
-            break;
+            return kname("k_quant_g128", DT, FP8);
         }
         case G_BLOCK128:
             hipLaunchKernelGGL((k_quant_block128<DT, FP8>), dim3((unsigned)((R >> 7) * (C >> 7))), dim3(256),
                                0, s, x, C, q, sc);
-            break;
+            return kname("k_quant_block128", DT, FP8);
         default: {
             const int64_t chunks = R * (C >> 3);
             hipLaunchKernelGGL(k_clear_amax, dim3(1), dim3(1), 0, s, sc);
             hipLaunchKernelGGL((k_amax_tensor<DT>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks, sc);
             hipLaunchKernelGGL((k_quant_tensor<DT, FP8>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks,
                                q, sc);
-            break;
+            return kname("k_quant_tensor", DT, FP8);
         }
     }
 }
 
-void launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8, void* q,
-                      float* scales, hipStream_t s) {
+const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8, void* q,
+                             float* scales, hipStream_t s) {
     if (out_fp8) {
-        if (dt == DT_F32) launch_typed<DT_F32, true>(x, R, C, gran, q, scales, s);
-        else if (dt == DT_F16) launch_typed<DT_F16, true>(x, R, C, gran, q, scales, s);
-        else launch_typed<DT_BF16, true>(x, R, C, gran, q, scales, s);
-    } else {
-        if (dt == DT_F32) launch_typed<DT_F32, false>(x, R, C, gran, q, scales, s);
-        else if (dt == DT_F16) launch_typed<DT_F16, false>(x, R, C, gran, q, scales, s);
-        else launch_typed<DT_BF16, false>(x, R, C, gran, q, scales, s);
+        if (dt == DT_F32) return launch_typed<DT_F32, true>(x, R, C, gran, q, scales, s);
+        if (dt == DT_F16) return launch_typed<DT_F16, true>(x, R, C, gran, q, scales, s);
+        return launch_typed<DT_BF16, true>(x, R, C, gran, q, scales, s);
     }
+    if (dt == DT_F32) return launch_typed<DT_F32, false>(x, R, C, gran, q, scales, s);
+    if (dt == DT_F16) return launch_typed<DT_F16, false>(x, R, C, gran, q, scales, s);
+    return launch_typed<DT_BF16, false>(x, R, C, gran, q, scales, s);
 }
 
 }  // namespace bg

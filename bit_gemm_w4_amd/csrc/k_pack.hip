@@ -85,21 +85,22 @@ __global__ __launch_bounds__(256) void k_w4_pack(const void* __restrict__ w, int
 }
 
 template <int DT>
-static void launch_dt(const void* w, int64_t N, int64_t K, bool asym, uint32_t* qw,
-                      uint16_t* sc, uint8_t* zr, hipStream_t s) {
+static const char* launch_dt(const void* w, int64_t N, int64_t K, bool asym, uint32_t* qw,
+                             uint16_t* sc, uint8_t* zr, hipStream_t s) {
     const int64_t threads = N * (K >> 3);
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (asym)
         hipLaunchKernelGGL((k_w4_pack<DT, true>), dim3(blocks), dim3(256), 0, s, w, N, K, qw, sc, zr);
     else
         hipLaunchKernelGGL((k_w4_pack<DT, false>), dim3(blocks), dim3(256), 0, s, w, N, K, qw, sc, zr);
+    return kname("k_w4_pack", DT, asym);
 }
 
-void launch_w4_pack(const void* w, int dt, int64_t N, int64_t K, bool asym, uint32_t* qweight,
-                    uint16_t* scales, uint8_t* zeros, hipStream_t s) {
-    if (dt == DT_F32) launch_dt<DT_F32>(w, N, K, asym, qweight, scales, zeros, s);
-    else if (dt == DT_F16) launch_dt<DT_F16>(w, N, K, asym, qweight, scales, zeros, s);
-    else launch_dt<DT_BF16>(w, N, K, asym, qweight, scales, zeros, s);
+const char* launch_w4_pack(const void* w, int dt, int64_t N, int64_t K, bool asym, uint32_t* qweight,
+                           uint16_t* scales, uint8_t* zeros, hipStream_t s) {
+    if (dt == DT_F32) return launch_dt<DT_F32>(w, N, K, asym, qweight, scales, zeros, s);
+    if (dt == DT_F16) return launch_dt<DT_F16>(w, N, K, asym, qweight, scales, zeros, s);
+    return launch_dt<DT_BF16>(w, N, K, asym, qweight, scales, zeros, s);
 }
 
 }  // namespace bg

@@ -304,55 +304,57 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
 // ---------------------------------------------------------------- launch ----
 
 template <bool BF16, int MB, int LPR, int RPW>
-static void gemv_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+static const char* gemv_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                      const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     constexpr int rows_per_block = 4 * RPW * (64 / LPR);
     dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)((M + MB - 1) / MB));
     hipLaunchKernelGGL((k_w4a16_gemv<BF16, MB, LPR, RPW>), grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
+    return kname("k_w4a16_gemv", BF16, MB, LPR, RPW);
 }
 
 template <bool BF16, int MB>
-static void gemv_mb(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+static const char* gemv_mb(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                     const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     const int64_t chunks = K >> 5;
-    if (chunks >= 256) gemv_cfg<BF16, MB, 64, 1>(x, M, K, qw, sc, zr, N, y, s);
-    else if (chunks >= 64) gemv_cfg<BF16, MB, 32, 1>(x, M, K, qw, sc, zr, N, y, s);
-    else gemv_cfg<BF16, MB, 16, 1>(x, M, K, qw, sc, zr, N, y, s);
+    if (chunks >= 256) return gemv_cfg<BF16, MB, 64, 1>(x, M, K, qw, sc, zr, N, y, s);
+    if (chunks >= 64) return gemv_cfg<BF16, MB, 32, 1>(x, M, K, qw, sc, zr, N, y, s);
+    return gemv_cfg<BF16, MB, 16, 1>(x, M, K, qw, sc, zr, N, y, s);
 }
 
 template <bool BF16>
-static void gemv_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+static const char* gemv_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                     const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (M <= 1) gemv_mb<BF16, 1>(x, M, K, qw, sc, zr, N, y, s);
-    else if (M <= 2) gemv_mb<BF16, 2>(x, M, K, qw, sc, zr, N, y, s);
-    else gemv_mb<BF16, 4>(x, M, K, qw, sc, zr, N, y, s);
+    if (M <= 1) return gemv_mb<BF16, 1>(x, M, K, qw, sc, zr, N, y, s);
+    if (M <= 2) return gemv_mb<BF16, 2>(x, M, K, qw, sc, zr, N, y, s);
+    return gemv_mb<BF16, 4>(x, M, K, qw, sc, zr, N, y, s);
 }
 
-void launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                       const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) gemv_dt<true>(x, M, K, qw, sc, zr, N, y, s);
-    else gemv_dt<false>(x, M, K, qw, sc, zr, N, y, s);
+const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    if (x_bf16) return gemv_dt<true>(x, M, K, qw, sc, zr, N, y, s);
+    return gemv_dt<false>(x, M, K, qw, sc, zr, N, y, s);
 }
 
 template <bool BF16, int BM, int BN, int WM, int WN>
-static void mfma_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+static const char* mfma_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                      const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     hipLaunchKernelGGL((k_w4a16_mfma<BF16, BM, BN, WM, WN>), grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
+    return kname("k_w4a16_mfma", BF16, BM, BN, WM, WN);
 }
 
-void launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                         const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) mfma_cfg<true, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
-    else mfma_cfg<false, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
+const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    if (x_bf16) return mfma_cfg<true, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
+    return mfma_cfg<false, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
 }
 
-void launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                        const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) mfma_cfg<true, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
-    else mfma_cfg<false, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
+const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    if (x_bf16) return mfma_cfg<true, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
+    return mfma_cfg<false, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
 }
 
 }  // namespace bg

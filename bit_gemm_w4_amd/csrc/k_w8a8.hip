@@ -175,22 +175,23 @@ __global__ __launch_bounds__(256) void k_w8a8_mfma(const uint8_t* __restrict__ a
 }
 
 template <bool FP8, bool BLOCK, int BM, int BN, int WM, int WN>
-static void cfg(const W8A8Args& g, hipStream_t s) {
+static const char* cfg(const W8A8Args& g, hipStream_t s) {
     dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
     hipLaunchKernelGGL((k_w8a8_mfma<FP8, BLOCK, BM, BN, WM, WN>), grid, dim3(256), 0, s,
                        static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
                        g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt);
+    return kname("k_w8a8_mfma", FP8, BLOCK, BM, BN, WM, WN);
 }
 
 template <int BM, int BN, int WM, int WN>
-static void dispatch(const W8A8Args& g, hipStream_t s) {
+static const char* dispatch(const W8A8Args& g, hipStream_t s) {
     const bool block = g.a_gran == GR128;
-    if (!g.in_fp8) cfg<false, false, BM, BN, WM, WN>(g, s);
-    else if (block) cfg<true, true, BM, BN, WM, WN>(g, s);
-    else cfg<true, false, BM, BN, WM, WN>(g, s);
+    if (!g.in_fp8) return cfg<false, false, BM, BN, WM, WN>(g, s);
+    if (block) return cfg<true, true, BM, BN, WM, WN>(g, s);
+    return cfg<true, false, BM, BN, WM, WN>(g, s);
 }
 
-void launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) { dispatch<128, 128, 2, 2>(g, s); }
-void launch_w8a8_skinny(const W8A8Args& g, hipStream_t s) { dispatch<16, 128, 1, 4>(g, s); }
+const char* launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) { return dispatch<128, 128, 2, 2>(g, s); }
+const char* launch_w8a8_skinny(const W8A8Args& g, hipStream_t s) { return dispatch<16, 128, 1, 4>(g, s); }
 
 }  // namespace bg

@@ -26,7 +26,7 @@ PACK_FORMAT_VERSION = 1
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w4a16_algo", "gemm_w8a8_algo", "bg_status_string", "bg_last_error",
-    "bg_pack_format_version",
+    "bg_pack_format_version", "bg_last_kernel",
 )
 
 _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
@@ -64,11 +64,13 @@ def lib() -> ctypes.CDLL:
             "bg_status_string": [I],
             "bg_last_error": [],
             "bg_pack_format_version": [],
+            "bg_last_kernel": [],
         }
         for name, argtypes in sig.items():
             fn = getattr(L, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_char_p if name in ("bg_status_string", "bg_last_error") else ctypes.c_int
+            fn.restype = (ctypes.c_char_p if name in ("bg_status_string", "bg_last_error", "bg_last_kernel")
+                          else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -91,6 +93,11 @@ def _stream(stream=None):
 def _check(status: int, fn: str):
     if status != 0:
         raise BitGemmError(status, fn)
+
+
+def last_kernel() -> str:
+    """Kernel instance enqueued by the last successful call on this thread."""
+    return lib().bg_last_kernel().decode()
 
 
 # --------------------------------------------------------------------- W4 ----

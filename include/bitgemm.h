@@ -182,6 +182,10 @@ const char* bg_status_string(int status);
 const char* bg_last_error(void);
 /* BG_PACK_FORMAT_VERSION of the library (layout of qweight/scales/zeros). */
 int bg_pack_format_version(void);
+/* Kernel template instance enqueued by the last successful call on this host
+ * thread, e.g. "k_w4a16_gemv<true, 1, 32, 1>" -- a substring of the name a
+ * profiler's kernel trace shows ([LPI] §24: record the kernel name). */
+const char* bg_last_kernel(void);
 
 #ifdef __cplusplus
 }

@@ -73,11 +73,12 @@ def _load():
                 "orc_quant_fp8": [P, I64, I64, I, P, P],
                 "orc_gemm_i8_acc": [P, P, I64, I64, I64, P],
                 "orc_gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P],
+                "orc_num_threads": [],
             }
             for name, argtypes in sig.items():
                 fn = getattr(lib, name)
                 fn.argtypes = argtypes
-                fn.restype = ctypes.c_int if name == "orc_gemm_i8_acc" else None
+                fn.restype = ctypes.c_int if name in ("orc_gemm_i8_acc", "orc_num_threads") else None
             _lib = lib
     return _lib
 
@@ -249,6 +250,11 @@ def gemm_w8a8(a, a_scales, a_gran: int, w, w_scales, w_gran: int, fp8: bool) -> 
     _load().orc_gemm_w8a8(_p(a), _p(a_scales), a_gran, _p(w), _p(w_scales), w_gran,
                           int(bool(fp8)), M, N, K, _p(y))
     return y
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops run on."""
+    return int(_load().orc_num_threads())
 
 
 def rel_l2(y, ref) -> float:

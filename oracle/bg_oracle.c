@@ -34,6 +34,9 @@
  */
 #include <math.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdlib.h>
 #include <string.h>
 
@@ -414,6 +417,15 @@ void orc_gemm_w8a8(const void* a, const float* a_s, int a_gran,
         }
     free(ad);
     free(wd);
+}
+
+/* Threads the OpenMP loops above use (1 without OpenMP). */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
 
 /* ------------------------------------------------------------------------ */
