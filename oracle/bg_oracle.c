@@ -216,16 +216,21 @@ void orc_w4_quantize(const float* w, int64_t N, int64_t K, int G, int asym,
     }
 }
 
-/* Pack codes into the kernel layout:
- *   qweight [N][K/8] u32: nibble i (bits 4i..4i+3) of word j holds u[n][8j+i];
+/* Pack codes into the kernel layout (a layout the page leaves to the target
+ * kernel: [LPI] §24 "is the weight packing order the one the kernel expects").
+ *   qweight [N][K/8] u32: word j holds k = 8j .. 8j+7; its low half-word holds
+ *     the even k in increasing order (nibble i <-> k = 8j + 2i, i = 0..3) and
+ *     its high half-word the odd k (nibble 4+i <-> k = 8j + 2i + 1);
  *   zeros   [N][K/(2G)] u8: low nibble = z of even group, high = odd group. */
+static int nibble_of_k(int kk) { return (kk % 2 == 0) ? kk / 2 : 4 + kk / 2; }
+
 void orc_w4_pack(const uint8_t* u, const uint8_t* z, int64_t N, int64_t K, int G,
                  int asym, uint32_t* qweight, uint8_t* zeros) {
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t j = 0; j < K / 8; ++j) {
             uint32_t word = 0;
-            for (int i = 0; i < 8; ++i)
-                word |= (uint32_t)(u[n * K + 8 * j + i] & 0xF) << (4 * i);
+            for (int kk = 0; kk < 8; ++kk)
+                word |= (uint32_t)(u[n * K + 8 * j + kk] & 0xF) << (4 * nibble_of_k(kk));
             qweight[n * (K / 8) + j] = word;
         }
         if (asym) {
@@ -245,7 +250,7 @@ void orc_w4_dequant(const uint32_t* qweight, const uint16_t* s16, const uint8_t*
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t k = 0; k < K; ++k) {
             int64_t g = k / G;
-            int uu = (qweight[n * (K / 8) + k / 8] >> (4 * (k % 8))) & 0xF;
+            int uu = (qweight[n * (K / 8) + k / 8] >> (4 * nibble_of_k((int)(k % 8)))) & 0xF;
             int zz = 8;
             if (zeros) zz = (zeros[n * (ng / 2) + g / 2] >> (4 * (g % 2))) & 0xF;
             what[n * K + k] = (double)orc_f16_to_f32(s16[n * ng + g]) * (double)(uu - zz);

@@ -23,7 +23,8 @@ from bit_gemm_w4_amd import synth
 
 def _np_dequant(qweight, s16, zeros, K, G=128):
     N = qweight.shape[0]
-    u = ((qweight[:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & 0xF).reshape(N, K)
+    nib = np.array([0, 4, 1, 5, 2, 6, 3, 7], dtype=np.uint32)   # nibble slot of k = 8j + i
+    u = ((qweight[:, :, None] >> (4 * nib)) & 0xF).reshape(N, K)
     if zeros is None:
         z = np.full((N, K // G), 8)
     else:

@@ -21,8 +21,12 @@ from bit_gemm_w4_amd import synth
 from pins import _e4m3_brute_force
 
 
+# nibble slot of k = 8j + i: even i in the low half-word, odd i in the high half-word
+NIBBLE_OF = np.array([0, 4, 1, 5, 2, 6, 3, 7], dtype=np.uint32)
+
+
 def _unpack_codes(qweight: np.ndarray, K: int) -> np.ndarray:
-    shifts = (4 * np.arange(8, dtype=np.uint32))
+    shifts = 4 * NIBBLE_OF
     return ((qweight[:, :, None] >> shifts) & 0xF).astype(np.uint8).reshape(qweight.shape[0], K)
 
 
@@ -90,8 +94,7 @@ def test_w4_round_half_to_even(orc):
     w[0, :len(vals)] = vals
     qweight, s16, _ = orc.w4_pack(w, 128, False)
     assert s16[0, 0] == np.float16(0.125).view(np.uint16)
-    q = ((int(qweight[0, 0]) | int(qweight[0, 1]) << 32) >> np.arange(0, 64, 4).astype(object)) & 0xF
-    codes = [int(c) - 8 for c in q[:len(vals)]]
+    codes = [int(c) - 8 for c in _unpack_codes(qweight, 128)[0, :len(vals)]]
     #        7, 0.5->0, 1.5->2, 2.5->2, 3.5->4, 4.5->4, 5.5->6, 6.5->6, and the negatives
     assert codes == [7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6]
 
@@ -155,19 +158,20 @@ def test_w4_all_zero_group(orc):
 
 def test_w4_pack_one_hot(orc):
     """Setting one weight changes exactly one nibble of one word (and nothing
-    else): nibble k%8 of word (n, k//8)."""
+    else): word (n, k//8), nibble (k%8)//2 for even k%8, 4 + (k%8)//2 for odd."""
     N, K = 4, 256
     base = np.zeros((N, K), np.float32)
     q0, _, _ = orc.w4_pack(base, 128, False)
-    for n, k in [(0, 0), (1, 7), (2, 8), (3, 255), (2, 130)]:
+    for n, k in [(0, 0), (1, 7), (2, 8), (3, 255), (2, 130), (1, 3), (0, 4)]:
         w = base.copy()
         w[n, k] = 0.5
         q, s, _ = orc.w4_pack(w, 128, False)
         diff = np.argwhere(q != q0)
         assert diff.tolist() == [[n, k // 8]]
+        slot = (k % 8) // 2 if k % 2 == 0 else 4 + (k % 8) // 2
         changed = int(q[n, k // 8]) ^ int(q0[n, k // 8])
-        assert changed != 0 and changed & ~(0xF << (4 * (k % 8))) == 0
-        assert (int(q[n, k // 8]) >> (4 * (k % 8))) & 0xF == 15     # +7 + 8
+        assert changed != 0 and changed & ~(0xF << (4 * slot)) == 0
+        assert (int(q[n, k // 8]) >> (4 * slot)) & 0xF == 15        # +7 + 8
 
 
 def test_w4_zero_nibble_order(orc):
