@@ -66,7 +66,8 @@ def _load():
                 "orc_e4m3_encode_n": [P, I64, P],
                 "orc_e4m3_decode_n": [P, I64, P],
                 "orc_w4_quantize": [P, I64, I64, I, I, P, P, P],
-                "orc_w4_pack": [P, P, I64, I64, I, I, P, P],
+                "orc_w4_pack": [P, P, P, I64, I64, I, P, P, P],
+                "orc_w4_unpack": [P, P, P, I64, I64, P, P, P],
                 "orc_w4_dequant": [P, P, P, I64, I64, I, P],
                 "orc_gemm_w4a16": [P, I, I64, I64, P, P, P, I64, I, P],
                 "orc_quant_int8": [P, I64, I64, I, P, P],
@@ -156,29 +157,45 @@ def w4_quantize(w, group: int = 128, asymmetric: bool = False):
     return u, s, z
 
 
-def w4_pack_codes(u, z, group: int = 128, asymmetric: bool = False):
+def w4_pack_codes(u, s16, z, asymmetric: bool = False):
+    """Lay codes u [N][K], scale bits [N][K/128], zero-points [N][K/128] out in
+    the tiled packed format -> (qweight u32 [N/16][K/128][64][4],
+    scales u16 [N/16][K/128][16], zeros u8 [N/16][K/256][16] or None)."""
     u = _c(u, np.uint8)
+    s16 = _c(s16, np.uint16)
     z = _c(z, np.uint8)
     N, K = u.shape
-    qweight = np.empty((N, K // 8), np.uint32)
-    zeros = np.empty((N, K // (2 * group)), np.uint8) if asymmetric else None
-    _load().orc_w4_pack(_p(u), _p(z), N, K, group, int(bool(asymmetric)), _p(qweight), _p(zeros))
-    return qweight, zeros
+    assert N % 16 == 0 and K % 256 == 0
+    qweight = np.empty((N // 16, K // 128, 64, 4), np.uint32)
+    scales = np.empty((N // 16, K // 128, 16), np.uint16)
+    zeros = np.empty((N // 16, K // 256, 16), np.uint8) if asymmetric else None
+    _load().orc_w4_pack(_p(u), _p(s16), _p(z), N, K, int(bool(asymmetric)), _p(qweight), _p(scales), _p(zeros))
+    return qweight, scales, zeros
 
 
 def w4_pack(w, group: int = 128, asymmetric: bool = False):
-    """Quantize + pack: returns (qweight u32 [N][K/8], scales fp16-bits [N][K/G],
-    zeros u8 [N][K/(2G)] or None when symmetric)."""
+    """Quantize + pack W [N][K] -> (qweight, scales, zeros) in the tiled format
+    (zeros None when symmetric)."""
     u, s, z = w4_quantize(w, group, asymmetric)
-    qweight, zeros = w4_pack_codes(u, z, group, asymmetric)
-    return qweight, s, zeros
+    return w4_pack_codes(u, s, z, asymmetric)
 
 
-def w4_dequant(qweight, scales, zeros, K: int, group: int = 128) -> np.ndarray:
+def w4_unpack(qweight, scales, zeros, N: int, K: int):
+    """Tiled packed format -> (codes u [N][K], scale bits [N][K/128], zero-points [N][K/128])."""
     qweight = _c(qweight, np.uint32)
     scales = _c(scales, np.uint16)
     zeros = None if zeros is None else _c(zeros, np.uint8)
-    N = qweight.shape[0]
+    u = np.empty((N, K), np.uint8)
+    s = np.empty((N, K // 128), np.uint16)
+    z = np.empty((N, K // 128), np.uint8)
+    _load().orc_w4_unpack(_p(qweight), _p(scales), _p(zeros), N, K, _p(u), _p(s), _p(z))
+    return u, s, z
+
+
+def w4_dequant(qweight, scales, zeros, N: int, K: int, group: int = 128) -> np.ndarray:
+    qweight = _c(qweight, np.uint32)
+    scales = _c(scales, np.uint16)
+    zeros = None if zeros is None else _c(zeros, np.uint8)
     out = np.empty((N, K), np.float64)
     _load().orc_w4_dequant(_p(qweight), _p(scales), _p(zeros), N, K, group, _p(out))
     return out
@@ -191,8 +208,8 @@ def gemm_w4a16(x_bits, x_dtype: str, qweight, scales, zeros, group: int = 128) -
     scales = _c(scales, np.uint16)
     zeros = None if zeros is None else _c(zeros, np.uint8)
     M, K = x_bits.shape
-    N = qweight.shape[0]
-    assert qweight.shape[1] * 8 == K
+    N = qweight.shape[0] * 16
+    assert qweight.shape[1] * 128 == K
     y = np.empty((M, N), np.float64)
     _load().orc_gemm_w4a16(_p(x_bits), int(x_dtype == "bf16"), M, K, _p(qweight), _p(scales),
                            _p(zeros), N, group, _p(y))

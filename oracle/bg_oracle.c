@@ -216,46 +216,77 @@ void orc_w4_quantize(const float* w, int64_t N, int64_t K, int G, int asym,
     }
 }
 
-/* Pack codes into the kernel layout (a layout the page leaves to the target
- * kernel: [LPI] §24 "is the weight packing order the one the kernel expects").
- *   qweight [N][K/8] u32: word j holds k = 8j .. 8j+7; its low half-word holds
- *     the even k in increasing order (nibble i <-> k = 8j + 2i, i = 0..3) and
- *     its high half-word the odd k (nibble 4+i <-> k = 8j + 2i + 1);
- *   zeros   [N][K/(2G)] u8: low nibble = z of even group, high = odd group. */
-static int nibble_of_k(int kk) { return (kk % 2 == 0) ? kk / 2 : 4 + kk / 2; }
+/* Packed layout -- a layout the page leaves to the target kernel ([LPI] §24:
+ * "is the weight packing order the one the kernel expects"; §11 pipeline:
+ * quantize, pack and lay out for the target kernel).  Weights are cut into
+ * tiles of 16 output channels x one group of G = 128 input channels; a tile is
+ * 1 KB of codes stored contiguously as 64 slots of 16 bytes.  For weight
+ * (n, k):  t = n / 16, r = n % 16, g = k / 128, c = k % 128,
+ *          slot = 16 * (c / 32) + r,  word = (c % 32) / 8,  i = k % 8,
+ *   qweight[((t * (K/128) + g) * 64 + slot) * 4 + word], nibble i/2 for even
+ *   i and 4 + i/2 for odd i (even k in the low half-word, odd k in the high);
+ *   scales[(t * (K/128) + g) * 16 + r]   (FP16 bits);
+ *   zeros [(t * (K/256) + g/2) * 16 + r], low nibble for even g, high for odd.
+ * Requires N % 16 == 0 and K % 256 == 0. */
+static int nibble_of_k(int i) { return (i % 2 == 0) ? i / 2 : 4 + i / 2; }
 
-void orc_w4_pack(const uint8_t* u, const uint8_t* z, int64_t N, int64_t K, int G,
-                 int asym, uint32_t* qweight, uint8_t* zeros) {
+static int64_t word_index(int64_t n, int64_t k, int64_t K) {
+    int64_t t = n / 16, r = n % 16, g = k / 128, c = k % 128;
+    int64_t slot = 16 * (c / 32) + r, word = (c % 32) / 8;
+    return ((t * (K / 128) + g) * 64 + slot) * 4 + word;
+}
+
+void orc_w4_pack(const uint8_t* u, const uint16_t* s16_rowmajor, const uint8_t* z, int64_t N, int64_t K,
+                 int asym, uint32_t* qweight, uint16_t* scales, uint8_t* zeros) {
+    int64_t ng = K / 128;
+    for (int64_t i = 0; i < N * K / 8; ++i) qweight[i] = 0;
     for (int64_t n = 0; n < N; ++n) {
-        for (int64_t j = 0; j < K / 8; ++j) {
-            uint32_t word = 0;
-            for (int kk = 0; kk < 8; ++kk)
-                word |= (uint32_t)(u[n * K + 8 * j + kk] & 0xF) << (4 * nibble_of_k(kk));
-            qweight[n * (K / 8) + j] = word;
+        for (int64_t k = 0; k < K; ++k)
+            qweight[word_index(n, k, K)] |= (uint32_t)(u[n * K + k] & 0xF) << (4 * nibble_of_k((int)(k % 8)));
+        for (int64_t g = 0; g < ng; ++g) {
+            int64_t t = n / 16, r = n % 16;
+            scales[(t * ng + g) * 16 + r] = s16_rowmajor[n * ng + g];
+            if (asym) {
+                int64_t zi = (t * (ng / 2) + g / 2) * 16 + r;
+                if (g % 2 == 0) zeros[zi] = (uint8_t)(z[n * ng + g] & 0xF);
+                else zeros[zi] |= (uint8_t)((z[n * ng + g] & 0xF) << 4);
+            }
         }
-        if (asym) {
-            int64_t ng = K / G;
-            for (int64_t h = 0; h < ng / 2; ++h)
-                zeros[n * (ng / 2) + h] =
-                    (uint8_t)((z[n * ng + 2 * h] & 0xF) | ((z[n * ng + 2 * h + 1] & 0xF) << 4));
+    }
+}
+
+/* Inverse of orc_w4_pack: codes u [N][K], scale bits [N][K/128] and
+ * zero-points [N][K/128] (8 when zeros == NULL) in row-major order. */
+void orc_w4_unpack(const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N, int64_t K,
+                   uint8_t* u, uint16_t* s16, uint8_t* z) {
+    int64_t ng = K / 128;
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t t = n / 16, r = n % 16;
+        for (int64_t k = 0; k < K; ++k)
+            u[n * K + k] = (uint8_t)((qweight[word_index(n, k, K)] >> (4 * nibble_of_k((int)(k % 8)))) & 0xF);
+        for (int64_t g = 0; g < ng; ++g) {
+            s16[n * ng + g] = scales[(t * ng + g) * 16 + r];
+            z[n * ng + g] = zeros ? (uint8_t)((zeros[(t * (ng / 2) + g / 2) * 16 + r] >> (4 * (g % 2))) & 0xF) : 8;
         }
     }
 }
 
 /* Dequantized weight from the packed form: w^[n,k] = s16 * (u - z), exact
  * in double.  z = 8 when zeros == NULL (symmetric). */
-void orc_w4_dequant(const uint32_t* qweight, const uint16_t* s16, const uint8_t* zeros,
+void orc_w4_dequant(const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                     int64_t N, int64_t K, int G, double* what) {
-    int64_t ng = K / G;
-    for (int64_t n = 0; n < N; ++n) {
-        for (int64_t k = 0; k < K; ++k) {
-            int64_t g = k / G;
-            int uu = (qweight[n * (K / 8) + k / 8] >> (4 * nibble_of_k((int)(k % 8)))) & 0xF;
-            int zz = 8;
-            if (zeros) zz = (zeros[n * (ng / 2) + g / 2] >> (4 * (g % 2))) & 0xF;
-            what[n * K + k] = (double)orc_f16_to_f32(s16[n * ng + g]) * (double)(uu - zz);
-        }
-    }
+    (void)G;
+    int64_t ng = K / 128;
+    uint8_t* u = (uint8_t*)malloc((size_t)(N * K));
+    uint16_t* s16 = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(N * ng));
+    uint8_t* z = (uint8_t*)malloc((size_t)(N * ng));
+    orc_w4_unpack(qweight, scales, zeros, N, K, u, s16, z);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            what[n * K + k] = (double)orc_f16_to_f32(s16[n * ng + k / 128]) * (double)((int)u[n * K + k] - (int)z[n * ng + k / 128]);
+    free(u);
+    free(s16);
+    free(z);
 }
 
 /* W4A16 linear: Y[m,n] = sum_k x[m,k] * w^[n,k], in double, where x is the

@@ -122,8 +122,9 @@ def test_gemm_w8a8_validation(L):
 
 def test_auto_dispatch_thresholds(L):
     GEMV, SKINNY, TILED = 1, 2, 3
-    assert L.gemm_w4a16_algo(1, 4096, 4096, BF16) == GEMV
+    assert L.gemm_w4a16_algo(1, 4096, 4096, BF16) == SKINNY
     assert L.gemm_w4a16_algo(4096, 4096, 4096, BF16) == TILED
     assert L.gemm_w8a8_algo(2048, 4096, 4096, I8) == TILED
     seen = {L.gemm_w4a16_algo(m, 4096, 4096, BF16) for m in range(1, 300)}
-    assert seen == {GEMV, SKINNY, TILED}
+    assert seen == {SKINNY, TILED}
+    assert GEMV not in seen        # the VALU GEMV is reachable through gemm_w4a16_ex only

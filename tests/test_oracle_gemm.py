@@ -19,18 +19,14 @@ import pytest
 import torch
 
 from bit_gemm_w4_amd import synth
+from pins import np_unpack_w4
 
 
 def _np_dequant(qweight, s16, zeros, K, G=128):
-    N = qweight.shape[0]
-    nib = np.array([0, 4, 1, 5, 2, 6, 3, 7], dtype=np.uint32)   # nibble slot of k = 8j + i
-    u = ((qweight[:, :, None] >> (4 * nib)) & 0xF).reshape(N, K)
-    if zeros is None:
-        z = np.full((N, K // G), 8)
-    else:
-        z = np.stack([zeros & 0xF, zeros >> 4], axis=2).reshape(N, K // G)
-    s = s16.view(np.float16).astype(np.float64)
-    return np.repeat(s, G, axis=1) * (u.astype(np.float64) - np.repeat(z, G, axis=1))
+    N = qweight.shape[0] * 16
+    u, s, z = np_unpack_w4(qweight, s16, zeros, N, K)
+    sv = s.view(np.float16).astype(np.float64)
+    return np.repeat(sv, G, axis=1) * (u.astype(np.float64) - np.repeat(z.astype(np.float64), G, axis=1))
 
 
 def _np_acts(bits, dtype):
@@ -69,7 +65,7 @@ def test_w4a16_special_cases(orc):
 
 
 def test_w4a16_exact_rational_tiny(orc):
-    M, N, K = 2, 8, 256
+    M, N, K = 2, 16, 256
     w, x = synth.layer(M, N, K, "bf16", seed=23)
     qweight, s16, zeros = orc.w4_pack(w, 128, True)
     y = orc.gemm_w4a16(x, "bf16", qweight, s16, zeros)

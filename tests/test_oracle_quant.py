@@ -18,24 +18,12 @@ import numpy as np
 import pytest
 
 from bit_gemm_w4_amd import synth
-from pins import _e4m3_brute_force
+from pins import _e4m3_brute_force, np_unpack_w4
 
 
-# nibble slot of k = 8j + i: even i in the low half-word, odd i in the high half-word
-NIBBLE_OF = np.array([0, 4, 1, 5, 2, 6, 3, 7], dtype=np.uint32)
-
-
-def _unpack_codes(qweight: np.ndarray, K: int) -> np.ndarray:
-    shifts = 4 * NIBBLE_OF
-    return ((qweight[:, :, None] >> shifts) & 0xF).astype(np.uint8).reshape(qweight.shape[0], K)
-
-
-def _zeros_per_group(zeros, N, K, G):
-    if zeros is None:
-        return np.full((N, K // G), 8, np.uint8)
-    lo = zeros & 0xF
-    hi = zeros >> 4
-    return np.stack([lo, hi], axis=2).reshape(N, K // G)
+def _unpack(orc_pack, N, K):
+    qweight, scales, zeros = orc_pack
+    return np_unpack_w4(qweight, scales, zeros, N, K)
 
 
 def _adversarial_weights(N=64, K=512, seed=3):
@@ -58,9 +46,9 @@ def _adversarial_weights(N=64, K=512, seed=3):
 def test_w4_codes_nearest_and_roundtrip(orc, asym):
     w = np.concatenate([_adversarial_weights(), synth.weights(64, 512, seed=5, outlier_frac=0.01)])
     N, K, G = w.shape[0], w.shape[1], 128
-    qweight, s16, zeros = orc.w4_pack(w, G, asym)
-    u = _unpack_codes(qweight, K).astype(np.int64)
-    z = _zeros_per_group(zeros, N, K, G).astype(np.int64)
+    u, s16, z = _unpack(orc.w4_pack(w, G, asym), N, K)
+    u = u.astype(np.int64)
+    z = z.astype(np.int64)
     s = s16.view(np.float16).astype(np.float64)
     assert np.all(s > 0) and np.all(np.isfinite(s))
     zk = np.repeat(z, G, axis=1)
@@ -88,20 +76,21 @@ def test_w4_round_half_to_even(orc):
     """Reading of round(): ties go to the even integer.  A group with amax
     0.875 gets the exact FP16 scale 0.125; elements at odd multiples of 0.0625
     sit exactly halfway between two codes."""
-    w = np.zeros((1, 128), np.float32)
+    w = np.zeros((16, 256), np.float32)
     vals = [0.875, 0.0625, 0.1875, 0.3125, 0.4375, 0.5625, 0.6875, 0.8125,
             -0.0625, -0.1875, -0.3125, -0.4375, -0.5625, -0.6875, -0.8125]
     w[0, :len(vals)] = vals
     qweight, s16, _ = orc.w4_pack(w, 128, False)
-    assert s16[0, 0] == np.float16(0.125).view(np.uint16)
-    codes = [int(c) - 8 for c in _unpack_codes(qweight, 128)[0, :len(vals)]]
+    assert s16[0, 0, 0] == np.float16(0.125).view(np.uint16)
+    u, _, _ = np_unpack_w4(qweight, s16, None, 16, 256)
+    codes = [int(c) - 8 for c in u[0, :len(vals)]]
     #        7, 0.5->0, 1.5->2, 2.5->2, 3.5->4, 4.5->4, 5.5->6, 6.5->6, and the negatives
     assert codes == [7, 0, 2, 2, 4, 4, 6, 6, 0, -2, -2, -4, -4, -6, -6]
 
 
 def test_w4_symmetric_scale_and_extreme_code(orc):
     w = synth.weights(32, 1024, seed=7)
-    qweight, s16, _ = orc.w4_pack(w, 128, False)
+    u_all, s16, _ = _unpack(orc.w4_pack(w, 128, False), 32, 1024)
     s = s16.view(np.float16).astype(np.float64)
     amax = np.abs(w.astype(np.float64)).reshape(32, 8, 128).max(axis=2)
     # s16 is the FP16 value nearest to amax/7 (exact rational comparison on a sample)
@@ -113,7 +102,7 @@ def test_w4_symmetric_scale_and_extreme_code(orc):
             i = np.searchsorted(f16, float(target))
             neigh = [Fraction(float(f16[j])) for j in (i - 1, i, i + 1) if 0 <= j < len(f16)]
             assert d <= min(abs(v - target) for v in neigh)
-    u = _unpack_codes(qweight, 1024).astype(np.int64).reshape(32, 8, 128)
+    u = u_all.astype(np.int64).reshape(32, 8, 128)
     arg = np.abs(w).reshape(32, 8, 128).argmax(axis=2)
     sign = np.sign(np.take_along_axis(w.reshape(32, 8, 128), arg[..., None], 2)[..., 0])
     extreme = np.take_along_axis(u, arg[..., None], 2)[..., 0] - 8
@@ -123,7 +112,7 @@ def test_w4_symmetric_scale_and_extreme_code(orc):
 def test_w4_symmetric_idempotent(orc):
     w = synth.weights(16, 512, seed=9, outlier_frac=0.01)
     qweight, s16, _ = orc.w4_pack(w, 128, False)
-    what = orc.w4_dequant(qweight, s16, None, 512)
+    what = orc.w4_dequant(qweight, s16, None, 16, 512)
     assert np.array_equal(what.astype(np.float32).astype(np.float64), what)   # exact in binary32
     q2, s2, _ = orc.w4_pack(what.astype(np.float32), 128, False)
     assert np.array_equal(q2, qweight) and np.array_equal(s2, s16)
@@ -131,10 +120,8 @@ def test_w4_symmetric_idempotent(orc):
 
 def test_w4_asym_zero_exact_and_range(orc):
     w = _adversarial_weights()
-    qweight, s16, zeros = orc.w4_pack(w, 128, True)
     N, K = w.shape
-    u = _unpack_codes(qweight, K)
-    z = _zeros_per_group(zeros, N, K, 128)
+    u, _, z = _unpack(orc.w4_pack(w, 128, True), N, K)
     assert u.max() <= 15 and z.max() <= 15
     # a zero weight is represented exactly: its code equals the zero-point
     zk = np.repeat(z, 128, axis=1)
@@ -148,42 +135,63 @@ def test_w4_asym_zero_exact_and_range(orc):
 
 
 def test_w4_all_zero_group(orc):
-    w = np.zeros((2, 256), np.float32)
+    w = np.zeros((16, 256), np.float32)
     for asym in (False, True):
         qweight, s16, zeros = orc.w4_pack(w, 128, asym)
         assert np.all(s16 == 0x3C00)                                  # scale 1.0
-        what = orc.w4_dequant(qweight, s16, zeros, 256)
+        what = orc.w4_dequant(qweight, s16, zeros, 16, 256)
         assert np.all(what == 0.0)
 
 
+def layout_position(n, k, K):
+    """(flat word index, nibble) of weight (n, k) as the packed-format spec states it."""
+    t, r, g, c = n // 16, n % 16, k // 128, k % 128
+    slot, word, i = 16 * (c // 32) + r, (c % 32) // 8, k % 8
+    nibble = i // 2 if i % 2 == 0 else 4 + i // 2
+    return ((t * (K // 128) + g) * 64 + slot) * 4 + word, nibble
+
+
 def test_w4_pack_one_hot(orc):
-    """Setting one weight changes exactly one nibble of one word (and nothing
-    else): word (n, k//8), nibble (k%8)//2 for even k%8, 4 + (k%8)//2 for odd."""
-    N, K = 4, 256
+    """Setting one weight changes exactly one nibble of one word, at the
+    position the tiled layout specifies, and nothing else."""
+    N, K = 32, 256
     base = np.zeros((N, K), np.float32)
-    q0, _, _ = orc.w4_pack(base, 128, False)
-    for n, k in [(0, 0), (1, 7), (2, 8), (3, 255), (2, 130), (1, 3), (0, 4)]:
+    q0 = orc.w4_pack(base, 128, False)[0].reshape(-1)
+    for n, k in [(0, 0), (1, 7), (2, 8), (3, 255), (2, 130), (1, 3), (0, 4), (17, 33), (31, 100), (16, 127)]:
         w = base.copy()
         w[n, k] = 0.5
-        q, s, _ = orc.w4_pack(w, 128, False)
-        diff = np.argwhere(q != q0)
-        assert diff.tolist() == [[n, k // 8]]
-        slot = (k % 8) // 2 if k % 2 == 0 else 4 + (k % 8) // 2
-        changed = int(q[n, k // 8]) ^ int(q0[n, k // 8])
-        assert changed != 0 and changed & ~(0xF << (4 * slot)) == 0
-        assert (int(q[n, k // 8]) >> (4 * slot)) & 0xF == 15        # +7 + 8
+        q = orc.w4_pack(w, 128, False)[0].reshape(-1)
+        widx, nib = layout_position(n, k, K)
+        assert np.flatnonzero(q != q0).tolist() == [widx]
+        changed = int(q[widx]) ^ int(q0[widx])
+        assert changed != 0 and changed & ~(0xF << (4 * nib)) == 0
+        assert (int(q[widx]) >> (4 * nib)) & 0xF == 15                 # +7 + 8
+
+
+def test_w4_scale_zero_layout(orc):
+    """Scale of (n, g) at [n/16][g][n%16]; zero-point byte at [n/16][g/2][n%16]."""
+    N, K = 32, 512
+    w = np.zeros((N, K), np.float32)
+    w[19, 256:384] = np.linspace(-0.05, 0.1, 128)   # group 2 of row 19: z = 5
+    w[19, 384:512] = np.linspace(-0.1, 0.05, 128)   # group 3: z = 10
+    _, scales, zeros = orc.w4_pack(w, 128, True)
+    assert scales.shape == (2, 4, 16) and zeros.shape == (2, 2, 16)
+    assert zeros[1, 1, 3] == 0xA5
+    assert np.count_nonzero(scales != 0x3C00) == 2
+    assert scales[1, 2, 3] != 0x3C00 and scales[1, 3, 3] != 0x3C00
 
 
 def test_w4_zero_nibble_order(orc):
-    """zeros byte h: low nibble = zero-point of group 2h, high = group 2h+1."""
-    N, K = 1, 512
+    """zero-point byte: low nibble = group 2h, high nibble = group 2h+1."""
+    N, K = 16, 512
     w = np.zeros((N, K), np.float32)
     w[0, 0:128] = np.linspace(-0.1, 0.0, 128)        # z = 15 (all <= 0)
     w[0, 128:256] = np.linspace(0.0, 0.1, 128)       # z = 0  (all >= 0)
     w[0, 256:384] = np.linspace(-0.05, 0.1, 128)     # z = 5
     w[0, 384:512] = np.linspace(-0.1, 0.05, 128)     # z = 10
     _, _, zeros = orc.w4_pack(w, 128, True)
-    assert zeros.tolist() == [[0x0F, 0xA5]]
+    assert zeros[0, :, 0].tolist() == [0x0F, 0xA5]
+    assert np.all(zeros[0, :, 1:] == 0)                # other rows: all-zero groups, z = 0
 
 
 @pytest.mark.parametrize("asym,bits", [(False, 4.125), (True, 4.15625)])
