@@ -41,10 +41,19 @@ const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gr
                       void* q, float* scales, hipStream_t s);
 
 // W4A16 kernels (x_bf16: activations/output are BF16, else FP16).
+// The VALU GEMV stages up to 4 activation rows of length K in LDS.
+bool w4a16_gemv_supported(int64_t M, int64_t K);
 const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                        const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
 const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                          const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
+// Split-K small-M kernel (M <= 64): needs a workspace of
+// w4a16_splitk_workspace(M, N, K) bytes (0: none) whose leading counter area
+// is zero on entry; it is left zero on return.
+int64_t w4a16_splitk_workspace(int64_t M, int64_t N, int64_t K);
+const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws,
+                                hipStream_t s);
 const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                         const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
 

@@ -42,9 +42,10 @@ constexpr int64_t kMaxDim = int64_t(1) << 20;    // K, cols
 constexpr int64_t kMaxM = int64_t(65535) * 16;   // GEMM M: grid.y stays below 65536
 constexpr int64_t kMaxGemvM = 256;               // explicit GEMV requests
 
-// Decode kernels up to this batch; MFMA skinny kernel up to kSkinnyMax; tiled beyond.
-constexpr int64_t kW4GemvMax = 4;
-constexpr int64_t kW4SkinnyMax = 32;
+// W4A16: small-M MFMA kernel up to kW4SkinnyMax rows, tiled MFMA kernel beyond;
+// the VALU GEMV is selected explicitly only (BG_ALGO_GEMV).
+constexpr int64_t kW4GemvMax = 0;
+constexpr int64_t kW4SkinnyMax = 64;
 constexpr int64_t kW8SkinnyMax = 32;
 
 int w4_auto_algo(int64_t M) {
@@ -54,6 +55,16 @@ int w4_auto_algo(int64_t M) {
 }
 
 int w8_auto_algo(int64_t M) { return M <= kW8SkinnyMax ? BG_ALGO_SKINNY : BG_ALGO_TILED; }
+
+// With a workspace, small M runs split-K where the small-M kernel's per-block
+// re-staging of the activation rows costs more than split-K's cross-block
+// reduction: from the measured crossovers (graph-replayed, cold weights) on
+// the 4096/14336-wide projection shapes.
+int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
+    if (M > kW4SkinnyMax) return BG_ALGO_TILED;
+    const bool split = (M >= 8 && N >= 16384) || (M >= 12 && K >= 8192) || (M >= 24 && N > 4096);
+    return split ? BG_ALGO_SPLITK : BG_ALGO_SKINNY;
+}
 
 }  // namespace
 
@@ -65,7 +76,7 @@ BG_EXPORT bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, in
     if (w_dtype != BG_F32 && w_dtype != BG_F16 && w_dtype != BG_BF16)
         return fail(BG_ERR_DTYPE, "w4_pack: w_dtype %lld is not F32/F16/BF16", w_dtype);
     if (group != 128) return fail(BG_ERR_UNSUPPORTED, "w4_pack: group %lld (only 128 is supported)", group);
-    if (N < 1 || N > kMaxRows) return fail(BG_ERR_SHAPE, "w4_pack: N=%lld out of range", N);
+    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "w4_pack: N=%lld must be a multiple of 16", N);
     if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "w4_pack: K=%lld must be a multiple of 256", K);
     if (N * (K / 8) / 256 >= (int64_t(1) << 31)) return fail(BG_ERR_SHAPE, "w4_pack: N*K=%lld too large", N * K);
     if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zeros && !aligned16(zeros)))
@@ -80,9 +91,9 @@ BG_EXPORT int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype) {
     return w4_auto_algo(M);
 }
 
-BG_EXPORT bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
-                                  const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
-                                  int algo, void* stream) {
+static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                            const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                            void* ws, int64_t ws_bytes, bool with_ws, int algo, void* stream) {
     if (!x || !qweight || !scales || !y) return fail(BG_ERR_NULL, "gemm_w4a16: x, qweight, scales and y must be non-NULL");
     if (x_dtype != BG_F16 && x_dtype != BG_BF16)
         return fail(BG_ERR_DTYPE, "gemm_w4a16: x_dtype %lld is not F16/BF16", x_dtype);
@@ -90,20 +101,51 @@ BG_EXPORT bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t
     if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w4a16: M=%lld out of range", M);
     if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w4a16: N=%lld must be a multiple of 16", N);
     if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a16: K=%lld must be a multiple of 256", K);
-    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || (zeros && !aligned16(zeros)))
+    if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || (zeros && !aligned16(zeros)) ||
+        (ws && !aligned16(ws)))
         return fail(BG_ERR_ALIGN, "gemm_w4a16: pointers must be 16-byte aligned");
-    if (algo == BG_ALGO_AUTO) algo = w4_auto_algo(M);
-    if (algo == BG_ALGO_GEMV && M > kMaxGemvM)
-        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 (M=%lld)", M);
+    if (algo == BG_ALGO_AUTO) algo = with_ws ? w4_auto_algo_ws(M, N, K) : w4_auto_algo(M);
+    if (algo == BG_ALGO_GEMV && (M > kMaxGemvM || !bg::w4a16_gemv_supported(M, K)))
+        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 20000 (M=%lld, K=%lld)", M, K);
+    if (algo == BG_ALGO_SPLITK) {
+        if (!with_ws) return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernel needs gemm_w4a16_ws");
+        if (M > kW4SkinnyMax) return fail(BG_ERR_SHAPE, "gemm_w4a16: the split-K kernel takes M <= 64 (M=%lld)", M);
+        const int64_t need = bg::w4a16_splitk_workspace(M, N, K);
+        if (need > 0 && (!ws || ws_bytes < need))
+            return fail(BG_ERR_WORKSPACE, "gemm_w4a16: workspace of %lld bytes needed (got %lld)", need, ws ? ws_bytes : 0);
+    }
     const bool bf16 = x_dtype == BG_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     switch (algo) {
         case BG_ALGO_GEMV: note_kernel(bg::launch_w4a16_gemv(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_SKINNY: note_kernel(bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_TILED: note_kernel(bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
+        case BG_ALGO_SPLITK:
+            note_kernel(bg::launch_w4a16_splitk(x, bf16, M, K, qweight, scales, zeros, N, y, ws, s));
+            break;
         default: return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16: unknown algo %lld", algo);
     }
     return launched("gemm_w4a16");
+}
+
+BG_EXPORT bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                                  const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                                  int algo, void* stream) {
+    return w4a16_impl(x, x_dtype, M, K, qweight, scales, zeros, N, group, y, nullptr, 0, false, algo, stream);
+}
+
+BG_EXPORT bg_status gemm_w4a16_ws(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                                  const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                                  void* workspace, int64_t workspace_bytes, int algo, void* stream) {
+    return w4a16_impl(x, x_dtype, M, K, qweight, scales, zeros, N, group, y, workspace, workspace_bytes, true, algo,
+                      stream);
+}
+
+BG_EXPORT int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo) {
+    if (M < 1 || M > kMaxM || N < 16 || N % 16 || K < 256 || K % 256) return 0;
+    if (algo == BG_ALGO_AUTO) algo = w4_auto_algo_ws(M, N, K);
+    if (algo != BG_ALGO_SPLITK || M > kW4SkinnyMax) return 0;
+    return bg::w4a16_splitk_workspace(M, N, K);
 }
 
 BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
@@ -198,6 +240,7 @@ BG_EXPORT const char* bg_status_string(int status) {
         case BG_ERR_DTYPE: return "unsupported dtype";
         case BG_ERR_UNSUPPORTED: return "unsupported combination";
         case BG_ERR_HIP: return "HIP runtime error";
+        case BG_ERR_WORKSPACE: return "workspace missing or too small";
         default: return "unknown status";
     }
 }

@@ -4,6 +4,15 @@
 // eq. (2) x^ = s(q-z); §3 symmetric s = max|x|/qmax (eq. 3), asymmetric from the
 // observed min/max; §4 one scale per group of 128 along K; §5 FP16 scales.
 //
+// Packed layout (tiled for the GEMM kernels): 16 output channels x one group
+// of 128 k form a 1 KB tile of 64 slots x 4 words, slot = 16 * (c / 32) + n % 16
+// and word = (c % 32) / 8 for c = k % 128 -- exactly the 16 bytes one MFMA
+// lane consumes per group, so a wave reads each tile with one contiguous
+// 1 KB load.  Inside a word, even k sit in the low half-word (nibble i <->
+// k = 8j + 2i) and odd k in the high half-word (nibble 4+i <-> k = 8j + 2i + 1),
+// so one mask per nibble pair yields two consecutive-k 16-bit lanes.  Scales
+// are [N/16][K/128][16] and zero-point bytes [N/16][K/256][16].
+//
 // One thread produces one packed word (8 consecutive k of one row); the 16
 // threads of a 128-wide group are 16 consecutive lanes, so the group
 // reduction is a 4-step xor shuffle and no LDS is needed.  A 256-thread
@@ -26,17 +35,24 @@ __device__ __forceinline__ uint16_t group_scale_bits(float v, bool all_zero) {
     return h;
 }
 
+// bit offset of k = 8j + i inside word j
+__device__ __forceinline__ constexpr int nibble_shift(int i) { return (i & 1) ? 16 + 4 * (i >> 1) : 4 * (i >> 1); }
+
 template <int DT, bool ASYM>
 __global__ __launch_bounds__(256) void k_w4_pack(const void* __restrict__ w, int64_t N, int64_t K,
                                                  uint32_t* __restrict__ qweight,
                                                  uint16_t* __restrict__ scales,
                                                  uint8_t* __restrict__ zeros) {
     const int64_t words_per_row = K >> 3;
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= N * words_per_row) return;     // whole 32-lane halves exit together
-    const int64_t n = t / words_per_row;
-    const int64_t j = t - n * words_per_row;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (tid >= N * words_per_row) return;   // whole 32-lane halves exit together
+    const int64_t n = tid / words_per_row;
+    const int64_t j = tid - n * words_per_row;
     const int64_t g = j >> 4;               // group of 128 = 16 words
+    const int64_t ngroups = K >> 7;
+    const int64_t t = n >> 4, r = n & 15;
+    const int c = (int)(j & 15) * 8;        // k offset inside the group
+    const int64_t out_word = ((t * ngroups + g) * 64 + 16 * (c >> 5) + r) * 4 + ((c & 31) >> 3);
     float v[8];
     load8_f32<DT>(w, n * K + j * 8, v);
 
@@ -52,9 +68,9 @@ __global__ __launch_bounds__(256) void k_w4_pack(const void* __restrict__ w, int
         for (int i = 0; i < 8; ++i) {
             float q = __builtin_rintf(v[i] / s);
             q = __builtin_fminf(__builtin_fmaxf(q, -8.0f), 7.0f);
-            word |= (uint32_t)((int)q + 8) << (4 * i);
+            word |= (uint32_t)((int)q + 8) << nibble_shift(i);
         }
-        if ((j & 15) == 0) scales[n * (K >> 7) + g] = sh;
+        if ((j & 15) == 0) scales[(t * ngroups + g) * 16 + r] = sh;
     } else {
         float mn = 0.0f, mx = 0.0f;
 #pragma unroll
@@ -73,15 +89,15 @@ __global__ __launch_bounds__(256) void k_w4_pack(const void* __restrict__ w, int
         for (int i = 0; i < 8; ++i) {
             float q = __builtin_rintf(v[i] / s) + zf;
             q = __builtin_fminf(__builtin_fmaxf(q, 0.0f), 15.0f);
-            word |= (uint32_t)(int)q << (4 * i);
+            word |= (uint32_t)(int)q << nibble_shift(i);
         }
         // groups 2h and 2h+1 sit in lanes [32h', 32h'+16) and [32h'+16, 32h'+32)
         const uint32_t zi = (uint32_t)(int)zf;
         const uint32_t z_odd = (uint32_t)__shfl_down((int)zi, 16, 32);
-        if ((j & 31) == 0) zeros[n * (K >> 8) + (j >> 5)] = (uint8_t)(zi | (z_odd << 4));
-        if ((j & 15) == 0) scales[n * (K >> 7) + g] = sh;
+        if ((j & 31) == 0) zeros[(t * (ngroups >> 1) + (g >> 1)) * 16 + r] = (uint8_t)(zi | (z_odd << 4));
+        if ((j & 15) == 0) scales[(t * ngroups + g) * 16 + r] = sh;
     }
-    qweight[t] = word;
+    qweight[out_word] = word;
 }
 
 template <int DT>

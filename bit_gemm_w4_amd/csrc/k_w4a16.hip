@@ -15,10 +15,10 @@
 // with Sx_g = sum_{k in g} x[k] shared by all output columns.  The group
 // scale then multiplies the FP32 partial sum once per group.
 //
-// Nibble pairing: from word w (k = 8j .. 8j+7, nibble i = k - 8j) the four
-// 32-bit pairs are (w >> 4p) & 0x000F000F | magic = (MV+u_p, MV+u_{p+4}),
-// p = 0..3; the activations are permuted to the same order
-// (x_p, x_{p+4}) with v_perm, so every dot product pairs matching k.
+// Packed word j holds k = 8j..8j+7 with even k in the low half-word and odd k
+// in the high half-word, so (w >> 4p) & 0x000F000F | magic is the pair
+// (MV + u[8j+2p], MV + u[8j+2p+1]) -- consecutive k, matching activations in
+// their natural order: no permutation is needed on either operand.
 #include "bg_device.h"
 #include "bg_internal.h"
 
@@ -30,11 +30,13 @@ template <>
 struct W4Magic<true> {
     static constexpr uint32_t bits = 0x43004300u;  // BF16 128.0 in both halves
     static constexpr float value = 128.0f;
+    static constexpr uint32_t ones = 0x3F803F80u;  // BF16 1.0 pair
 };
 template <>
 struct W4Magic<false> {
     static constexpr uint32_t bits = 0x64006400u;  // FP16 1024.0 in both halves
     static constexpr float value = 1024.0f;
+    static constexpr uint32_t ones = 0x3C003C00u;  // FP16 1.0 pair
 };
 
 // dot2 of two packed 16-bit pairs into an FP32 accumulator.
@@ -48,139 +50,525 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                       false);
 }
 
-// (x_p, x_{p+4}) pairs of 8 consecutive 16-bit activations held as 4 dwords.
-__device__ __forceinline__ void pair_perm(const uint32_t X[4], uint32_t P[4]) {
-    P[0] = __builtin_amdgcn_perm(X[2], X[0], 0x05040100u);
-    P[1] = __builtin_amdgcn_perm(X[2], X[0], 0x07060302u);
-    P[2] = __builtin_amdgcn_perm(X[3], X[1], 0x05040100u);
-    P[3] = __builtin_amdgcn_perm(X[3], X[1], 0x07060302u);
+// (a & b) | c in one v_and_or_b32 (the compiler otherwise emits and + or).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
 }
 
-// The four (MV+u_p, MV+u_{p+4}) pairs of one packed word.
+// The four (MV+u[2p], MV+u[2p+1]) pairs of one packed word: 3 shifts + 4 and_or.
 template <bool BF16>
 __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t D[4]) {
     constexpr uint32_t m = W4Magic<BF16>::bits;
-    D[0] = (w & 0x000F000Fu) | m;
-    D[1] = ((w >> 4) & 0x000F000Fu) | m;
-    D[2] = ((w >> 8) & 0x000F000Fu) | m;
-    D[3] = ((w >> 12) & 0x000F000Fu) | m;
+    D[0] = and_or(w, 0x000F000Fu, m);
+    D[1] = and_or(w >> 4, 0x000F000Fu, m);
+    D[2] = and_or(w >> 8, 0x000F000Fu, m);
+    D[3] = and_or(w >> 12, 0x000F000Fu, m);
 }
 
-__device__ __forceinline__ uint32_t zero_point(const uint8_t* __restrict__ zr, int64_t n, int64_t ngroups,
-                                               int64_t g) {
-    if (zr == nullptr) return 8u;
-    return (uint32_t)(zr[n * (ngroups >> 1) + (g >> 1)] >> (4 * (g & 1))) & 0xFu;
+template <bool BF16>
+__device__ __forceinline__ float4_t mfma16(const uint32_t a[4], const uint32_t b[4], float4_t c) {
+    const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+    const uint4 bv = make_uint4(b[0], b[1], b[2], b[3]);
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, av), __builtin_bit_cast(bf168_t, bv),
+                                                       c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), __builtin_bit_cast(half8_t, bv),
+                                                      c, 0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_out(float v) {
+    return BF16 ? f32_to_bf16(v) : f32_to_f16(v);
 }
 
 // ============================================================================
-// Decode GEMV (VALU).  A row of W is split over LPR lanes; each lane handles
-// 16-byte chunks (32 k, a quarter group) and RPW rows per wave slot, reusing
-// its activations across those rows.  MB batch rows per block (grid.y tiles M).
-// Partial sums are combined with an LPR-lane xor reduction.
-// ============================================================================
-template <bool BF16, int MB, int LPR, int RPW>
-__global__ __launch_bounds__(256) void k_w4a16_gemv(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                    const uint32_t* __restrict__ qw,
-                                                    const uint16_t* __restrict__ sc,
-                                                    const uint8_t* __restrict__ zr, int64_t N,
-                                                    uint16_t* __restrict__ y) {
-    constexpr int ROWS_PER_SLOT = 64 / LPR;
-    constexpr int ROWS_PER_WAVE = RPW * ROWS_PER_SLOT;
-    constexpr int ROWS_PER_BLOCK = 4 * ROWS_PER_WAVE;
+// Small-M kernel (decode).  A block owns 16*TN output columns (TN weight tiles)
+// and a band of activation rows for the WHOLE of K; its NW waves split the
+// 128-wide groups of K between them and their partial results are summed
+// through LDS at the end.  This gives thousands of waves even for N = 4096
+// (enough loads in flight to cover HBM latency) without any cross-block
+// reduction or scratch memory.  Groups are dealt to the waves round-robin, so
+// the block sweeps its tiles front to back as one contiguous stream.
+//
+// Lane l (l16 = l % 16, q = l / 16) consumes, per group, slot l of each 1 KB
+// weight tile -- words 4q..4q+3 of the group row of column l16, i.e.
+// k = 32q .. 32q+31 -- so a wave reads a tile with one contiguous load.
+//
+// Two inner products share everything else:
+//  * MFMA (VROWS == 0), rows m0 .. m0+16*TM: v_mfma_f32_16x16x32_{bf16,f16};
+//    in K step kk the lane supplies word 4q+kk and activations k = 32q+8kk..+7
+//    of row l16 (same k assignment for both operands).  One extra MFMA per
+//    m-tile against an all-ones operand yields Sx_g directly in the output
+//    layout (lane l, register e -> row 4(l/16)+e, column l%16).
+//  * VALU (VROWS = 1, 2 or 4 rows): v_dot2_f32_{bf16,f16} of the lane's 32 k
+//    against each row; Sx_g comes from a per-block table built in LDS.
+//
+// Software pipeline: the loads of one group form a stage; STAGES stages are
+// in flight in registers and the loads of group g + STAGES are issued right
+// after group g is consumed.  The vector-memory counter retires loads in issue
+// order, so consuming group g waits only for g's own loads.
+//
+// XLDS: the block first copies its activation rows (all of K) into LDS and the
+// activation operand is read from there (ds_read, a separate counter), so a
+// stage holds only 16 bytes of weights plus scale/zero per tile and the
+// pipeline runs deep.  Without XLDS the activation fragments travel in the
+// stage registers and the pipeline is shallower.  Rows >= M only ever feed
+// output rows >= M (MFMA row i reads only operand row i), so lanes for such
+// rows read row M-1 instead of zero-filling.
+template <int TM, int TN, bool XLDS>
+struct DecStage {
+    uint4 w[TN];
+    uint4 a[XLDS ? 1 : TM][XLDS ? 1 : 4];
+    uint32_t s[TN];
+    uint32_t z[TN];
+};
+
+template <bool BF16, int TM, int TN, int NW, bool XLDS, int VROWS>
+__global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          const uint32_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ sc,
+                                                          const uint8_t* __restrict__ zr, int64_t N,
+                                                          uint16_t* __restrict__ y) {
+    constexpr bool VALU = VROWS > 0;
+    static_assert(!VALU || (XLDS && TM == 1), "the VALU product reads activations from LDS");
+    constexpr int STAGES = XLDS ? 4 : 3;
+    constexpr int BAND = VALU ? VROWS : 16 * TM;                       // activation rows per block
     constexpr float MV = W4Magic<BF16>::value;
-    constexpr uint32_t ONES = BF16 ? 0x3F803F80u : 0x3C003C00u;
+    constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
+    constexpr int TILE_FLOATS = VALU ? TN * VROWS * 64 : TM * TN * 4 * 64;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+    float* red = reinterpret_cast<float*>(dyn_lds);
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int kl = lane % LPR;
-    const int rsub = lane / LPR;
-    const int64_t m0 = (int64_t)blockIdx.y * MB;
-    const int64_t nrow0 = (int64_t)blockIdx.x * ROWS_PER_BLOCK + wave * ROWS_PER_WAVE + rsub;
-    const int64_t nchunks = K >> 5;
-    const int64_t ngroups = K >> 7;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+    const int l16 = lane & 15, q = lane >> 4;
+    const int64_t ntiles = N >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * TN;
+    const int64_t m0 = (int64_t)blockIdx.y * BAND;
+    const int ngroups = (int)(K >> 7);
+    // wave w takes groups w, w + NW, w + 2 NW, ...: at any moment the waves of
+    // a block read neighbouring 1 KB tiles, i.e. one contiguous stretch of HBM
+    const int n_mine = ngroups > wave ? (ngroups - wave + NW - 1) / NW : 0;
+    const int i_last = n_mine > 0 ? n_mine - 1 : 0;
+    const int64_t rows = (M - m0) < BAND ? (M - m0) : BAND;           // real rows of this block
+    const int64_t xstride = K + 8;                                    // LDS row pitch in halves
+    const int64_t x_bytes = XLDS ? rows * xstride * 2 : 0;
+    float* sxt = reinterpret_cast<float*>(dyn_lds + x_bytes);         // VALU: Sx[row][group]
 
-    float acc[RPW][MB];
+    // Buffer descriptors over this block's tiles: per-lane offsets live in
+    // VGPRs, the group offset is wave-uniform (scalar unit), and reads past the
+    // last tile of N (or of a missing zero-point tensor) return 0.
+    const int64_t my_tiles = (ntiles - t0) < TN ? (ntiles - t0) : TN;
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw + t0 * ngroups * 256), (short)0,
+                                                      (int)(my_tiles * ngroups * 1024), 0x00020000);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc + t0 * ngroups * 16), (short)0,
+                                                      (int)(my_tiles * ngroups * 32), 0x00020000);
+    const bool has_z = zr != nullptr;
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(has_z ? zr + t0 * (ngroups >> 1) * 16 : zr),
+                                                      (short)0, has_z ? (int)(my_tiles * (ngroups >> 1) * 16) : 0,
+                                                      0x00020000);
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + m0 * K), (short)0,
+                                                      (int)(rows * K * 2), 0x00020000);
+    int arow[VALU ? 1 : TM];                  // MFMA: activation row each lane feeds (clamped)
+    if constexpr (!VALU) {
 #pragma unroll
-    for (int s = 0; s < RPW; ++s)
-#pragma unroll
-        for (int b = 0; b < MB; ++b) acc[s][b] = 0.0f;
-
-    for (int64_t c = kl; c < nchunks; c += LPR) {
-        const int64_t g = c >> 2;
-        uint4 wv[RPW];
-        float scale[RPW];
-        float corr[RPW];
-#pragma unroll
-        for (int s = 0; s < RPW; ++s) {
-            const int64_t n = nrow0 + s * ROWS_PER_SLOT;
-            if (n < N) {
-                wv[s] = reinterpret_cast<const uint4*>(qw + n * (K >> 3))[c];
-                scale[s] = f16_to_f32(sc[n * ngroups + g]);
-                corr[s] = MV + (float)zero_point(zr, n, ngroups, g);
-            } else {
-                wv[s] = make_uint4(0, 0, 0, 0);
-                scale[s] = 0.0f;
-                corr[s] = 0.0f;
-            }
-        }
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            if (m0 + b >= M) break;
-            const uint4* xp = reinterpret_cast<const uint4*>(x + (m0 + b) * K + c * 32);
-            uint32_t P[4][4];
-            float sx = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint4 r = xp[q];
-                const uint32_t X[4] = {r.x, r.y, r.z, r.w};
-                pair_perm(X, P[q]);
-#pragma unroll
-                for (int p = 0; p < 4; ++p) sx = dot2<BF16>(P[q][p], ONES, sx);
-            }
-#pragma unroll
-            for (int s = 0; s < RPW; ++s) {
-                const uint32_t W[4] = {wv[s].x, wv[s].y, wv[s].z, wv[s].w};
-                float d = 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    uint32_t D[4];
-                    dequant_word<BF16>(W[q], D);
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) d = dot2<BF16>(D[p], P[q][p], d);
-                }
-                acc[s][b] += scale[s] * (d - corr[s] * sx);
-            }
+        for (int i = 0; i < TM; ++i) {
+            const int r = 16 * i + l16;
+            arow[i] = r < rows ? r : (int)rows - 1;
         }
     }
+    const uint32_t ones[4] = {ONE2, ONE2, ONE2, ONE2};
+
+    // Every stage issues the same loads (the group index is clamped to the
+    // wave's last group), so the compiler can wait for exactly one stage.
+    auto issue = [&](DecStage<TM, TN, XLDS>& st, int i) {
+        const int g = (i < i_last ? i : i_last) * NW + wave;
 #pragma unroll
-    for (int s = 0; s < RPW; ++s) {
-        const int64_t n = nrow0 + s * ROWS_PER_SLOT;
+        for (int j = 0; j < TN; ++j) {
+            st.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rw, lane * 16, (j * ngroups + g) * 1024, 0));
+            st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, l16 * 2, (j * ngroups + g) * 32, 0);
+            st.z[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, (j * (ngroups >> 1) + (g >> 1)) * 16, 0);
+        }
+        if constexpr (!XLDS) {
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            const float v = wave_sum<LPR>(acc[s][b]);
-            if (kl == 0 && n < N && m0 + b < M)
-                y[(m0 + b) * N + n] = BF16 ? f32_to_bf16(v) : f32_to_f16(v);
+            for (int ii = 0; ii < TM; ++ii)
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    st.a[ii][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                 rx, (int)(arow[ii] * K * 2) + q * 64 + kk * 16,
+                                                                 g * 256, 0));
+        }
+    };
+
+    DecStage<TM, TN, XLDS> stage[STAGES];
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) issue(stage[s], s);
+
+    if constexpr (XLDS) {
+        // copy rows [m0, m0 + rows) of X into LDS, 16 bytes per thread per pass
+        const int64_t chunks_per_row = K >> 3;
+        for (int64_t c = threadIdx.x; c < rows * chunks_per_row; c += NW * 64) {
+            const int64_t r = c / chunks_per_row, kc = c - r * chunks_per_row;
+            *reinterpret_cast<uint4*>(dyn_lds + (r * xstride + kc * 8) * 2) =
+                *reinterpret_cast<const uint4*>(x + (m0 + r) * K + kc * 8);
+        }
+        __syncthreads();
+        if constexpr (VALU) {
+            // Sx[row][g]: sum of the 128 activations of each group
+            for (int64_t e = threadIdx.x; e < rows * ngroups; e += NW * 64) {
+                const int64_t r = e / ngroups, g = e - r * ngroups;
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(dyn_lds + (r * xstride + g * 128) * 2);
+                float sum = 0.0f;
+                for (int k2 = 0; k2 < 64; ++k2) sum = dot2<BF16>(p[k2], ONE2, sum);
+                sxt[e] = sum;
+            }
+            __syncthreads();
+        }
+    }
+
+    float4_t acc[VALU ? 1 : TM][TN];
+    float vacc[TN][VALU ? VROWS : 1];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int i = 0; i < (VALU ? 1 : TM); ++i) acc[i][j] = float4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < (VALU ? VROWS : 1); ++b) vacc[j][b] = 0.0f;
+    }
+
+    auto consume = [&](const DecStage<TM, TN, XLDS>& st, int g) {
+        float scale[TN], corr[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            scale[j] = f16_to_f32(st.s[j] & 0xFFFFu);
+            corr[j] = MV + (float)(has_z ? (st.z[j] >> (4 * (g & 1))) & 0xF : 8u);
+        }
+        if constexpr (VALU) {
+            uint32_t D[TN][4][4];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const uint32_t wd[4] = {st.w[j].x, st.w[j].y, st.w[j].z, st.w[j].w};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) dequant_word<BF16>(wd[kk], D[j][kk]);
+            }
+#pragma unroll
+            for (int b = 0; b < VROWS; ++b) {
+                if (b >= rows) break;
+                const uint8_t* xr = dyn_lds + (b * xstride + (int64_t)g * 128 + q * 32) * 2;
+                uint4 xv[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) xv[kk] = *reinterpret_cast<const uint4*>(xr + kk * 16);
+                // only quarter 0 subtracts the whole group's correction
+                const float sx = q == 0 ? sxt[b * ngroups + g] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        d = dot2<BF16>(D[j][kk][0], xv[kk].x, d);
+                        d = dot2<BF16>(D[j][kk][1], xv[kk].y, d);
+                        d = dot2<BF16>(D[j][kk][2], xv[kk].z, d);
+                        d = dot2<BF16>(D[j][kk][3], xv[kk].w, d);
+                    }
+                    vacc[j][b] += scale[j] * (d - corr[j] * sx);
+                }
+            }
+        } else {
+            float4_t part[TM][TN], sx[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                sx[i] = float4_t{0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < TN; ++j) part[i][j] = float4_t{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                uint32_t bfrag[TN][4];
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const uint32_t w = kk == 0 ? st.w[j].x : kk == 1 ? st.w[j].y : kk == 2 ? st.w[j].z : st.w[j].w;
+                    dequant_word<BF16>(w, bfrag[j]);
+                }
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    uint4 av;
+                    if constexpr (XLDS)
+                        av = *reinterpret_cast<const uint4*>(dyn_lds +
+                                                             (arow[i] * xstride + (int64_t)g * 128 + q * 32 + kk * 8) * 2);
+                    else
+                        av = st.a[i][kk];
+                    const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+                    sx[i] = mfma16<BF16>(a, ones, sx[i]);
+#pragma unroll
+                    for (int j = 0; j < TN; ++j) part[i][j] = mfma16<BF16>(a, bfrag[j], part[i][j]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[i][j][e] += scale[j] * (part[i][j][e] - corr[j] * sx[i][e]);
+        }
+    };
+
+    for (int i = 0; i < n_mine; i += STAGES) {
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) {
+            if (i + s < n_mine) consume(stage[s], (i + s) * NW + wave);
+            issue(stage[s], i + s + STAGES);
+        }
+    }
+
+    // ---- sum the NW partial tiles through LDS (reusing the activation space) ----
+    if constexpr (XLDS) __syncthreads();
+    if constexpr (VALU) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int b = 0; b < VROWS; ++b) red[wave * TILE_FLOATS + (j * VROWS + b) * 64 + lane] = vacc[j][b];
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    red[wave * TILE_FLOATS + ((i * TN + j) * 4 + e) * 64 + lane] = acc[i][j][e];
+    }
+    __syncthreads();
+    if constexpr (VALU) {
+        // output (j, b, column l16): sum over waves and the 4 lane quarters
+        for (int t = threadIdx.x; t < TN * VROWS * 16; t += NW * 64) {
+            const int c16 = t & 15, jb = t >> 4;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) v += red[w * TILE_FLOATS + jb * 64 + qq * 16 + c16];
+            const int j = jb / VROWS, b = jb % VROWS;
+            const int64_t m = m0 + b;
+            const int64_t n = (t0 + j) * 16 + c16;
+            if (m < M && n < N) y[m * N + n] = to_out<BF16>(v);
+        }
+    } else {
+        for (int t = threadIdx.x; t < TILE_FLOATS; t += NW * 64) {
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[w * TILE_FLOATS + t];
+            const int ln = t & 63, e = (t >> 6) & 3, ij = t >> 8;
+            const int i = ij / TN, j = ij % TN;
+            const int64_t m = m0 + 16 * i + 4 * (ln >> 4) + e;
+            const int64_t n = (t0 + j) * 16 + (ln & 15);
+            if (m < M && n < N) y[m * N + n] = to_out<BF16>(v);
         }
     }
 }
 
 // ============================================================================
-// MFMA kernel (v_mfma_f32_16x16x32_{bf16,f16}).  Block tile BM x BN, one
-// 128-wide group per K step; 4 waves as WM x WN, each wave TM x TN 16x16
-// tiles.  The activation tile is staged in LDS (XOR-swizzled 16-byte chunks
-// so the 16 rows read by one MFMA operand hit distinct banks); each lane
-// reads its packed weights straight from HBM (16 bytes = its quarter of a
-// group row) and dequantizes them in registers.
+// Split-K small-M kernel (M <= 64), for callers that provide a workspace.
 //
-// Operand k-assignment: in K step kk (0..3) of a group, lane quarter q
-// (lane / 16) supplies word 4q + kk of the group row, i.e. k = 32q + 8kk +
-// {0,4,1,5,2,6,3,7}; the activation operand uses the same k order, so the
-// hardware's fixed pairing of operand slots multiplies matching k.  Output
-// layout of a 16x16 f32 tile: lane l, register i holds row 4(l/16) + i,
-// column l % 16.
+// Grid (column groups of SPK_NW weight tiles) x (S slices of K).  A block
+// stages only its K-slice of the activation rows in LDS -- once, shared by
+// its 16 waves -- and every wave streams the slice of ONE weight tile, so the
+// activation bytes each CU reads are amortised over 16 tiles (at M = 16 the
+// activations of a group are 4x the bytes of one weight tile).  The FP32
+// partial tiles of the S slices go to the workspace; the block that
+// completes a column group last (atomic counter per group) adds the S
+// partials in slice order -- a fixed order, so results do not depend on
+// timing -- writes the output and resets the counter, leaving the workspace
+// ready for the next call.  Nothing waits on another block, so no block can
+// stall the grid.
 //
-// Sx_g for the zero-point/magic correction comes from one extra MFMA per
-// m-tile per K step against an all-ones operand: its accumulator holds
-// sum_k x[row][k] in exactly the rows the epilogue needs.
+// Workspace: SPK_COUNTERS ints of counters at offset 0 (a fixed place, so a
+// workspace reused for calls of other shapes never finds counters in memory
+// that held partial tiles), then the partial tiles.  Only rows < M of a
+// partial tile are written and read back.
+//
+// Inner product as in the MFMA variant of k_w4a16_decode; Sx_g comes from a
+// table the block builds next to the staged activations.
+// ============================================================================
+constexpr int SPK_NW = 16;
+constexpr int SPK_STAGES = 4;
+constexpr int SPK_COUNTERS = 65536;         // one per column group: N <= 2^24 gives at most 65536
+
+struct SpkStage {
+    uint4 w;
+    uint32_t s;
+    uint32_t z;
+};
+
+template <bool BF16, int TM>
+__global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __restrict__ x, int64_t M,
+                                                              int64_t K, const uint32_t* __restrict__ qw,
+                                                              const uint16_t* __restrict__ sc,
+                                                              const uint8_t* __restrict__ zr, int64_t N,
+                                                              uint16_t* __restrict__ y, float* __restrict__ ws,
+                                                              int S, int gs) {
+    constexpr int NW = SPK_NW, STAGES = SPK_STAGES, BAND = 16 * TM;
+    constexpr float MV = W4Magic<BF16>::value;
+    constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, q = lane >> 4;
+    const int ntiles = (int)(N >> 4);
+    const int ngroups = (int)(K >> 7);
+    const int cg = blockIdx.x, sl = blockIdx.y;
+    const int g0 = sl * gs;
+    const int ng = (ngroups - g0) < gs ? (ngroups - g0) : gs;        // >= 1 by construction of S
+    const int tile = cg * NW + wave;
+    const bool tok = tile < ntiles;
+    const int tt = tok ? tile : 0;
+    const int rows = M < BAND ? (int)M : BAND;
+    const int xpitch = ng * 128 + 8;                                   // halves per staged row
+    uint16_t* xl = reinterpret_cast<uint16_t*>(dyn_lds);
+    float* sxt = reinterpret_cast<float*>(dyn_lds + rows * xpitch * 2);   // Sx[group][row]
+    int* last_block = reinterpret_cast<int*>(sxt + ng * BAND);               // one flag after the table
+
+    const int zb0 = g0 >> 1;
+    const int zb1 = (g0 + ng - 1) >> 1;
+    const bool has_z = zr != nullptr;
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw + ((int64_t)tt * ngroups + g0) * 256),
+                                                      (short)0, tok ? ng * 1024 : 0, 0x00020000);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc + ((int64_t)tt * ngroups + g0) * 16),
+                                                      (short)0, tok ? ng * 32 : 0, 0x00020000);
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(has_z ? zr + ((int64_t)tt * (ngroups >> 1) + zb0) * 16 : zr), (short)0,
+        (tok && has_z) ? (zb1 - zb0 + 1) * 16 : 0, 0x00020000);
+
+    auto issue = [&](SpkStage& st, int i) {
+        const int gl = i < ng - 1 ? i : ng - 1;
+        st.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, gl * 1024, 0));
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, l16 * 2, gl * 32, 0);
+        st.z = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, (((g0 + gl) >> 1) - zb0) * 16, 0);
+    };
+    SpkStage stage[STAGES];
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st) issue(stage[st], st);
+
+    // stage X[0:rows, slice] (16-byte chunks), then the per-group row sums
+    const int cpr = ng * 16;                                            // chunks per row
+    for (int c = threadIdx.x; c < rows * cpr; c += NW * 64) {
+        const int r = c / cpr, kc = c - r * cpr;
+        *reinterpret_cast<uint4*>(xl + r * xpitch + kc * 8) =
+            *reinterpret_cast<const uint4*>(x + (int64_t)r * K + (int64_t)g0 * 128 + kc * 8);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < ng * BAND; e += NW * 64) {
+        const int gl = e / BAND, r0 = e - gl * BAND;
+        const int r = r0 < rows ? r0 : rows - 1;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(xl + r * xpitch + gl * 128);
+        float sum = 0.0f;
+        for (int k2 = 0; k2 < 64; ++k2) sum = dot2<BF16>(p[k2], ONE2, sum);
+        sxt[e] = sum;
+    }
+    __syncthreads();
+
+    int arow[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = 16 * i + l16;
+        arow[i] = r < rows ? r : rows - 1;
+    }
+    float4_t acc[TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) acc[i] = float4_t{0, 0, 0, 0};
+
+    auto consume = [&](const SpkStage& st, int gl) {
+        const float scale = f16_to_f32(st.s & 0xFFFFu);
+        const float corr = MV + (float)(has_z ? (st.z >> (4 * ((g0 + gl) & 1))) & 0xF : 8u);
+        float4_t part[TM];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) part[i] = float4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            uint32_t b[4];
+            dequant_word<BF16>(kk == 0 ? st.w.x : kk == 1 ? st.w.y : kk == 2 ? st.w.z : st.w.w, b);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const uint4 av = *reinterpret_cast<const uint4*>(xl + arow[i] * xpitch + gl * 128 + q * 32 + kk * 8);
+                const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+                part[i] = mfma16<BF16>(a, b, part[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const float4 sx = *reinterpret_cast<const float4*>(sxt + gl * BAND + 16 * i + 4 * q);
+            acc[i][0] += scale * (part[i][0] - corr * sx.x);
+            acc[i][1] += scale * (part[i][1] - corr * sx.y);
+            acc[i][2] += scale * (part[i][2] - corr * sx.z);
+            acc[i][3] += scale * (part[i][3] - corr * sx.w);
+        }
+    };
+    for (int i = 0; i < ng; i += STAGES) {
+#pragma unroll
+        for (int st = 0; st < STAGES; ++st) {
+            if (i + st < ng) consume(stage[st], i + st);
+            issue(stage[st], i + st + STAGES);
+        }
+    }
+
+    auto store_y = [&](int i, const float4_t& v) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t m = 16 * i + 4 * q + e;
+            const int64_t n = (int64_t)tile * 16 + l16;
+            if (tok && m < M) y[m * N + n] = to_out<BF16>(v[e]);
+        }
+    };
+    if (S == 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) store_y(i, acc[i]);
+        return;
+    }
+    // ---- partial tile -> workspace; the last block of the column group reduces ----
+    const int64_t tiles_pad = (int64_t)gridDim.x * NW;
+    int* counters = reinterpret_cast<int*>(ws);
+    float* part = ws + SPK_COUNTERS;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+        if (16 * i + 4 * q < M)
+            *reinterpret_cast<float4_t*>(part + (((int64_t)sl * tiles_pad + tile) * TM + i) * 256 + lane * 4) =
+                acc[i];
+    // Each wave waits until its partial stores are complete at its L2, so the
+    // single agent-scope acquire-release add below (one wave per block: its
+    // release writes back the L2 lines of all 16 waves, its acquire
+    // invalidates stale lines for the whole block) publishes the block's
+    // partials and, for the last block, makes the others' visible.  One
+    // release/acquire per block instead of one per wave: those are
+    // whole-cache operations on a multi-L2 device.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *last_block = __hip_atomic_fetch_add(counters + cg, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (!*last_block) return;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (16 * i + 4 * q >= M) continue;
+        float4_t v = float4_t{0, 0, 0, 0};
+        for (int s2 = 0; s2 < S; ++s2)
+            v += *reinterpret_cast<const float4_t*>(part + (((int64_t)s2 * tiles_pad + tile) * TM + i) * 256 +
+                                                    lane * 4);
+        store_y(i, v);
+    }
+    if (threadIdx.x == 0) atomicExch(counters + cg, 0);
+}
+
+// ============================================================================
+// Large-M MFMA kernel.  Block tile BM x BN, one 128-wide group per K step;
+// 4 waves as WM x WN, each wave TM x TN 16x16 tiles.  The activation tile is
+// staged in LDS (XOR-swizzled 16-byte chunks so the 16 rows read by one MFMA
+// operand hit distinct banks); each lane reads its packed weights straight
+// from HBM (16 bytes = its quarter of a group row) and dequantizes them in
+// registers (slot `lane` of the tile, one contiguous 1 KB load per wave).
+// k assignment and the Sx MFMA as in k_w4a16_decode.
 // ============================================================================
 template <bool BF16, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__ x, int64_t M, int64_t K,
@@ -192,7 +580,7 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 16, TN = WTN / 16;
     constexpr float MV = W4Magic<BF16>::value;
-    constexpr uint32_t ONES = BF16 ? 0x3F803F80u : 0x3C003C00u;
+    constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
     __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -200,7 +588,7 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
     const int l16 = lane & 15, q = lane >> 4;
     const int64_t m_blk = (int64_t)blockIdx.y * BM, n_blk = (int64_t)blockIdx.x * BN;
     const int64_t ngroups = K >> 7;
-    const int64_t kwords = K >> 3;
+    const uint32_t ones[4] = {ONE2, ONE2, ONE2, ONE2};
 
     float4_t acc[TM][TN];
 #pragma unroll
@@ -222,11 +610,11 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
         float scale[TN], corr[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int64_t n = n_blk + wn * WTN + j * 16 + l16;
-            if (n < N) {
-                wv[j] = *reinterpret_cast<const uint4*>(qw + n * kwords + g * 16 + q * 4);
-                scale[j] = f16_to_f32(sc[n * ngroups + g]);
-                corr[j] = MV + (float)zero_point(zr, n, ngroups, g);
+            const int64_t t = (n_blk + wn * WTN + j * 16) >> 4;     // weight tile (16 columns)
+            if (t < (N >> 4)) {
+                wv[j] = *reinterpret_cast<const uint4*>(qw + ((t * ngroups + g) * 64 + lane) * 4);
+                scale[j] = f16_to_f32(sc[(t * ngroups + g) * 16 + l16]);
+                corr[j] = MV + (float)(zr ? (zr[(t * (ngroups >> 1) + (g >> 1)) * 16 + l16] >> (4 * (g & 1))) & 0xF : 8);
             } else {
                 wv[j] = make_uint4(0, 0, 0, 0);
                 scale[j] = 0.0f;
@@ -255,27 +643,10 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
                 const int r = wm * WTM + i * 16 + l16;
                 const int ch = q * 4 + kk;
                 const uint4 v = *reinterpret_cast<const uint4*>(lds_a + r * 256 + ((ch ^ (r & 15)) << 4));
-                const uint32_t X[4] = {v.x, v.y, v.z, v.w};
-                uint32_t A[4];
-                pair_perm(X, A);
-                const uint32_t ones[4] = {ONES, ONES, ONES, ONES};
-                if constexpr (BF16) {
-                    const bf168_t a = __builtin_bit_cast(bf168_t, A);
-                    sx[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        a, __builtin_bit_cast(bf168_t, ones), sx[i], 0, 0, 0);
+                const uint32_t a[4] = {v.x, v.y, v.z, v.w};
+                sx[i] = mfma16<BF16>(a, ones, sx[i]);
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, __builtin_bit_cast(bf168_t, bfrag[j]), part[i][j], 0, 0, 0);
-                } else {
-                    const half8_t a = __builtin_bit_cast(half8_t, A);
-                    sx[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(half8_t, ones), sx[i],
-                                                                   0, 0, 0);
-#pragma unroll
-                    for (int j = 0; j < TN; ++j)
-                        part[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            a, __builtin_bit_cast(half8_t, bfrag[j]), part[i][j], 0, 0, 0);
-                }
+                for (int j = 0; j < TN; ++j) part[i][j] = mfma16<BF16>(a, bfrag[j], part[i][j]);
             }
         }
         // ---- per-group epilogue: acc += s * (part - (MV + z) * Sx) ----
@@ -284,8 +655,7 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    acc[i][j][e] += scale[j] * (part[i][j][e] - corr[j] * sx[i][e]);
+                for (int e = 0; e < 4; ++e) acc[i][j][e] += scale[j] * (part[i][j][e] - corr[j] * sx[i][e]);
     }
 
 #pragma unroll
@@ -296,39 +666,113 @@ __global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t m = m_blk + wm * WTM + i * 16 + q * 4 + e;
-                if (m < M && n < N) y[m * N + n] = BF16 ? f32_to_bf16(acc[i][j][e]) : f32_to_f16(acc[i][j][e]);
+                if (m < M && n < N) y[m * N + n] = to_out<BF16>(acc[i][j][e]);
             }
         }
 }
 
 // ---------------------------------------------------------------- launch ----
 
-template <bool BF16, int MB, int LPR, int RPW>
-static const char* gemv_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                     const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    constexpr int rows_per_block = 4 * RPW * (64 / LPR);
-    dim3 grid((unsigned)((N + rows_per_block - 1) / rows_per_block), (unsigned)((M + MB - 1) / MB));
-    hipLaunchKernelGGL((k_w4a16_gemv<BF16, MB, LPR, RPW>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
-    return kname("k_w4a16_gemv", BF16, MB, LPR, RPW);
+// gfx950 gives a workgroup up to 160 KB of LDS; the runtime needs the larger
+// dynamic size declared once per kernel.
+constexpr int64_t kLdsMax = 160 * 1024;
+
+template <typename Kern>
+static void allow_lds(Kern kernel, size_t bytes) {
+    if (bytes > 64 * 1024)
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)bytes);
 }
 
-template <bool BF16, int MB>
-static const char* gemv_mb(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                    const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    const int64_t chunks = K >> 5;
-    if (chunks >= 256) return gemv_cfg<BF16, MB, 64, 1>(x, M, K, qw, sc, zr, N, y, s);
-    if (chunks >= 64) return gemv_cfg<BF16, MB, 32, 1>(x, M, K, qw, sc, zr, N, y, s);
-    return gemv_cfg<BF16, MB, 16, 1>(x, M, K, qw, sc, zr, N, y, s);
+// LDS bytes of the decode kernel: staged activation rows (+ Sx table for the
+// VALU product) or the cross-wave reduction buffer, whichever is larger.
+static int64_t decode_lds(int tile_floats, int NW, bool xlds, bool valu, int64_t rows, int64_t K) {
+    const int64_t red = (int64_t)NW * tile_floats * 4;
+    const int64_t xb = xlds ? rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) : 0;
+    return red > xb ? red : xb;
+}
+
+template <bool BF16, int TM, int TN, int NW, bool XLDS, int VROWS>
+static const char* decode_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+                              const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    constexpr int BAND = VROWS > 0 ? VROWS : 16 * TM;
+    constexpr int TILE_FLOATS = VROWS > 0 ? TN * VROWS * 64 : TM * TN * 4 * 64;
+    dim3 grid((unsigned)(((N >> 4) + TN - 1) / TN), (unsigned)((M + BAND - 1) / BAND));
+    const int64_t rows = M < BAND ? M : BAND;
+    const size_t lds = (size_t)decode_lds(TILE_FLOATS, NW, XLDS, VROWS > 0, rows, K);
+    auto kern = k_w4a16_decode<BF16, TM, TN, NW, XLDS, VROWS>;
+    allow_lds(kern, lds);
+    hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N,
+                       static_cast<uint16_t*>(y));
+    return kname("k_w4a16_decode", BF16, TM, TN, NW, XLDS, VROWS);
+}
+
+// Waves per block: enough blocks x waves to keep ~16 waves per CU resident,
+// never more waves than K has groups.
+template <bool BF16, int TM, int TN, bool XLDS, int VROWS>
+static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+                             const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    constexpr int BAND = VROWS > 0 ? VROWS : 16 * TM;
+    const int64_t blocks = (((N >> 4) + TN - 1) / TN) * ((M + BAND - 1) / BAND);
+    const int64_t ngroups = K >> 7;
+    int64_t want = (4096 + blocks - 1) / blocks;
+    if (want > ngroups) want = ngroups;
+    // 16 waves per block caps a thread at 128 VGPRs: only the light variants
+    constexpr bool fits16 = VROWS > 0 ? (VROWS == 1 && TN == 1) : (TM * TN == 1 || (XLDS && TM * TN == 2));
+    if constexpr (fits16) {
+        if (want >= 16) return decode_cfg<BF16, TM, TN, 16, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
+    }
+    if constexpr (TM < 4) {
+        if (want >= 8) return decode_cfg<BF16, TM, TN, 8, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
+    }
+    if (want >= 4) return decode_cfg<BF16, TM, TN, 4, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
+    return decode_cfg<BF16, TM, TN, 1, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
+}
+
+static bool xlds_fits(int64_t rows, int64_t K, bool valu) {
+    return rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
 }
 
 template <bool BF16>
-static const char* gemv_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                    const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (M <= 1) return gemv_mb<BF16, 1>(x, M, K, qw, sc, zr, N, y, s);
-    if (M <= 2) return gemv_mb<BF16, 2>(x, M, K, qw, sc, zr, N, y, s);
-    return gemv_mb<BF16, 4>(x, M, K, qw, sc, zr, N, y, s);
+static const char* decode_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+                             const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    const bool wide = N >= 16384;
+    if (M <= 16) {
+        if (xlds_fits(M, K, false)) {
+            if (wide) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+            return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+        }
+        if (wide) return decode_nw<BF16, 1, 2, false, 0>(x, M, K, qw, sc, zr, N, y, s);
+        return decode_nw<BF16, 1, 1, false, 0>(x, M, K, qw, sc, zr, N, y, s);
+    }
+    if (M <= 32) return decode_nw<BF16, 2, 1, false, 0>(x, M, K, qw, sc, zr, N, y, s);
+    return decode_nw<BF16, 4, 1, false, 0>(x, M, K, qw, sc, zr, N, y, s);
 }
+
+const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    if (x_bf16) return decode_dt<true>(x, M, K, qw, sc, zr, N, y, s);
+    return decode_dt<false>(x, M, K, qw, sc, zr, N, y, s);
+}
+
+// VALU GEMV: row bands of 1, 2 or 4 activation rows (grid.y covers larger M).
+template <bool BF16>
+static const char* gemv_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+                           const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+    const bool wide = N >= 16384;
+    if (M <= 1) {
+        if (wide) return decode_nw<BF16, 1, 2, true, 1>(x, M, K, qw, sc, zr, N, y, s);
+        return decode_nw<BF16, 1, 1, true, 1>(x, M, K, qw, sc, zr, N, y, s);
+    }
+    if (M <= 2) {
+        if (wide) return decode_nw<BF16, 1, 2, true, 2>(x, M, K, qw, sc, zr, N, y, s);
+        return decode_nw<BF16, 1, 1, true, 2>(x, M, K, qw, sc, zr, N, y, s);
+    }
+    if (wide) return decode_nw<BF16, 1, 2, true, 4>(x, M, K, qw, sc, zr, N, y, s);
+    return decode_nw<BF16, 1, 1, true, 4>(x, M, K, qw, sc, zr, N, y, s);
+}
+
+bool w4a16_gemv_supported(int64_t M, int64_t K) { return xlds_fits(M < 4 ? M : 4, K, true); }
 
 const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
@@ -336,19 +780,70 @@ const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, 
     return gemv_dt<false>(x, M, K, qw, sc, zr, N, y, s);
 }
 
+// ---- split-K configuration (shared by the workspace query and the launch) ----
+struct SplitCfg {
+    int TM, S, gs, colgroups;
+    int64_t ws_bytes, lds_bytes;
+};
+
+static SplitCfg splitk_cfg(int64_t M, int64_t N, int64_t K) {
+    SplitCfg c{};
+    c.TM = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+    const int64_t rows = M < 16 * c.TM ? M : 16 * c.TM;
+    const int64_t ntiles = N >> 4, ngroups = K >> 7;
+    c.colgroups = (int)((ntiles + SPK_NW - 1) / SPK_NW);
+    // slices: about one block per CU, at least one group per slice, LDS-bounded
+    int64_t S = (256 + c.colgroups / 2) / c.colgroups;
+    if (S < 1) S = 1;
+    if (S > ngroups) S = ngroups;
+    int64_t gs = (ngroups + S - 1) / S;
+    const int64_t per_group = rows * 256 + 16 * c.TM * 4;                   // staged halves + Sx table
+    int64_t gs_max = (96 * 1024 - rows * 16) / per_group;
+    if (gs_max < 1) gs_max = 1;
+    if (gs > gs_max) gs = gs_max;
+    S = (ngroups + gs - 1) / gs;
+    c.S = (int)S;
+    c.gs = (int)gs;
+    c.lds_bytes = rows * (gs * 128 + 8) * 2 + gs * 16 * c.TM * 4 + 16;
+    c.ws_bytes = S > 1 ? SPK_COUNTERS * 4 + S * c.colgroups * SPK_NW * c.TM * 1024 : 0;
+    return c;
+}
+
+int64_t w4a16_splitk_workspace(int64_t M, int64_t N, int64_t K) { return splitk_cfg(M, N, K).ws_bytes; }
+
+template <bool BF16, int TM>
+static const char* splitk_launch(const SplitCfg& c, const void* x, int64_t M, int64_t K, const uint32_t* qw,
+                                 const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws,
+                                 hipStream_t s) {
+    auto kern = k_w4a16_splitk<BF16, TM>;
+    allow_lds(kern, (size_t)c.lds_bytes);
+    hipLaunchKernelGGL(kern, dim3((unsigned)c.colgroups, (unsigned)c.S), dim3(SPK_NW * 64), (size_t)c.lds_bytes, s,
+                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y),
+                       static_cast<float*>(ws), c.S, c.gs);
+    return kname("k_w4a16_splitk", BF16, TM);
+}
+
+const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws,
+                                hipStream_t s) {
+    const SplitCfg c = splitk_cfg(M, N, K);
+    if (x_bf16) {
+        if (c.TM == 1) return splitk_launch<true, 1>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+        if (c.TM == 2) return splitk_launch<true, 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+        return splitk_launch<true, 4>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    }
+    if (c.TM == 1) return splitk_launch<false, 1>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    if (c.TM == 2) return splitk_launch<false, 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    return splitk_launch<false, 4>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+}
+
 template <bool BF16, int BM, int BN, int WM, int WN>
 static const char* mfma_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                     const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+                            const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
     hipLaunchKernelGGL((k_w4a16_mfma<BF16, BM, BN, WM, WN>), grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
     return kname("k_w4a16_mfma", BF16, BM, BN, WM, WN);
-}
-
-const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) return mfma_cfg<true, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
-    return mfma_cfg<false, 16, 128, 1, 4>(x, M, K, qw, sc, zr, N, y, s);
 }
 
 const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,

@@ -20,11 +20,11 @@ LIB_PATH = os.path.join(_PKG, "libbitgemm.so")
 # enums of include/bitgemm.h
 F32, F16, BF16, I8, FP8_E4M3, I32 = 0, 1, 2, 3, 4, 5
 GRAN_TENSOR, GRAN_ROW, GRAN_ROW_G128, GRAN_BLOCK128 = 0, 1, 2, 3
-ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED = 0, 1, 2, 3
+ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED, ALGO_SPLITK = 0, 1, 2, 3, 4
 PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
-    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
+    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w4a16_algo", "gemm_w8a8_algo", "bg_status_string", "bg_last_error",
     "bg_pack_format_version", "bg_last_kernel",
 )
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
             "w4_pack": [P, I, I64, I64, I, I, P, P, P, P],
             "gemm_w4a16": [P, I, I64, I64, P, P, P, I64, I, P, P],
             "gemm_w4a16_ex": [P, I, I64, I64, P, P, P, I64, I, P, I, P],
+            "gemm_w4a16_ws": [P, I, I64, I64, P, P, P, I64, I, P, P, I64, I, P],
+            "gemm_w4a16_workspace_bytes": [I64, I64, I64, I],
             "act_quant_int8": [P, I, I64, I64, I, P, P, P],
             "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
@@ -70,7 +72,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = argtypes
             fn.restype = (ctypes.c_char_p if name in ("bg_status_string", "bg_last_error", "bg_last_kernel")
-                          else ctypes.c_int)
+                          else ctypes.c_int64 if name == "gemm_w4a16_workspace_bytes" else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -104,10 +106,11 @@ def last_kernel() -> str:
 
 @dataclass
 class PackedW4:
-    """INT4 weights in the w4_pack layout (BG_PACK_FORMAT_VERSION 1)."""
-    qweight: torch.Tensor        # int32 [N][K/8], nibble i of word j = k 8j+i
-    scales: torch.Tensor         # float16 [N][K/128]
-    zeros: torch.Tensor | None   # uint8 [N][K/256] (two 4-bit zero-points) or None
+    """INT4 weights in the tiled w4_pack layout (BG_PACK_FORMAT_VERSION 1):
+    one 1 KB tile per (16 output channels, 128-wide group)."""
+    qweight: torch.Tensor        # int32 [N/16][K/128][64][4]
+    scales: torch.Tensor         # float16 [N/16][K/128][16]
+    zeros: torch.Tensor | None   # uint8 [N/16][K/256][16] (two 4-bit zero-points) or None
     N: int
     K: int
     group: int = 128
@@ -123,16 +126,40 @@ def w4_pack(w: torch.Tensor, group: int = 128, asymmetric: bool = False, stream=
     dt = _TORCH_DT.get(w.dtype)
     if dt is None:
         raise ValueError(f"w4_pack: unsupported dtype {w.dtype}")
-    qweight = torch.empty((N, K // 8), dtype=torch.int32, device=w.device)
-    scales = torch.empty((N, K // group), dtype=torch.float16, device=w.device)
-    zeros = torch.empty((N, K // (2 * group)), dtype=torch.uint8, device=w.device) if asymmetric else None
+    if N % 16 or K % 256 or group != 128:
+        raise ValueError(f"w4_pack: need N % 16 == 0, K % 256 == 0, group == 128 (N={N}, K={K}, group={group})")
+    qweight = torch.empty((N // 16, K // 128, 64, 4), dtype=torch.int32, device=w.device)
+    scales = torch.empty((N // 16, K // 128, 16), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((N // 16, K // 256, 16), dtype=torch.uint8, device=w.device) if asymmetric else None
     _check(lib().w4_pack(_ptr(w), dt, N, K, group, int(asymmetric), _ptr(qweight), _ptr(scales), _ptr(zeros),
                          _stream(stream)), "w4_pack")
     return PackedW4(qweight, scales, zeros, N, K, group)
 
 
+_workspaces: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A device workspace of at least nbytes, cached per device, zero-filled
+    when allocated.  The library leaves its counter area zeroed after every
+    call; calls sharing it must not overlap in time (use one per stream when
+    streams run concurrently)."""
+    key = torch.device(device).index or 0
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def gemm_w4a16_workspace_bytes(M: int, N: int, K: int, algo: int = ALGO_AUTO) -> int:
+    return int(lib().gemm_w4a16_workspace_bytes(M, N, K, algo))
+
+
 def gemm_w4a16(x: torch.Tensor, packed: PackedW4, out: torch.Tensor | None = None, algo: int = ALGO_AUTO,
-               stream=None) -> torch.Tensor:
+               ws: torch.Tensor | None | bool = None, stream=None) -> torch.Tensor:
+    """Y = X W^T.  ws: a workspace tensor, None to use the cached per-device
+    workspace (enables the split-K small-M kernel), or False for none."""
     M, K = x.shape
     if K != packed.K:
         raise ValueError(f"gemm_w4a16: x has K={K}, weights K={packed.K}")
@@ -141,8 +168,17 @@ def gemm_w4a16(x: torch.Tensor, packed: PackedW4, out: torch.Tensor | None = Non
         raise ValueError(f"gemm_w4a16: activations must be float16/bfloat16, got {x.dtype}")
     if out is None:
         out = torch.empty((M, packed.N), dtype=x.dtype, device=x.device)
-    _check(lib().gemm_w4a16_ex(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales), _ptr(packed.zeros),
+    L = lib()
+    if ws is False:
+        _check(L.gemm_w4a16_ex(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales), _ptr(packed.zeros),
                                packed.N, packed.group, _ptr(out), algo, _stream(stream)), "gemm_w4a16")
+        return out
+    if ws is None:
+        need = gemm_w4a16_workspace_bytes(M, packed.N, K, algo)
+        ws = workspace(need, x.device) if need > 0 else None
+    _check(L.gemm_w4a16_ws(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales), _ptr(packed.zeros),
+                           packed.N, packed.group, _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), algo,
+                           _stream(stream)), "gemm_w4a16")
     return out
 
 

@@ -42,7 +42,8 @@ typedef enum bg_status {
     BG_ERR_ALIGN = 3,        /* a pointer is not 16-byte aligned                 */
     BG_ERR_DTYPE = 4,        /* dtype not accepted by this entry point           */
     BG_ERR_UNSUPPORTED = 5,  /* granularity / dtype combination not implemented  */
-    BG_ERR_HIP = 6           /* the HIP runtime rejected a launch                */
+    BG_ERR_HIP = 6,          /* the HIP runtime rejected a launch                */
+    BG_ERR_WORKSPACE = 7     /* workspace missing or smaller than required       */
 } bg_status;
 
 typedef enum bg_dtype {
@@ -62,7 +63,8 @@ typedef enum bg_algo {
     BG_ALGO_AUTO = 0,
     BG_ALGO_GEMV = 1,      /* W4A16 small-M: VALU dot products, wave reductions    */
     BG_ALGO_SKINNY = 2,    /* small-M on MFMA (M padded to the MFMA tile)          */
-    BG_ALGO_TILED = 3      /* large-M LDS-tiled MFMA GEMM                          */
+    BG_ALGO_TILED = 3,     /* large-M LDS-tiled MFMA GEMM                          */
+    BG_ALGO_SPLITK = 4     /* W4A16 M <= 64: K split over blocks, needs a workspace */
 } bg_algo;
 
 /*
@@ -80,12 +82,17 @@ typedef enum bg_algo {
  *
  *   w        [N][K] of w_dtype (BG_F32, BG_F16 or BG_BF16), finite values
  *   group    must be 128
- *   qweight  out [N][K/8] uint32; nibble i (bits 4i..4i+3) of word j holds
- *            the code of k = 8j + i
- *   scales   out [N][K/group] FP16 bit patterns
- *   zeros    out [N][K/(2*group)] uint8 (low nibble: even group, high: odd
- *            group) when asymmetric != 0; must be NULL when symmetric
- * Requires N >= 1, K % 256 == 0 (two groups per zeros byte, 16-byte rows).
+ * Output layout (tiled for the GEMM kernels, [LPI] §24 packing order of the
+ * target kernel): 16 output channels x one 128-wide group form a 1 KB tile of
+ * 64 slots x 4 uint32 words.  Weight (n, k) with t = n/16, r = n%16,
+ * g = k/128, c = k%128 lives in slot 16*(c/32) + r, word (c%32)/8, nibble
+ * i/2 (even i) or 4 + i/2 (odd i) for i = k%8 (even k in the low half-word):
+ *   qweight  out [N/16][K/128][64][4] uint32
+ *   scales   out [N/16][K/128][16] FP16 bit patterns, scale of (n, g) at [t][g][r]
+ *   zeros    out [N/16][K/256][16] uint8, zero-points of groups 2h (low
+ *            nibble) and 2h+1 (high nibble) at [t][h][r], when asymmetric != 0;
+ *            must be NULL when symmetric
+ * Requires N % 16 == 0, K % 256 == 0.
  */
 bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, int asymmetric,
                   uint32_t* qweight, uint16_t* scales, uint8_t* zeros, void* stream);
@@ -108,10 +115,40 @@ bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
                      const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                      int64_t N, int group, void* y, void* stream);
 
-/* Same as gemm_w4a16 with an explicit kernel choice (BG_ALGO_*). */
+/* Same as gemm_w4a16 with an explicit kernel choice (BG_ALGO_*; not SPLITK). */
 bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
                         const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                         int64_t N, int group, void* y, int algo, void* stream);
+
+/*
+ * gemm_w4a16_ws -- gemm_w4a16 with a caller-provided device workspace, which
+ * enables the split-K small-M kernel (BG_ALGO_SPLITK, M <= 64; BG_ALGO_AUTO
+ * picks it for M from 8 to 64 where it measured faster than BG_ALGO_SKINNY:
+ * M >= 8 with N >= 16384, M >= 12 with K >= 8192, or M >= 24 with N > 4096).
+ * Splitting K across workgroups lets each workgroup reuse its
+ * activations across 16 weight tiles; FP32 partial tiles are summed in a
+ * fixed order, so results are deterministic.
+ *   workspace        16-byte aligned device memory of at least
+ *                    gemm_w4a16_workspace_bytes(M, N, K, algo) bytes,
+ *                    whose first 256 KiB (per-column-group arrival
+ *                    counters) are zero before its first use; every call
+ *                    leaves them zero again, so the workspace can be reused
+ *                    by later calls of any shape.  The rest holds FP32
+ *                    partial tiles and needs no initialisation.
+ *                    Calls that share a workspace must not overlap in time
+ *                    (same stream, or otherwise ordered).  May be NULL when
+ *                    the required size is 0.
+ *   workspace_bytes  its size; BG_ERR_WORKSPACE if smaller than required.
+ * Other arguments, layouts and errors as gemm_w4a16.
+ */
+bg_status gemm_w4a16_ws(const void* x, int x_dtype, int64_t M, int64_t K,
+                        const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                        int64_t N, int group, void* y, void* workspace, int64_t workspace_bytes,
+                        int algo, void* stream);
+
+/* Workspace bytes gemm_w4a16_ws needs for this shape and kernel choice
+ * (0 if none; BG_ALGO_AUTO = the kernel AUTO selects when given a workspace). */
+int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo);
 
 /*
  * act_quant_int8 -- dynamic symmetric INT8 quantization of a [rows][cols]

@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bitgemm.h")
 
-OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_UNSUP, E_HIP = range(7)
+OK, E_NULL, E_SHAPE, E_ALIGN, E_DTYPE, E_UNSUP, E_HIP, E_WS = range(8)
 F32, F16, BF16, I8, FP8, I32 = range(6)
 
 
@@ -54,6 +54,7 @@ def test_status_strings_and_version(L):
     assert L.bg_status_string(0) == b"ok"
     assert L.bg_status_string(2) == b"unsupported shape"
     assert L.bg_status_string(99) == b"unknown status"
+    assert L.bg_status_string(7) == b"workspace missing or too small"
     assert L.bg_pack_format_version() == 1
 
 
@@ -88,6 +89,20 @@ def test_gemm_w4a16_validation(L):
     assert f(P, BF16, 1, 256, P, Q, None, 16, 256, P, 0, None) == E_UNSUP   # group
     assert f(P, BF16, 1, 256, P, Q + 2, None, 16, 128, P, 0, None) == E_ALIGN
     assert f(P, BF16, 1, 256, P, Q, None, 16, 128, P, 9, None) == E_UNSUP   # algo
+    assert f(P, BF16, 1, 256, P, Q, None, 16, 128, P, 4, None) == E_WS      # split-K needs _ws
+
+
+def test_gemm_w4a16_workspace(L):
+    f = L.gemm_w4a16_ws
+    need = L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 0)
+    assert need > 0 and need % 16 == 0
+    assert L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 3) == 0            # tiled: none
+    assert L.gemm_w4a16_workspace_bytes(1000, 4096, 14336, 0) == 0          # AUTO -> tiled at large M
+    assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, None, 0, 0, None) == E_WS
+    assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, P, need - 16, 0, None) == E_WS
+    assert "needed" in _last(L)
+    assert f(P, BF16, 100, 14336, P, Q, None, 4096, 128, P, P, need, 4, None) == E_SHAPE   # split-K M <= 64
+    assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, P + 8, need, 0, None) == E_ALIGN
 
 
 def test_act_quant_validation(L):

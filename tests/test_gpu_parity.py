@@ -119,10 +119,12 @@ def _w4a16_case(ops, orc, M, N, K, x_dtype, asym, algo, seed, rows=None):
     check_close(yv, ref, orc, f"w4a16 M={M} N={N} K={K} {x_dtype} asym={asym} algo={algo}")
 
 
-@pytest.mark.parametrize("algo", [1, 2, 3])
+@pytest.mark.parametrize("algo", [1, 2, 3, 4])
 @pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 17, 33, 74, 130])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 17, 33, 64, 74, 130])
 def test_w4a16_small(ops, orc, algo, x_dtype, asym, M):
+    if algo == 4 and M > 64:
+        pytest.skip("the split-K kernel serves M <= 64")
     _w4a16_case(ops, orc, M, 272, 768, x_dtype, asym, algo, seed=M)
 
 
@@ -144,25 +146,47 @@ def test_w4a16_decode_shapes(ops, orc, name, B):
     _w4a16_case(ops, orc, B, N, K, "bf16", True, 0, seed=0, rows=rows)
 
 
+def test_w4a16_splitk_workspace_reuse(ops, orc):
+    """One workspace shared by split-K calls of different shapes: the partial
+    tile area may hold anything (here 0xFF bytes); only the counter area must
+    start at zero, and each call leaves it zero again."""
+    cases = [(64, 272, 768), (1, 1024, 1024), (17, 512, 2048), (3, 272, 768), (1, 1024, 1024)]
+    need = max(ops.gemm_w4a16_workspace_bytes(M, N, K, 4) for M, N, K in cases)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[:256 * 1024] = 0
+    for i, (M, N, K) in enumerate(cases):
+        w, x = synth.layer(M, N, K, "bf16", seed=100 + i)
+        p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, True)
+        y = ops.gemm_w4a16(dev_bits(x, "bf16"), p, algo=4, ws=ws)
+        assert "splitk" in ops.last_kernel()
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(ws[:256 * 1024]) == 0
+        qw, s, z = orc.w4_pack(w, 128, True)
+        ref = orc.gemm_w4a16(x, "bf16", qw, s, z)
+        check_close(orc.bits_to_f32(host_bits(y), "bf16").astype(np.float64), ref, orc, f"reuse {M}x{N}x{K}")
+
+
 def test_w4a16_edge_cases(ops, orc):
     N, K = 16, 256
     w = adversarial_weights(N, K, seed=5)
     for asym in (False, True):
         p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, asym)
         qw, s, z = orc.w4_pack(w, 128, asym)
-        for algo in (1, 2, 3):
+        xo = np.zeros((K, K), np.float32)                          # one-hot rows -> weight columns
+        xo[np.arange(K), np.arange(K)] = 1.0
+        xb = torch.from_numpy(xo).to(torch.bfloat16)
+        ref = orc.gemm_w4a16(host_bits(xb), "bf16", qw, s, z)
+        # one-hot rows select one dequantized weight each: exact up to the final BF16 rounding
+        expect = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
+        for algo in (1, 2, 3, 4):
             x = np.zeros((3, K), np.uint16)                       # zero activations
             y = ops.gemm_w4a16(dev_bits(x, "bf16"), p, algo=algo)
             assert torch.count_nonzero(y.float()) == 0
-            xo = np.zeros((K, K), np.float32)                      # one-hot rows -> weight columns
-            xo[np.arange(K), np.arange(K)] = 1.0
-            xb = torch.from_numpy(xo).to(torch.bfloat16)
-            y = ops.gemm_w4a16(xb.cuda(), p, algo=algo)
-            ref = orc.gemm_w4a16(host_bits(xb), "bf16", qw, s, z)
-            yv = orc.bits_to_f32(host_bits(y), "bf16").astype(np.float64)
-            # one-hot rows select one dequantized weight each: exact up to the final BF16 rounding
-            expect = torch.from_numpy(ref).to(torch.bfloat16).double().numpy()
-            assert np.array_equal(yv, expect)
+            step = 64 if algo == 4 else K                         # split-K serves M <= 64
+            for r0 in range(0, K, step):
+                y = ops.gemm_w4a16(xb[r0:r0 + step].contiguous().cuda(), p, algo=algo)
+                yv = orc.bits_to_f32(host_bits(y), "bf16").astype(np.float64)
+                assert np.array_equal(yv, expect[r0:r0 + step]), (asym, algo, r0)
 
 
 # ----------------------------------------------------------------- act_quant ----
