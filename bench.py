@@ -169,10 +169,13 @@ def main():
     dom = max(by_kernel, key=lambda k: by_kernel[k][0])
     t_dom, b_dom, n_dom = by_kernel[dom]
     achieved = b_dom / (t_dom * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
     roof = {"bound": "hbm", "kernel": dom, "launches_per_step": n_dom,
             "bytes_per_launch": b_dom / n_dom, "avg_launch_us": t_dom / n_dom * 1e3,
             "achieved": round(achieved, 1), "peak": roofline.HBM_GBPS, "unit": "GB/s",
-            "frac": round(achieved / roofline.HBM_GBPS, 4), "traffic": None}
+            "frac": round(achieved / roofline.HBM_GBPS, 4),
+            "traffic": None if traffic is None else round(traffic)}
+    calibration_copy(torch, dev)
 
     out = {
         "metric": "W4A16/W8A8 linear: HBM GB/s at B=1..16, TFLOPS at M=2048; % of roofline",
@@ -197,6 +200,52 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w_host, xs, calls, args.cpu_seconds, np, synth, roofline)
 
     print(json.dumps(out), flush=True)
+
+
+CALIB_BYTES = 512 << 20
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "hbm_traffic_w4a16_decode_llama3_8b.md")
+
+
+def calibration_copy(torch, dev):
+    """A plain copy of known size (torch.neg over 512 MiB of FP32: reads and
+    writes CALIB_BYTES each) that hardware-counter runs of this script use to
+    scale FETCH_SIZE / WRITE_SIZE to bytes.  Not part of any timed region."""
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def library_digest() -> str:
+    """sha256 over the HIP sources, so counters taken on other code are not reused."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "bit_gemm_w4_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the calibration copy), or None
+    when there is none for this kernel or the sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = library_digest()
+    for line in open(TRAFFIC_FILE):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == f"`{kernel}`" and cells[1] == digest:
+            try:
+                return float(cells[6])
+            except ValueError:
+                return None
+    return None
 
 
 def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph):
