@@ -2,21 +2,15 @@
 //
 // "Quantization throughput by method" (hrletsgo.me), W8A8/FP8 section: weights
 // and activations both in 8 bits, the GEMM runs on the low-precision matrix
-// cores with no upcast.  "Low-precision LLM inference" §9 (FP8 GEMM contract:
-// operand formats, scale mode and shape, accumulator/output dtype), §22
-// (INT32 / FP32 accumulators), §8 block scaling.
+// cores with no upcast.  "Low-precision LLM inference" §8 (scale recipe and
+// 128-wide block scaling), §14 (W8A8), §22 (INT32 / FP32 accumulators).
 //
-// Y = A W^T, A [M][K], W [N][K], both K-contiguous.  INT8 uses
-// v_mfma_i32_16x16x64_i8 (exact INT32 accumulators), FP8 uses
-// v_mfma_f32_16x16x128_f8f6f4 with both operands E4M3 (one instruction covers
-// a whole 128-wide scale block).  Block tile BM x BN x 128, four waves as
-// WM x WN, A and W tiles staged in LDS with the 16-byte chunk index XOR-ed by
-// (row & 7) so that the 8 lanes served per LDS cycle hit distinct banks.
-//
-// Operand k-assignment: lane quarter q = lane/16 supplies bytes
-// [16*(4kk+q), +16) (INT8, K step kk = 0..1) or [32q, +32) (FP8); A and W use
-// the same assignment, so matching k are multiplied.  Output: lane l,
-// register e of a 16x16 tile is row 4(l/16)+e, column l%16.
+// Y = A W^T, A [M][K], W [N][K], both K-contiguous.  Two kernels:
+//  * k_w8a8_mfma, small M: 16x16 MFMA tiles (v_mfma_i32_16x16x64_i8,
+//    v_mfma_f32_16x16x128_f8f6f4), one 128-wide K step per LDS fill;
+//  * k_w8a8_gemm, large M: 32x32 MFMA tiles, multi-stage LDS pipeline (below).
+// In both, the K assignment of operand bytes to lanes is the same for A and W,
+// so matching k are multiplied whatever the hardware's own k order is.
 #include <type_traits>
 
 #include "bg_device.h"
@@ -174,6 +168,328 @@ __global__ __launch_bounds__(256) void k_w8a8_mfma(const uint8_t* __restrict__ a
         }
 }
 
+// ============================================================================
+// Large-M GEMM.  Block tile BM x BN; K advances in stages of 64 bytes (one LDS
+// row per operand row), NB stage buffers (5 when they fit in 160 KB, else 4),
+// so NB - 2 stages are in flight while one is read.  Global -> LDS copies are
+// buffer_load_dwordx4 ... lds (no trip through VGPRs): lane i of a wave writes
+// bytes [16i, 16i+16) of a 1 KB LDS run = 16 rows x 64 bytes, so the 16-byte
+// chunk swizzle is applied on the global side (lane i fetches chunk
+// (i & 3) ^ swz(row)).  swz(r) = ((r >> 1) ^ (r >> 3)) & 3 keeps the 8 or 16
+// rows read together by one ds_read_b128 phase on distinct banks.
+// Four waves as 2 x 2; each owns a (BM/2) x (BN/2) tile of 32x32 MFMA tiles:
+// v_mfma_i32_32x32x32_i8 (lane l supplies 16 bytes of row l%32: chunk l/32
+// in the first half of the stage, 2 + l/32 in the second) or
+// v_mfma_f32_32x32x64_f8f6f4 (32 bytes: both chunks).  The W fragment is the
+// first operand, so output lane l, register e holds row l%32 of the A tile
+// and column 8(e/4) + 4(l/32) + e%4 of the W tile.
+// Block order: blocks are dealt round-robin to the 8 XCDs, so block b is
+// remapped to tile (b % 8) * (tiles / 8) + b / 8, giving each XCD a contiguous
+// run of tiles; runs are ordered in bands of 8 row tiles, so the ~32 blocks
+// resident on one XCD share A row tiles and W column tiles in its L2.
+// ============================================================================
+constexpr int GK = 64;                                           // K bytes per stage
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int gswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// 16 bytes per lane from a buffer resource into LDS: lane i writes dst + 16 i.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
+                                              int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS reads of operand fragments are issued as inline assembly: the
+// compiler's wait insertion cannot see which copy into LDS a read depends on
+// and would drain all copies in flight before every read.  The kernel orders
+// them itself -- s_waitcnt vmcnt before the block barrier that publishes a
+// stage, s_waitcnt lgkmcnt(0) before the fragments are used (each fragment is
+// passed through an empty asm after the wait, so no MFMA can move above it).
+__device__ __forceinline__ int4_t ds_read16(uint32_t addr) {
+    int4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void settle(int4_t& v) { asm volatile("" : "+v"(v)); }
+
+template <int TM, int TN>
+struct Frags {
+    int4_t a[TM][2], b[TN][2];                  // two 16-byte K chunks per 32-row fragment
+};
+
+template <bool FP8, bool BLOCK, int BM, int BN>
+__global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
+                                                      int a_gran, const uint8_t* __restrict__ w,
+                                                      const float* __restrict__ ws, int w_gran, int64_t M,
+                                                      int64_t N, int64_t K, void* __restrict__ y, int out_dt) {
+    constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+    constexpr int ROWS = BM + BN;                                // LDS rows per stage
+    constexpr int STAGE_BYTES = ROWS * GK;
+    constexpr int LOADS = ROWS / 64;                             // 1 KB wave-loads per wave per stage
+    constexpr int NB = (160 * 1024) / STAGE_BYTES >= 5 ? 5 : 4;  // stage buffers
+    static_assert(ROWS % 64 == 0 && BM % 32 == 0 && BN % 32 == 0, "tile shape");
+    static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
+    static_assert((NB - 2) * LOADS < 64, "vmcnt range");
+    constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
+    constexpr int EPI_BYTES = 4 * WTM * EPI_PITCH;
+    constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // ---- tile of this block ----
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int nt = tiles_m * tiles_n;
+    int pid = blockIdx.x;
+    if (nt % 8 == 0) pid = (pid % 8) * (nt / 8) + pid / 8;
+    constexpr int GROUP_M = 8;
+    const int band = pid / (GROUP_M * tiles_n);
+    const int local = pid - band * GROUP_M * tiles_n;
+    const int first_m = band * GROUP_M;
+    const int gsz = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
+    const int tm = first_m + local % gsz, tn = local / gsz;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    // ---- global -> LDS copies (rows past M or N read as zero) ----
+    const int64_t rows_a = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a + m0 * K), (short)0,
+                                                      (int)(rows_a * K), 0x00020000);
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + n0 * K), (short)0,
+                                                      (int)(rows_w * K), 0x00020000);
+    uint32_t voff[LOADS];
+#pragma unroll
+    for (int t = 0; t < LOADS; ++t) {
+        const int j = wave * LOADS + t;                          // wave-load index in the stage
+        const int r = (j < BM / 16 ? 16 * j : 16 * (j - BM / 16)) + (lane >> 2);
+        voff[t] = (uint32_t)(r * K) + (uint32_t)((((lane & 3) ^ gswz(r)) << 4));
+    }
+    const int nkb = (int)(K / GK);
+    // Stage kb goes to buffer kb % NB.  Stages past the end load bytes into a
+    // free buffer that is never consumed.
+    auto issue = [&](int kb) {
+        uint8_t* buf = lds + (kb % NB) * STAGE_BYTES;
+        const int soff = kb * GK;
+#pragma unroll
+        for (int t = 0; t < LOADS; ++t) {
+            const int j = wave * LOADS + t;
+            copy16_to_lds(j < BM / 16 ? ra : rw, buf + j * 16 * GK, voff[t], soff);
+        }
+    };
+
+    // ---- fragment addresses: lane l reads chunks h and 2 + h of row l % 32 ----
+    // (the same K chunks for A and W, so matching k meet in the MFMA).  The
+    // swizzle of row r depends on bits 1..4 of r only, so fragments 32 rows
+    // apart differ by a constant 2 KB.
+    const uint32_t lds0 = lds_addr(lds);
+    const int ra0 = wm * WTM + l32, rb0 = BM + wn * WTN + l32;
+    const uint32_t offa0 = (uint32_t)(ra0 * GK + ((h ^ gswz(ra0)) << 4));
+    const uint32_t offa1 = (uint32_t)(ra0 * GK + (((2 + h) ^ gswz(ra0)) << 4));
+    const uint32_t offb0 = (uint32_t)(rb0 * GK + ((h ^ gswz(rb0)) << 4));
+    const uint32_t offb1 = (uint32_t)(rb0 * GK + (((2 + h) ^ gswz(rb0)) << 4));
+    // read number r of a stage (0 .. 2(TM+TN)-1): A fragments first, then W
+    auto read_one = [&](Frags<TM, TN>& f, uint32_t base, int r) {
+        const int frag = r >> 1, c = r & 1;
+        if (frag < TM)
+            f.a[frag][c] = ds_read16(base + (c ? offa1 : offa0) + (uint32_t)(frag * 32 * GK));
+        else
+            f.b[frag - TM][c] = ds_read16(base + (c ? offb1 : offb0) + (uint32_t)((frag - TM) * 32 * GK));
+    };
+    auto stage_base = [&](int kb) { return lds0 + (uint32_t)((kb % NB) * STAGE_BYTES); };
+    auto settle_frags = [&](Frags<TM, TN>& f) {
+        wait_lgkm0();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) settle(f.a[i][0]), settle(f.a[i][1]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) settle(f.b[j][0]), settle(f.b[j][1]);
+    };
+
+    using acc_t = typename std::conditional<FP8, float16_t, int16_t_v>::type;
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
+    float16_t facc[BLOCK ? TM : 1][BLOCK ? TN : 1];
+    if constexpr (BLOCK) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) facc[i][j] = float16_t{};
+    }
+    // every second stage closes a 128-wide K block: facc += partial * s_a[m][kb] * s_w[n/128][kb]
+    auto close_block = [&](int kb) {
+        if constexpr (BLOCK) {
+            const int64_t nkb128 = K >> 7, kb128 = kb >> 1;
+            const int64_t nb = (n0 + wn * WTN) >> 7;
+            const float sw = n0 + wn * WTN < N ? ws[nb * nkb128 + kb128] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int64_t m = m0 + wm * WTM + i * 32 + l32;
+                const float sc = (m < M ? as[m * nkb128 + kb128] : 0.0f) * sw;
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) facc[i][j][e] += acc[i][j][e] * sc;
+                    acc[i][j] = acc_t{};
+                }
+            }
+        }
+    };
+
+    // One step: stage kb's fragments were requested into `cur`; after they
+    // land, the barrier (a) shows every wave holds its stage-kb fragments, so
+    // the buffer of stage kb-1 is free and receives stage kb+NB-1, and (b)
+    // publishes stage kb+1, whose fragment reads are then spread between the
+    // MFMAs of stage kb.
+    constexpr int NREAD = 2 * (TM + TN);
+    constexpr int NMFMA = FP8 ? TM * TN : 2 * TM * TN;
+    auto step = [&](Frags<TM, TN>& cur, Frags<TM, TN>& nxt, int kb) {
+        settle_frags(cur);
+        wait_vmcnt<(NB - 3) * LOADS>();                          // this wave's copies of stage kb+1 landed
+        block_barrier();
+        issue(kb + NB - 1);
+        const uint32_t nb_base = stage_base(kb + 1);
+#pragma unroll
+        for (int t = 0; t < NMFMA; ++t) {
+            if constexpr (FP8) {
+                const int i = t / TN, j = t % TN;
+                const int8_t_v av = __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                const int8_t_v bv = __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+            } else {
+                const int half = t / (TM * TN), i = (t % (TM * TN)) / TN, j = t % TN;
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.b[j][half], cur.a[i][half], acc[i][j], 0, 0, 0);
+            }
+            // reads t*NREAD/NMFMA .. (t+1)*NREAD/NMFMA - 1 go with MFMA t (every read
+            // exactly once); the scheduling barrier keeps the compiler from regrouping them
+#pragma unroll
+            for (int r = t * NREAD / NMFMA; r < (t + 1) * NREAD / NMFMA; ++r) read_one(nxt, nb_base, r);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (BLOCK && (kb & 1)) close_block(kb);
+    };
+
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t) issue(t);
+    wait_vmcnt<(NB - 2) * LOADS>();
+    block_barrier();
+    Frags<TM, TN> f0, f1;
+#pragma unroll
+    for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(0), r);
+    for (int kb = 0; kb < nkb; kb += 2) {                        // K is a multiple of 128: nkb is even
+        step(f0, f1, kb);
+        step(f1, f0, kb + 1);
+    }
+    wait_vmcnt<0>();                                             // no copy may land after the block exits
+    wait_lgkm0();
+
+    // ---- epilogue ----
+    // The W fragment is the MFMA's first operand, so lane l, register e of
+    // tile (i, j) holds output row m = 32i + l%32 and column
+    // n = 32j + 8(e/4) + 4(l/32) + e%4: four consecutive columns per group.
+    // Scales: one per row (TENSOR or ROW), four consecutive per column group.
+    // 16-bit outputs are staged per wave in LDS (rows padded by 16 bytes) and
+    // written back as 16-byte row segments; FP32 / INT32 go out directly as
+    // 16-byte groups.
+    block_barrier();                                             // all waves done with the stage buffers
+    const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+    const bool out16 = out_dt == O_BF16 || out_dt == O_F16;
+    uint8_t* stage = lds + wave * WTM * EPI_PITCH;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int64_t m = mw + i * 32 + l32;
+        const bool m_ok = m < M;
+        float sa = 1.0f;
+        if (!BLOCK && out_dt != O_I32) sa = a_gran == GT ? as[0] : (m_ok ? as[m] : 0.0f);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;          // first of four columns
+                const bool n_ok = n < N;                                 // N % 16 == 0: all four or none
+                float v[4];
+                if (!FP8 && out_dt == O_I32) {
+                    if (m_ok && n_ok) {
+                        int4_t o;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) o[r] = (int)acc[i][j][4 * q4 + r];
+                        *reinterpret_cast<int4_t*>(static_cast<int32_t*>(y) + m * N + n) = o;
+                    }
+                    continue;
+                }
+                float4 sw4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+                if (!BLOCK) {
+                    if (w_gran == GT) sw4 = make_float4(ws[0], ws[0], ws[0], ws[0]);
+                    else if (n_ok) sw4 = *reinterpret_cast<const float4*>(ws + n);
+                }
+                const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (BLOCK) v[r] = facc[i][j][4 * q4 + r];
+                    else v[r] = ((float)acc[i][j][4 * q4 + r] * sa) * swv[r];
+                }
+                if (out16) {
+                    uint2 packed;
+                    if (out_dt == O_BF16) {
+                        packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                        packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    } else {
+                        packed.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+                        packed.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+                    }
+                    *reinterpret_cast<uint2*>(stage + (i * 32 + l32) * EPI_PITCH + (j * 32 + 8 * q4 + 4 * h) * 2) =
+                        packed;
+                } else if (m_ok && n_ok) {
+                    *reinterpret_cast<float4*>(static_cast<float*>(y) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+                }
+            }
+    }
+    if (out16) {
+        // this wave's WTM x WTN tile, row by row: WTN * 2 bytes = WTN / 8 lanes per row
+        constexpr int LPR = WTN / 8, RPI = 64 / LPR;             // lanes per row, rows per instruction
+        const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll 4
+        for (int r0 = 0; r0 < WTM; r0 += RPI) {
+            const int r = r0 + rr;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * EPI_PITCH + cc * 16);
+            const int64_t m = mw + r, n = nw + cc * 8;
+            if (m < M && n < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + m * N + n) = v;
+        }
+    }
+}
+
+template <bool FP8, bool BLOCK, int BM, int BN>
+static const char* gemm_cfg(const W8A8Args& g, hipStream_t s) {
+    const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
+                       g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt);
+    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN);
+}
+
 template <bool FP8, bool BLOCK, int BM, int BN, int WM, int WN>
 static const char* cfg(const W8A8Args& g, hipStream_t s) {
     dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM));
@@ -191,7 +507,27 @@ static const char* dispatch(const W8A8Args& g, hipStream_t s) {
     return cfg<true, false, BM, BN, WM, WN>(g, s);
 }
 
-const char* launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) { return dispatch<128, 128, 2, 2>(g, s); }
+// Tile choice for the large-M GEMM: estimated time = rounds of resident
+// blocks x time of one round.  Relative round times (K fixed) measured on the
+// 4096..28672-wide projection shapes: 256 x 256 (one block per CU) 75,
+// 256 x 128 (one per CU) 46.4; 128 x 128 (two per CU, 47) never won on that
+// model, so only block-scaled FP8, which keeps two accumulator sets, uses it.
+template <int BM, int BN>
+static const char* gemm_dispatch(const W8A8Args& g, hipStream_t s) {
+    if (!g.in_fp8) return gemm_cfg<false, false, BM, BN>(g, s);
+    return gemm_cfg<true, false, BM, BN>(g, s);
+}
+
+const char* launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) {
+    if (g.in_fp8 && g.a_gran == GR128) return gemm_cfg<true, true, 128, 128>(g, s);
+    auto cost = [&](int64_t bm, int64_t bn, double round) {
+        const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
+        return (double)((tiles + 255) / 256) * round;
+    };
+    if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) return gemm_dispatch<256, 256>(g, s);
+    return gemm_dispatch<256, 128>(g, s);
+}
+
 const char* launch_w8a8_skinny(const W8A8Args& g, hipStream_t s) { return dispatch<16, 128, 1, 4>(g, s); }
 
 }  // namespace bg
