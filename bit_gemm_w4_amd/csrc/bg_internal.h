@@ -48,8 +48,8 @@ const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, 
 const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                          const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
 // Split-K small-M kernel (M <= 64): needs a workspace of
-// w4a16_splitk_workspace(M, N, K) bytes (0: none) whose leading counter area
-// is zero on entry; it is left zero on return.
+// w4a16_splitk_workspace(M, N, K) bytes (0: none), any contents; enqueues
+// the partial-product kernel and, when K is split, the reduction kernel.
 int64_t w4a16_splitk_workspace(int64_t M, int64_t N, int64_t K);
 const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                                 const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws,

@@ -62,7 +62,7 @@ int w8_auto_algo(int64_t M) { return M <= kW8SkinnyMax ? BG_ALGO_SKINNY : BG_ALG
 // the 4096/14336-wide projection shapes.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
     if (M > kW4SkinnyMax) return BG_ALGO_TILED;
-    const bool split = (M >= 8 && N >= 16384) || (M >= 12 && K >= 8192) || (M >= 24 && N > 4096);
+    const bool split = (M >= 8 && (N >= 16384 || K >= 8192)) || (M >= 12 && N > 4096) || M >= 24;
     return split ? BG_ALGO_SPLITK : BG_ALGO_SKINNY;
 }
 

@@ -376,25 +376,20 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
 // stages only its K-slice of the activation rows in LDS -- once, shared by
 // its 16 waves -- and every wave streams the slice of ONE weight tile, so the
 // activation bytes each CU reads are amortised over 16 tiles (at M = 16 the
-// activations of a group are 4x the bytes of one weight tile).  The FP32
-// partial tiles of the S slices go to the workspace; the block that
-// completes a column group last (atomic counter per group) adds the S
-// partials in slice order -- a fixed order, so results do not depend on
-// timing -- writes the output and resets the counter, leaving the workspace
-// ready for the next call.  Nothing waits on another block, so no block can
-// stall the grid.
-//
-// Workspace: SPK_COUNTERS ints of counters at offset 0 (a fixed place, so a
-// workspace reused for calls of other shapes never finds counters in memory
-// that held partial tiles), then the partial tiles.  Only rows < M of a
-// partial tile are written and read back.
+// activations of a group are 4x the bytes of one weight tile).  With S = 1 the
+// block writes the output; otherwise it writes its FP32 partial tile (rows
+// < M only) to the workspace and k_w4a16_splitk_reduce, launched next on the
+// same stream, adds the S partials in slice order -- a fixed order, so
+// results do not depend on timing.  Stream order makes the partials visible
+// to the second kernel; an in-kernel handoff would need a device-scope
+// release/acquire per block, which on a multi-L2 device writes back and
+// invalidates whole caches and measured slower than the second launch.
 //
 // Inner product as in the MFMA variant of k_w4a16_decode; Sx_g comes from a
 // table the block builds next to the staged activations.
 // ============================================================================
 constexpr int SPK_NW = 16;
 constexpr int SPK_STAGES = 4;
-constexpr int SPK_COUNTERS = 65536;         // one per column group: N <= 2^24 gives at most 65536
 
 struct SpkStage {
     uint4 w;
@@ -429,7 +424,6 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
     const int xpitch = ng * 128 + 8;                                   // halves per staged row
     uint16_t* xl = reinterpret_cast<uint16_t*>(dyn_lds);
     float* sxt = reinterpret_cast<float*>(dyn_lds + rows * xpitch * 2);   // Sx[group][row]
-    int* last_block = reinterpret_cast<int*>(sxt + ng * BAND);               // one flag after the table
 
     const int zb0 = g0 >> 1;
     const int zb1 = (g0 + ng - 1) >> 1;
@@ -527,38 +521,35 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
         for (int i = 0; i < TM; ++i) store_y(i, acc[i]);
         return;
     }
-    // ---- partial tile -> workspace; the last block of the column group reduces ----
+    // ---- partial tile -> workspace (summed by k_w4a16_splitk_reduce) ----
     const int64_t tiles_pad = (int64_t)gridDim.x * NW;
-    int* counters = reinterpret_cast<int*>(ws);
-    float* part = ws + SPK_COUNTERS;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
         if (16 * i + 4 * q < M)
-            *reinterpret_cast<float4_t*>(part + (((int64_t)sl * tiles_pad + tile) * TM + i) * 256 + lane * 4) =
-                acc[i];
-    // Each wave waits until its partial stores are complete at its L2, so the
-    // single agent-scope acquire-release add below (one wave per block: its
-    // release writes back the L2 lines of all 16 waves, its acquire
-    // invalidates stale lines for the whole block) publishes the block's
-    // partials and, for the last block, makes the others' visible.  One
-    // release/acquire per block instead of one per wave: those are
-    // whole-cache operations on a multi-L2 device.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (threadIdx.x == 0)
-        *last_block = __hip_atomic_fetch_add(counters + cg, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
-    __syncthreads();
-    if (!*last_block) return;
+            *reinterpret_cast<float4_t*>(ws + (((int64_t)sl * tiles_pad + tile) * TM + i) * 256 + lane * 4) = acc[i];
+}
+
+// Sum of the S partial tiles of the split-K kernel, in slice order.  One
+// thread per (tile, 16-row band, lane): the lane's four rows of one column.
+template <bool BF16, int TM>
+__global__ __launch_bounds__(256) void k_w4a16_splitk_reduce(const float* __restrict__ ws, int S, int64_t tiles_pad,
+                                                             int64_t M, int64_t N, uint16_t* __restrict__ y) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (tile, i, lane)
+    const int lane = (int)(t & 63);
+    const int64_t ti = t >> 6;
+    const int i = (int)(ti % TM);
+    const int64_t tile = ti / TM;
+    const int q = lane >> 4, l16 = lane & 15;
+    if (tile * 16 >= N || 16 * i + 4 * q >= M) return;
+    const int64_t slice = tiles_pad * TM * 256;
+    const float* p = ws + (tile * TM + i) * 256 + lane * 4;
+    float4_t v = *reinterpret_cast<const float4_t*>(p);
+    for (int s2 = 1; s2 < S; ++s2) v += *reinterpret_cast<const float4_t*>(p + s2 * slice);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        if (16 * i + 4 * q >= M) continue;
-        float4_t v = float4_t{0, 0, 0, 0};
-        for (int s2 = 0; s2 < S; ++s2)
-            v += *reinterpret_cast<const float4_t*>(part + (((int64_t)s2 * tiles_pad + tile) * TM + i) * 256 +
-                                                    lane * 4);
-        store_y(i, v);
+    for (int e = 0; e < 4; ++e) {
+        const int64_t m = 16 * i + 4 * q + e;
+        if (m < M) y[m * N + tile * 16 + l16] = to_out<BF16>(v[e]);
     }
-    if (threadIdx.x == 0) atomicExch(counters + cg, 0);
 }
 
 // ============================================================================
@@ -804,8 +795,8 @@ static SplitCfg splitk_cfg(int64_t M, int64_t N, int64_t K) {
     S = (ngroups + gs - 1) / gs;
     c.S = (int)S;
     c.gs = (int)gs;
-    c.lds_bytes = rows * (gs * 128 + 8) * 2 + gs * 16 * c.TM * 4 + 16;
-    c.ws_bytes = S > 1 ? SPK_COUNTERS * 4 + S * c.colgroups * SPK_NW * c.TM * 1024 : 0;
+    c.lds_bytes = rows * (gs * 128 + 8) * 2 + gs * 16 * c.TM * 4;
+    c.ws_bytes = S > 1 ? S * c.colgroups * SPK_NW * c.TM * 1024 : 0;
     return c;
 }
 
@@ -820,6 +811,12 @@ static const char* splitk_launch(const SplitCfg& c, const void* x, int64_t M, in
     hipLaunchKernelGGL(kern, dim3((unsigned)c.colgroups, (unsigned)c.S), dim3(SPK_NW * 64), (size_t)c.lds_bytes, s,
                        static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y),
                        static_cast<float*>(ws), c.S, c.gs);
+    if (c.S > 1) {
+        const int64_t tiles_pad = (int64_t)c.colgroups * SPK_NW;
+        const int64_t threads = tiles_pad * TM * 64;
+        hipLaunchKernelGGL((k_w4a16_splitk_reduce<BF16, TM>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(ws), c.S, tiles_pad, M, N, static_cast<uint16_t*>(y));
+    }
     return kname("k_w4a16_splitk", BF16, TM);
 }
 

@@ -140,14 +140,13 @@ _workspaces: dict = {}
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
-    """A device workspace of at least nbytes, cached per device, zero-filled
-    when allocated.  The library leaves its counter area zeroed after every
-    call; calls sharing it must not overlap in time (use one per stream when
-    streams run concurrently)."""
+    """A device workspace of at least nbytes, cached per device.  It needs no
+    initialisation; calls sharing it must not overlap in time (use one per
+    stream when streams run concurrently)."""
     key = torch.device(device).index or 0
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

@@ -124,20 +124,17 @@ bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
  * gemm_w4a16_ws -- gemm_w4a16 with a caller-provided device workspace, which
  * enables the split-K small-M kernel (BG_ALGO_SPLITK, M <= 64; BG_ALGO_AUTO
  * picks it for M from 8 to 64 where it measured faster than BG_ALGO_SKINNY:
- * M >= 8 with N >= 16384, M >= 12 with K >= 8192, or M >= 24 with N > 4096).
+ * M >= 8 with N >= 16384 or K >= 8192, M >= 12 with N > 4096, or M >= 24).
  * Splitting K across workgroups lets each workgroup reuse its
- * activations across 16 weight tiles; FP32 partial tiles are summed in a
+ * activations across 16 weight tiles; the FP32 partial tiles go to the
+ * workspace and a second kernel, enqueued on the same stream, sums them in a
  * fixed order, so results are deterministic.
  *   workspace        16-byte aligned device memory of at least
- *                    gemm_w4a16_workspace_bytes(M, N, K, algo) bytes,
- *                    whose first 256 KiB (per-column-group arrival
- *                    counters) are zero before its first use; every call
- *                    leaves them zero again, so the workspace can be reused
- *                    by later calls of any shape.  The rest holds FP32
- *                    partial tiles and needs no initialisation.
- *                    Calls that share a workspace must not overlap in time
- *                    (same stream, or otherwise ordered).  May be NULL when
- *                    the required size is 0.
+ *                    gemm_w4a16_workspace_bytes(M, N, K, algo) bytes.  It
+ *                    needs no initialisation and its contents afterwards
+ *                    are unspecified.  Calls that share a workspace must
+ *                    not overlap in time (same stream, or otherwise
+ *                    ordered).  May be NULL when the required size is 0.
  *   workspace_bytes  its size; BG_ERR_WORKSPACE if smaller than required.
  * Other arguments, layouts and errors as gemm_w4a16.
  */

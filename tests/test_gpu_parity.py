@@ -147,20 +147,18 @@ def test_w4a16_decode_shapes(ops, orc, name, B):
 
 
 def test_w4a16_splitk_workspace_reuse(ops, orc):
-    """One workspace shared by split-K calls of different shapes: the partial
-    tile area may hold anything (here 0xFF bytes); only the counter area must
-    start at zero, and each call leaves it zero again."""
+    """One workspace shared by split-K calls of different shapes; it starts
+    filled with 0xFF bytes (NaN as FP32): the workspace needs no
+    initialisation and no call depends on what an earlier one left in it."""
     cases = [(64, 272, 768), (1, 1024, 1024), (17, 512, 2048), (3, 272, 768), (1, 1024, 1024)]
     need = max(ops.gemm_w4a16_workspace_bytes(M, N, K, 4) for M, N, K in cases)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
-    ws[:256 * 1024] = 0
     for i, (M, N, K) in enumerate(cases):
         w, x = synth.layer(M, N, K, "bf16", seed=100 + i)
         p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, True)
         y = ops.gemm_w4a16(dev_bits(x, "bf16"), p, algo=4, ws=ws)
         assert "splitk" in ops.last_kernel()
         torch.cuda.synchronize()
-        assert torch.count_nonzero(ws[:256 * 1024]) == 0
         qw, s, z = orc.w4_pack(w, 128, True)
         ref = orc.gemm_w4a16(x, "bf16", qw, s, z)
         check_close(orc.bits_to_f32(host_bits(y), "bf16").astype(np.float64), ref, orc, f"reuse {M}x{N}x{K}")
