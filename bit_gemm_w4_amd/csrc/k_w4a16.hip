@@ -21,68 +21,9 @@
 // their natural order: no permutation is needed on either operand.
 #include "bg_device.h"
 #include "bg_internal.h"
+#include "bg_w4.h"
 
 namespace bg {
-
-template <bool BF16>
-struct W4Magic;
-template <>
-struct W4Magic<true> {
-    static constexpr uint32_t bits = 0x43004300u;  // BF16 128.0 in both halves
-    static constexpr float value = 128.0f;
-    static constexpr uint32_t ones = 0x3F803F80u;  // BF16 1.0 pair
-};
-template <>
-struct W4Magic<false> {
-    static constexpr uint32_t bits = 0x64006400u;  // FP16 1024.0 in both halves
-    static constexpr float value = 1024.0f;
-    static constexpr uint32_t ones = 0x3C003C00u;  // FP16 1.0 pair
-};
-
-// dot2 of two packed 16-bit pairs into an FP32 accumulator.
-template <bool BF16>
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-    if constexpr (BF16)
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a),
-                                               __builtin_bit_cast(bf162_t, b), c, false);
-    else
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
-                                      false);
-}
-
-// (a & b) | c in one v_and_or_b32 (the compiler otherwise emits and + or).
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
-    return d;
-}
-
-// The four (MV+u[2p], MV+u[2p+1]) pairs of one packed word: 3 shifts + 4 and_or.
-template <bool BF16>
-__device__ __forceinline__ void dequant_word(uint32_t w, uint32_t D[4]) {
-    constexpr uint32_t m = W4Magic<BF16>::bits;
-    D[0] = and_or(w, 0x000F000Fu, m);
-    D[1] = and_or(w >> 4, 0x000F000Fu, m);
-    D[2] = and_or(w >> 8, 0x000F000Fu, m);
-    D[3] = and_or(w >> 12, 0x000F000Fu, m);
-}
-
-template <bool BF16>
-__device__ __forceinline__ float4_t mfma16(const uint32_t a[4], const uint32_t b[4], float4_t c) {
-    const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
-    const uint4 bv = make_uint4(b[0], b[1], b[2], b[3]);
-    if constexpr (BF16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf168_t, av), __builtin_bit_cast(bf168_t, bv),
-                                                       c, 0, 0, 0);
-    else
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av), __builtin_bit_cast(half8_t, bv),
-                                                      c, 0, 0, 0);
-}
-
-template <bool BF16>
-__device__ __forceinline__ uint16_t to_out(float v) {
-    return BF16 ? f32_to_bf16(v) : f32_to_f16(v);
-}
 
 // ============================================================================
 // Small-M kernel (decode).  A block owns 16*TN output columns (TN weight tiles)
@@ -552,120 +493,6 @@ __global__ __launch_bounds__(256) void k_w4a16_splitk_reduce(const float* __rest
     }
 }
 
-// ============================================================================
-// Large-M MFMA kernel.  Block tile BM x BN, one 128-wide group per K step;
-// 4 waves as WM x WN, each wave TM x TN 16x16 tiles.  The activation tile is
-// staged in LDS (XOR-swizzled 16-byte chunks so the 16 rows read by one MFMA
-// operand hit distinct banks); each lane reads its packed weights straight
-// from HBM (16 bytes = its quarter of a group row) and dequantizes them in
-// registers (slot `lane` of the tile, one contiguous 1 KB load per wave).
-// k assignment and the Sx MFMA as in k_w4a16_decode.
-// ============================================================================
-template <bool BF16, int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_w4a16_mfma(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                    const uint32_t* __restrict__ qw,
-                                                    const uint16_t* __restrict__ sc,
-                                                    const uint8_t* __restrict__ zr, int64_t N,
-                                                    uint16_t* __restrict__ y) {
-    static_assert(WM * WN == 4, "four waves");
-    constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int TM = WTM / 16, TN = WTN / 16;
-    constexpr float MV = W4Magic<BF16>::value;
-    constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_a[BM * 256];
-
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int l16 = lane & 15, q = lane >> 4;
-    const int64_t m_blk = (int64_t)blockIdx.y * BM, n_blk = (int64_t)blockIdx.x * BN;
-    const int64_t ngroups = K >> 7;
-    const uint32_t ones[4] = {ONE2, ONE2, ONE2, ONE2};
-
-    float4_t acc[TM][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = float4_t{0, 0, 0, 0};
-
-    for (int64_t g = 0; g < ngroups; ++g) {
-        // ---- stage the BM x 128 activation tile (16 chunks of 16 B per row) ----
-        __syncthreads();
-        for (int c = threadIdx.x; c < BM * 16; c += 256) {
-            const int r = c >> 4, ch = c & 15;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (m_blk + r < M) v = *reinterpret_cast<const uint4*>(x + (m_blk + r) * K + g * 128 + ch * 8);
-            *reinterpret_cast<uint4*>(lds_a + r * 256 + ((ch ^ (r & 15)) << 4)) = v;
-        }
-        // ---- this lane's packed weights for the group: 16 B per n-tile ----
-        uint4 wv[TN];
-        float scale[TN], corr[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t t = (n_blk + wn * WTN + j * 16) >> 4;     // weight tile (16 columns)
-            if (t < (N >> 4)) {
-                wv[j] = *reinterpret_cast<const uint4*>(qw + ((t * ngroups + g) * 64 + lane) * 4);
-                scale[j] = f16_to_f32(sc[(t * ngroups + g) * 16 + l16]);
-                corr[j] = MV + (float)(zr ? (zr[(t * (ngroups >> 1) + (g >> 1)) * 16 + l16] >> (4 * (g & 1))) & 0xF : 8);
-            } else {
-                wv[j] = make_uint4(0, 0, 0, 0);
-                scale[j] = 0.0f;
-                corr[j] = 0.0f;
-            }
-        }
-        __syncthreads();
-
-        float4_t part[TM][TN], sx[TM];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            sx[i] = float4_t{0, 0, 0, 0};
-#pragma unroll
-            for (int j = 0; j < TN; ++j) part[i][j] = float4_t{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            uint32_t bfrag[TN][4];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t w = kk == 0 ? wv[j].x : kk == 1 ? wv[j].y : kk == 2 ? wv[j].z : wv[j].w;
-                dequant_word<BF16>(w, bfrag[j]);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * WTM + i * 16 + l16;
-                const int ch = q * 4 + kk;
-                const uint4 v = *reinterpret_cast<const uint4*>(lds_a + r * 256 + ((ch ^ (r & 15)) << 4));
-                const uint32_t a[4] = {v.x, v.y, v.z, v.w};
-                sx[i] = mfma16<BF16>(a, ones, sx[i]);
-#pragma unroll
-                for (int j = 0; j < TN; ++j) part[i][j] = mfma16<BF16>(a, bfrag[j], part[i][j]);
-            }
-        }
-        // ---- per-group epilogue: acc += s * (part - (MV + z) * Sx) ----
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[i][j][e] += scale[j] * (part[i][j][e] - corr[j] * sx[i][e]);
-    }
-
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int64_t n = n_blk + wn * WTN + j * 16 + l16;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t m = m_blk + wm * WTM + i * 16 + q * 4 + e;
-                if (m < M && n < N) y[m * N + n] = to_out<BF16>(acc[i][j][e]);
-            }
-        }
-}
-
-// ---------------------------------------------------------------- launch ----
-
-// gfx950 gives a workgroup up to 160 KB of LDS; the runtime needs the larger
-// dynamic size declared once per kernel.
 constexpr int64_t kLdsMax = 160 * 1024;
 
 template <typename Kern>
@@ -834,19 +661,9 @@ const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K
     return splitk_launch<false, 4>(c, x, M, K, qw, sc, zr, N, y, ws, s);
 }
 
-template <bool BF16, int BM, int BN, int WM, int WN>
-static const char* mfma_cfg(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                            const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM));
-    hipLaunchKernelGGL((k_w4a16_mfma<BF16, BM, BN, WM, WN>), grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
-    return kname("k_w4a16_mfma", BF16, BM, BN, WM, WN);
-}
-
 const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) return mfma_cfg<true, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
-    return mfma_cfg<false, 128, 128, 2, 2>(x, M, K, qw, sc, zr, N, y, s);
+    return launch_w4a16_gemm(x, x_bf16, M, K, qw, sc, zr, N, y, s);
 }
 
 }  // namespace bg

@@ -15,6 +15,7 @@
 
 #include "bg_device.h"
 #include "bg_internal.h"
+#include "bg_pipe.h"
 
 namespace bg {
 
@@ -183,53 +184,11 @@ __global__ __launch_bounds__(256) void k_w8a8_mfma(const uint8_t* __restrict__ a
 // v_mfma_f32_32x32x64_f8f6f4 (32 bytes: both chunks).  The W fragment is the
 // first operand, so output lane l, register e holds row l%32 of the A tile
 // and column 8(e/4) + 4(l/32) + e%4 of the W tile.
-// Block order: blocks are dealt round-robin to the 8 XCDs, so block b is
-// remapped to tile (b % 8) * (tiles / 8) + b / 8, giving each XCD a contiguous
-// run of tiles; runs are ordered in bands of 8 row tiles, so the ~32 blocks
-// resident on one XCD share A row tiles and W column tiles in its L2.
+// Block order: grouped_tile (XCD-aware, bands of 8 row tiles).
 // ============================================================================
 constexpr int GK = 64;                                           // K bytes per stage
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 __device__ __forceinline__ int gswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// 16 bytes per lane from a buffer resource into LDS: lane i writes dst + 16 i.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
-                                              int soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voff, soff, 0, 0);
-}
-
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void block_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// LDS reads of operand fragments are issued as inline assembly: the
-// compiler's wait insertion cannot see which copy into LDS a read depends on
-// and would drain all copies in flight before every read.  The kernel orders
-// them itself -- s_waitcnt vmcnt before the block barrier that publishes a
-// stage, s_waitcnt lgkmcnt(0) before the fragments are used (each fragment is
-// passed through an empty asm after the wait, so no MFMA can move above it).
-__device__ __forceinline__ int4_t ds_read16(uint32_t addr) {
-    int4_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr) : "memory");
-    return v;
-}
-__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void settle(int4_t& v) { asm volatile("" : "+v"(v)); }
 
 template <int TM, int TN>
 struct Frags {
@@ -261,16 +220,8 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
     const int l32 = lane & 31, h = lane >> 5;
 
     // ---- tile of this block ----
-    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
-    const int nt = tiles_m * tiles_n;
-    int pid = blockIdx.x;
-    if (nt % 8 == 0) pid = (pid % 8) * (nt / 8) + pid / 8;
-    constexpr int GROUP_M = 8;
-    const int band = pid / (GROUP_M * tiles_n);
-    const int local = pid - band * GROUP_M * tiles_n;
-    const int first_m = band * GROUP_M;
-    const int gsz = tiles_m - first_m < GROUP_M ? tiles_m - first_m : GROUP_M;
-    const int tm = first_m + local % gsz, tn = local / gsz;
+    int tm, tn;
+    grouped_tile(blockIdx.x, (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     // ---- global -> LDS copies (rows past M or N read as zero) ----
@@ -316,6 +267,17 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
             f.a[frag][c] = ds_read16(base + (c ? offa1 : offa0) + (uint32_t)(frag * 32 * GK));
         else
             f.b[frag - TM][c] = ds_read16(base + (c ? offb1 : offb0) + (uint32_t)((frag - TM) * 32 * GK));
+    };
+    // the same, issued right after MFMAs whose operands must stay untouched
+    using op_t = typename std::conditional<FP8, int8_t_v, int4_t>::type;
+    auto read_one_after = [&](Frags<TM, TN>& f, uint32_t base, int r, const op_t& a1, const op_t& b1,
+                              const op_t& a0, const op_t& b0) {
+        const int frag = r >> 1, c = r & 1;
+        if (frag < TM)
+            f.a[frag][c] = ds_read16_after(base + (c ? offa1 : offa0) + (uint32_t)(frag * 32 * GK), a1, b1, a0, b0);
+        else
+            f.b[frag - TM][c] =
+                ds_read16_after(base + (c ? offb1 : offb0) + (uint32_t)((frag - TM) * 32 * GK), a1, b1, a0, b0);
     };
     auto stage_base = [&](int kb) { return lds0 + (uint32_t)((kb % NB) * STAGE_BYTES); };
     auto settle_frags = [&](Frags<TM, TN>& f) {
@@ -372,21 +334,31 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
         block_barrier();
         issue(kb + NB - 1);
         const uint32_t nb_base = stage_base(kb + 1);
+        // MFMA t, then reads t*NREAD/NMFMA .. (t+1)*NREAD/NMFMA - 1 (every read exactly
+        // once); scheduling barriers keep the compiler from regrouping them
+        op_t pa = op_t{}, pb = op_t{};                           // operands of the previous MFMA
 #pragma unroll
         for (int t = 0; t < NMFMA; ++t) {
+            op_t av, bv;
+            int i, j;
             if constexpr (FP8) {
-                const int i = t / TN, j = t % TN;
-                const int8_t_v av = __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                const int8_t_v bv = __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                i = t / TN, j = t % TN;
+                av = __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+                bv = __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
             } else {
-                const int half = t / (TM * TN), i = (t % (TM * TN)) / TN, j = t % TN;
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur.b[j][half], cur.a[i][half], acc[i][j], 0, 0, 0);
+                const int half = t / (TM * TN);
+                i = (t % (TM * TN)) / TN, j = t % TN;
+                av = cur.a[i][half];
+                bv = cur.b[j][half];
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bv, av, acc[i][j], 0, 0, 0);
             }
-            // reads t*NREAD/NMFMA .. (t+1)*NREAD/NMFMA - 1 go with MFMA t (every read
-            // exactly once); the scheduling barrier keeps the compiler from regrouping them
+            if (t == 0) pa = av, pb = bv;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = t * NREAD / NMFMA; r < (t + 1) * NREAD / NMFMA; ++r) read_one(nxt, nb_base, r);
+            for (int r = t * NREAD / NMFMA; r < (t + 1) * NREAD / NMFMA; ++r)
+                read_one_after(nxt, nb_base, r, av, bv, pa, pb);
+            pa = av, pb = bv;
             __builtin_amdgcn_sched_barrier(0);
         }
         if (BLOCK && (kb & 1)) close_block(kb);
