@@ -194,6 +194,7 @@ def main():
     # -------------------------------------------------------- secondary ----
     if not args.no_secondary:
         out["secondary"] = secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
+        out["secondary"]["crossover_down"] = crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph)
 
     # ----------------------------------------------------- cpu baseline ----
     if not args.no_cpu_baseline:
@@ -295,6 +296,61 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4),
                 "kernel": ops.last_kernel()}
             log(f"  w4a16 {name:8s} B={B:3d} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s")
+    return res
+
+
+def crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
+    """Down-projection shape (K=14336, N=4096), B = 1, 2, 4, ..., 4096: a BF16
+    GEMM (torch.matmul, the library GEMM) against W4A16 (asymmetric INT4, G=128)
+    and W8A8 INT8 (per-token x per-channel) and FP8 (per-tensor), the W8A8
+    times including the activation quantization they need.  Weights are
+    rotated over copies that together exceed the 256 MB last-level cache, so
+    every call reads them from HBM.  Returns the times and the first batch
+    where each W8A8 variant beats W4A16."""
+    K, N = synth.LLAMA3_8B_SHAPES["down"]
+    w = synth.weights(N, K, seed=0, outlier_frac=0.01)
+    wd = torch.from_numpy(w).to(dev)
+    def copies(nbytes):
+        return max(2, -(-(320 << 20) // nbytes))
+    p0 = ops.w4_pack(wd, 128, True)
+    w4 = [p0] + [ops.PackedW4(p0.qweight.clone(), p0.scales.clone(), p0.zeros.clone(), N, K)
+                 for _ in range(copies(p0.nbytes) - 1)]
+    q8, s8 = ops.act_quant_int8(wd, ops.GRAN_ROW)
+    i8 = [(q8, s8)] + [(q8.clone(), s8.clone()) for _ in range(copies(N * K) - 1)]
+    qf, sf = ops.act_quant_fp8(wd, ops.GRAN_TENSOR)
+    f8 = [(qf, sf)] + [(qf.clone(), sf.clone()) for _ in range(copies(N * K) - 1)]
+    wb = wd.to(torch.bfloat16)
+    bf = [wb] + [wb.clone() for _ in range(copies(2 * N * K) - 1)]
+    del wd
+    rows, res = [], {"batches": [], "us": {"bf16": [], "w4a16": [], "w8a8_int8": [], "w8a8_fp8": []}}
+    for lb in range(13):
+        B = 1 << lb
+        g = torch.Generator(device="cpu")
+        g.manual_seed(lb)
+        x = torch.randn((B, K), generator=g).to(torch.bfloat16).to(dev)
+        y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+        def t_of(fn, n):
+            gr = graph_of(lambda: [fn(c) for c in range(n)], torch)
+            return time_graph(gr, 5, torch) / n * 1e3
+        def i8_call(c):
+            a, a_s = ops.act_quant_int8(x, ops.GRAN_ROW)
+            ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, i8[c][0], i8[c][1], ops.GRAN_ROW, out=y)
+        def f8_call(c):
+            a, a_s = ops.act_quant_fp8(x, ops.GRAN_TENSOR)
+            ops.gemm_w8a8(a, a_s, ops.GRAN_TENSOR, f8[c][0], f8[c][1], ops.GRAN_TENSOR, out=y)
+        t = {"bf16": t_of(lambda c: torch.matmul(x, bf[c].t(), out=y), len(bf)),
+             "w4a16": t_of(lambda c: ops.gemm_w4a16(x, w4[c], out=y), len(w4)),
+             "w8a8_int8": t_of(i8_call, len(i8)),
+             "w8a8_fp8": t_of(f8_call, len(f8))}
+        res["batches"].append(B)
+        for k, v in t.items():
+            res["us"][k].append(round(v, 2))
+        log(f"  crossover down B={B:5d}  bf16 {t['bf16']:8.1f}  w4a16 {t['w4a16']:8.1f}  "
+            f"int8 {t['w8a8_int8']:8.1f}  fp8 {t['w8a8_fp8']:8.1f} us")
+    for k in ("w8a8_int8", "w8a8_fp8"):
+        won = [B for B, a, b in zip(res["batches"], res["us"][k], res["us"]["w4a16"]) if a < b]
+        res[f"crossover_batch_{k}"] = won[0] if won else None
+    res["roofline_crossover_batch"] = round(roofline.PEAK_TFLOPS["bf16"] * 1e12 / (2 * roofline.HBM_GBPS * 1e9), 1)
     return res
 
 

@@ -54,7 +54,19 @@ int w4_auto_algo(int64_t M) {
     return BG_ALGO_TILED;
 }
 
-int w8_auto_algo(int64_t M) { return M <= kW8SkinnyMax ? BG_ALGO_SKINNY : BG_ALGO_TILED; }
+// W8A8: the small-M kernel streams the weights once per band of up to 64
+// rows; the tiled kernel is flat in M until its 256 x 128 tiles fill the
+// device. Measured on the 8B projection shapes: the tiled grid wins once it
+// has >= 128 tiles and M > 8, or M > 64 with a short K; the small-M kernel
+// wins below that.
+int w8_auto_algo(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
+    if (M <= 8) return BG_ALGO_SKINNY;
+    if (tiles >= 128 || M > 128) return BG_ALGO_TILED;
+    if (M <= kW8SkinnyMax) return BG_ALGO_SKINNY;
+    if (tiles < 48 && (M <= 64 || K >= 8192)) return BG_ALGO_SKINNY;
+    return BG_ALGO_TILED;
+}
 
 // With a workspace, small M runs split-K where the small-M kernel's per-block
 // re-staging of the activation rows costs more than split-K's cross-block
@@ -183,8 +195,8 @@ BG_EXPORT bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int6
 }
 
 BG_EXPORT int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype) {
-    (void)N; (void)K; (void)in_dtype;
-    return w8_auto_algo(M);
+    (void)in_dtype;
+    return w8_auto_algo(M, N, K);
 }
 
 BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran, const void* w,
@@ -212,7 +224,7 @@ BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gra
     if (!aligned16(a) || !aligned16(w) || !aligned16(y) || (a_scales && !aligned16(a_scales)) ||
         (w_scales && !aligned16(w_scales)))
         return fail(BG_ERR_ALIGN, "gemm_w8a8: pointers must be 16-byte aligned");
-    if (algo == BG_ALGO_AUTO) algo = w8_auto_algo(M);
+    if (algo == BG_ALGO_AUTO) algo = w8_auto_algo(M, N, K);
     bg::W8A8Args g{a, a_scales, raw ? BG_GRAN_ROW : a_gran, w, w_scales, raw ? BG_GRAN_ROW : w_gran,
                    in_dtype == BG_FP8_E4M3, M, N, K, y, out_dtype};
     hipStream_t s = static_cast<hipStream_t>(stream);

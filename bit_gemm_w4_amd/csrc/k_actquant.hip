@@ -158,16 +158,24 @@ __global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__
 // ---- whole tensor ----
 __global__ void k_clear_amax(float* __restrict__ scales) { scales[1] = 0.0f; }
 
+// Grid-stride passes over the whole tensor, TU chunks of 8 elements per
+// thread and iteration so that several 16-byte loads are in flight at once.
+constexpr int TU = 4;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x, int64_t nchunk,
                                                      float* __restrict__ scales) {
     __shared__ float red[4];
-    float v[8];
     float a = 0.0f;
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk;
-         c += (int64_t)gridDim.x * 256) {
-        load8_f32<DT>(x, c * 8, v);
-        a = __builtin_fmaxf(a, amax8(v));
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < nchunk; c0 += TU * stride) {
+        float v[TU][8];
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+            if (c0 + u * stride < nchunk) load8_f32<DT>(x, (c0 + u * stride) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+            if (c0 + u * stride < nchunk) a = __builtin_fmaxf(a, amax8(v[u]));
     }
     a = block_max256(a, red);
     if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(scales + 1), __float_as_uint(a));
@@ -178,18 +186,22 @@ __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x
                                                       void* __restrict__ q,
                                                       float* __restrict__ scales) {
     const float s = unit_scale<FP8>(scales[1]);
-    float v[8];
-    for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk;
-         c += (int64_t)gridDim.x * 256) {
-        load8_f32<DT>(x, c * 8, v);
-        quant_store8<FP8>(v, s, q, c * 8);
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < nchunk; c0 += TU * stride) {
+        float v[TU][8];
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+            if (c0 + u * stride < nchunk) load8_f32<DT>(x, (c0 + u * stride) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+            if (c0 + u * stride < nchunk) quant_store8<FP8>(v[u], s, q, (c0 + u * stride) * 8);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
 }
 
 static unsigned grid_for(int64_t nchunk) {
-    int64_t b = (nchunk + 255) / 256;
-    if (b > 256 * 16) b = 256 * 16;        // grid-stride beyond 16 blocks per CU
+    int64_t b = (nchunk + 256 * TU - 1) / (256 * TU);
+    if (b > 256 * 8) b = 256 * 8;          // grid-stride beyond 8 blocks per CU
     return (unsigned)(b < 1 ? 1 : b);
 }
 

@@ -143,3 +143,12 @@ def test_auto_dispatch_thresholds(L):
     seen = {L.gemm_w4a16_algo(m, 4096, 4096, BF16) for m in range(1, 300)}
     assert seen == {SKINNY, TILED}
     assert GEMV not in seen        # the VALU GEMV is reachable through gemm_w4a16_ex only
+    # W8A8: small-M kernel at decode sizes, tiled once the 256 x 128 tiles fill the device
+    for n, k in ((6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)):
+        assert L.gemm_w8a8_algo(1, n, k, I8) == SKINNY
+        assert L.gemm_w8a8_algo(8, n, k, FP8) == SKINNY
+        assert L.gemm_w8a8_algo(129, n, k, I8) == TILED
+    assert L.gemm_w8a8_algo(16, 28672, 4096, I8) == TILED      # 224 tiles already
+    assert L.gemm_w8a8_algo(32, 4096, 14336, I8) == SKINNY
+    assert L.gemm_w8a8_algo(128, 4096, 14336, I8) == SKINNY    # 32 tiles, long K
+    assert L.gemm_w8a8_algo(128, 4096, 4096, I8) == TILED      # 32 tiles, short K
