@@ -484,8 +484,19 @@ __global__ __launch_bounds__(256) void k_w4a16_splitk_reduce(const float* __rest
     if (tile * 16 >= N || 16 * i + 4 * q >= M) return;
     const int64_t slice = tiles_pad * TM * 256;
     const float* p = ws + (tile * TM + i) * 256 + lane * 4;
-    float4_t v = *reinterpret_cast<const float4_t*>(p);
-    for (int s2 = 1; s2 < S; ++s2) v += *reinterpret_cast<const float4_t*>(p + s2 * slice);
+    // all loads of a batch of up to 16 slices are in flight together; the sum
+    // still runs in slice order
+    constexpr int RB = 16;
+    float4_t v = float4_t{0, 0, 0, 0};
+    for (int b0 = 0; b0 < S; b0 += RB) {
+        float4_t part[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            part[r] = b0 + r < S ? *reinterpret_cast<const float4_t*>(p + (b0 + r) * slice) : float4_t{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+            if (b0 + r < S) v = b0 + r == 0 ? part[r] : v + part[r];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int64_t m = 16 * i + 4 * q + e;

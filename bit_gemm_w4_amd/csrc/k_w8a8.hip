@@ -23,8 +23,10 @@ enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3 };
 
 // ============================================================================
 // Large-M GEMM.  Block tile BM x BN; K advances in stages of 64 bytes (one LDS
-// row per operand row), NB stage buffers (5 when they fit in 160 KB, else 4),
-// so NB - 2 stages are in flight while one is read.  Global -> LDS copies are
+// row per operand row), NB stage buffers (as many as fit in 160 KB, at most 6;
+// 5 for 128 x 128 tiles, which run two blocks per CU):
+// while stage kb + 1 is read, stages kb + 2 .. kb + NB are in flight (the
+// buffer of stage kb is refilled as soon as every wave holds its fragments).  Global -> LDS copies are
 // buffer_load_dwordx4 ... lds (no trip through VGPRs): lane i of a wave writes
 // bytes [16i, 16i+16) of a 1 KB LDS run = 16 rows x 64 bytes, so the 16-byte
 // chunk swizzle is applied on the global side (lane i fetches chunk
@@ -56,10 +58,13 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
     constexpr int STAGE_BYTES = ROWS * GK;
     constexpr int LOADS = ROWS / 64;                             // 1 KB wave-loads per wave per stage
-    constexpr int NB = (160 * 1024) / STAGE_BYTES >= 5 ? 5 : 4;  // stage buffers
+    // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
+    constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
+    constexpr int NB_MAX = BM * BN <= 128 * 128 ? 5 : 6;
+    constexpr int NB = NB_FIT > NB_MAX ? NB_MAX : NB_FIT;
     static_assert(ROWS % 64 == 0 && BM % 32 == 0 && BN % 32 == 0, "tile shape");
     static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
-    static_assert((NB - 2) * LOADS < 64, "vmcnt range");
+    static_assert(NB >= 3 && (NB - 1) * LOADS < 64, "stage count / vmcnt range");
     constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
     constexpr int EPI_BYTES = 4 * WTM * EPI_PITCH;
     constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
@@ -90,16 +95,16 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
         voff[t] = (uint32_t)(r * K) + (uint32_t)((((lane & 3) ^ gswz(r)) << 4));
     }
     const int nkb = (int)(K / GK);
-    // Stage kb goes to buffer kb % NB.  Stages past the end load bytes into a
-    // free buffer that is never consumed.
+    // Stage kb goes to buffer kb % NB.  Stages past the end of K copy bytes of
+    // later rows (zeros past the end of the buffer resource) into a free
+    // buffer that is never consumed.
+    auto issue_one = [&](int kb, int t) {
+        const int j = wave * LOADS + t;
+        copy16_to_lds(j < BM / 16 ? ra : rw, lds + (kb % NB) * STAGE_BYTES + j * 16 * GK, voff[t], kb * GK);
+    };
     auto issue = [&](int kb) {
-        uint8_t* buf = lds + (kb % NB) * STAGE_BYTES;
-        const int soff = kb * GK;
 #pragma unroll
-        for (int t = 0; t < LOADS; ++t) {
-            const int j = wave * LOADS + t;
-            copy16_to_lds(j < BM / 16 ? ra : rw, buf + j * 16 * GK, voff[t], soff);
-        }
+        for (int t = 0; t < LOADS; ++t) issue_one(kb, t);
     };
 
     // ---- fragment addresses: lane l reads chunks h and 2 + h of row l % 32 ----
@@ -175,19 +180,22 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
 
     // One step: stage kb's fragments were requested into `cur`; after they
     // land, the barrier (a) shows every wave holds its stage-kb fragments, so
-    // the buffer of stage kb-1 is free and receives stage kb+NB-1, and (b)
+    // the buffer of stage kb is free and receives stage kb+NB, and (b)
     // publishes stage kb+1, whose fragment reads are then spread between the
     // MFMAs of stage kb.
     constexpr int NREAD = 2 * (TM + TN);
     constexpr int NMFMA = FP8 ? TM * TN : 2 * TM * TN;
+    constexpr int NSLOT = NMFMA - NMFMA / 4;
     auto step = [&](Frags<TM, TN>& cur, Frags<TM, TN>& nxt, int kb) {
         settle_frags(cur);
-        wait_vmcnt<(NB - 3) * LOADS>();                          // this wave's copies of stage kb+1 landed
+        wait_vmcnt<(NB - 2) * LOADS>();                          // this wave's copies of stage kb+1 landed
         block_barrier();
-        issue(kb + NB - 1);
         const uint32_t nb_base = stage_base(kb + 1);
-        // MFMA t, then reads t*NREAD/NMFMA .. (t+1)*NREAD/NMFMA - 1 (every read exactly
-        // once); scheduling barriers keep the compiler from regrouping them
+        // reads of stage kb+1 follow the first NSLOT MFMAs (NREAD/NSLOT per MFMA,
+        // every read exactly once), so the last quarter of the MFMAs covers
+        // their latency; the copies of stage kb+NB are spread over all MFMAs
+        // (a burst of them would hold up the first MFMA); scheduling barriers
+        // keep the compiler from regrouping
         op_t pa = op_t{}, pb = op_t{};                           // operands of the previous MFMA
 #pragma unroll
         for (int t = 0; t < NMFMA; ++t) {
@@ -208,8 +216,11 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
             if (t == 0) pa = av, pb = bv;
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = t * NREAD / NMFMA; r < (t + 1) * NREAD / NMFMA; ++r)
+            for (int r = t < NSLOT ? t * NREAD / NSLOT : NREAD; r < (t < NSLOT ? (t + 1) * NREAD / NSLOT : NREAD); ++r)
                 read_one_after(nxt, nb_base, r, av, bv, pa, pb);
+#pragma unroll
+            for (int l = (t * LOADS + NMFMA - 1) / NMFMA; l < ((t + 1) * LOADS + NMFMA - 1) / NMFMA; ++l)
+                issue_one(kb + NB, l);
             pa = av, pb = bv;
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -217,8 +228,8 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
     };
 
 #pragma unroll
-    for (int t = 0; t < NB - 1; ++t) issue(t);
-    wait_vmcnt<(NB - 2) * LOADS>();
+    for (int t = 0; t < NB; ++t) issue(t);
+    wait_vmcnt<(NB - 1) * LOADS>();
     block_barrier();
     Frags<TM, TN> f0, f1;
 #pragma unroll
@@ -240,68 +251,85 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
     // 16-byte groups.
     block_barrier();                                             // all waves done with the stage buffers
     const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
-    const bool out16 = out_dt == O_BF16 || out_dt == O_F16;
-    uint8_t* stage = lds + wave * WTM * EPI_PITCH;
+    if (!FP8 && out_dt == O_I32) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + i * 32 + l32;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;      // N % 16 == 0: all four or none
+                    int4_t o;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o[r] = (int)acc[i][j][4 * q4 + r];
+                    if (m < M && n < N) *reinterpret_cast<int4_t*>(static_cast<int32_t*>(y) + m * N + n) = o;
+                }
+        }
+        return;
+    }
+    // scales: sa per row; for each 32-column strip j, its 16 sw (four
+    // consecutive per column group) are loaded together -- one wait per strip
+    float sa[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int64_t m = mw + i * 32 + l32;
-        const bool m_ok = m < M;
-        float sa = 1.0f;
-        if (!BLOCK && out_dt != O_I32) sa = a_gran == GT ? as[0] : (m_ok ? as[m] : 0.0f);
+        sa[i] = BLOCK ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
+    }
+    uint8_t* stage = lds + wave * WTM * EPI_PITCH;
+    const bool bf = out_dt == O_BF16;
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
+        float sw[4][4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;
+            float4 w4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+            if (!BLOCK) {
+                if (w_gran == GT) w4 = make_float4(ws[0], ws[0], ws[0], ws[0]);
+                else w4 = n < N ? *reinterpret_cast<const float4*>(ws + n) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            sw[q4][0] = w4.x, sw[q4][1] = w4.y, sw[q4][2] = w4.z, sw[q4][3] = w4.w;
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + i * 32 + l32;
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;          // first of four columns
-                const bool n_ok = n < N;                                 // N % 16 == 0: all four or none
+                const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;          // N % 16 == 0: all four or none
                 float v[4];
-                if (!FP8 && out_dt == O_I32) {
-                    if (m_ok && n_ok) {
-                        int4_t o;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) o[r] = (int)acc[i][j][4 * q4 + r];
-                        *reinterpret_cast<int4_t*>(static_cast<int32_t*>(y) + m * N + n) = o;
-                    }
-                    continue;
-                }
-                float4 sw4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-                if (!BLOCK) {
-                    if (w_gran == GT) sw4 = make_float4(ws[0], ws[0], ws[0], ws[0]);
-                    else if (n_ok) sw4 = *reinterpret_cast<const float4*>(ws + n);
-                }
-                const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if constexpr (BLOCK) v[r] = facc[i][j][4 * q4 + r];
-                    else v[r] = ((float)acc[i][j][4 * q4 + r] * sa) * swv[r];
+                    else v[r] = ((float)acc[i][j][4 * q4 + r] * sa[i]) * sw[q4][r];
                 }
-                if (out16) {
+                if (out_dt == O_F32) {
+                    if (m < M && n < N)
+                        *reinterpret_cast<float4*>(static_cast<float*>(y) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
                     uint2 packed;
-                    if (out_dt == O_BF16) {
-                        packed.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-                        packed.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-                    } else {
-                        packed.x = (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
-                        packed.y = (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
-                    }
+                    packed.x = bf ? (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16)
+                                  : (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+                    packed.y = bf ? (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)
+                                  : (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
                     *reinterpret_cast<uint2*>(stage + (i * 32 + l32) * EPI_PITCH + (j * 32 + 8 * q4 + 4 * h) * 2) =
                         packed;
-                } else if (m_ok && n_ok) {
-                    *reinterpret_cast<float4*>(static_cast<float*>(y) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
                 }
             }
-    }
-    if (out16) {
-        // this wave's WTM x WTN tile, row by row: WTN * 2 bytes = WTN / 8 lanes per row
-        constexpr int LPR = WTN / 8, RPI = 64 / LPR;             // lanes per row, rows per instruction
-        const int rr = lane / LPR, cc = lane % LPR;
-#pragma unroll 4
-        for (int r0 = 0; r0 < WTM; r0 += RPI) {
-            const int r = r0 + rr;
-            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * EPI_PITCH + cc * 16);
-            const int64_t m = mw + r, n = nw + cc * 8;
-            if (m < M && n < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + m * N + n) = v;
         }
+    }
+    if (out_dt == O_F32) return;
+    // 16-bit outputs: this wave's tile was staged in LDS (rows padded by 16
+    // bytes) and goes out as 16-byte row segments,
+    // row by row: WTN * 2 bytes = WTN / 8 lanes per row
+    constexpr int LPR = WTN / 8, RPI = 64 / LPR;                 // lanes per row, rows per instruction
+    const int rr = lane / LPR, cc = lane % LPR;
+#pragma unroll 4
+    for (int r0 = 0; r0 < WTM; r0 += RPI) {
+        const int r = r0 + rr;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage + r * EPI_PITCH + cc * 16);
+        const int64_t m = mw + r, n = nw + cc * 8;
+        if (m < M && n < N) *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + m * N + n) = v;
     }
 }
 

@@ -298,6 +298,15 @@ def test_w8a8_small(ops, orc, algo, M, fp8, a_gran, w_gran, out):
     _w8a8_case(ops, orc, M, 256, 384, fp8, a_gran, w_gran, algo, out_dtype=out, seed=M)
 
 
+@pytest.mark.parametrize("fp8,a_gran,w_gran,out", [
+    (False, 1, 1, torch.float32), (False, 0, 1, torch.float16), (True, 1, 0, torch.float32),
+    (True, 0, 0, torch.float16)])
+def test_w8a8_out_dtypes_wide_tiles(ops, orc, fp8, a_gran, w_gran, out):
+    # 2048 x 8192 is one full round of 256 x 256 tiles: every output type and
+    # scale granularity through the widest tile's epilogue
+    _w8a8_case(ops, orc, 2048, 8192, 256, fp8, a_gran, w_gran, 3, out_dtype=out, rows=[0, 255, 256, 1000, 2047])
+
+
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
 def test_w8a8_int8_prefill_shapes(ops, orc, name):
     K, N = synth.LLAMA3_8B_SHAPES[name]
