@@ -75,6 +75,12 @@ __device__ __forceinline__ uint2 ds_read8_after(uint32_t addr, const int4_t& a1,
     asm volatile("ds_read_b64 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
     return v;
 }
+__device__ __forceinline__ uint32_t ds_read4_after(uint32_t addr, const int4_t& a1, const int4_t& b1,
+                                                   const int4_t& a0, const int4_t& b0) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
+    return v;
+}
 __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");

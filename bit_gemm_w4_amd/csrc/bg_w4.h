@@ -54,6 +54,11 @@ __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t D[4]) {
     D[3] = and_or(w >> 12, 0x000F000Fu, m);
 }
 
+// Difference of two FP16 pairs (one v_pk_add_f16 with negation).
+__device__ __forceinline__ uint32_t sub_h2(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) - __builtin_bit_cast(half2_t, b));
+}
+
 template <bool BF16>
 __device__ __forceinline__ float4_t mfma16(const uint32_t a[4], const uint32_t b[4], float4_t c) {
     const uint4 av = make_uint4(a[0], a[1], a[2], a[3]);

@@ -536,8 +536,8 @@ static const char* decode_cfg(const void* x, int64_t M, int64_t K, const uint32_
     return kname("k_w4a16_decode", BF16, TM, TN, NW, XLDS, VROWS);
 }
 
-// Waves per block: enough blocks x waves to keep ~16 waves per CU resident,
-// never more waves than K has groups.
+// Waves per block: enough blocks x waves to keep ~16 waves per CU resident
+// (at least 4), never more waves than K has groups.
 template <bool BF16, int TM, int TN, bool XLDS, int VROWS>
 static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                              const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
@@ -554,7 +554,8 @@ static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t
     if constexpr (TM < 4) {
         if (want >= 8) return decode_cfg<BF16, TM, TN, 8, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
     }
-    if (want >= 4) return decode_cfg<BF16, TM, TN, 4, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
+    // at least 4 waves: a single wave per block cannot keep enough loads in flight
+    if (ngroups >= 4) return decode_cfg<BF16, TM, TN, 4, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
     return decode_cfg<BF16, TM, TN, 1, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
 }
 

@@ -8,19 +8,24 @@
 // dequantization in registers, one output write), §22 (FP32 accumulation).
 //
 // Exactness: a nibble OR-ed into the mantissa of MV (BF16 128.0 / FP16
-// 1024.0) is the exact 16-bit value MV + u, so each 128-wide group is
-// accumulated as T = sum_k x (MV + u) in FP32 by the MFMA, and the group's
-// contribution s * (T - (MV + z) * Sx) is added once per group, with
-// Sx = sum_k x over the group -- no rounding of the dequantized weight.
+// 1024.0) is the exact 16-bit value MV + u.  FP16: one packed subtraction of
+// (MV + z) gives the exact integer u - z, and the MFMA accumulates the group's
+// T = sum_k x (u - z).  BF16 (no packed BF16 arithmetic): the MFMA
+// accumulates sum_k x (MV + u) and one extra K step per group adds
+// -(MV + z) * Sx, Sx = sum_k x over the group, split exactly into three BF16
+// parts.  Either way the group's contribution s * T is added once per group in
+// FP32 -- no rounding of the dequantized weight.
 //
-// Block tile 256 (rows of X) x 128 (output columns = 8 weight tiles), four
-// waves as 2 x 2, each 128 x 64 = 4 x 2 tiles of v_mfma_f32_32x32x16.  K
-// advances in stages of 64 (half a group); each stage buffer holds
+// Block tile 256 (rows of X) x 128 (output columns = 8 weight tiles), WM x 2
+// waves, each (256 / WM) x 64 of v_mfma_f32_32x32x16 tiles.  K advances in
+// stages of 64 (half a group); each stage buffer holds
 //   A: 256 rows x 128 bytes, 16-byte chunks XOR-swizzled by (row & 7),
 //   W: the matching halves (512 bytes) of the 8 weight tiles,
-//   the group's FP16 scales (8 x 32 bytes) and zero-point bytes (8 x 16),
-// all copied by buffer_load ... lds; four buffers, two stages in flight while
-// one is read (the pipeline of k_w8a8_gemm).
+// all copied by buffer_load ... lds; four buffers: while stage ks + 1 is read,
+// stages ks + 2 .. ks + 4 are in flight (the buffer of stage ks is refilled as
+// soon as every wave holds its fragments).  The group's FP16 scales (8 x 32
+// bytes) and zero-point bytes (8 x 16) go to slot g % 4 of a separate ring,
+// so they stay put until the group is closed.
 //
 // K assignment: in K step s (16 k) of a stage, lane l (h = l / 32) supplies
 // the 8 consecutive k starting at 32 (s / 2) + 16 h + 8 (s % 2) of its row of
@@ -44,24 +49,31 @@ constexpr int P_A = PBM * PKS * 2;                  // 32 KB of activations
 constexpr int P_W = (PBN / 16) * 512;               // 4 KB: half of each of 8 weight tiles
 constexpr int P_S = (PBN / 16) * 32;                // 256 B: FP16 scales of the group
 constexpr int P_Z = (PBN / 16) * 16;                // 128 B: zero-point bytes of the group pair
-constexpr int P_STAGE = P_A + P_W + P_S + P_Z;
+constexpr int P_STAGE = P_A + P_W;
+constexpr int P_META = P_S + P_Z;                   // scales + zero bytes of one group
+constexpr int P_MSLOTS = 4;                         // group g's metadata lives in slot g % 4
 constexpr int P_NB = 4;
-constexpr int P_LOADS = P_A / 4096 + 1 + 1;         // per wave per stage: 8 A, 1 W, 1 scales-or-zeros
-static_assert((P_NB - 2) * P_LOADS < 64, "vmcnt range");
 }  // namespace
 
-template <bool BF16>
-__global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+template <bool BF16, int WM>
+__global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const uint32_t* __restrict__ qw,
                                                        const uint16_t* __restrict__ sc,
                                                        const uint8_t* __restrict__ zr, int64_t N,
                                                        uint16_t* __restrict__ y) {
-    constexpr int WTM = PBM / 2, WTN = PBN / 2, TM = WTM / 32, TN = WTN / 32;
+    constexpr int NW = 2 * WM;                                   // waves: WM x 2
+    constexpr int WTM = PBM / WM, WTN = PBN / 2, TM = WTM / 32, TN = WTN / 32;
+    // copies per wave per stage: A_LD of X (1 KB each), then one of W and one of
+    // metadata (4 waves) or one of W-or-metadata (8 waves)
+    constexpr int A_LD = P_A / 1024 / NW;
+    constexpr int P_LOADS = A_LD + (NW == 4 ? 2 : 1);
+    static_assert((P_NB - 1) * P_LOADS < 64, "vmcnt range");
     constexpr float MV = W4Magic<BF16>::value;
     constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
     constexpr int EPI_PITCH = WTN * 2 + 16;
-    constexpr int EPI_BYTES = 4 * WTM * EPI_PITCH;
-    constexpr int LDS_BYTES = P_NB * P_STAGE > EPI_BYTES ? P_NB * P_STAGE : EPI_BYTES;
+    constexpr int EPI_BYTES = NW * WTM * EPI_PITCH;
+    constexpr int RING_BYTES = P_NB * P_STAGE + P_MSLOTS * P_META;
+    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -90,35 +102,51 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restric
         has_z ? (int)(tiles_here * (ngroups >> 1) * 16) : 0, 0x00020000);
 
     // per-lane global offsets (the stage index goes into the scalar offset)
-    uint32_t voff_a[P_A / 4096];
+    uint32_t voff_a[A_LD];
 #pragma unroll
-    for (int t = 0; t < P_A / 4096; ++t) {
-        const int j = wave * (P_A / 4096) + t;                   // 1 KB run = 8 rows
+    for (int t = 0; t < A_LD; ++t) {
+        const int j = wave * A_LD + t;                           // 1 KB run = 8 rows
         const int r = 8 * j + (lane >> 3);
         voff_a[t] = (uint32_t)(r * K * 2) + (uint32_t)((((lane & 7) ^ (r & 7)) << 4));
     }
-    // W: wave w copies the stage halves of weight tiles 2w, 2w + 1
-    const uint32_t voff_w = (uint32_t)((2 * wave + (lane >> 5)) * ngroups * 1024) + (uint32_t)((lane & 31) * 16);
-    // scales (waves 0, 1: tiles 4w .. 4w+3, 32 bytes each) or zero bytes (waves 2, 3: 8 tiles x 16 bytes)
+    // W: wave w < 4 copies the stage halves of weight tiles 2w, 2w + 1
+    const int ww = wave & 3;
+    const uint32_t voff_w = (uint32_t)((2 * ww + (lane >> 5)) * ngroups * 1024) + (uint32_t)((lane & 31) * 16);
+    // metadata role mrole: 0, 1 = scales of tiles 4 mrole .. +3 (32 bytes each),
+    // 2, 3 = zero bytes of the 8 tiles (16 each; two waves copy the same bytes);
+    // waves 0..3 with four waves, waves 4..7 with eight
+    const int mrole = wave & 3;
     const bool meta_lane = lane < 8;
-    const uint32_t voff_m = wave < 2 ? (uint32_t)((4 * wave + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
-                                     : (uint32_t)(lane * (ngroups >> 1) * 16);
-    auto issue = [&](int ks) {                                   // stage ks = half group
-        uint8_t* buf = lds + (ks % P_NB) * P_STAGE;
-#pragma unroll
-        for (int t = 0; t < P_A / 4096; ++t)
-            copy16_to_lds(ra, buf + (wave * (P_A / 4096) + t) * 1024, voff_a[t], ks * PKS * 2);
-        copy16_to_lds(rw, buf + P_A + wave * 1024, voff_w, ks * 512);
+    const uint32_t voff_m = mrole < 2 ? (uint32_t)((4 * mrole + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
+                                   : (uint32_t)(lane * (ngroups >> 1) * 16);
+    auto copy_meta = [&](int ks) {
+        // both stages of group g copy its metadata to slot g % 4 (the same bytes)
         const int g = ks >> 1;
+        uint8_t* meta = lds + P_NB * P_STAGE + (g % P_MSLOTS) * P_META;
         if (meta_lane) {
-            if (wave < 2) copy16_to_lds(rs, buf + P_A + P_W + wave * 128, voff_m, g * 32);
-            else copy16_to_lds(rz, buf + P_A + P_W + P_S, voff_m, (g >> 1) * 16);
+            if (mrole < 2) copy16_to_lds(rs, meta + mrole * 128, voff_m, g * 32);
+            else copy16_to_lds(rz, meta + P_S, voff_m, (g >> 1) * 16);
         }
+    };
+    // copy number t (0 .. P_LOADS-1) of stage ks = half group
+    auto issue_one = [&](int ks, int t) {
+        uint8_t* buf = lds + (ks % P_NB) * P_STAGE;
+        if (t < A_LD) {
+            copy16_to_lds(ra, buf + (wave * A_LD + t) * 1024, voff_a[t], ks * PKS * 2);
+        } else if (t == A_LD && (NW == 4 || wave < 4)) {
+            copy16_to_lds(rw, buf + P_A + ww * 1024, voff_w, ks * 512);
+        } else {
+            copy_meta(ks);
+        }
+    };
+    auto issue = [&](int ks) {
+#pragma unroll
+        for (int t = 0; t < P_LOADS; ++t) issue_one(ks, t);
     };
 
     // ---- fragment addresses ----
     const uint32_t lds0 = lds_addr(lds);
-    // X row wm*128 + 32i + l32 (swizzle depends on l32 only); chunk c = 4(s/2) + 2h + s%2
+    // X row wm*WTM + 32i + l32 (swizzle depends on l32 only); chunk c = 4(s/2) + 2h + s%2
     uint32_t offa[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -159,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restric
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = float16_t{}, tmp[i][j] = float16_t{};
-    float sx[TM];
+    float sx[TM];                                                // BF16: Sx partials of this lane's k
 #pragma unroll
     for (int i = 0; i < TM; ++i) sx[i] = 0.0f;
 
@@ -171,72 +199,122 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restric
             return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, bv),
                                                           __builtin_bit_cast(half8_t, av), c, 0, 0, 0);
     };
-    // group end: acc += s * (T - (MV + z) * Sx), scales and zeros from the stage buffer
-    auto close_group = [&](int ks) {
-        const uint8_t* buf = lds + (ks % P_NB) * P_STAGE;
-        const int g = ks >> 1;
-        float sxf[TM];
+
+    // Zero point of this lane's weight column (row l32 of W fragment j) for a
+    // group, from the zero bytes of a stage buffer: FP16 keeps the pair
+    // (MV + z, MV + z) to subtract, BF16 the bits of -(MV + z).
+    const int zcol = l32 & 15;
+    const uint32_t meta0 = lds_addr(lds) + (uint32_t)(P_NB * P_STAGE);
+    auto zaddr = [&](int g, int j) {
+        return meta0 + (uint32_t)((g % P_MSLOTS) * P_META + P_S + (wn * 4 + 2 * j + (l32 >> 4)) * 16 + (zcol & ~3));
+    };
+    auto zword = [&](uint32_t zd, int g) -> uint32_t {
+        const uint32_t z = has_z ? (zd >> (8 * (zcol & 3) + 4 * (g & 1))) & 0xFu : 8u;
+        if constexpr (BF16) return 0xC300u | z;                  // -(128 + z)
+        else return (0x6400u | z) * 0x00010001u;                 // (1024 + z) in both halves
+    };
+    uint32_t zw[TN], zd_next[TN];
+    // scales of this lane's columns 8 q4 + 4h .. +3 of the j-th 32 (weight tile
+    // wn*4 + 2j + q4/2, column 8 (q4 % 2) + 4h) in the metadata slot of group g
+    auto saddr = [&](int g, int j, int q4) {
+        return meta0 + (uint32_t)((g % P_MSLOTS) * P_META + (wn * 4 + 2 * j + (q4 >> 1)) * 32 + (8 * (q4 & 1) + 4 * h) * 2);
+    };
+
+    // Group end.  BF16: one more MFMA K step per tile adds -(MV + z) * Sx,
+    // with Sx split exactly into three BF16 parts (hi + mid + lo, truncation
+    // leaves at most 16 then 8 significant bits) -- products of BF16 pairs
+    // are exact in the FP32 accumulator.  FP16 dequantized u - z directly.
+    // Then acc += s * T with the group's FP16 scales (16 reads issued
+    // together, one wait; they follow MFMAs whose operands b1, a1, b0, a0
+    // they must not overwrite).
+    auto close_group = [&](int g, int4_t b1, int4_t a1, int4_t b0, int4_t a0) {
+        if constexpr (BF16) {
+            int4_t xf[TM], wf[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sxf[i] = sx[i] + __shfl_xor(sx[i], 32), sx[i] = 0.0f;
+            for (int i = 0; i < TM; ++i) {
+                const float sxf = sx[i] + __shfl_xor(sx[i], 32);
+                sx[i] = 0.0f;
+                const uint32_t hi = __float_as_uint(sxf) >> 16;
+                const float r1 = sxf - __uint_as_float(hi << 16);
+                const uint32_t mid = __float_as_uint(r1) >> 16;
+                const float r2 = r1 - __uint_as_float(mid << 16);
+                const uint32_t lo = __float_as_uint(r2) >> 16;
+                xf[i] = h ? int4_t{0, 0, 0, 0} : int4_t{(int)(hi | (mid << 16)), (int)lo, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                wf[j] = h ? int4_t{0, 0, 0, 0} : int4_t{(int)(zw[j] | (zw[j] << 16)), (int)zw[j], 0, 0};
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    tmp[i][j] = mfma(wf[j], xf[i], tmp[i][j]);
+                    b0 = b1, a0 = a1, b1 = wf[j], a1 = xf[i];
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        uint2 s4[TN][4];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) s4[j][q4] = ds_read8_after(saddr(g, j, q4), b1, a1, b0, a0);
+        wait_lgkm0();
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                // columns 8 q4 + 4h .. +3 of the j-th 32: tile wn*4 + 2j + q4/2, column 8 (q4 % 2) + 4h
-                const int tt = wn * 4 + 2 * j + (q4 >> 1), col = 8 * (q4 & 1) + 4 * h;
-                uint2 s4 = ds_read8(lds_addr(buf + P_A + P_W + tt * 32 + col * 2));
-                uint32_t z4 = ds_read4(lds_addr(buf + P_A + P_W + P_S + tt * 16 + col));
-                wait_lgkm0();
-                settle(s4), settle(z4);
-                const float sv[4] = {f16_to_f32(s4.x & 0xFFFF), f16_to_f32(s4.x >> 16), f16_to_f32(s4.y & 0xFFFF),
-                                     f16_to_f32(s4.y >> 16)};
+                settle(s4[j][q4]);
+                const uint2 sv2 = s4[j][q4];
+                const float sv[4] = {f16_to_f32(sv2.x & 0xFFFF), f16_to_f32(sv2.x >> 16), f16_to_f32(sv2.y & 0xFFFF),
+                                     f16_to_f32(sv2.y >> 16)};
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float c = MV + (has_z ? (float)((z4 >> (8 * r + 4 * (g & 1))) & 0xF) : 8.0f);
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                    for (int i = 0; i < TM; ++i) {
-                        const float t = tmp[i][j][4 * q4 + r] - c * sxf[i];
-                        acc[i][j][4 * q4 + r] += sv[r] * t;
-                    }
-                }
+                    for (int i = 0; i < TM; ++i) acc[i][j][4 * q4 + r] += sv[r] * tmp[i][j][4 * q4 + r];
             }
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) tmp[i][j] = float16_t{};
     };
 
     // One step: stage ks's fragments were requested into `cur`; the barrier
-    // publishes stage ks + 1 and frees the buffer of stage ks - 1 (every wave
-    // holds its stage-ks fragments), which receives stage ks + P_NB - 1.
+    // publishes stage ks + 1 and frees the buffer of stage ks (every wave
+    // holds its stage-ks fragments), which receives stage ks + P_NB.
+    // first: ks opens a group (its first MFMA per tile starts from zero);
+    // otherwise ks closes the group and reads the zero points of the next one.
+    // Copies and reads of stage ks + 1 are spread between the MFMAs.
     const int nks = (int)(K / PKS);
-    auto step = [&](StageFr& cur, StageFr& nxt, int ks) {
+    auto step = [&](StageFr& cur, StageFr& nxt, int ks, bool first) {
         settle_frags(cur);
-        wait_vmcnt<(P_NB - 3) * P_LOADS>();
+        wait_vmcnt<(P_NB - 2) * P_LOADS>();
         block_barrier();
-        issue(ks + P_NB - 1);
-        // Sx partials of this stage (VALU, overlaps the MFMAs)
+        issue(ks + P_NB);
+        if constexpr (BF16) {
+            // Sx partials of this stage (VALU, overlaps the MFMAs)
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+            for (int s2 = 0; s2 < 4; ++s2)
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                sx[i] = dot2<BF16>((uint32_t)cur.a[i][s].x, ONE2, sx[i]);
-                sx[i] = dot2<BF16>((uint32_t)cur.a[i][s].y, ONE2, sx[i]);
-                sx[i] = dot2<BF16>((uint32_t)cur.a[i][s].z, ONE2, sx[i]);
-                sx[i] = dot2<BF16>((uint32_t)cur.a[i][s].w, ONE2, sx[i]);
-            }
+                for (int i = 0; i < TM; ++i) {
+                    sx[i] = dot2<BF16>((uint32_t)cur.a[i][s2].x, ONE2, sx[i]);
+                    sx[i] = dot2<BF16>((uint32_t)cur.a[i][s2].y, ONE2, sx[i]);
+                    sx[i] = dot2<BF16>((uint32_t)cur.a[i][s2].z, ONE2, sx[i]);
+                    sx[i] = dot2<BF16>((uint32_t)cur.a[i][s2].w, ONE2, sx[i]);
+                }
+        }
         // 32 MFMAs; the 20 reads of the next stage spread between them
         constexpr int NMF = 4 * TM * TN, NRD = 4 * TM + 2 * TN;
         const uint32_t nb = lds0 + (uint32_t)(((ks + 1) % P_NB) * P_STAGE);
         int4_t pbv = int4_t{}, pav = int4_t{};                   // operands of the previous MFMA
+        int4_t ppbv = int4_t{}, ppav = int4_t{};                 // ... and of the one before
 #pragma unroll
         for (int t = 0; t < NMF; ++t) {
             const int s = t / (TM * TN), i = (t / TN) % TM, j = t % TN;
             const uint2 wp = cur.w[j][s >> 1];
             uint32_t d[4];
             dequant_word<BF16>((s & 1) ? wp.y : wp.x, d);
+            if constexpr (!BF16) {
+#pragma unroll
+                for (int p = 0; p < 4; ++p) d[p] = sub_h2(d[p], zw[j]);
+            }
             const int4_t bv = int4_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-            tmp[i][j] = mfma(bv, cur.a[i][s], tmp[i][j]);
+            tmp[i][j] = mfma(bv, cur.a[i][s], (first && s == 0) ? float16_t{} : tmp[i][j]);
             if (t == 0) pbv = bv, pav = cur.a[i][s];
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -251,22 +329,34 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restric
                                                    cur.a[i][s], pbv, pav);
                 }
             }
+            if (!first && t < TN) zd_next[t] = ds_read4_after(zaddr((ks + 1) >> 1, t), bv, cur.a[i][s], pbv, pav);
+
+            ppbv = pbv, ppav = pav;
             pbv = bv, pav = cur.a[i][s];
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (ks & 1) close_group(ks);
+        if (!first) {
+            close_group(ks >> 1, pbv, pav, ppbv, ppav);
+            wait_lgkm0();                                        // the zero-point reads (stage ks + 1 stays put)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) settle(zd_next[j]), zw[j] = zword(zd_next[j], (ks + 1) >> 1);
+        }
     };
 
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_vmcnt<(P_NB - 2) * P_LOADS>();
+#pragma unroll
+    for (int t = 0; t < P_NB; ++t) issue(t);
+    wait_vmcnt<(P_NB - 1) * P_LOADS>();
     block_barrier();
     StageFr f0, f1;
     read_frags(f0, 0);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) zd_next[j] = ds_read4(zaddr(0, j));
+    wait_lgkm0();
+#pragma unroll
+    for (int j = 0; j < TN; ++j) settle(zd_next[j]), zw[j] = zword(zd_next[j], 0);
     for (int ks = 0; ks < nks; ks += 2) {                        // K is a multiple of 256: nks is even
-        step(f0, f1, ks);
-        step(f1, f0, ks + 1);
+        step(f0, f1, ks, true);
+        step(f1, f0, ks + 1, false);
     }
     wait_vmcnt<0>();
     wait_lgkm0();
@@ -298,19 +388,22 @@ __global__ __launch_bounds__(256, 1) void k_w4a16_gemm(const uint16_t* __restric
     }
 }
 
-template <bool BF16>
+template <bool BF16, int WM>
 static const char* gemm_launch(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                                const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     const int64_t tiles = ((M + PBM - 1) / PBM) * ((N + PBN - 1) / PBN);
-    hipLaunchKernelGGL(k_w4a16_gemm<BF16>, dim3((unsigned)tiles), dim3(256), 0, s, static_cast<const uint16_t*>(x), M,
-                       K, qw, sc, zr, N, static_cast<uint16_t*>(y));
-    return kname("k_w4a16_gemm", BF16);
+    hipLaunchKernelGGL((k_w4a16_gemm<BF16, WM>), dim3((unsigned)tiles), dim3(128 * WM), 0, s,
+                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
+    return kname("k_w4a16_gemm", BF16, WM);
 }
 
 const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    if (x_bf16) return gemm_launch<true>(x, M, K, qw, sc, zr, N, y, s);
-    return gemm_launch<false>(x, M, K, qw, sc, zr, N, y, s);
+    // eight waves (two per SIMD): one wave's dequantization and group
+    // arithmetic overlap the other's MFMAs (measured 15% faster than four)
+    constexpr int WM = 4;
+    if (x_bf16) return gemm_launch<true, WM>(x, M, K, qw, sc, zr, N, y, s);
+    return gemm_launch<false, WM>(x, M, K, qw, sc, zr, N, y, s);
 }
 
 }  // namespace bg

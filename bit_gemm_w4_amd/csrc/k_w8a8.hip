@@ -32,7 +32,9 @@ enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3 };
 // chunk swizzle is applied on the global side (lane i fetches chunk
 // (i & 3) ^ swz(row)).  swz(r) = ((r >> 1) ^ (r >> 3)) & 3 keeps the 8 or 16
 // rows read together by one ds_read_b128 phase on distinct banks.
-// Four waves as 2 x 2; each owns a (BM/2) x (BN/2) tile of 32x32 MFMA tiles:
+// 2 x WN waves (WN = 2: one wave per SIMD; WN = 4: two, so one wave's LDS
+// and memory waits overlap the other's MFMAs); each owns a (BM/2) x (BN/WN)
+// tile of 32x32 MFMA tiles:
 // v_mfma_i32_32x32x32_i8 (lane l supplies 16 bytes of row l%32: chunk l/32
 // in the first half of the stage, 2 + l/32 in the second) or
 // v_mfma_f32_32x32x64_f8f6f4 (32 bytes: both chunks).  The W fragment is the
@@ -49,31 +51,32 @@ struct Frags {
     int4_t a[TM][2], b[TN][2];                  // two 16-byte K chunks per 32-row fragment
 };
 
-template <bool FP8, bool BLOCK, int BM, int BN>
-__global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
+template <bool FP8, bool BLOCK, int BM, int BN, int WN>
+__global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       int a_gran, const uint8_t* __restrict__ w,
                                                       const float* __restrict__ ws, int w_gran, int64_t M,
                                                       int64_t N, int64_t K, void* __restrict__ y, int out_dt) {
-    constexpr int WTM = BM / 2, WTN = BN / 2, TM = WTM / 32, TN = WTN / 32;
+    constexpr int NW = 2 * WN;                                   // waves
+    constexpr int WTM = BM / 2, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
     constexpr int STAGE_BYTES = ROWS * GK;
-    constexpr int LOADS = ROWS / 64;                             // 1 KB wave-loads per wave per stage
+    constexpr int LOADS = ROWS / (16 * NW);                      // 1 KB wave-loads per wave per stage
     // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
     constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
     constexpr int NB_MAX = BM * BN <= 128 * 128 ? 5 : 6;
     constexpr int NB = NB_FIT > NB_MAX ? NB_MAX : NB_FIT;
-    static_assert(ROWS % 64 == 0 && BM % 32 == 0 && BN % 32 == 0, "tile shape");
+    static_assert(ROWS % (16 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
     static_assert(NB >= 3 && (NB - 1) * LOADS < 64, "stage count / vmcnt range");
     constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
-    constexpr int EPI_BYTES = 4 * WTM * EPI_PITCH;
+    constexpr int EPI_BYTES = NW * WTM * EPI_PITCH;
     constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
     // ---- tile of this block ----
@@ -333,13 +336,13 @@ __global__ __launch_bounds__(256, 1) void k_w8a8_gemm(const uint8_t* __restrict_
     }
 }
 
-template <bool FP8, bool BLOCK, int BM, int BN>
+template <bool FP8, bool BLOCK, int BM, int BN, int WN>
 static const char* gemm_cfg(const W8A8Args& g, hipStream_t s) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN>), dim3((unsigned)tiles), dim3(256), 0, s,
+    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN>), dim3((unsigned)tiles), dim3(128 * WN), 0, s,
                        static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
                        g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt);
-    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN);
+    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN);
 }
 
 // Tile choice for the large-M GEMM: estimated time = rounds of resident
@@ -347,20 +350,20 @@ static const char* gemm_cfg(const W8A8Args& g, hipStream_t s) {
 // 4096..28672-wide projection shapes: 256 x 256 (one block per CU) 75,
 // 256 x 128 (one per CU) 46.4; 128 x 128 (two per CU, 47) never won on that
 // model, so only block-scaled FP8, which keeps two accumulator sets, uses it.
-template <int BM, int BN>
+template <int BM, int BN, int WN>
 static const char* gemm_dispatch(const W8A8Args& g, hipStream_t s) {
-    if (!g.in_fp8) return gemm_cfg<false, false, BM, BN>(g, s);
-    return gemm_cfg<true, false, BM, BN>(g, s);
+    if (!g.in_fp8) return gemm_cfg<false, false, BM, BN, WN>(g, s);
+    return gemm_cfg<true, false, BM, BN, WN>(g, s);
 }
 
 const char* launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) {
-    if (g.in_fp8 && g.a_gran == GR128) return gemm_cfg<true, true, 128, 128>(g, s);
+    if (g.in_fp8 && g.a_gran == GR128) return gemm_cfg<true, true, 128, 128, 2>(g, s);
     auto cost = [&](int64_t bm, int64_t bn, double round) {
         const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
         return (double)((tiles + 255) / 256) * round;
     };
-    if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) return gemm_dispatch<256, 256>(g, s);
-    return gemm_dispatch<256, 128>(g, s);
+    if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) return gemm_dispatch<256, 256, 2>(g, s);
+    return gemm_dispatch<256, 128, 2>(g, s);
 }
 
 
