@@ -56,9 +56,17 @@ const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K
                                 hipStream_t s);
 const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                         const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
-// Large-M LDS-pipelined kernel behind launch_w4a16_tiled (k_w4a16_gemm.hip).
+// Large-M LDS-pipelined kernel (k_w4a16_gemm.hip).  With a workspace (ws
+// non-NULL, at least w4a16_gemm_split(M, N, K).ws_bytes, any contents) K is
+// split into S slices when the output tiles do not fill the device; the FP32
+// partials are then summed by a second kernel on the same stream.
+struct W4GemmSplit {
+    int S, gs;              // slices, groups per slice
+    int64_t ws_bytes;       // S * M * N * 4 when S > 1, else 0
+};
+W4GemmSplit w4a16_gemm_split(int64_t M, int64_t N, int64_t K);
 const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
+                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s);
 
 // W8A8: in_fp8 selects E4M3 x E4M3 (else INT8 x INT8); out_dt: 0 f32, 1 f16, 2 bf16, 5 i32.
 // block_scaled: a_gran = ROW_G128 and w_gran = BLOCK128 (FP8 only).

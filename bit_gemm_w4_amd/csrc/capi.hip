@@ -72,8 +72,10 @@ int w8_auto_algo(int64_t M, int64_t N, int64_t K) {
 // re-staging of the activation rows costs more than split-K's cross-block
 // reduction: from the measured crossovers (graph-replayed, cold weights) on
 // the 4096/14336-wide projection shapes.
+// Past the small-M range, split-K (of the large-M kernel) while its output
+// tiles do not fill the device.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
-    if (M > kW4SkinnyMax) return BG_ALGO_TILED;
+    if (M > kW4SkinnyMax) return bg::w4a16_gemm_split(M, N, K).S > 1 ? BG_ALGO_SPLITK : BG_ALGO_TILED;
     const bool split = (M >= 8 && (N >= 16384 || K >= 8192)) || (M >= 12 && N > 4096) || M >= 24;
     return split ? BG_ALGO_SPLITK : BG_ALGO_SKINNY;
 }
@@ -120,9 +122,9 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
     if (algo == BG_ALGO_GEMV && (M > kMaxGemvM || !bg::w4a16_gemv_supported(M, K)))
         return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 20000 (M=%lld, K=%lld)", M, K);
     if (algo == BG_ALGO_SPLITK) {
-        if (!with_ws) return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernel needs gemm_w4a16_ws");
-        if (M > kW4SkinnyMax) return fail(BG_ERR_SHAPE, "gemm_w4a16: the split-K kernel takes M <= 64 (M=%lld)", M);
-        const int64_t need = bg::w4a16_splitk_workspace(M, N, K);
+        if (!with_ws) return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernels need gemm_w4a16_ws");
+        const int64_t need =
+            M > kW4SkinnyMax ? bg::w4a16_gemm_split(M, N, K).ws_bytes : bg::w4a16_splitk_workspace(M, N, K);
         if (need > 0 && (!ws || ws_bytes < need))
             return fail(BG_ERR_WORKSPACE, "gemm_w4a16: workspace of %lld bytes needed (got %lld)", need, ws ? ws_bytes : 0);
     }
@@ -133,7 +135,10 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
         case BG_ALGO_SKINNY: note_kernel(bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_TILED: note_kernel(bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_SPLITK:
-            note_kernel(bg::launch_w4a16_splitk(x, bf16, M, K, qweight, scales, zeros, N, y, ws, s));
+            if (M > kW4SkinnyMax)
+                note_kernel(bg::launch_w4a16_gemm(x, bf16, M, K, qweight, scales, zeros, N, y, ws, s));
+            else
+                note_kernel(bg::launch_w4a16_splitk(x, bf16, M, K, qweight, scales, zeros, N, y, ws, s));
             break;
         default: return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16: unknown algo %lld", algo);
     }
@@ -156,8 +161,8 @@ BG_EXPORT bg_status gemm_w4a16_ws(const void* x, int x_dtype, int64_t M, int64_t
 BG_EXPORT int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo) {
     if (M < 1 || M > kMaxM || N < 16 || N % 16 || K < 256 || K % 256) return 0;
     if (algo == BG_ALGO_AUTO) algo = w4_auto_algo_ws(M, N, K);
-    if (algo != BG_ALGO_SPLITK || M > kW4SkinnyMax) return 0;
-    return bg::w4a16_splitk_workspace(M, N, K);
+    if (algo != BG_ALGO_SPLITK) return 0;
+    return M > kW4SkinnyMax ? bg::w4a16_gemm_split(M, N, K).ws_bytes : bg::w4a16_splitk_workspace(M, N, K);
 }
 
 BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,

@@ -675,7 +675,7 @@ const char* launch_w4a16_splitk(const void* x, bool x_bf16, int64_t M, int64_t K
 
 const char* launch_w4a16_tiled(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                                const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    return launch_w4a16_gemm(x, x_bf16, M, K, qw, sc, zr, N, y, s);
+    return launch_w4a16_gemm(x, x_bf16, M, K, qw, sc, zr, N, y, nullptr, s);
 }
 
 }  // namespace bg

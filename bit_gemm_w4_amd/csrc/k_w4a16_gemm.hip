@@ -60,7 +60,8 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
                                                        const uint32_t* __restrict__ qw,
                                                        const uint16_t* __restrict__ sc,
                                                        const uint8_t* __restrict__ zr, int64_t N,
-                                                       uint16_t* __restrict__ y) {
+                                                       uint16_t* __restrict__ y, float* __restrict__ ws, int S,
+                                                       int gs) {
     constexpr int NW = 2 * WM;                                   // waves: WM x 2
     constexpr int WTM = PBM / WM, WTN = PBN / 2, TM = WTM / 32, TN = WTN / 32;
     // copies per wave per stage: A_LD of X (1 KB each), then one of W and one of
@@ -83,10 +84,14 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     const int l32 = lane & 31, h = lane >> 5;
     const bool has_z = zr != nullptr;
 
+    // block b: output tile b % T, K slice b / T (groups [sl gs, sl gs + gs))
     int tm, tn;
-    grouped_tile(blockIdx.x, (int)((M + PBM - 1) / PBM), (int)((N + PBN - 1) / PBN), tm, tn);
+    const int tiles_m = (int)((M + PBM - 1) / PBM), tiles_n = (int)((N + PBN - 1) / PBN);
+    const int sl = blockIdx.x / (tiles_m * tiles_n);
+    grouped_tile(blockIdx.x - sl * tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * PBM, n0 = (int64_t)tn * PBN;
     const int64_t ngroups = K >> 7, ntiles = N >> 4, t0 = n0 >> 4;
+    const int g_beg = sl * gs, g_end = g_beg + gs < ngroups ? g_beg + gs : (int)ngroups;
     const int64_t tiles_here = ntiles - t0 < PBN / 16 ? ntiles - t0 : PBN / 16;
 
     // ---- buffer resources (rows / tiles past the end read as zero) ----
@@ -280,7 +285,6 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     // first: ks opens a group (its first MFMA per tile starts from zero);
     // otherwise ks closes the group and reads the zero points of the next one.
     // Copies and reads of stage ks + 1 are spread between the MFMAs.
-    const int nks = (int)(K / PKS);
     auto step = [&](StageFr& cur, StageFr& nxt, int ks, bool first) {
         settle_frags(cur);
         wait_vmcnt<(P_NB - 2) * P_LOADS>();
@@ -343,27 +347,50 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
         }
     };
 
+    // stages 2 g_beg .. 2 g_end - 1 (stages past the slice copy bytes never consumed)
+    const int ks0 = 2 * g_beg, ks1 = 2 * g_end;
 #pragma unroll
-    for (int t = 0; t < P_NB; ++t) issue(t);
+    for (int t = 0; t < P_NB; ++t) issue(ks0 + t);
     wait_vmcnt<(P_NB - 1) * P_LOADS>();
     block_barrier();
     StageFr f0, f1;
-    read_frags(f0, 0);
+    read_frags(f0, ks0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) zd_next[j] = ds_read4(zaddr(0, j));
+    for (int j = 0; j < TN; ++j) zd_next[j] = ds_read4(zaddr(g_beg, j));
     wait_lgkm0();
 #pragma unroll
-    for (int j = 0; j < TN; ++j) settle(zd_next[j]), zw[j] = zword(zd_next[j], 0);
-    for (int ks = 0; ks < nks; ks += 2) {                        // K is a multiple of 256: nks is even
+    for (int j = 0; j < TN; ++j) settle(zd_next[j]), zw[j] = zword(zd_next[j], g_beg);
+    for (int ks = ks0; ks < ks1; ks += 2) {
         step(f0, f1, ks, true);
         step(f1, f0, ks + 1, false);
     }
     wait_vmcnt<0>();
     wait_lgkm0();
-
-    // ---- epilogue: stage this wave's 128 x 64 tile in LDS, write 16-byte row segments ----
-    block_barrier();
     const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+    if (S > 1) {
+        // FP32 partial tile of slice sl -> ws[sl][M][N] (k_w4a16_gemm_reduce adds
+        // the slices): lane l, register e of tile (i, j) holds row 32 i + l % 32,
+        // columns 32 j + 8 (e / 4) + 4 h + e % 4 -- four consecutive floats
+        float* part = ws + (int64_t)sl * M * N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = mw + 32 * i + l32;
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int64_t n = nw + 32 * j + 8 * q4 + 4 * h;
+                    if (m < M && n < N)
+                        *reinterpret_cast<float4*>(part + m * N + n) =
+                            make_float4(acc[i][j][4 * q4], acc[i][j][4 * q4 + 1], acc[i][j][4 * q4 + 2],
+                                        acc[i][j][4 * q4 + 3]);
+                }
+        }
+        return;
+    }
+
+    // ---- epilogue: stage this wave's tile in LDS, write 16-byte row segments ----
+    block_barrier();
     uint8_t* stage = lds + wave * WTM * EPI_PITCH;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -388,22 +415,82 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     }
 }
 
+// y[m][n] = sum over the S slices of ws[s][m][n], in slice order (results do
+// not depend on timing).  One thread per 8 consecutive outputs of a row.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_w4a16_gemm_reduce(const float* __restrict__ ws, int S, int64_t M, int64_t N,
+                                                           uint16_t* __restrict__ y) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e >= M * N) return;
+    const int64_t slice = M * N;
+    constexpr int RB = 8;                                      // slices in flight per batch
+    float v[8];
+    for (int b0 = 0; b0 < S; b0 += RB) {
+        float4 lo[RB], hi[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r < S) {
+                lo[r] = *reinterpret_cast<const float4*>(ws + (b0 + r) * slice + e);
+                hi[r] = *reinterpret_cast<const float4*>(ws + (b0 + r) * slice + e + 4);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r >= S) break;
+            const float p[8] = {lo[r].x, lo[r].y, lo[r].z, lo[r].w, hi[r].x, hi[r].y, hi[r].z, hi[r].w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = b0 + r == 0 ? p[c] : v[c] + p[c];
+        }
+    }
+    uint4 o;
+    o.x = (uint32_t)to_out<BF16>(v[0]) | ((uint32_t)to_out<BF16>(v[1]) << 16);
+    o.y = (uint32_t)to_out<BF16>(v[2]) | ((uint32_t)to_out<BF16>(v[3]) << 16);
+    o.z = (uint32_t)to_out<BF16>(v[4]) | ((uint32_t)to_out<BF16>(v[5]) << 16);
+    o.w = (uint32_t)to_out<BF16>(v[6]) | ((uint32_t)to_out<BF16>(v[7]) << 16);
+    *reinterpret_cast<uint4*>(y + e) = o;
+}
+
+// K slices for the large-M kernel: while its tiles do not fill one round (one
+// block per CU), split K into whole groups, at least 4 per slice.
+W4GemmSplit w4a16_gemm_split(int64_t M, int64_t N, int64_t K) {
+    W4GemmSplit c{1, (int)(K >> 7), 0};
+    const int64_t tiles = ((M + PBM - 1) / PBM) * ((N + PBN - 1) / PBN), ngroups = K >> 7;
+    int64_t S = 256 / tiles;
+    if (S > ngroups / 4) S = ngroups / 4;
+    if (S < 2) return c;
+    const int64_t gs = (ngroups + S - 1) / S;
+    c.S = (int)((ngroups + gs - 1) / gs);
+    c.gs = (int)gs;
+    c.ws_bytes = c.S > 1 ? (int64_t)c.S * M * N * 4 : 0;
+    if (c.S < 2) c = W4GemmSplit{1, (int)ngroups, 0};
+    return c;
+}
+
 template <bool BF16, int WM>
 static const char* gemm_launch(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                               const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+                               const uint8_t* zr, int64_t N, void* y, float* ws, const W4GemmSplit& c,
+                               hipStream_t s) {
     const int64_t tiles = ((M + PBM - 1) / PBM) * ((N + PBN - 1) / PBN);
-    hipLaunchKernelGGL((k_w4a16_gemm<BF16, WM>), dim3((unsigned)tiles), dim3(128 * WM), 0, s,
-                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y));
+    hipLaunchKernelGGL((k_w4a16_gemm<BF16, WM>), dim3((unsigned)(tiles * c.S)), dim3(128 * WM), 0, s,
+                       static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N, static_cast<uint16_t*>(y), ws, c.S,
+                       c.gs);
+    if (c.S > 1) {
+        const int64_t threads = M * N / 8;
+        hipLaunchKernelGGL((k_w4a16_gemm_reduce<BF16>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(ws), c.S, M, N, static_cast<uint16_t*>(y));
+    }
     return kname("k_w4a16_gemm", BF16, WM);
 }
 
 const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
-                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
+                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s) {
     // eight waves (two per SIMD): one wave's dequantization and group
     // arithmetic overlap the other's MFMAs (measured 15% faster than four)
     constexpr int WM = 4;
-    if (x_bf16) return gemm_launch<true, WM>(x, M, K, qw, sc, zr, N, y, s);
-    return gemm_launch<false, WM>(x, M, K, qw, sc, zr, N, y, s);
+    const W4GemmSplit c = ws ? w4a16_gemm_split(M, N, K) : W4GemmSplit{1, (int)(K >> 7), 0};
+    float* wsf = static_cast<float*>(ws);
+    if (x_bf16) return gemm_launch<true, WM>(x, M, K, qw, sc, zr, N, y, wsf, c, s);
+    return gemm_launch<false, WM>(x, M, K, qw, sc, zr, N, y, wsf, c, s);
 }
 
 }  // namespace bg

@@ -64,7 +64,7 @@ typedef enum bg_algo {
     BG_ALGO_GEMV = 1,      /* W4A16 small-M: VALU dot products, wave reductions    */
     BG_ALGO_SKINNY = 2,    /* small-M on MFMA (M padded to the MFMA tile)          */
     BG_ALGO_TILED = 3,     /* large-M LDS-tiled MFMA GEMM                          */
-    BG_ALGO_SPLITK = 4     /* W4A16 M <= 64: K split over blocks, needs a workspace */
+    BG_ALGO_SPLITK = 4     /* W4A16: K split over blocks, needs a workspace        */
 } bg_algo;
 
 /*
@@ -122,13 +122,19 @@ bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
 
 /*
  * gemm_w4a16_ws -- gemm_w4a16 with a caller-provided device workspace, which
- * enables the split-K small-M kernel (BG_ALGO_SPLITK, M <= 64; BG_ALGO_AUTO
- * picks it for M from 8 to 64 where it measured faster than BG_ALGO_SKINNY:
- * M >= 8 with N >= 16384 or K >= 8192, M >= 12 with N > 4096, or M >= 24).
- * Splitting K across workgroups lets each workgroup reuse its
- * activations across 16 weight tiles; the FP32 partial tiles go to the
- * workspace and a second kernel, enqueued on the same stream, sums them in a
- * fixed order, so results are deterministic.
+ * enables the split-K kernels (BG_ALGO_SPLITK):
+ *   M <= 64  the small-M split-K kernel.  BG_ALGO_AUTO picks it for M from 8
+ *            to 64 where it measured faster than BG_ALGO_SKINNY: M >= 8 with
+ *            N >= 16384 or K >= 8192, M >= 12 with N > 4096, or M >= 24.
+ *            Splitting K across workgroups lets each workgroup reuse its
+ *            activations across 16 weight tiles.
+ *   M > 64   the large-M kernel with K split into S slices of whole groups
+ *            while its 256 x 128 output tiles do not fill one round of the
+ *            device (S = min(256 / tiles, groups / 4); S = 1 is the plain
+ *            kernel and needs no workspace).  BG_ALGO_AUTO picks it whenever
+ *            S > 1.
+ * The FP32 partials go to the workspace and a second kernel, enqueued on the
+ * same stream, sums them in a fixed order, so results are deterministic.
  *   workspace        16-byte aligned device memory of at least
  *                    gemm_w4a16_workspace_bytes(M, N, K, algo) bytes.  It
  *                    needs no initialisation and its contents afterwards

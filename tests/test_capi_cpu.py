@@ -97,11 +97,16 @@ def test_gemm_w4a16_workspace(L):
     need = L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 0)
     assert need > 0 and need % 16 == 0
     assert L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 3) == 0            # tiled: none
-    assert L.gemm_w4a16_workspace_bytes(1000, 4096, 14336, 0) == 0          # AUTO -> tiled at large M
+    # past M = 64: split-K of the large-M kernel while its 256 x 128 tiles fill
+    # less than one round (S = min(256 / tiles, groups / 4) slices of FP32 M x N)
+    assert L.gemm_w4a16_workspace_bytes(1000, 4096, 14336, 0) == 2 * 1000 * 4096 * 4   # 128 tiles: S = 2
+    assert L.gemm_w4a16_workspace_bytes(130, 4096, 14336, 4) == 8 * 130 * 4096 * 4     # 32 tiles: S = 8
+    assert L.gemm_w4a16_workspace_bytes(130, 4096, 512, 4) == 0                        # 4 groups: no split
+    assert L.gemm_w4a16_workspace_bytes(2048, 4096, 14336, 0) == 0                     # 256 tiles: one round
     assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, None, 0, 0, None) == E_WS
     assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, P, need - 16, 0, None) == E_WS
     assert "needed" in _last(L)
-    assert f(P, BF16, 100, 14336, P, Q, None, 4096, 128, P, P, need, 4, None) == E_SHAPE   # split-K M <= 64
+    assert f(P, BF16, 100, 14336, P, Q, None, 4096, 128, P, P, need, 4, None) == E_WS      # large-M split needs more
     assert f(P, BF16, 16, 14336, P, Q, None, 4096, 128, P, P + 8, need, 0, None) == E_ALIGN
 
 

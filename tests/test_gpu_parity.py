@@ -123,9 +123,17 @@ def _w4a16_case(ops, orc, M, N, K, x_dtype, asym, algo, seed, rows=None):
 @pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 16, 17, 33, 64, 74, 130])
 def test_w4a16_small(ops, orc, algo, x_dtype, asym, M):
-    if algo == 4 and M > 64:
-        pytest.skip("the split-K kernel serves M <= 64")
     _w4a16_case(ops, orc, M, 272, 768, x_dtype, asym, algo, seed=M)
+
+
+@pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
+@pytest.mark.parametrize("M", [65, 130, 300])
+def test_w4a16_splitk_large_m(ops, orc, x_dtype, asym, M):
+    """Large-M kernel with K split into slices (9 or 18 output tiles, 16 groups:
+    4 slices), ragged in M and N."""
+    N, K = 1040, 2048
+    assert ops.gemm_w4a16_workspace_bytes(M, N, K, 4) == 4 * M * N * 4
+    _w4a16_case(ops, orc, M, N, K, x_dtype, asym, 4, seed=M)
 
 
 def test_w4a16_qwen_layer(ops, orc):
@@ -150,14 +158,14 @@ def test_w4a16_splitk_workspace_reuse(ops, orc):
     """One workspace shared by split-K calls of different shapes; it starts
     filled with 0xFF bytes (NaN as FP32): the workspace needs no
     initialisation and no call depends on what an earlier one left in it."""
-    cases = [(64, 272, 768), (1, 1024, 1024), (17, 512, 2048), (3, 272, 768), (1, 1024, 1024)]
+    cases = [(64, 272, 768), (1, 1024, 1024), (130, 1040, 2048), (17, 512, 2048), (3, 272, 768), (1, 1024, 1024)]
     need = max(ops.gemm_w4a16_workspace_bytes(M, N, K, 4) for M, N, K in cases)
     ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     for i, (M, N, K) in enumerate(cases):
         w, x = synth.layer(M, N, K, "bf16", seed=100 + i)
         p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, True)
         y = ops.gemm_w4a16(dev_bits(x, "bf16"), p, algo=4, ws=ws)
-        assert "splitk" in ops.last_kernel()
+        assert ("splitk" if M <= 64 else "gemm") in ops.last_kernel()
         torch.cuda.synchronize()
         qw, s, z = orc.w4_pack(w, 128, True)
         ref = orc.gemm_w4a16(x, "bf16", qw, s, z)
