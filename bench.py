@@ -156,7 +156,7 @@ def main():
             for c in range(R_COPIES):
                 ops.gemm_w4a16(xs[(name, B)], packs[name][c], out=ys[(name, B)])
         ops.gemm_w4a16(xs[(name, B)], packs[name][0], out=ys[(name, B)])
-        kernel_of[(name, B)] = ops.last_kernel()
+        kernel_of[(name, B)] = call_kernels(ops, ops.last_kernel(), B, *reversed(synth.LLAMA3_8B_SHAPES[name]))
         g = graph_of(one, torch)
         ms = time_graph(g, 20, torch) / R_COPIES
         per_call[(name, B)] = ms
@@ -170,7 +170,7 @@ def main():
     t_dom, b_dom, n_dom = by_kernel[dom]
     achieved = b_dom / (t_dom * 1e-3) / 1e9
     traffic = measured_traffic(dom)
-    roof = {"bound": "hbm", "kernel": dom, "launches_per_step": n_dom,
+    roof = {"bound": "hbm", "kernel": dom, "kernels_per_call": len(dom.split(" + ")), "launches_per_step": n_dom,
             "bytes_per_launch": b_dom / n_dom, "avg_launch_us": t_dom / n_dom * 1e3,
             "achieved": round(achieved, 1), "peak": roofline.HBM_GBPS, "unit": "GB/s",
             "frac": round(achieved / roofline.HBM_GBPS, 4),
@@ -232,21 +232,36 @@ def library_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE, each scaled by the calibration copy), or None
-    when there is none for this kernel or the sources changed since."""
+def call_kernels(ops, main: str, M: int, N: int, K: int) -> str:
+    """The kernels one gemm_w4a16 call enqueues, joined by " + ": the split-K
+    paths add a fixed-order reduction kernel when they split K."""
+    if ops.gemm_w4a16_workspace_bytes(M, N, K) > 0 and "k_w4a16_splitk<" in main:
+        return main + " + " + main.replace("k_w4a16_splitk<", "k_w4a16_splitk_reduce<")
+    if ops.gemm_w4a16_workspace_bytes(M, N, K) > 0 and "k_w4a16_gemm<" in main:
+        return main + " + " + "k_w4a16_gemm_reduce<" + main.split("<", 1)[1].split(",")[0] + ">"
+    return main
+
+
+def measured_traffic(call: str):
+    """HBM bytes per call from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE per dispatch, each scaled by the calibration copy, summed over
+    the call's kernels), or None when a kernel has no row or the sources
+    changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     digest = library_digest()
+    rows = {}
     for line in open(TRAFFIC_FILE):
         cells = [c.strip() for c in line.strip().strip("|").split("|")]
-        if len(cells) == 7 and cells[0] == f"`{kernel}`" and cells[1] == digest:
+        if len(cells) == 7 and cells[1] == digest:
             try:
-                return float(cells[6])
+                rows[cells[0].strip("`")] = float(cells[6])
             except ValueError:
-                return None
-    return None
+                pass
+    parts = call.split(" + ")
+    if not all(k in rows for k in parts):
+        return None
+    return sum(rows[k] for k in parts)
 
 
 def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph):
