@@ -82,7 +82,16 @@ struct W8A8Args {
     void* y;
     int out_dt;
 };
-const char* launch_w8a8_tiled(const W8A8Args& args, hipStream_t s);
+// Large-M W8A8 tile shape and K split.  With a workspace (at least ws_bytes,
+// any contents) grids of less than one round split K into S slices of spl
+// 64-byte stages; the partials are then summed (and scaled) by a second
+// kernel on the same stream.
+struct W8Split {
+    int bm, bn, S, spl;
+    int64_t ws_bytes;
+};
+W8Split w8a8_tiled_split(const W8A8Args& args, bool with_ws);
+const char* launch_w8a8_tiled(const W8A8Args& args, void* ws, hipStream_t s);
 const char* launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
 
 }  // namespace bg

@@ -57,15 +57,24 @@ int w4_auto_algo(int64_t M) {
 // W8A8: the small-M kernel streams the weights once per band of up to 64
 // rows; the tiled kernel is flat in M until its 256 x 128 tiles fill the
 // device. Measured on the 8B projection shapes: the tiled grid wins once it
-// has >= 128 tiles and M > 8, or M > 64 with a short K; the small-M kernel
-// wins below that.
+// has >= 128 tiles (from M = 1) or M > 128, or M > 64 with a short K; the
+// small-M kernel wins below that.
 int w8_auto_algo(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
-    if (M <= 8) return BG_ALGO_SKINNY;
     if (tiles >= 128 || M > 128) return BG_ALGO_TILED;
     if (M <= kW8SkinnyMax) return BG_ALGO_SKINNY;
     if (tiles < 48 && (M <= 64 || K >= 8192)) return BG_ALGO_SKINNY;
     return BG_ALGO_TILED;
+}
+
+// W8A8 with a workspace: the large-M kernel with K split wherever it measured
+// faster than the small-M kernel on the projection shapes (N >= 6144 at any
+// M; K >= 8192 from M = 4; otherwise from M = 32), else the choice above.
+int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
+    bg::W8A8Args g{nullptr, nullptr, a_gran, nullptr, nullptr, 0, in_dtype == BG_FP8_E4M3, M, N, K, nullptr, BG_BF16};
+    const bool fits = N >= 6144 || (K >= 8192 && M >= 4) || M >= 32;
+    if (fits && bg::w8a8_tiled_split(g, true).S > 1) return BG_ALGO_TILED;
+    return w8_auto_algo(M, N, K);
 }
 
 // With a workspace, small M runs split-K where the small-M kernel's per-block
@@ -204,9 +213,9 @@ BG_EXPORT int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype) {
     return w8_auto_algo(M, N, K);
 }
 
-BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran, const void* w,
-                                 const float* w_scales, int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K,
-                                 void* y, int out_dtype, int algo, void* stream) {
+static bg_status w8a8_impl(const void* a, const float* a_scales, int a_gran, const void* w, const float* w_scales,
+                           int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K, void* y, int out_dtype,
+                           void* ws, int64_t ws_bytes, bool with_ws, int algo, void* stream) {
     if (!a || !w || !y) return fail(BG_ERR_NULL, "gemm_w8a8: a, w and y must be non-NULL");
     if (in_dtype != BG_I8 && in_dtype != BG_FP8_E4M3)
         return fail(BG_ERR_DTYPE, "gemm_w8a8: in_dtype %lld is not I8/FP8_E4M3", in_dtype);
@@ -227,18 +236,46 @@ BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gra
         return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld too long for exact INT32 accumulation", K);
     if (block && N % 128) return fail(BG_ERR_SHAPE, "gemm_w8a8: BLOCK128 weights need N %% 128 == 0 (N=%lld)", N);
     if (!aligned16(a) || !aligned16(w) || !aligned16(y) || (a_scales && !aligned16(a_scales)) ||
-        (w_scales && !aligned16(w_scales)))
+        (w_scales && !aligned16(w_scales)) || (ws && !aligned16(ws)))
         return fail(BG_ERR_ALIGN, "gemm_w8a8: pointers must be 16-byte aligned");
-    if (algo == BG_ALGO_AUTO) algo = w8_auto_algo(M, N, K);
+    if (algo == BG_ALGO_AUTO) algo = with_ws ? w8_auto_algo_ws(M, N, K, in_dtype, a_gran) : w8_auto_algo(M, N, K);
     bg::W8A8Args g{a, a_scales, raw ? BG_GRAN_ROW : a_gran, w, w_scales, raw ? BG_GRAN_ROW : w_gran,
                    in_dtype == BG_FP8_E4M3, M, N, K, y, out_dtype};
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (algo == BG_ALGO_TILED && with_ws) {
+        const int64_t need = bg::w8a8_tiled_split(g, true).ws_bytes;
+        if (need > 0 && (!ws || ws_bytes < need))
+            return fail(BG_ERR_WORKSPACE, "gemm_w8a8: workspace of %lld bytes needed (got %lld)", need, ws ? ws_bytes : 0);
+    }
     switch (algo) {
         case BG_ALGO_SKINNY: note_kernel(bg::launch_w8a8_skinny(g, s)); break;
-        case BG_ALGO_TILED: note_kernel(bg::launch_w8a8_tiled(g, s)); break;
+        case BG_ALGO_TILED: note_kernel(bg::launch_w8a8_tiled(g, with_ws ? ws : nullptr, s)); break;
         default: return fail(BG_ERR_UNSUPPORTED, "gemm_w8a8: unknown algo %lld", algo);
     }
     return launched("gemm_w8a8");
+}
+
+BG_EXPORT bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran, const void* w,
+                                 const float* w_scales, int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K,
+                                 void* y, int out_dtype, int algo, void* stream) {
+    return w8a8_impl(a, a_scales, a_gran, w, w_scales, w_gran, in_dtype, M, N, K, y, out_dtype, nullptr, 0, false,
+                     algo, stream);
+}
+
+BG_EXPORT bg_status gemm_w8a8_ws(const void* a, const float* a_scales, int a_gran, const void* w,
+                                 const float* w_scales, int w_gran, int in_dtype, int64_t M, int64_t N, int64_t K,
+                                 void* y, int out_dtype, void* workspace, int64_t workspace_bytes, int algo,
+                                 void* stream) {
+    return w8a8_impl(a, a_scales, a_gran, w, w_scales, w_gran, in_dtype, M, N, K, y, out_dtype, workspace,
+                     workspace_bytes, true, algo, stream);
+}
+
+BG_EXPORT int64_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran, int algo) {
+    if (M < 1 || M > kMaxM || N < 16 || N > kMaxRows || N % 16 || K < 128 || K > kMaxDim || K % 128) return 0;
+    if (algo == BG_ALGO_AUTO) algo = w8_auto_algo_ws(M, N, K, in_dtype, a_gran);
+    if (algo != BG_ALGO_TILED) return 0;
+    bg::W8A8Args g{nullptr, nullptr, a_gran, nullptr, nullptr, 0, in_dtype == BG_FP8_E4M3, M, N, K, nullptr, BG_BF16};
+    return bg::w8a8_tiled_split(g, true).ws_bytes;
 }
 
 BG_EXPORT bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran, const void* w,

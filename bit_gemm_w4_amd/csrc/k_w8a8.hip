@@ -55,7 +55,8 @@ template <bool FP8, bool BLOCK, int BM, int BN, int WN>
 __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       int a_gran, const uint8_t* __restrict__ w,
                                                       const float* __restrict__ ws, int w_gran, int64_t M,
-                                                      int64_t N, int64_t K, void* __restrict__ y, int out_dt) {
+                                                      int64_t N, int64_t K, void* __restrict__ y, int out_dt,
+                                                      void* __restrict__ part, int S, int spl) {
     constexpr int NW = 2 * WN;                                   // waves
     constexpr int WTM = BM / 2, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
@@ -79,9 +80,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31, h = lane >> 5;
 
-    // ---- tile of this block ----
+    // ---- tile and K slice of this block: tile b % T, slice b / T (stages
+    // [sl spl, sl spl + spl) of 64 bytes) ----
     int tm, tn;
-    grouped_tile(blockIdx.x, (int)((M + BM - 1) / BM), (int)((N + BN - 1) / BN), tm, tn);
+    const int tiles_m = (int)((M + BM - 1) / BM), tiles_n = (int)((N + BN - 1) / BN);
+    const int sl = blockIdx.x / (tiles_m * tiles_n);
+    grouped_tile(blockIdx.x - sl * tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     // ---- global -> LDS copies (rows past M or N read as zero) ----
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         voff[t] = (uint32_t)(r * K) + (uint32_t)((((lane & 3) ^ gswz(r)) << 4));
     }
     const int nkb = (int)(K / GK);
+    const int kb0 = sl * spl, kb1 = kb0 + spl < nkb ? kb0 + spl : nkb;
     // Stage kb goes to buffer kb % NB.  Stages past the end of K copy bytes of
     // later rows (zeros past the end of the buffer resource) into a free
     // buffer that is never consumed.
@@ -231,13 +236,13 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     };
 
 #pragma unroll
-    for (int t = 0; t < NB; ++t) issue(t);
+    for (int t = 0; t < NB; ++t) issue(kb0 + t);
     wait_vmcnt<(NB - 1) * LOADS>();
     block_barrier();
     Frags<TM, TN> f0, f1;
 #pragma unroll
-    for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(0), r);
-    for (int kb = 0; kb < nkb; kb += 2) {                        // K is a multiple of 128: nkb is even
+    for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(kb0), r);
+    for (int kb = kb0; kb < kb1; kb += 2) {                      // slices hold whole 128-byte K blocks
         step(f0, f1, kb);
         step(f1, f0, kb + 1);
     }
@@ -252,9 +257,15 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // 16-bit outputs are staged per wave in LDS (rows padded by 16 bytes) and
     // written back as 16-byte row segments; FP32 / INT32 go out directly as
     // 16-byte groups.
+    // A K slice of a split GEMM (S > 1) writes its raw partial through the same
+    // code to part[sl][M][N]: INT32 accumulators for INT8, FP32 for FP8 (block
+    // scales already applied); k_w8a8_reduce adds the slices and scales them.
     block_barrier();                                             // all waves done with the stage buffers
     const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
-    if (!FP8 && out_dt == O_I32) {
+    const bool split = S > 1;
+    if (split) y = static_cast<uint8_t*>(part) + (int64_t)sl * M * N * 4;
+    const int odt = split ? (FP8 ? O_F32 : O_I32) : out_dt;
+    if (!FP8 && odt == O_I32) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int64_t m = mw + i * 32 + l32;
@@ -277,10 +288,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int64_t m = mw + i * 32 + l32;
-        sa[i] = BLOCK ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
+        sa[i] = BLOCK || split ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
     }
     uint8_t* stage = lds + wave * WTM * EPI_PITCH;
-    const bool bf = out_dt == O_BF16;
+    const bool bf = odt == O_BF16;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         float sw[4][4];
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         for (int q4 = 0; q4 < 4; ++q4) {
             const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;
             float4 w4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            if (!BLOCK) {
+            if (!BLOCK && !split) {
                 if (w_gran == GT) w4 = make_float4(ws[0], ws[0], ws[0], ws[0]);
                 else w4 = n < N ? *reinterpret_cast<const float4*>(ws + n) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
@@ -306,7 +317,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                     if constexpr (BLOCK) v[r] = facc[i][j][4 * q4 + r];
                     else v[r] = ((float)acc[i][j][4 * q4 + r] * sa[i]) * sw[q4][r];
                 }
-                if (out_dt == O_F32) {
+                if (odt == O_F32) {
                     if (m < M && n < N)
                         *reinterpret_cast<float4*>(static_cast<float*>(y) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
                 } else {
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
             }
         }
     }
-    if (out_dt == O_F32) return;
+    if (odt == O_F32) return;
     // 16-bit outputs: this wave's tile was staged in LDS (rows padded by 16
     // bytes) and goes out as 16-byte row segments,
     // row by row: WTN * 2 bytes = WTN / 8 lanes per row
@@ -336,34 +347,137 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     }
 }
 
+// Sum of the S partial slices of the split-K GEMM, in slice order, then the
+// epilogue of the unsplit kernel: y = ((float)acc * s_a[m]) * s_w[n] (INT32
+// sums are exact, so INT8 results equal the unsplit kernel's), or the sum
+// itself for block-scaled FP8 (scales already applied) and raw INT32 output.
+// One thread per four consecutive outputs of a row.
+template <bool INT_PART>
+__global__ __launch_bounds__(256) void k_w8a8_reduce(const void* __restrict__ part, int S, int64_t M, int64_t N,
+                                                     const float* __restrict__ as, int a_gran,
+                                                     const float* __restrict__ ws, int w_gran, bool scaled,
+                                                     void* __restrict__ y, int out_dt) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= M * N) return;
+    const int64_t m = e / N, n = e - m * N;
+    constexpr int RB = 8;                                        // slices in flight per batch
+    int4_t vi = int4_t{0, 0, 0, 0};
+    float4 vf = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int b0 = 0; b0 < S; b0 += RB) {
+        int4_t pi[RB];
+        float4 pf[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r >= S) break;
+            if constexpr (INT_PART) pi[r] = *reinterpret_cast<const int4_t*>(static_cast<const int32_t*>(part) + (b0 + r) * M * N + e);
+            else pf[r] = *reinterpret_cast<const float4*>(static_cast<const float*>(part) + (b0 + r) * M * N + e);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r >= S) break;
+            if constexpr (INT_PART) vi += pi[r];
+            else if (b0 + r == 0) vf = pf[r];
+            else vf = make_float4(vf.x + pf[r].x, vf.y + pf[r].y, vf.z + pf[r].z, vf.w + pf[r].w);
+        }
+    }
+    if (INT_PART && out_dt == O_I32) {
+        *reinterpret_cast<int4_t*>(static_cast<int32_t*>(y) + e) = vi;
+        return;
+    }
+    float v[4];
+    if constexpr (INT_PART) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (float)vi[r];
+    } else {
+        v[0] = vf.x, v[1] = vf.y, v[2] = vf.z, v[3] = vf.w;
+    }
+    if (scaled) {
+        const float sa = a_gran == GT ? as[0] : as[m];
+        const float4 sw4 = w_gran == GT ? make_float4(ws[0], ws[0], ws[0], ws[0])
+                                        : *reinterpret_cast<const float4*>(ws + n);
+        v[0] = (v[0] * sa) * sw4.x, v[1] = (v[1] * sa) * sw4.y, v[2] = (v[2] * sa) * sw4.z, v[3] = (v[3] * sa) * sw4.w;
+    }
+    if (out_dt == O_F32) {
+        *reinterpret_cast<float4*>(static_cast<float*>(y) + e) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+        const bool bf = out_dt == O_BF16;
+        uint2 o;
+        o.x = bf ? (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16)
+                 : (uint32_t)f32_to_f16(v[0]) | ((uint32_t)f32_to_f16(v[1]) << 16);
+        o.y = bf ? (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16)
+                 : (uint32_t)f32_to_f16(v[2]) | ((uint32_t)f32_to_f16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + e) = o;
+    }
+}
+
 template <bool FP8, bool BLOCK, int BM, int BN, int WN>
-static const char* gemm_cfg(const W8A8Args& g, hipStream_t s) {
+static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN>), dim3((unsigned)tiles), dim3(128 * WN), 0, s,
+    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0, s,
                        static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
-                       g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt);
+                       g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt, ws, c.S, c.spl);
+    if (c.S > 1) {
+        const int64_t threads = g.M * g.N / 4;
+        const bool scaled = !BLOCK && g.out_dt != O_I32;
+        hipLaunchKernelGGL((k_w8a8_reduce<!FP8>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const void*>(ws), c.S, g.M, g.N, g.a_scales, g.a_gran, g.w_scales, g.w_gran,
+                           scaled, g.y, g.out_dt);
+    }
     return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN);
 }
 
 // Tile choice for the large-M GEMM: estimated time = rounds of resident
 // blocks x time of one round.  Relative round times (K fixed) measured on the
 // 4096..28672-wide projection shapes: 256 x 256 (one block per CU) 75,
-// 256 x 128 (one per CU) 46.4; 128 x 128 (two per CU, 47) never won on that
-// model, so only block-scaled FP8, which keeps two accumulator sets, uses it.
-template <int BM, int BN, int WN>
-static const char* gemm_dispatch(const W8A8Args& g, hipStream_t s) {
-    if (!g.in_fp8) return gemm_cfg<false, false, BM, BN, WN>(g, s);
-    return gemm_cfg<true, false, BM, BN, WN>(g, s);
+// 256 x 128 (one per CU) 46.4; block-scaled FP8, which keeps two accumulator
+// sets, uses 128 x 128 (two per CU).  With a workspace, grids of less than
+// half a round split K (S = min(blocks per round / tiles, 128-byte K blocks /
+// 8) slices of whole 128-byte blocks); M <= 128 then uses 128 x 128 tiles
+// (two blocks per CU) rather than half-empty 256-row ones.
+W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
+    W8Split c{};
+    c.S = 1;
+    c.spl = (int)(g.K / GK);
+    const bool block = g.in_fp8 && g.a_gran == GR128;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
+    auto cost = [&](int64_t bm, int64_t bn, double round) { return (double)((tiles(bm, bn) + 255) / 256) * round; };
+    if (block) c.bm = 128, c.bn = 128;
+    else if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) c.bm = 256, c.bn = 256;
+    else c.bm = 256, c.bn = 128;
+    if (!with_ws || tiles(c.bm, c.bn) >= 128) return c;         // half a round or more: no split
+    const int64_t nk128 = g.K >> 7;
+    const bool small_m = g.M <= 128;
+    const int64_t bm = small_m ? 128 : c.bm, bn = small_m ? 128 : c.bn;
+    const int64_t per_round = bm == 128 ? 512 : 256;             // resident blocks per round
+    const int64_t t = tiles(bm, bn);
+    int64_t S = per_round / t;
+    if (S > nk128 / 8) S = nk128 / 8;
+    if (S < 2) return c;
+    const int64_t per = (nk128 + S - 1) / S;                     // 128-byte K blocks per slice
+    S = (nk128 + per - 1) / per;
+    if (S < 2) return c;
+    c.bm = (int)bm, c.bn = (int)bn;
+    c.S = (int)S;
+    c.spl = (int)(2 * per);
+    c.ws_bytes = S * g.M * g.N * 4;
+    return c;
 }
 
-const char* launch_w8a8_tiled(const W8A8Args& g, hipStream_t s) {
-    if (g.in_fp8 && g.a_gran == GR128) return gemm_cfg<true, true, 128, 128, 2>(g, s);
-    auto cost = [&](int64_t bm, int64_t bn, double round) {
-        const int64_t tiles = ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn);
-        return (double)((tiles + 255) / 256) * round;
-    };
-    if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) return gemm_dispatch<256, 256, 2>(g, s);
-    return gemm_dispatch<256, 128, 2>(g, s);
+template <bool FP8, bool BLOCK>
+static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
+    if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2>(g, c, ws, s);
+    if constexpr (!BLOCK) {
+        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 2>(g, c, ws, s);
+        return gemm_cfg<FP8, false, 256, 128, 2>(g, c, ws, s);
+    }
+    return nullptr;
+}
+
+const char* launch_w8a8_tiled(const W8A8Args& g, void* ws, hipStream_t s) {
+    const W8Split c = w8a8_tiled_split(g, ws != nullptr);
+    if (g.in_fp8 && g.a_gran == GR128) return gemm_shape<true, true>(g, c, ws, s);
+    if (g.in_fp8) return gemm_shape<true, false>(g, c, ws, s);
+    return gemm_shape<false, false>(g, c, ws, s);
 }
 
 

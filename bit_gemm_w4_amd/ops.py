@@ -25,7 +25,7 @@ PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
-    "gemm_w8a8_ex", "gemm_w4a16_algo", "gemm_w8a8_algo", "bg_status_string", "bg_last_error",
+    "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a16_algo", "gemm_w8a8_algo", "bg_status_string", "bg_last_error",
     "bg_pack_format_version", "bg_last_kernel",
 )
 
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
             "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
             "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
+            "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
+            "gemm_w8a8_workspace_bytes": [I64, I64, I64, I, I, I],
             "gemm_w4a16_algo": [I64, I64, I64, I],
             "gemm_w8a8_algo": [I64, I64, I64, I],
             "bg_status_string": [I],
@@ -72,7 +74,7 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = argtypes
             fn.restype = (ctypes.c_char_p if name in ("bg_status_string", "bg_last_error", "bg_last_kernel")
-                          else ctypes.c_int64 if name == "gemm_w4a16_workspace_bytes" else ctypes.c_int)
+                          else ctypes.c_int64 if name.endswith("_workspace_bytes") else ctypes.c_int)
         _lib = L
     return _lib
 
@@ -216,9 +218,18 @@ def act_quant_fp8(x: torch.Tensor, gran: int = GRAN_ROW, stream=None):
 _OUT_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32}
 
 
+def gemm_w8a8_workspace_bytes(M: int, N: int, K: int, fp8: bool = False, a_gran: int = GRAN_ROW,
+                              algo: int = ALGO_AUTO) -> int:
+    return int(lib().gemm_w8a8_workspace_bytes(M, N, K, FP8_E4M3 if fp8 else I8, a_gran, algo))
+
+
 def gemm_w8a8(a: torch.Tensor, a_scales: torch.Tensor | None, a_gran: int, w: torch.Tensor,
               w_scales: torch.Tensor | None, w_gran: int, out_dtype: torch.dtype = torch.bfloat16,
-              out: torch.Tensor | None = None, algo: int = ALGO_AUTO, stream=None) -> torch.Tensor:
+              out: torch.Tensor | None = None, algo: int = ALGO_AUTO, ws: torch.Tensor | None | bool = None,
+              stream=None) -> torch.Tensor:
+    """Y = A W^T on the INT8 / FP8 matrix cores.  ws: a workspace tensor, None
+    to use the cached per-device workspace (enables split-K of the large-M
+    kernel), or False for none."""
     M, K = a.shape
     N, K2 = w.shape
     if K != K2:
@@ -231,8 +242,17 @@ def gemm_w8a8(a: torch.Tensor, a_scales: torch.Tensor | None, a_gran: int, w: to
         raise ValueError("gemm_w8a8: operands must both be int8 or both E4M3 bytes (uint8)")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
-    _check(lib().gemm_w8a8_ex(_ptr(a), _ptr(a_scales), a_gran, _ptr(w), _ptr(w_scales), w_gran, in_dt, M, N, K,
+    L = lib()
+    if ws is False:
+        _check(L.gemm_w8a8_ex(_ptr(a), _ptr(a_scales), a_gran, _ptr(w), _ptr(w_scales), w_gran, in_dt, M, N, K,
                               _ptr(out), _OUT_DT[out.dtype], algo, _stream(stream)), "gemm_w8a8")
+        return out
+    if ws is None:
+        need = int(L.gemm_w8a8_workspace_bytes(M, N, K, in_dt, a_gran, algo))
+        ws = workspace(need, a.device) if need > 0 else None
+    _check(L.gemm_w8a8_ws(_ptr(a), _ptr(a_scales), a_gran, _ptr(w), _ptr(w_scales), w_gran, in_dt, M, N, K,
+                          _ptr(out), _OUT_DT[out.dtype], _ptr(ws), 0 if ws is None else ws.numel(), algo,
+                          _stream(stream)), "gemm_w8a8")
     return out
 
 

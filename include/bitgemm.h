@@ -212,6 +212,35 @@ bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran,
                        int in_dtype, int64_t M, int64_t N, int64_t K,
                        void* y, int out_dtype, int algo, void* stream);
 
+/*
+ * gemm_w8a8_ws -- gemm_w8a8 with a caller-provided device workspace, which
+ * lets the large-M kernel (BG_ALGO_TILED, or AUTO when it picks that kernel)
+ * split K across workgroups when its output tiles would fill less than one
+ * round of the device: S = min(tiles per round / tiles, (K / 128) / 8) slices
+ * of whole 128-wide K blocks, 128 x 128 tiles for M <= 128.  Each slice writes
+ * its raw partial sums (INT32 for INT8, so the result equals the unsplit
+ * kernel's bit for bit; FP32 for FP8, already block-scaled for 128 x 128
+ * blocks) to the workspace, and a second kernel, enqueued on the same stream,
+ * adds the slices in a fixed order and applies the scales.
+ *   workspace        16-byte aligned device memory of at least
+ *                    gemm_w8a8_workspace_bytes(M, N, K, in_dtype, a_gran,
+ *                    algo) bytes (S * M * N * 4 when K is split, else 0).  It
+ *                    needs no initialisation and its contents afterwards
+ *                    are unspecified.  Calls that share a workspace must not
+ *                    overlap in time.  May be NULL when the size is 0.
+ *   workspace_bytes  its size; BG_ERR_WORKSPACE if smaller than required.
+ * Other arguments, layouts and errors as gemm_w8a8.
+ */
+bg_status gemm_w8a8_ws(const void* a, const float* a_scales, int a_gran,
+                       const void* w, const float* w_scales, int w_gran,
+                       int in_dtype, int64_t M, int64_t N, int64_t K,
+                       void* y, int out_dtype, void* workspace, int64_t workspace_bytes,
+                       int algo, void* stream);
+
+/* Workspace bytes gemm_w8a8_ws needs for this shape, input type, activation
+ * granularity and kernel choice (0 if none; BG_ALGO_AUTO = AUTO's choice). */
+int64_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran, int algo);
+
 /* The kernel BG_ALGO_AUTO selects for a call of this shape (a BG_ALGO_* value). */
 int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype);
 int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype);

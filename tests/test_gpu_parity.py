@@ -315,6 +315,34 @@ def test_w8a8_out_dtypes_wide_tiles(ops, orc, fp8, a_gran, w_gran, out):
     _w8a8_case(ops, orc, 2048, 8192, 256, fp8, a_gran, w_gran, 3, out_dtype=out, rows=[0, 255, 256, 1000, 2047])
 
 
+@pytest.mark.parametrize("M", [64, 130, 300])
+@pytest.mark.parametrize("fp8,a_gran,w_gran,out", [
+    (False, 1, 1, torch.int32), (False, 1, 1, torch.bfloat16), (True, 0, 0, torch.float32),
+    (True, 2, 3, torch.bfloat16)])
+def test_w8a8_splitk(ops, orc, M, fp8, a_gran, w_gran, out):
+    # 8 or 16 output tiles over 32 K blocks of 128: K is split into 4 slices
+    N, K = 1024, 4096
+    assert ops.gemm_w8a8_workspace_bytes(M, N, K, fp8, a_gran, 3) == 4 * M * N * 4
+    _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, 3, out_dtype=out, seed=M)
+
+
+def test_w8a8_splitk_matches_unsplit_int8(ops):
+    """INT32 slice sums are exact: split and unsplit INT8 results agree bit for bit."""
+    M, N, K = 130, 1024, 4096
+    g = torch.Generator().manual_seed(7)
+    a = torch.randint(-127, 128, (M, K), generator=g, dtype=torch.int8).cuda()
+    w = torch.randint(-127, 128, (N, K), generator=g, dtype=torch.int8).cuda()
+    sa = (torch.rand(M, generator=g) * 0.01 + 1e-3).cuda()
+    sw = (torch.rand(N, generator=g) * 0.01 + 1e-3).cuda()
+    for out in (torch.int32, torch.bfloat16, torch.float32):
+        s_a, s_w = (None, None) if out == torch.int32 else (sa, sw)
+        y1 = ops.gemm_w8a8(a, s_a, 1, w, s_w, 1, out_dtype=out, algo=3, ws=False)
+        y2 = ops.gemm_w8a8(a, s_a, 1, w, s_w, 1, out_dtype=out, algo=3)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int32) if out != torch.bfloat16 else y1.view(torch.int16),
+                           y2.view(torch.int32) if out != torch.bfloat16 else y2.view(torch.int16)), out
+
+
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
 def test_w8a8_int8_prefill_shapes(ops, orc, name):
     K, N = synth.LLAMA3_8B_SHAPES[name]
