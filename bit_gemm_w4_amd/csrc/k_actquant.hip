@@ -66,19 +66,21 @@ __device__ __forceinline__ float block_max256(float a, float* red) {
     return a;
 }
 
-// ---- per row (token / output channel), rows up to 256 * 8 * MAXIT long ----
+// ---- per row (token / output channel), rows up to 256 * 8 * IT long ----
+// IT (chunks of 8 per thread) is sized to the row, so short rows keep few
+// registers and many rows resident per CU.
 constexpr int ROW_MAXIT = 8;
 
-template <int DT, bool FP8>
+template <int DT, bool FP8, int IT>
 __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, int64_t C,
                                                    void* __restrict__ q, float* __restrict__ scales) {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const int64_t nchunk = C >> 3;
-    float v[ROW_MAXIT][8];
+    float v[IT][8];
     float a = 0.0f;
 #pragma unroll
-    for (int it = 0; it < ROW_MAXIT; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int64_t c = (int64_t)it * 256 + threadIdx.x;
         if (c < nchunk) {
             load8_f32<DT>(x, r * C + c * 8, v[it]);
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, i
     }
     const float s = unit_scale<FP8>(block_max256(a, red));
 #pragma unroll
-    for (int it = 0; it < ROW_MAXIT; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int64_t c = (int64_t)it * 256 + threadIdx.x;
         if (c < nchunk) quant_store8<FP8>(v[it], s, q, r * C + c * 8);
     }
@@ -178,7 +180,15 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x,
             if (c0 + u * stride < nchunk) a = __builtin_fmaxf(a, amax8(v[u]));
     }
     a = block_max256(a, red);
-    if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(scales + 1), __float_as_uint(a));
+    // Only blocks that would raise the running maximum take the atomic (all
+    // blocks hitting one address serialize); the check reads the slot at
+    // agent scope (not a stale cache line), and the value only grows, so a
+    // skipped block never held a larger maximum.
+    if (threadIdx.x == 0) {
+        const unsigned cur = __hip_atomic_load(reinterpret_cast<unsigned int*>(scales + 1), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (__float_as_uint(a) > cur) atomicMax(reinterpret_cast<unsigned int*>(scales + 1), __float_as_uint(a));
+    }
 }
 
 template <int DT, bool FP8>
@@ -210,9 +220,17 @@ static const char* launch_typed(const void* x, int64_t R, int64_t C, int gran, v
                          hipStream_t s) {
     switch (gran) {
         case G_ROW:
-            if (C <= 256 * 8 * ROW_MAXIT)
-            {
-                hipLaunchKernelGGL((k_quant_row<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+            if (C <= 256 * 8 * ROW_MAXIT) {
+                const int64_t per = (C / 8 + 255) / 256;         // chunks per thread
+                if (per <= 1)
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 1>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                else if (per <= 2)
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 2>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                else if (per <= 4)
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 4>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                else
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, ROW_MAXIT>), dim3((unsigned)R), dim3(256), 0, s, x, C,
+                                       q, sc);
                 return kname("k_quant_row", DT, FP8);
             }
             hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);

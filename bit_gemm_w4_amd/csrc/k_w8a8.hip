@@ -430,7 +430,7 @@ static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipSt
 // blocks x time of one round.  Relative round times (K fixed) measured on the
 // 4096..28672-wide projection shapes: 256 x 256 (one block per CU) 75,
 // 256 x 128 (one per CU) 46.4; block-scaled FP8, which keeps two accumulator
-// sets, uses 128 x 128 (two per CU).  With a workspace, grids of less than
+// sets, uses 128 x 128 (two per CU).  With a workspace, grids of at most
 // half a round split K (S = min(blocks per round / tiles, 128-byte K blocks /
 // 8) slices of whole 128-byte blocks); M <= 128 then uses 128 x 128 tiles
 // (two blocks per CU) rather than half-empty 256-row ones.
@@ -444,7 +444,7 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     if (block) c.bm = 128, c.bn = 128;
     else if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) c.bm = 256, c.bn = 256;
     else c.bm = 256, c.bn = 128;
-    if (!with_ws || tiles(c.bm, c.bn) >= 128) return c;         // half a round or more: no split
+    if (!with_ws || tiles(c.bm, c.bn) > 128) return c;          // over half a round: no split
     const int64_t nk128 = g.K >> 7;
     const bool small_m = g.M <= 128;
     const int64_t bm = small_m ? 128 : c.bm, bn = small_m ? 128 : c.bn;

@@ -139,6 +139,7 @@ def w4_pack(w: torch.Tensor, group: int = 128, asymmetric: bool = False, stream=
 
 
 _workspaces: dict = {}
+_retired: list = []
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:
@@ -148,6 +149,8 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     key = torch.device(device).index or 0
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if ws is not None:
+            _retired.append(ws)       # HIP graphs captured earlier may still use it
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
