@@ -215,9 +215,12 @@ bg_status gemm_w8a8_ex(const void* a, const float* a_scales, int a_gran,
 /*
  * gemm_w8a8_ws -- gemm_w8a8 with a caller-provided device workspace, which
  * lets the large-M kernel (BG_ALGO_TILED, or AUTO when it picks that kernel)
- * split K across workgroups when its output tiles would fill less than one
- * round of the device: S = min(tiles per round / tiles, (K / 128) / 8) slices
- * of whole 128-wide K blocks, 128 x 128 tiles for M <= 128.  Each slice writes
+ * split K across workgroups when its output tiles would fill at most half a
+ * round of the device (128 tiles): S = min(tiles per round / tiles,
+ * (K / 128) / 8) slices of whole 128-wide K blocks, 128 x 128 tiles for
+ * M <= 128.  AUTO with a workspace picks this path where it measured faster
+ * than the small-M kernel: N >= 6144 at any M, K >= 8192 from M = 4, and
+ * otherwise from M = 32.  Each slice writes
  * its raw partial sums (INT32 for INT8, so the result equals the unsplit
  * kernel's bit for bit; FP32 for FP8, already block-scaled for 128 x 128
  * blocks) to the workspace, and a second kernel, enqueued on the same stream,
