@@ -68,7 +68,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int NB = NB_FIT > NB_MAX ? NB_MAX : NB_FIT;
     static_assert(ROWS % (16 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
-    static_assert(NB >= 3 && (NB - 1) * LOADS < 64, "stage count / vmcnt range");
+    static_assert(NB >= 3 && (NB - 1) * LOADS + (BLOCK ? 4 * TM : 0) < 64, "stage count / vmcnt range");
+    static_assert(!BLOCK || NB == 5, "the block-scale load count in the stage waits assumes five buffers");
     constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
     constexpr int EPI_BYTES = NW * WTM * EPI_PITCH;
     constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
@@ -166,16 +167,36 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
             for (int j = 0; j < TN; ++j) facc[i][j] = float16_t{};
     }
-    // every second stage closes a 128-wide K block: facc += partial * s_a[m][kb] * s_w[n/128][kb]
-    auto close_block = [&](int kb) {
+    // every second stage closes a 128-wide K block: facc += partial * s_a[m][kb] * s_w[n/128][kb].
+    // The scales of K block c are loaded at the close of block c - SCP (a ring
+    // of SCP blocks in registers, rotated at every close), so most of their
+    // latency is hidden.  The loads are unconditional (rows past M read row
+    // M - 1, blocks past the end of K the last one): every wave issues exactly
+    // TM vector loads per close, which the stage waits below count.
+    constexpr int SCP = 4;
+    const int64_t nkb128 = K >> 7;
+    const int64_t nbw = (n0 + wn * WTN) >> 7;                    // this wave's 128-column weight block
+    float sa_ring[BLOCK ? SCP : 1][BLOCK ? TM : 1];
+    float sw_ring[BLOCK ? SCP : 1];
+    auto load_scales = [&](float (&sa)[BLOCK ? TM : 1], float& sw, int64_t c) {
         if constexpr (BLOCK) {
-            const int64_t nkb128 = K >> 7, kb128 = kb >> 1;
-            const int64_t nb = (n0 + wn * WTN) >> 7;
-            const float sw = n0 + wn * WTN < N ? ws[nb * nkb128 + kb128] : 0.0f;
+            const int64_t cc = c < nkb128 ? c : nkb128 - 1;
+            sw = ws[(nbw < (N >> 7) ? nbw : (N >> 7) - 1) * nkb128 + cc];
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int64_t m = m0 + wm * WTM + i * 32 + l32;
-                const float sc = (m < M ? as[m * nkb128 + kb128] : 0.0f) * sw;
+                sa[i] = as[(m < M ? m : M - 1) * nkb128 + cc];
+            }
+        }
+    };
+    auto close_block = [&](int kb) {
+        if constexpr (BLOCK) {
+            const int64_t kb128 = kb >> 1;
+            const bool n_ok = n0 + wn * WTN < N;
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int64_t m = m0 + wm * WTM + i * 32 + l32;
+                const float sc = (m < M && n_ok) ? sa_ring[0][i] * sw_ring[0] : 0.0f;
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
 #pragma unroll
@@ -183,6 +204,13 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                     acc[i][j] = acc_t{};
                 }
             }
+#pragma unroll
+            for (int r = 0; r + 1 < SCP; ++r) {
+                sw_ring[r] = sw_ring[r + 1];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) sa_ring[r][i] = sa_ring[r + 1][i];
+            }
+            load_scales(sa_ring[SCP - 1], sw_ring[SCP - 1], kb128 + SCP);
         }
     };
 
@@ -196,7 +224,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int NSLOT = NMFMA - NMFMA / 4;
     auto step = [&](Frags<TM, TN>& cur, Frags<TM, TN>& nxt, int kb) {
         settle_frags(cur);
-        wait_vmcnt<(NB - 2) * LOADS>();                          // this wave's copies of stage kb+1 landed
+        // this wave's copies of stage kb+1 landed: younger than them are the
+        // copies of the NB-2 later stages and, with block scales, the scale
+        // loads of the two closes among the last four steps (NB = 5)
+        wait_vmcnt<(NB - 2) * LOADS + (BLOCK ? 2 * TM : 0)>();
         block_barrier();
         const uint32_t nb_base = stage_base(kb + 1);
         // reads of stage kb+1 follow the first NSLOT MFMAs (NREAD/NSLOT per MFMA,
@@ -237,7 +268,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 
 #pragma unroll
     for (int t = 0; t < NB; ++t) issue(kb0 + t);
-    wait_vmcnt<(NB - 1) * LOADS>();
+    if constexpr (BLOCK) {
+        // ring for the first SCP blocks, issued after the copies (so at least
+        // 2 TM scale loads are younger than every stage's copies, as the step
+        // waits assume)
+#pragma unroll
+        for (int r = 0; r < SCP; ++r) load_scales(sa_ring[r], sw_ring[r], kb0 / 2 + r);
+    }
+    wait_vmcnt<(NB - 1) * LOADS + (BLOCK ? SCP * TM : 0)>();
     block_barrier();
     Frags<TM, TN> f0, f1;
 #pragma unroll
