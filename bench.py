@@ -396,8 +396,16 @@ def cpu_baseline(w_host, xs, calls, target_s, np, synth, roofline):
         if done_s >= target_s or time.time() - t_start > 3 * target_s or sample >= 28672:
             break
         sample = min(28672, int(sample * max(2.0, min(8.0, target_s / max(s_round, 1e-3)))))
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(done_bytes / done_s / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model, "kind": "oracle",
             "sample": f"same 12 W4A16 decode calls restricted to the first <= {sample} output channels "
                       f"of each layer; {done_s:.1f} s of oracle time (binary64 dequantized GEMM)"}
 
