@@ -106,10 +106,10 @@ def test_w4_pack_full_shape(ops, orc, name):
 
 # --------------------------------------------------------------- gemm_w4a16 ----
 
-def _w4a16_case(ops, orc, M, N, K, x_dtype, asym, algo, seed, rows=None):
+def _w4a16_case(ops, orc, M, N, K, x_dtype, asym, algo, seed, rows=None, ws=None):
     w, x = synth.layer(M, N, K, x_dtype, seed=seed, w_outlier_frac=0.01)
     p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, asym)
-    y = ops.gemm_w4a16(dev_bits(x, x_dtype), p, algo=algo)
+    y = ops.gemm_w4a16(dev_bits(x, x_dtype), p, algo=algo, ws=ws)
     torch.cuda.synchronize()
     qw, s, z = orc.w4_pack(w, 128, asym)
     sel = np.arange(M) if rows is None else np.asarray(rows)
@@ -272,14 +272,15 @@ def test_fp8_encoder_rounding(ops, orc):
 
 # ----------------------------------------------------------------- gemm_w8a8 ----
 
-def _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, algo, out_dtype=torch.bfloat16, rows=None, seed=0):
+def _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, algo, out_dtype=torch.bfloat16, rows=None, seed=0,
+               ws=None):
     w, x = synth.prefill_layer(M, N, K, seed=seed)
     xt = dev_bits(x, "bf16")
     wt = torch.from_numpy(w).cuda()
     quant = ops.act_quant_fp8 if fp8 else ops.act_quant_int8
     a, a_s = quant(xt, a_gran)
     wq, w_s = quant(wt, w_gran)
-    y = ops.gemm_w8a8(a, a_s, a_gran, wq, w_s, w_gran, out_dtype=out_dtype, algo=algo)
+    y = ops.gemm_w8a8(a, a_s, a_gran, wq, w_s, w_gran, out_dtype=out_dtype, algo=algo, ws=ws)
     torch.cuda.synchronize()
     oquant = orc.act_quant_fp8 if fp8 else orc.act_quant_int8
     ao, aso = oquant(orc.bits_to_f32(x, "bf16"), a_gran)
@@ -357,3 +358,63 @@ def test_w8a8_fp8_shapes(ops, orc, name, variant):
     K, N = synth.LLAMA3_8B_SHAPES[name]
     a_gran, w_gran = (0, 0) if variant == "tensor" else (2, 3)
     _w8a8_case(ops, orc, 512, N, K, True, a_gran, w_gran, 0, rows=[0, 5, 300, 511])
+
+
+# ------------------------------------------------------------------ fuzz ----
+# Seeded random shapes, types, granularities and kernel choices (with and
+# without a workspace), each against the oracle: ragged M, N and K across the
+# small-M, tiled and split-K paths.
+
+def _w4_fuzz_cases(n=60, seed=20261):
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        M = int(rs.choice([1, 2, 3, 5, 8, 13, 16, 21, 33, 47, 64, 65, 97, 130, 200, 257, 300]))
+        N = 16 * int(rs.randint(1, 96))
+        K = 256 * int(rs.randint(1, 24))
+        dt = str(rs.choice(["bf16", "f16"]))
+        asym = bool(rs.randint(2))
+        algo = int(rs.choice([0, 1, 2, 3, 4]))
+        if algo == 1 and M > 256:
+            algo = 2
+        ws = None if (algo == 4 or rs.randint(2)) else False
+        out.append((M, N, K, dt, asym, algo, ws, 1000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _w4_fuzz_cases(), ids=lambda c: "M%d_N%d_K%d_%s_a%d_algo%d_%s" % (
+    c[0], c[1], c[2], c[3], c[4], c[5], "ws" if c[6] is None else "nows"))
+def test_w4a16_fuzz(ops, orc, case):
+    M, N, K, dt, asym, algo, ws, seed = case
+    _w4a16_case(ops, orc, M, N, K, dt, asym, algo, seed=seed, ws=ws)
+
+
+def _w8_fuzz_cases(n=60, seed=20262):
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        M = int(rs.choice([1, 2, 4, 7, 16, 31, 64, 100, 128, 129, 200, 300]))
+        fp8 = bool(rs.randint(2))
+        if fp8:
+            a_gran, w_gran = [(0, 0), (1, 1), (0, 1), (1, 0), (2, 3)][rs.randint(5)]
+        else:
+            a_gran, w_gran = [(1, 1), (0, 1), (1, 0), (0, 0)][rs.randint(4)]
+        block = (a_gran, w_gran) == (2, 3)
+        N = 128 * int(rs.randint(1, 12)) if block else 16 * int(rs.randint(1, 96))
+        K = 128 * int(rs.randint(1, 40))
+        outs = [torch.bfloat16, torch.float16, torch.float32] + ([torch.int32] if not fp8 else [])
+        out_dtype = outs[rs.randint(len(outs))]
+        if out_dtype == torch.int32:
+            a_gran, w_gran = 1, 1
+        algo = int(rs.choice([0, 2, 3]))
+        ws = None if rs.randint(2) else False
+        out.append((M, N, K, fp8, a_gran, w_gran, out_dtype, algo, ws, 2000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _w8_fuzz_cases(), ids=lambda c: "M%d_N%d_K%d_%s_g%d%d_%s_algo%d_%s" % (
+    c[0], c[1], c[2], "fp8" if c[3] else "i8", c[4], c[5], str(c[6]).split(".")[-1], c[7],
+    "ws" if c[8] is None else "nows"))
+def test_w8a8_fuzz(ops, orc, case):
+    M, N, K, fp8, a_gran, w_gran, out_dtype, algo, ws, seed = case
+    _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, algo, out_dtype=out_dtype, seed=seed, ws=ws)
