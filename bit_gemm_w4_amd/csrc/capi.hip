@@ -80,12 +80,13 @@ int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
 // With a workspace, small M runs split-K where the small-M kernel's per-block
 // re-staging of the activation rows costs more than split-K's cross-block
 // reduction: from the measured crossovers (graph-replayed, cold weights) on
-// the 4096/14336-wide projection shapes.
+// the 4096/14336-wide projection shapes (N = 6144 and 4096 at K = 4096 stay
+// on the small-M kernel through M = 16).
 // Past the small-M range, split-K (of the large-M kernel) while its output
 // tiles do not fill the device.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
     if (M > kW4SkinnyMax) return bg::w4a16_gemm_split(M, N, K).S > 1 ? BG_ALGO_SPLITK : BG_ALGO_TILED;
-    const bool split = (M >= 8 && (N >= 16384 || K >= 8192)) || (M >= 12 && N > 4096) || M >= 24;
+    const bool split = (M >= 8 && (N >= 16384 || K >= 8192)) || (M > 16 && N > 4096) || M >= 24;
     return split ? BG_ALGO_SPLITK : BG_ALGO_SKINNY;
 }
 

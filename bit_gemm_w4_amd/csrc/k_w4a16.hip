@@ -76,6 +76,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     constexpr bool VALU = VROWS > 0;
     static_assert(!VALU || (XLDS && TM == 1), "the VALU product reads activations from LDS");
     constexpr int STAGES = XLDS ? 4 : 3;
+    constexpr int XB = 8;                                              // X staging batch
     constexpr int BAND = VALU ? VROWS : 16 * TM;                       // activation rows per block
     constexpr float MV = W4Magic<BF16>::value;
     constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
@@ -150,12 +151,25 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     for (int s = 0; s < STAGES; ++s) issue(stage[s], s);
 
     if constexpr (XLDS) {
-        // copy rows [m0, m0 + rows) of X into LDS, 16 bytes per thread per pass
-        const int64_t chunks_per_row = K >> 3;
-        for (int64_t c = threadIdx.x; c < rows * chunks_per_row; c += NW * 64) {
-            const int64_t r = c / chunks_per_row, kc = c - r * chunks_per_row;
-            *reinterpret_cast<uint4*>(dyn_lds + (r * xstride + kc * 8) * 2) =
-                *reinterpret_cast<const uint4*>(x + (m0 + r) * K + kc * 8);
+        // copy rows [m0, m0 + rows) of X into LDS: 16-byte chunks, XB per
+        // thread in flight together (one memory round trip per batch)
+        const int cpr = (int)(K >> 3);                                 // chunks per row
+        const int total = (int)rows * cpr;
+        for (int c0 = threadIdx.x; c0 < total; c0 += XB * NW * 64) {
+            uint4 v[XB];
+#pragma unroll
+            for (int u = 0; u < XB; ++u)
+                if (c0 + u * NW * 64 < total)
+                    v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rx, (c0 + u * NW * 64) * 16, 0, 0));
+#pragma unroll
+            for (int u = 0; u < XB; ++u) {
+                const int c = c0 + u * NW * 64;
+                if (c < total) {
+                    const int r = c / cpr, kc = c - r * cpr;
+                    *reinterpret_cast<uint4*>(dyn_lds + ((int64_t)r * xstride + kc * 8) * 2) = v[u];
+                }
+            }
         }
         __syncthreads();
         if constexpr (VALU) {
@@ -376,6 +390,9 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
     const auto rz = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(has_z ? zr + ((int64_t)tt * (ngroups >> 1) + zb0) * 16 : zr), (short)0,
         (tok && has_z) ? (zb1 - zb0 + 1) * 16 : 0, 0x00020000);
+    // X from the slice's first column; the last valid byte is the end of row rows-1
+    const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (int64_t)g0 * 128), (short)0,
+                                                      (int)(((int64_t)(rows - 1) * K + ng * 128) * 2), 0x00020000);
 
     auto issue = [&](SpkStage& st, int i) {
         const int gl = i < ng - 1 ? i : ng - 1;
@@ -387,12 +404,29 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
 #pragma unroll
     for (int st = 0; st < STAGES; ++st) issue(stage[st], st);
 
-    // stage X[0:rows, slice] (16-byte chunks), then the per-group row sums
+    // stage X[0:rows, slice] (16-byte chunks, XB per thread in flight
+    // together), then the per-group row sums
+    constexpr int XB = 4;
     const int cpr = ng * 16;                                            // chunks per row
-    for (int c = threadIdx.x; c < rows * cpr; c += NW * 64) {
-        const int r = c / cpr, kc = c - r * cpr;
-        *reinterpret_cast<uint4*>(xl + r * xpitch + kc * 8) =
-            *reinterpret_cast<const uint4*>(x + (int64_t)r * K + (int64_t)g0 * 128 + kc * 8);
+    const int total = rows * cpr;
+    for (int c0 = threadIdx.x; c0 < total; c0 += XB * NW * 64) {
+        uint4 v[XB];
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            const int c = c0 + u * NW * 64;
+            const int r = c / cpr, kc = c - r * cpr;
+            if (c < total)
+                v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rx, (int)(r * (int)K * 2) + kc * 16, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            const int c = c0 + u * NW * 64;
+            if (c < total) {
+                const int r = c / cpr, kc = c - r * cpr;
+                *reinterpret_cast<uint4*>(xl + r * xpitch + kc * 8) = v[u];
+            }
+        }
     }
     __syncthreads();
     for (int e = threadIdx.x; e < ng * BAND; e += NW * 64) {

@@ -125,7 +125,7 @@ bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
  * enables the split-K kernels (BG_ALGO_SPLITK):
  *   M <= 64  the small-M split-K kernel.  BG_ALGO_AUTO picks it for M from 8
  *            to 64 where it measured faster than BG_ALGO_SKINNY: M >= 8 with
- *            N >= 16384 or K >= 8192, M >= 12 with N > 4096, or M >= 24.
+ *            N >= 16384 or K >= 8192, M >= 17 with N > 4096, or M >= 24.
  *            Splitting K across workgroups lets each workgroup reuse its
  *            activations across 16 weight tiles.
  *   M > 64   the large-M kernel with K split into S slices of whole groups

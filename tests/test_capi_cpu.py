@@ -97,6 +97,14 @@ def test_gemm_w4a16_workspace(L):
     need = L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 0)
     assert need > 0 and need % 16 == 0
     assert L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 3) == 0            # tiled: none
+    # AUTO with a workspace: split-K from M = 8 on wide or deep layers, from
+    # M = 17 on N > 4096, from M = 24 everywhere; the small-M kernel otherwise
+    assert L.gemm_w4a16_workspace_bytes(7, 28672, 4096, 0) == 0
+    assert L.gemm_w4a16_workspace_bytes(8, 28672, 4096, 0) > 0
+    assert L.gemm_w4a16_workspace_bytes(16, 6144, 4096, 0) == 0
+    assert L.gemm_w4a16_workspace_bytes(17, 6144, 4096, 0) > 0
+    assert L.gemm_w4a16_workspace_bytes(23, 4096, 4096, 0) == 0
+    assert L.gemm_w4a16_workspace_bytes(24, 4096, 4096, 0) > 0
     # past M = 64: split-K of the large-M kernel while its 256 x 128 tiles fill
     # less than one round (S = min(256 / tiles, groups / 4) slices of FP32 M x N)
     assert L.gemm_w4a16_workspace_bytes(1000, 4096, 14336, 0) == 2 * 1000 * 4096 * 4   # 128 tiles: S = 2
