@@ -146,30 +146,42 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
         }
     };
 
+    // XLDS: rows [m0, m0 + rows) of X are copied into LDS in 16-byte chunks,
+    // XB per thread in flight together (one memory round trip per batch).  The
+    // first batch is requested before the weight stages, so that the
+    // in-order memory counter releases it first.
+    const int cpr = (int)(K >> 3);                                     // chunks per row
+    const int total = XLDS ? (int)rows * cpr : 0;
+    auto x_load = [&](uint4 (&v)[XB], int c0) {
+#pragma unroll
+        for (int u = 0; u < XB; ++u)
+            if (c0 + u * NW * 64 < total)
+                v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (c0 + u * NW * 64) * 16,
+                                                                                       0, 0));
+    };
+    auto x_store = [&](const uint4 (&v)[XB], int c0) {
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            const int c = c0 + u * NW * 64;
+            if (c < total) {
+                const int r = c / cpr, kc = c - r * cpr;
+                *reinterpret_cast<uint4*>(dyn_lds + ((int64_t)r * xstride + kc * 8) * 2) = v[u];
+            }
+        }
+    };
+    uint4 xv0[XB];
+    if constexpr (XLDS) x_load(xv0, threadIdx.x);
+
     DecStage<TM, TN, XLDS> stage[STAGES];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue(stage[s], s);
 
     if constexpr (XLDS) {
-        // copy rows [m0, m0 + rows) of X into LDS: 16-byte chunks, XB per
-        // thread in flight together (one memory round trip per batch)
-        const int cpr = (int)(K >> 3);                                 // chunks per row
-        const int total = (int)rows * cpr;
-        for (int c0 = threadIdx.x; c0 < total; c0 += XB * NW * 64) {
+        x_store(xv0, threadIdx.x);
+        for (int c0 = threadIdx.x + XB * NW * 64; c0 < total; c0 += XB * NW * 64) {
             uint4 v[XB];
-#pragma unroll
-            for (int u = 0; u < XB; ++u)
-                if (c0 + u * NW * 64 < total)
-                    v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         rx, (c0 + u * NW * 64) * 16, 0, 0));
-#pragma unroll
-            for (int u = 0; u < XB; ++u) {
-                const int c = c0 + u * NW * 64;
-                if (c < total) {
-                    const int r = c / cpr, kc = c - r * cpr;
-                    *reinterpret_cast<uint4*>(dyn_lds + ((int64_t)r * xstride + kc * 8) * 2) = v[u];
-                }
-            }
+            x_load(v, c0);
+            x_store(v, c0);
         }
         __syncthreads();
         if constexpr (VALU) {

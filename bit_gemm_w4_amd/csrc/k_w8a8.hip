@@ -467,7 +467,8 @@ static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipSt
 // Tile choice for the large-M GEMM: estimated time = rounds of resident
 // blocks x time of one round.  Relative round times (K fixed) measured on the
 // 4096..28672-wide projection shapes: 256 x 256 (one block per CU) 75,
-// 256 x 128 (one per CU) 46.4; block-scaled FP8, which keeps two accumulator
+// 256 x 128 (one per CU) 46.4 (256 x 256 now runs 8 waves, two per SIMD,
+// about 8 % faster than those rounds: no decision on these shapes changes); block-scaled FP8, which keeps two accumulator
 // sets, uses 128 x 128 (two per CU).  With a workspace, grids of at most
 // half a round split K (S = min(blocks per round / tiles, 128-byte K blocks /
 // 8) slices of whole 128-byte blocks); M <= 128 then uses 128 x 128 tiles
@@ -505,7 +506,7 @@ template <bool FP8, bool BLOCK>
 static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2>(g, c, ws, s);
     if constexpr (!BLOCK) {
-        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 2>(g, c, ws, s);
+        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4>(g, c, ws, s);
         return gemm_cfg<FP8, false, 256, 128, 2>(g, c, ws, s);
     }
     return nullptr;

@@ -308,8 +308,8 @@ def test_w8a8_small(ops, orc, algo, M, fp8, a_gran, w_gran, out):
 
 
 @pytest.mark.parametrize("fp8,a_gran,w_gran,out", [
-    (False, 1, 1, torch.float32), (False, 0, 1, torch.float16), (True, 1, 0, torch.float32),
-    (True, 0, 0, torch.float16)])
+    (False, 1, 1, torch.float32), (False, 0, 1, torch.float16), (False, 1, 1, torch.int32),
+    (True, 1, 0, torch.float32), (True, 0, 0, torch.float16)])
 def test_w8a8_out_dtypes_wide_tiles(ops, orc, fp8, a_gran, w_gran, out):
     # 2048 x 8192 is one full round of 256 x 256 tiles: every output type and
     # scale granularity through the widest tile's epilogue
