@@ -10,7 +10,8 @@ with gcc, loads it with ctypes and marshals numpy arrays.  Every function
 names the passage of the pages it follows in the C source:
 
 * [LPI] "Low-precision LLM inference: FP8/INT8/INT4/FP4 kernels and
-  calibration (8/10)", blog.ruahverce.com -- §2 eq. (1)-(2), §3 eq. (3),
+  calibration (8/10)", blog.ruahverce.com -- §1 notation table and precision
+  manifest (W4A8), §2 eq. (1)-(2), §3 eq. (3),
   §4 granularity, §5 effective bits, §7 FP8 formats, §8 FP8 scale recipes,
   §22 accumulator precision.
 * [AIB] "Quantization throughput by method: why W4A16 is overtaken by W8A8 as
@@ -74,6 +75,7 @@ def _load():
                 "orc_quant_fp8": [P, I64, I64, I, P, P],
                 "orc_gemm_i8_acc": [P, P, I64, I64, I64, P],
                 "orc_gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P],
+                "orc_gemm_w4a8": [P, P, I, I64, I64, P, P, P, I64, I, P],
                 "orc_num_threads": [],
             }
             for name, argtypes in sig.items():
@@ -266,6 +268,23 @@ def gemm_w8a8(a, a_scales, a_gran: int, w, w_scales, w_gran: int, fp8: bool) -> 
     y = np.empty((M, N), np.float64)
     _load().orc_gemm_w8a8(_p(a), _p(a_scales), a_gran, _p(w), _p(w_scales), w_gran,
                           int(bool(fp8)), M, N, K, _p(y))
+    return y
+
+
+def gemm_w4a8(a, a_scales, a_gran: int, qweight, scales, zeros, group: int = 128) -> np.ndarray:
+    """W4A8: Y = (A*s_a) W^T in binary64, A the INT8 activation codes with per-row
+    (or per-tensor) scales, W^ the dequantized packed INT4 weights."""
+    assert a_gran in (GRAN_TENSOR, GRAN_ROW)
+    a = _c(a, np.int8)
+    a_scales = _c(a_scales, np.float32)
+    qweight = _c(qweight, np.uint32)
+    scales = _c(scales, np.uint16)
+    zeros = None if zeros is None else _c(zeros, np.uint8)
+    M, K = a.shape
+    N = qweight.shape[0] * 16
+    assert qweight.shape[1] * 128 == K
+    y = np.empty((M, N), np.float64)
+    _load().orc_gemm_w4a8(_p(a), _p(a_scales), a_gran, M, K, _p(qweight), _p(scales), _p(zeros), N, group, _p(y))
     return y
 
 

@@ -455,6 +455,36 @@ void orc_gemm_w8a8(const void* a, const float* a_s, int a_gran,
     free(wd);
 }
 
+/* W4A8 linear (the variant between W4A16 and W8A8: INT4 weights, dynamic
+ * INT8 activations).  [LPI] §1 (the W4A8 row of the notation table and its
+ * precision manifest: INT32/FP32 accumulation, BF16 or FP16 output), §14
+ * (per-token activation scales), §20 and self-check Q2 (W4A8 lowers the
+ * activations to 8 bits for a native low-precision GEMM; the INT4 weights
+ * are dequantized on the way).  With a[m,k] the INT8 code of the
+ * activation, s_a its scale (per row, or one per tensor) and w^ the dequantized
+ * weight s16 * (u - z) of the packed form, the layer is the exact dequantized
+ * product Y[m,n] = sum_k (a[m,k] * s_a) * w^[n,k], in double. */
+void orc_gemm_w4a8(const int8_t* a, const float* a_s, int a_gran, int64_t M, int64_t K,
+                   const uint32_t* qweight, const uint16_t* s16, const uint8_t* zeros,
+                   int64_t N, int G, double* y) {
+    double* what = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    double* ad = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    orc_w4_dequant(qweight, s16, zeros, N, K, G, what);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            ad[m * K + k] = (double)a[m * K + k] * scale_at(a_s, a_gran, m, k, K);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t m = 0; m < M; ++m) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += ad[m * K + k] * what[n * K + k];
+            y[m * N + n] = acc;
+        }
+    }
+    free(what);
+    free(ad);
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int orc_num_threads(void) {
 #ifdef _OPENMP

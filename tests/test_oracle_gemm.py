@@ -152,3 +152,73 @@ def test_w8a8_unit_scales_integer_exact(orc):
         for n in range(8):
             exact = sum(Fraction(float(av[m, k])) * Fraction(float(wv[n, k])) for k in range(256))
             assert Fraction(float(y[m, n])) == exact      # all partial sums exact in binary64
+
+
+# ------------------------------------------------------------------- W4A8 ----
+# "Low-precision LLM inference", §1 (W4A8: INT4 weights, INT8 activations,
+# INT32/FP32 accumulation) and §14 (per-token activation scales).
+
+def _w4a8_inputs(M, N, K, seed, asym):
+    w, x = synth.layer(M, N, K, "f32", seed=seed, w_outlier_frac=0.01, x_outlier_cols=8)
+    return w, x
+
+
+@pytest.mark.parametrize("a_gran,asym", [(1, True), (1, False), (0, True)])
+def test_w4a8_vs_numpy(orc, a_gran, asym):
+    M, N, K = 37, 80, 768
+    w, x = _w4a8_inputs(M, N, K, 28, asym)
+    qweight, s16, zeros = orc.w4_pack(w, 128, asym)
+    a, a_s = orc.act_quant_int8(x, a_gran)
+    y = orc.gemm_w4a8(a, a_s, a_gran, qweight, s16, zeros)
+    sa = np.full(M, float(a_s[0])) if a_gran == 0 else a_s.astype(np.float64)
+    ref = (a.astype(np.float64) * sa[:, None]) @ _np_dequant(qweight, s16, zeros, K).T
+    assert orc.rel_l2(y, ref) <= 1e-13
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_w4a8_unit_scales_integer_exact(orc):
+    """Unit scales: Y is the exact integer sum_k a (u - z), i.e. the INT8 GEMM of
+    the activation codes against the signed codes u - z."""
+    rng = np.random.default_rng(29)
+    M, N, K = 9, 32, 512
+    u = rng.integers(0, 16, size=(N, K), dtype=np.int64).astype(np.uint8)
+    z = rng.integers(0, 16, size=(N, K // 128), dtype=np.int64).astype(np.uint8)
+    s16 = np.full((N, K // 128), 0x3C00, np.uint16)                     # FP16 1.0
+    qweight, scales, zeros = orc.w4_pack_codes(u, s16, z, True)
+    a = rng.integers(-128, 128, size=(M, K), dtype=np.int64).astype(np.int8)
+    a[0, :] = -128
+    y = orc.gemm_w4a8(a, np.ones(M, np.float32), 1, qweight, scales, zeros)
+    signed = (u.astype(np.int64) - np.repeat(z.astype(np.int64), 128, axis=1)).astype(np.int8)
+    acc = orc.gemm_i8_acc(a, signed)
+    assert np.array_equal(y, acc.astype(np.float64))
+
+
+def test_w4a8_matches_w4a16_on_representable_activations(orc):
+    """With power-of-two activation scales every a * s_a is a BF16 value, and the
+    W4A8 layer must equal the W4A16 layer on those activations bit for bit."""
+    rng = np.random.default_rng(30)
+    M, N, K = 6, 48, 512
+    w = synth.weights(N, K, seed=31, outlier_frac=0.01)
+    qweight, s16, zeros = orc.w4_pack(w, 128, True)
+    a = rng.integers(-127, 128, size=(M, K), dtype=np.int64).astype(np.int8)
+    a_s = (2.0 ** rng.integers(-12, 3, size=M)).astype(np.float32)
+    y = orc.gemm_w4a8(a, a_s, 1, qweight, s16, zeros)
+    xv = torch.from_numpy(a.astype(np.float32) * a_s[:, None]).to(torch.bfloat16)
+    assert torch.equal(xv.float(), torch.from_numpy(a.astype(np.float32) * a_s[:, None]))   # exact
+    x_bits = xv.view(torch.int16).numpy().view(np.uint16)
+    y16 = orc.gemm_w4a16(x_bits, "bf16", qweight, s16, zeros)
+    assert np.array_equal(y, y16)
+
+
+def test_w4a8_exact_rational_tiny(orc):
+    M, N, K = 2, 16, 256
+    w, x = _w4a8_inputs(M, N, K, 32, True)
+    qweight, s16, zeros = orc.w4_pack(w, 128, True)
+    a, a_s = orc.act_quant_int8(x, 1)
+    y = orc.gemm_w4a8(a, a_s, 1, qweight, s16, zeros)
+    what = _np_dequant(qweight, s16, zeros, K)
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(int(a[m, k])) * Fraction(float(a_s[m])) * Fraction(float(what[n, k]))
+                        for k in range(K))
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 40) + Fraction(1, 2 ** 60)
