@@ -94,4 +94,9 @@ W8Split w8a8_tiled_split(const W8A8Args& args, bool with_ws);
 const char* launch_w8a8_tiled(const W8A8Args& args, void* ws, hipStream_t s);
 const char* launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
 
+// W4A8: INT8 activation codes a [M][K] with per-row (a_row) or per-tensor
+// scales, packed INT4 weights; out_dt: 0 f32, 1 f16, 2 bf16.
+const char* launch_w4a8_gemm(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
+                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, hipStream_t s);
+
 }  // namespace bg

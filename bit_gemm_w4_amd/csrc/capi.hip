@@ -286,6 +286,28 @@ BG_EXPORT bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran, 
                         stream);
 }
 
+BG_EXPORT bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                              const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                              int group, void* y, int out_dtype, void* stream) {
+    if (!a || !a_scales || !qweight || !scales || !y)
+        return fail(BG_ERR_NULL, "gemm_w4a8: a, a_scales, qweight, scales and y must be non-NULL");
+    if (a_gran != BG_GRAN_TENSOR && a_gran != BG_GRAN_ROW)
+        return fail(BG_ERR_UNSUPPORTED, "gemm_w4a8: a_gran %lld is not TENSOR/ROW", a_gran);
+    if (out_dtype != BG_BF16 && out_dtype != BG_F16 && out_dtype != BG_F32)
+        return fail(BG_ERR_DTYPE, "gemm_w4a8: out_dtype %lld is not BF16/F16/F32", out_dtype);
+    if (group != 128) return fail(BG_ERR_UNSUPPORTED, "gemm_w4a8: group %lld (only 128 is supported)", group);
+    if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w4a8: M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w4a8: N=%lld must be a multiple of 16", N);
+    if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a8: K=%lld must be a multiple of 256", K);
+    if (M * K >= (int64_t(1) << 31)) return fail(BG_ERR_SHAPE, "gemm_w4a8: M*K=%lld too large", M * K);
+    if (!aligned16(a) || !aligned16(a_scales) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) ||
+        (zeros && !aligned16(zeros)))
+        return fail(BG_ERR_ALIGN, "gemm_w4a8: pointers must be 16-byte aligned");
+    note_kernel(bg::launch_w4a8_gemm(a, a_scales, a_gran == BG_GRAN_ROW, M, K, qweight, scales, zeros, N, y,
+                                     out_dtype, static_cast<hipStream_t>(stream)));
+    return launched("gemm_w4a8");
+}
+
 BG_EXPORT const char* bg_status_string(int status) {
     switch (status) {
         case BG_OK: return "ok";

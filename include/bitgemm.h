@@ -244,6 +244,33 @@ bg_status gemm_w8a8_ws(const void* a, const float* a_scales, int a_gran,
  * granularity and kernel choice (0 if none; BG_ALGO_AUTO = AUTO's choice). */
 int64_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran, int algo);
 
+/*
+ * gemm_w4a8 -- W4A8 linear: INT8 activation codes times packed INT4 weights
+ * on the INT8 matrix cores ([LPI] §1, the W4A8 row of the notation table and
+ * its precision manifest: INT4 weights, INT8 activations, INT32/FP32
+ * accumulation, BF16 or FP16 output; §14 per-token activation scales; §20
+ * and self-check Q2: a native low-precision GEMM whose INT4 weights are
+ * dequantized on the way).
+ *
+ *   y[m,n] = s_a[m] * sum_g s[n,g] * sum_{k in g} a[m,k] * (u[n,k] - z[n,g])
+ *
+ * The inner sums are exact INT32; each group's sum is scaled by its FP16
+ * scale and accumulated in FP32, and s_a scales the row at the end.
+ *   a, a_scales, a_gran  INT8 codes [M][K] and scales as act_quant_int8
+ *                        produces them: BG_GRAN_ROW (per token, [M]) or
+ *                        BG_GRAN_TENSOR (scales[0])
+ *   qweight, scales, zeros, N, group   the packed weights of w4_pack
+ *                        (zeros NULL = symmetric, z = 8), group == 128
+ *   y, out_dtype         out [M][N], BG_BF16, BG_F16 or BG_F32
+ *                        (round-to-nearest-even)
+ * Requires 1 <= M, N % 16 == 0, K % 256 == 0, M * K < 2^31, 16-byte aligned
+ * pointers.  One large-M kernel serves every M (256 x 128 output tiles); it
+ * allocates nothing and needs no workspace.
+ */
+bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                    const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                    int64_t N, int group, void* y, int out_dtype, void* stream);
+
 /* The kernel BG_ALGO_AUTO selects for a call of this shape (a BG_ALGO_* value). */
 int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype);
 int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype);

@@ -418,3 +418,51 @@ def _w8_fuzz_cases(n=60, seed=20262):
 def test_w8a8_fuzz(ops, orc, case):
     M, N, K, fp8, a_gran, w_gran, out_dtype, algo, ws, seed = case
     _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, algo, out_dtype=out_dtype, seed=seed, ws=ws)
+
+
+# ---------------------------------------------------------------- gemm_w4a8 ----
+
+def _w4a8_case(ops, orc, M, N, K, asym, a_gran, out_dtype=torch.bfloat16, rows=None, seed=0):
+    w, x = synth.layer(M, N, K, "bf16", seed=seed, w_outlier_frac=0.01, x_outlier_cols=8)
+    p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, asym)
+    a, a_s = ops.act_quant_int8(dev_bits(x, "bf16"), a_gran)
+    y = ops.gemm_w4a8(a, a_s, a_gran, p, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    qw, s, z = orc.w4_pack(w, 128, asym)
+    assert np.array_equal(p.qweight.cpu().numpy().view(np.uint32), qw)
+    ao, aso = orc.act_quant_int8(orc.bits_to_f32(x, "bf16"), a_gran)
+    assert np.array_equal(a.cpu().numpy(), ao)
+    assert np.array_equal(a_s.cpu().numpy().view(np.uint32), aso.view(np.uint32))
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    ref = orc.gemm_w4a8(ao[sel], aso if a_gran == 0 else aso[sel], a_gran, qw, s, z)
+    yv = y.float().cpu().numpy()[sel].astype(np.float64)
+    check_close(yv, ref, orc, f"w4a8 M={M} N={N} K={K} asym={asym} gran={a_gran} out={out_dtype}")
+
+
+@pytest.mark.parametrize("M", [1, 17, 130, 300])
+@pytest.mark.parametrize("asym,a_gran", [(True, 1), (False, 1), (True, 0)])
+def test_w4a8_small(ops, orc, M, asym, a_gran):
+    # 1040 columns: 8 full 128-column tiles and a 16-column tail; 16 groups
+    _w4a8_case(ops, orc, M, 1040, 2048, asym, a_gran, seed=M)
+
+
+@pytest.mark.parametrize("out", [torch.float16, torch.float32])
+def test_w4a8_out_dtypes(ops, orc, out):
+    _w4a8_case(ops, orc, 257, 272, 768, True, 1, out_dtype=out, seed=3)
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_w4a8_full_shape_sampled(ops, orc, name):
+    """Prefill M = 2048 on the projection shapes, rows sampled across all row tiles."""
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _w4a8_case(ops, orc, 2048, N, K, True, 1, rows=[0, 1, 255, 256, 777, 1024, 2047])
+
+
+def test_w4a8_rejects(ops):
+    a = torch.zeros((4, 256), dtype=torch.int8, device="cuda")
+    s = torch.ones(4, device="cuda")
+    p = ops.w4_pack(torch.zeros((16, 256), device="cuda"), 128, False)
+    with pytest.raises(ops.BitGemmError):
+        ops.gemm_w4a8(a, s, ops.GRAN_ROW_G128, p)                       # granularity
+    with pytest.raises(ValueError):
+        ops.gemm_w4a8(a.float(), s, ops.GRAN_ROW, p)                    # dtype
