@@ -266,8 +266,10 @@ def measured_traffic(call: str):
 
 def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph):
     """W8A8 at M=2048 (INT8 per-token x per-channel; FP8 per-tensor and
-    128x128 / 1x128 blocks) and W4A16 at B=74/256, each timed alone."""
-    res = {"w8a8_m2048": {}, "w4a16_large_batch": {}}
+    128x128 / 1x128 blocks), W4A8 at M=2048 (the decode step's packed INT4
+    weights x per-token INT8 activations) and W4A16 at B=74/256, each timed
+    alone."""
+    res = {"w8a8_m2048": {}, "w4a8_m2048": {}, "w4a16_large_batch": {}}
     M = 2048
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]
@@ -296,6 +298,17 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "kernel": kname}
             log(f"  w8a8 {name:8s} {tag:10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
                 f"act_quant {ms_q * 1e3:6.1f} us")
+        # W4A8: the same activations as per-token INT8 codes, the packed weights
+        a, a_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
+        p = packs[name][0]
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        g = graph_of(lambda: ops.gemm_w4a8(a, a_s, ops.GRAN_ROW, p, out=y), torch)
+        ms = time_graph(g, 10, torch)
+        tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+        peak = roofline.PEAK_TFLOPS["i8"]
+        res["w4a8_m2048"][name] = {"gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                                   "frac": round(tf / peak, 4), "kernel": ops.last_kernel()}
+        log(f"  w4a8 {name:8s} {ms * 1e3:8.1f} us {tf:7.1f} TOP/s ({tf / peak:.1%})")
         del wt
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]
@@ -337,7 +350,7 @@ def crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
     wb = wd.to(torch.bfloat16)
     bf = [wb] + [wb.clone() for _ in range(copies(2 * N * K) - 1)]
     del wd
-    rows, res = [], {"batches": [], "us": {"bf16": [], "w4a16": [], "w8a8_int8": [], "w8a8_fp8": []}}
+    rows, res = [], {"batches": [], "us": {"bf16": [], "w4a16": [], "w4a8": [], "w8a8_int8": [], "w8a8_fp8": []}}
     for lb in range(13):
         B = 1 << lb
         g = torch.Generator(device="cpu")
@@ -350,19 +363,23 @@ def crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
         def i8_call(c):
             a, a_s = ops.act_quant_int8(x, ops.GRAN_ROW)
             ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, i8[c][0], i8[c][1], ops.GRAN_ROW, out=y)
+        def w4a8_call(c):
+            a, a_s = ops.act_quant_int8(x, ops.GRAN_ROW)
+            ops.gemm_w4a8(a, a_s, ops.GRAN_ROW, w4[c], out=y)
         def f8_call(c):
             a, a_s = ops.act_quant_fp8(x, ops.GRAN_TENSOR)
             ops.gemm_w8a8(a, a_s, ops.GRAN_TENSOR, f8[c][0], f8[c][1], ops.GRAN_TENSOR, out=y)
         t = {"bf16": t_of(lambda c: torch.matmul(x, bf[c].t(), out=y), len(bf)),
              "w4a16": t_of(lambda c: ops.gemm_w4a16(x, w4[c], out=y), len(w4)),
+             "w4a8": t_of(w4a8_call, len(w4)),
              "w8a8_int8": t_of(i8_call, len(i8)),
              "w8a8_fp8": t_of(f8_call, len(f8))}
         res["batches"].append(B)
         for k, v in t.items():
             res["us"][k].append(round(v, 2))
-        log(f"  crossover down B={B:5d}  bf16 {t['bf16']:8.1f}  w4a16 {t['w4a16']:8.1f}  "
+        log(f"  crossover down B={B:5d}  bf16 {t['bf16']:8.1f}  w4a16 {t['w4a16']:8.1f}  w4a8 {t['w4a8']:8.1f}  "
             f"int8 {t['w8a8_int8']:8.1f}  fp8 {t['w8a8_fp8']:8.1f} us")
-    for k in ("w8a8_int8", "w8a8_fp8"):
+    for k in ("w4a8", "w8a8_int8", "w8a8_fp8"):
         won = [B for B, a, b in zip(res["batches"], res["us"][k], res["us"]["w4a16"]) if a < b]
         res[f"crossover_batch_{k}"] = won[0] if won else None
     res["roofline_crossover_batch"] = round(roofline.PEAK_TFLOPS["bf16"] * 1e12 / (2 * roofline.HBM_GBPS * 1e9), 1)

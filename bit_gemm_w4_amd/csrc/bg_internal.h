@@ -95,8 +95,13 @@ const char* launch_w8a8_tiled(const W8A8Args& args, void* ws, hipStream_t s);
 const char* launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
 
 // W4A8: INT8 activation codes a [M][K] with per-row (a_row) or per-tensor
-// scales, packed INT4 weights; out_dt: 0 f32, 1 f16, 2 bf16.
+// scales, packed INT4 weights; out_dt: 0 f32, 1 f16, 2 bf16.  With a
+// workspace (non-NULL, at least w4a8_gemm_split(M, N, K).ws_bytes, any
+// contents) K is split into S slices when the output tiles do not fill the
+// device; a second kernel on the same stream sums the FP32 partials.
+W4GemmSplit w4a8_gemm_split(int64_t M, int64_t N, int64_t K);
 const char* launch_w4a8_gemm(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
-                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, hipStream_t s);
+                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, void* ws,
+                             hipStream_t s);
 
 }  // namespace bg

@@ -286,9 +286,9 @@ BG_EXPORT bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran, 
                         stream);
 }
 
-BG_EXPORT bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
-                              const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N,
-                              int group, void* y, int out_dtype, void* stream) {
+static bg_status w4a8_impl(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                           const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
+                           void* y, int out_dtype, void* ws, int64_t ws_bytes, bool with_ws, void* stream) {
     if (!a || !a_scales || !qweight || !scales || !y)
         return fail(BG_ERR_NULL, "gemm_w4a8: a, a_scales, qweight, scales and y must be non-NULL");
     if (a_gran != BG_GRAN_TENSOR && a_gran != BG_GRAN_ROW)
@@ -301,11 +301,41 @@ BG_EXPORT bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran
     if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a8: K=%lld must be a multiple of 256", K);
     if (M * K >= (int64_t(1) << 31)) return fail(BG_ERR_SHAPE, "gemm_w4a8: M*K=%lld too large", M * K);
     if (!aligned16(a) || !aligned16(a_scales) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) ||
-        (zeros && !aligned16(zeros)))
+        (zeros && !aligned16(zeros)) || (ws && !aligned16(ws)))
         return fail(BG_ERR_ALIGN, "gemm_w4a8: pointers must be 16-byte aligned");
+    void* use_ws = nullptr;
+    if (with_ws) {
+        const int64_t need = bg::w4a8_gemm_split(M, N, K).ws_bytes;
+        if (need > 0) {
+            if (!ws || ws_bytes < need)
+                return fail(BG_ERR_WORKSPACE, "gemm_w4a8: workspace of %lld bytes needed (got %lld)", need,
+                            ws ? ws_bytes : 0);
+            use_ws = ws;
+        }
+    }
     note_kernel(bg::launch_w4a8_gemm(a, a_scales, a_gran == BG_GRAN_ROW, M, K, qweight, scales, zeros, N, y,
-                                     out_dtype, static_cast<hipStream_t>(stream)));
+                                     out_dtype, use_ws, static_cast<hipStream_t>(stream)));
     return launched("gemm_w4a8");
+}
+
+BG_EXPORT bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                              const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                              int group, void* y, int out_dtype, void* stream) {
+    return w4a8_impl(a, a_scales, a_gran, M, K, qweight, scales, zeros, N, group, y, out_dtype, nullptr, 0, false,
+                     stream);
+}
+
+BG_EXPORT bg_status gemm_w4a8_ws(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                                 const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N,
+                                 int group, void* y, int out_dtype, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+    return w4a8_impl(a, a_scales, a_gran, M, K, qweight, scales, zeros, N, group, y, out_dtype, workspace,
+                     workspace_bytes, true, stream);
+}
+
+BG_EXPORT int64_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || M > kMaxM || N < 16 || N > kMaxRows || N % 16 || K < 256 || K > kMaxDim || K % 256) return 0;
+    return bg::w4a8_gemm_split(M, N, K).ws_bytes;
 }
 
 BG_EXPORT const char* bg_status_string(int status) {

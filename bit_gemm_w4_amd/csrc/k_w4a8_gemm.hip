@@ -81,7 +81,8 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
                                                           int64_t M, int64_t K, const uint32_t* __restrict__ qw,
                                                           const uint16_t* __restrict__ sc,
                                                           const uint8_t* __restrict__ zr, int64_t N,
-                                                          void* __restrict__ y, int out_dt) {
+                                                          void* __restrict__ y, int out_dt, float* __restrict__ ws,
+                                                          int S, int gs) {
     constexpr int NW = Q_NW;
     constexpr int WTM = QBM / Q_WM, WTN = QBN / 2, TM = WTM / 32, TN = WTN / 32;
     // copies per wave per stage: A_LD of A (1 KB = 16 rows each), then one of W
@@ -102,11 +103,14 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
     const int l32 = lane & 31, h = lane >> 5;
     const bool has_z = zr != nullptr;
 
+    // block b: output tile b % T, K slice b / T (groups [sl gs, sl gs + gs))
     int tm, tn;
     const int tiles_m = (int)((M + QBM - 1) / QBM), tiles_n = (int)((N + QBN - 1) / QBN);
-    grouped_tile(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int sl = blockIdx.x / (tiles_m * tiles_n);
+    grouped_tile(blockIdx.x - sl * tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
     const int64_t m0 = (int64_t)tm * QBM, n0 = (int64_t)tn * QBN;
     const int64_t ngroups = K >> 7, ntiles = N >> 4, t0 = n0 >> 4;
+    const int g_beg = sl * gs, g_end = g_beg + gs < ngroups ? g_beg + gs : (int)ngroups;
     const int64_t tiles_here = ntiles - t0 < QBN / 16 ? ntiles - t0 : QBN / 16;
 
     // ---- buffer resources (rows / tiles past the end read as zero) ----
@@ -139,9 +143,10 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
     const uint32_t voff_m = mrole < 2 ? (uint32_t)((4 * mrole + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
                                       : (uint32_t)(lane * (ngroups >> 1) * 16);
     // Every step issues the same number of copies (the stage waits count
-    // them); the stages past the end of K repeat the last stage's bytes into a
-    // free buffer that is never consumed, so no copy leaves its tensor.
-    const int ks_last = (int)(2 * ngroups) - 1;
+    // them); the stages past the end of the slice repeat its last stage's
+    // bytes into a free buffer that is never consumed, so no copy leaves its
+    // tensor.
+    const int ks0 = 2 * g_beg, ks1 = 2 * g_end, ks_last = ks1 - 1;
     auto issue_one = [&](int ks, int t) {
         uint8_t* buf = lds + (ks % Q_NB) * Q_STAGE;
         const int kc = ks < ks_last ? ks : ks_last;
@@ -291,19 +296,18 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
         }
     };
 
-    const int ks1 = (int)(2 * ngroups);
 #pragma unroll
-    for (int t = 0; t < Q_NB; ++t) issue(t);
+    for (int t = 0; t < Q_NB; ++t) issue(ks0 + t);
     wait_vmcnt<(Q_NB - 1) * LOADS>();
     block_barrier();
     StageFr f0, f1;
-    read_frags(f0, 0);
+    read_frags(f0, ks0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) zd_next[j] = ds_read4(zaddr(0, j));
+    for (int j = 0; j < TN; ++j) zd_next[j] = ds_read4(zaddr(g_beg, j));
     wait_lgkm0();
 #pragma unroll
-    for (int j = 0; j < TN; ++j) settle(zd_next[j]), zc[j] = zconst(zd_next[j], 0);
-    for (int ks = 0; ks < ks1; ks += 2) {
+    for (int j = 0; j < TN; ++j) settle(zd_next[j]), zc[j] = zconst(zd_next[j], g_beg);
+    for (int ks = ks0; ks < ks1; ks += 2) {
         step(f0, f1, ks, true);
         step(f1, f0, ks + 1, false);
     }
@@ -318,7 +322,10 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
         const int64_t m = mw + 32 * i + l32;
         sa[i] = a_row ? (m < M ? as[m] : 0.0f) : as[0];
     }
-    if (out_dt == QO_F32) {
+    // F32 output, or (S > 1) this slice's partial tile -> ws[sl][M][N], which
+    // k_w4a8_reduce adds up in slice order
+    if (out_dt == QO_F32 || S > 1) {
+        float* yf = S > 1 ? ws + (int64_t)sl * M * N : static_cast<float*>(y);
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int64_t m = mw + 32 * i + l32;
@@ -328,7 +335,7 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int64_t n = nw + 32 * j + 8 * q4 + 4 * h;      // N % 16 == 0: all four or none
                     if (m < M && n < N)
-                        *reinterpret_cast<float4*>(static_cast<float*>(y) + m * N + n) =
+                        *reinterpret_cast<float4*>(yf + m * N + n) =
                             make_float4(acc[i][j][4 * q4] * sa[i], acc[i][j][4 * q4 + 1] * sa[i],
                                         acc[i][j][4 * q4 + 2] * sa[i], acc[i][j][4 * q4 + 3] * sa[i]);
                 }
@@ -365,11 +372,77 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
     }
 }
 
+// y[m][n] = sum over the S slices of ws[s][m][n], in slice order (results do
+// not depend on timing), written as out_dt.  One thread per 8 consecutive
+// outputs of a row (N % 16 == 0).
+__global__ __launch_bounds__(256) void k_w4a8_reduce(const float* __restrict__ ws, int S, int64_t M, int64_t N,
+                                                     void* __restrict__ y, int out_dt) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (e >= M * N) return;
+    const int64_t slice = M * N;
+    constexpr int RB = 8;                                      // slices in flight per batch
+    float v[8];
+    for (int b0 = 0; b0 < S; b0 += RB) {
+        float4 lo[RB], hi[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r < S) {
+                lo[r] = *reinterpret_cast<const float4*>(ws + (b0 + r) * slice + e);
+                hi[r] = *reinterpret_cast<const float4*>(ws + (b0 + r) * slice + e + 4);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (b0 + r >= S) break;
+            const float p[8] = {lo[r].x, lo[r].y, lo[r].z, lo[r].w, hi[r].x, hi[r].y, hi[r].z, hi[r].w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = b0 + r == 0 ? p[c] : v[c] + p[c];
+        }
+    }
+    if (out_dt == QO_F32) {
+        float* yf = static_cast<float*>(y) + e;
+        *reinterpret_cast<float4*>(yf) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(yf + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        return;
+    }
+    const bool bf = out_dt == QO_BF16;
+    uint32_t o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = bf ? f32_to_bf16(v[c]) : f32_to_f16(v[c]);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + e) =
+        make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16), o[6] | (o[7] << 16));
+}
+
+// K slices: while the output tiles do not fill one round (one block per CU),
+// split K into whole groups, at least 4 per slice.
+W4GemmSplit w4a8_gemm_split(int64_t M, int64_t N, int64_t K) {
+    W4GemmSplit c{1, (int)(K >> 7), 0};
+    const int64_t tiles = ((M + QBM - 1) / QBM) * ((N + QBN - 1) / QBN), ngroups = K >> 7;
+    int64_t S = 256 / tiles;
+    if (S > ngroups / 4) S = ngroups / 4;
+    if (S < 2) return c;
+    const int64_t gs = (ngroups + S - 1) / S;
+    S = (ngroups + gs - 1) / gs;
+    if (S < 2) return c;
+    c.S = (int)S;
+    c.gs = (int)gs;
+    c.ws_bytes = S * M * N * 4;
+    return c;
+}
+
 const char* launch_w4a8_gemm(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
-                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, hipStream_t s) {
+                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, void* ws,
+                             hipStream_t s) {
+    const W4GemmSplit c = ws ? w4a8_gemm_split(M, N, K) : W4GemmSplit{1, (int)(K >> 7), 0};
     const int64_t tiles = ((M + QBM - 1) / QBM) * ((N + QBN - 1) / QBN);
-    hipLaunchKernelGGL(k_w4a8_gemm, dim3((unsigned)tiles), dim3(64 * Q_NW), 0, s, a, as, a_row ? 1 : 0, M, K, qw, sc,
-                       zr, N, y, out_dt);
+    hipLaunchKernelGGL(k_w4a8_gemm, dim3((unsigned)(tiles * c.S)), dim3(64 * Q_NW), 0, s, a, as, a_row ? 1 : 0, M, K,
+                       qw, sc, zr, N, y, out_dt, static_cast<float*>(ws), c.S, c.gs);
+    if (c.S > 1) {
+        const int64_t threads = M * N / 8;
+        hipLaunchKernelGGL(k_w4a8_reduce, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(ws), c.S, M, N, y, out_dt);
+        return "k_w4a8_gemm + k_w4a8_reduce";
+    }
     return "k_w4a8_gemm";
 }
 

@@ -25,7 +25,8 @@ PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
-    "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a16_algo", "gemm_w8a8_algo",
+    "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
+    "gemm_w4a16_algo", "gemm_w8a8_algo",
     "bg_status_string", "bg_last_error",
     "bg_pack_format_version", "bg_last_kernel",
 )
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
             "gemm_w8a8_workspace_bytes": [I64, I64, I64, I, I, I],
             "gemm_w4a8": [P, P, I, I64, I64, P, P, P, I64, I, P, I, P],
+            "gemm_w4a8_ws": [P, P, I, I64, I64, P, P, P, I64, I, P, I, P, I64, P],
+            "gemm_w4a8_workspace_bytes": [I64, I64, I64],
             "gemm_w4a16_algo": [I64, I64, I64, I],
             "gemm_w8a8_algo": [I64, I64, I64, I],
             "bg_status_string": [I],
@@ -261,10 +264,17 @@ def gemm_w8a8(a: torch.Tensor, a_scales: torch.Tensor | None, a_gran: int, w: to
     return out
 
 
+def gemm_w4a8_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().gemm_w4a8_workspace_bytes(M, N, K))
+
+
 def gemm_w4a8(a: torch.Tensor, a_scales: torch.Tensor, a_gran: int, packed: PackedW4,
-              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+              out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None | bool = None, stream=None) -> torch.Tensor:
     """Y = (A s_a) W^T: INT8 activation codes (act_quant_int8 with GRAN_ROW or
-    GRAN_TENSOR) times packed INT4 weights, on the INT8 matrix cores."""
+    GRAN_TENSOR) times packed INT4 weights, on the INT8 matrix cores.  ws: a
+    workspace tensor, None to use the cached per-device workspace (enables the
+    K split when the output tiles do not fill the device), or False for none."""
     M, K = a.shape
     if a.dtype != torch.int8:
         raise ValueError(f"gemm_w4a8: activations must be int8 codes, got {a.dtype}")
@@ -274,9 +284,18 @@ def gemm_w4a8(a: torch.Tensor, a_scales: torch.Tensor, a_gran: int, packed: Pack
         out = torch.empty((M, packed.N), dtype=out_dtype, device=a.device)
     if out.dtype not in (torch.bfloat16, torch.float16, torch.float32):
         raise ValueError(f"gemm_w4a8: output must be bfloat16/float16/float32, got {out.dtype}")
-    _check(lib().gemm_w4a8(_ptr(a), _ptr(a_scales), a_gran, M, K, _ptr(packed.qweight), _ptr(packed.scales),
+    L = lib()
+    if ws is False:
+        _check(L.gemm_w4a8(_ptr(a), _ptr(a_scales), a_gran, M, K, _ptr(packed.qweight), _ptr(packed.scales),
                            _ptr(packed.zeros), packed.N, packed.group, _ptr(out), _OUT_DT[out.dtype],
                            _stream(stream)), "gemm_w4a8")
+        return out
+    if ws is None:
+        need = gemm_w4a8_workspace_bytes(M, packed.N, K)
+        ws = workspace(need, a.device) if need > 0 else None
+    _check(L.gemm_w4a8_ws(_ptr(a), _ptr(a_scales), a_gran, M, K, _ptr(packed.qweight), _ptr(packed.scales),
+                          _ptr(packed.zeros), packed.N, packed.group, _ptr(out), _OUT_DT[out.dtype], _ptr(ws),
+                          0 if ws is None else ws.numel(), _stream(stream)), "gemm_w4a8")
     return out
 
 

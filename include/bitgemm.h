@@ -264,12 +264,34 @@ int64_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int in_dtype,
  *   y, out_dtype         out [M][N], BG_BF16, BG_F16 or BG_F32
  *                        (round-to-nearest-even)
  * Requires 1 <= M, N % 16 == 0, K % 256 == 0, M * K < 2^31, 16-byte aligned
- * pointers.  One large-M kernel serves every M (256 x 128 output tiles); it
- * allocates nothing and needs no workspace.
+ * pointers.  One kernel (256 x 128 output tiles) serves every M.
  */
 bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
                     const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                     int64_t N, int group, void* y, int out_dtype, void* stream);
+
+/*
+ * gemm_w4a8_ws -- gemm_w4a8 with a caller-provided device workspace: while the
+ * output tiles do not fill one round of the device (fewer than 256), K is
+ * split into S = min(256 / tiles, groups / 4) slices of whole groups; each
+ * slice writes its FP32 partial (row scale applied) to the workspace and a
+ * second kernel, enqueued on the same stream, adds the slices in a fixed order
+ * and writes out_dtype.
+ *   workspace        16-byte aligned device memory of at least
+ *                    gemm_w4a8_workspace_bytes(M, N, K) bytes (S * M * N * 4
+ *                    when K is split, else 0); no initialisation needed,
+ *                    contents afterwards unspecified; calls that share it
+ *                    must not overlap in time.  May be NULL when the size is 0.
+ *   workspace_bytes  its size; BG_ERR_WORKSPACE if smaller than required.
+ * Other arguments, layouts and errors as gemm_w4a8.
+ */
+bg_status gemm_w4a8_ws(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
+                       const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                       int64_t N, int group, void* y, int out_dtype, void* workspace,
+                       int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes gemm_w4a8_ws needs for this shape (0 if K is not split). */
+int64_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* The kernel BG_ALGO_AUTO selects for a call of this shape (a BG_ALGO_* value). */
 int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype);

@@ -92,6 +92,17 @@ def test_gemm_w4a16_validation(L):
     assert f(P, BF16, 1, 256, P, Q, None, 16, 128, P, 4, None) == E_WS      # split-K needs _ws
 
 
+def test_gemm_w4a8_workspace(L):
+    # split while the 256 x 128 tiles fill less than one round: S = min(256 / tiles, groups / 4)
+    assert L.gemm_w4a8_workspace_bytes(256, 4096, 14336) == 8 * 256 * 4096 * 4       # 32 tiles
+    assert L.gemm_w4a8_workspace_bytes(300, 4096, 14336) == 4 * 300 * 4096 * 4       # 64 tiles
+    assert L.gemm_w4a8_workspace_bytes(2048, 4096, 14336) == 0                       # 256 tiles
+    assert L.gemm_w4a8_workspace_bytes(16, 1024, 512) == 0                           # 4 groups
+    assert L.gemm_w4a8_workspace_bytes(16, 1000, 512) == 0                           # N % 16
+    f = L.gemm_w4a8_ws
+    assert f(P, P, 1, 16, 14336, P, Q, None, 4096, 128, P, BF16, None, 0, None) == E_WS
+
+
 def test_gemm_w4a16_workspace(L):
     f = L.gemm_w4a16_ws
     need = L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 0)

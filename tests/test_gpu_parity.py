@@ -422,11 +422,11 @@ def test_w8a8_fuzz(ops, orc, case):
 
 # ---------------------------------------------------------------- gemm_w4a8 ----
 
-def _w4a8_case(ops, orc, M, N, K, asym, a_gran, out_dtype=torch.bfloat16, rows=None, seed=0):
+def _w4a8_case(ops, orc, M, N, K, asym, a_gran, out_dtype=torch.bfloat16, rows=None, seed=0, ws=None):
     w, x = synth.layer(M, N, K, "bf16", seed=seed, w_outlier_frac=0.01, x_outlier_cols=8)
     p = ops.w4_pack(torch.from_numpy(w).cuda(), 128, asym)
     a, a_s = ops.act_quant_int8(dev_bits(x, "bf16"), a_gran)
-    y = ops.gemm_w4a8(a, a_s, a_gran, p, out_dtype=out_dtype)
+    y = ops.gemm_w4a8(a, a_s, a_gran, p, out_dtype=out_dtype, ws=ws)
     torch.cuda.synchronize()
     qw, s, z = orc.w4_pack(w, 128, asym)
     assert np.array_equal(p.qweight.cpu().numpy().view(np.uint32), qw)
@@ -439,11 +439,23 @@ def _w4a8_case(ops, orc, M, N, K, asym, a_gran, out_dtype=torch.bfloat16, rows=N
     check_close(yv, ref, orc, f"w4a8 M={M} N={N} K={K} asym={asym} gran={a_gran} out={out_dtype}")
 
 
+@pytest.mark.parametrize("ws", [None, False], ids=["split", "nosplit"])
 @pytest.mark.parametrize("M", [1, 17, 130, 300])
 @pytest.mark.parametrize("asym,a_gran", [(True, 1), (False, 1), (True, 0)])
-def test_w4a8_small(ops, orc, M, asym, a_gran):
-    # 1040 columns: 8 full 128-column tiles and a 16-column tail; 16 groups
-    _w4a8_case(ops, orc, M, 1040, 2048, asym, a_gran, seed=M)
+def test_w4a8_small(ops, orc, M, asym, a_gran, ws):
+    # 1040 columns: 8 full 128-column tiles and a 16-column tail; 16 groups,
+    # split into 4 slices of 4 when a workspace is given
+    if ws is None:
+        assert ops.gemm_w4a8_workspace_bytes(M, 1040, 2048) == 4 * M * 1040 * 4
+    _w4a8_case(ops, orc, M, 1040, 2048, asym, a_gran, seed=M, ws=ws)
+
+
+@pytest.mark.parametrize("out", [torch.bfloat16, torch.float32])
+def test_w4a8_split_down_shape(ops, orc, out):
+    """Down projection (K = 14336, N = 4096) at M = 300: 64 tiles, K in 4 slices."""
+    K, N = synth.LLAMA3_8B_SHAPES["down"]
+    assert ops.gemm_w4a8_workspace_bytes(300, N, K) == 4 * 300 * N * 4
+    _w4a8_case(ops, orc, 300, N, K, True, 1, out_dtype=out, rows=[0, 1, 100, 255, 256, 299], seed=5)
 
 
 @pytest.mark.parametrize("out", [torch.float16, torch.float32])
