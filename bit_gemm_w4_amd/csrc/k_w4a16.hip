@@ -609,12 +609,16 @@ static bool xlds_fits(int64_t rows, int64_t K, bool valu) {
     return rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
 }
 
+// Two weight tiles per block on wide layers, and from M = 9 on N > 4096 (the
+// activation rows a block stages are then shared by twice the weight bytes),
+// four on wide layers from M = 9; one otherwise (more blocks for short layers).
 template <bool BF16>
 static const char* decode_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                              const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
-    const bool wide = N >= 16384;
+    const bool wide = N >= 16384 || (M > 8 && N > 4096);
     if (M <= 16) {
         if (xlds_fits(M, K, false)) {
+            if (N >= 16384 && M > 8) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             if (wide) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
         }

@@ -126,6 +126,13 @@ def test_w4a16_small(ops, orc, algo, x_dtype, asym, M):
     _w4a16_case(ops, orc, M, 272, 768, x_dtype, asym, algo, seed=M)
 
 
+@pytest.mark.parametrize("M,N", [(9, 16400), (16, 16400), (12, 4112), (16, 4112), (8, 4112)])
+def test_w4a16_small_m_tile_widths(ops, orc, M, N):
+    """Small-M kernel blocks of four weight tiles (N >= 16384, M > 8), two
+    (N > 4096, M > 8) and one, each with a ragged last block (1025 or 257 tiles)."""
+    _w4a16_case(ops, orc, M, N, 512, "bf16", True, 2, seed=M + N, ws=False)
+
+
 @pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
 @pytest.mark.parametrize("M", [65, 130, 300])
 def test_w4a16_splitk_large_m(ops, orc, x_dtype, asym, M):
