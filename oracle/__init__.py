@@ -11,7 +11,7 @@ names the passage of the pages it follows in the C source:
 
 * [LPI] "Low-precision LLM inference: FP8/INT8/INT4/FP4 kernels and
   calibration (8/10)", blog.ruahverce.com -- §1 notation table and precision
-  manifest (W4A8), §2 eq. (1)-(2), §3 eq. (3),
+  manifest (W4A8), §2 eq. (1)-(2), §3 eq. (3), §15 SmoothQuant fold,
   §4 granularity, §5 effective bits, §7 FP8 formats, §8 FP8 scale recipes,
   §22 accumulator precision.
 * [AIB] "Quantization throughput by method: why W4A16 is overtaken by W8A8 as
@@ -76,6 +76,9 @@ def _load():
                 "orc_gemm_i8_acc": [P, P, I64, I64, I64, P],
                 "orc_gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P],
                 "orc_gemm_w4a8": [P, P, I, I64, I64, P, P, P, I64, I, P],
+                "orc_col_amax": [P, I64, I64, P],
+                "orc_smooth_scales": [P, P, I64, ctypes.c_double, P],
+                "orc_col_mul": [P, I64, I64, P, P],
                 "orc_num_threads": [],
             }
             for name, argtypes in sig.items():
@@ -286,6 +289,37 @@ def gemm_w4a8(a, a_scales, a_gran: int, qweight, scales, zeros, group: int = 128
     y = np.empty((M, N), np.float64)
     _load().orc_gemm_w4a8(_p(a), _p(a_scales), a_gran, M, K, _p(qweight), _p(scales), _p(zeros), N, group, _p(y))
     return y
+
+
+# ------------------------------------------------------------ SmoothQuant ----
+
+def col_amax(x) -> np.ndarray:
+    """max_r |x[r, j]| of a binary32 matrix [R][C]."""
+    x = _c(x, np.float32)
+    R, C = x.shape
+    out = np.empty(C, np.float32)
+    _load().orc_col_amax(_p(x), R, C, _p(out))
+    return out
+
+
+def smooth_scales(amax_x, amax_w, alpha: float = 0.5) -> np.ndarray:
+    """Per-input-channel smoothing factors s_j = amax_x^alpha / amax_w^(1-alpha)
+    (binary64, rounded once to binary32; 1 where a maximum is 0)."""
+    amax_x = _c(amax_x, np.float32)
+    amax_w = _c(amax_w, np.float32)
+    s = np.empty(amax_x.shape, np.float32)
+    _load().orc_smooth_scales(_p(amax_x), _p(amax_w), amax_x.size, float(alpha), _p(s))
+    return s
+
+
+def col_mul(x, m) -> np.ndarray:
+    """x[r][j] * m[j] in binary32 (one rounding per element)."""
+    x = _c(x, np.float32)
+    m = _c(m, np.float32)
+    R, C = x.shape
+    out = np.empty((R, C), np.float32)
+    _load().orc_col_mul(_p(x), R, C, _p(m), _p(out))
+    return out
 
 
 def num_threads() -> int:

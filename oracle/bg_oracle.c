@@ -485,6 +485,43 @@ void orc_gemm_w4a8(const int8_t* a, const float* a_s, int a_gran, int64_t M, int
     free(ad);
 }
 
+/* ------------------------------------------------------------------------ */
+/* SmoothQuant fold.  [LPI] §15: Y = X W^T = (X S^-1)(W S)^T for a diagonal  */
+/* S over the input channels; S comes from calibration statistics and a      */
+/* smoothing strength and is folded into the static weights, so the         */
+/* activations reach the quantizer with their outlier channels shrunk.  The  */
+/* page gives no formula for S; the reading here is the SmoothQuant rule     */
+/* s_j = amax_x[j]^alpha / amax_w[j]^(1-alpha) (binary64, rounded once to    */
+/* binary32), with s_j = 1 where either column maximum is 0.                 */
+/* ------------------------------------------------------------------------ */
+
+/* Column maxima |x[:, j]| of a binary32 matrix [R][C]. */
+void orc_col_amax(const float* x, int64_t R, int64_t C, float* amax) {
+    for (int64_t j = 0; j < C; ++j) amax[j] = 0.0f;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t j = 0; j < C; ++j) {
+            float a = fabsf(x[r * C + j]);
+            if (a > amax[j]) amax[j] = a;
+        }
+}
+
+void orc_smooth_scales(const float* amax_x, const float* amax_w, int64_t C, double alpha, float* s) {
+    for (int64_t j = 0; j < C; ++j) {
+        if (amax_x[j] == 0.0f || amax_w[j] == 0.0f) {
+            s[j] = 1.0f;
+            continue;
+        }
+        s[j] = (float)(pow((double)amax_x[j], alpha) / pow((double)amax_w[j], 1.0 - alpha));
+    }
+}
+
+/* out[r][j] = x[r][j] * m[j], one binary32 multiplication per element (X S^-1
+ * with m = 1/s, or W S with m = s). */
+void orc_col_mul(const float* x, int64_t R, int64_t C, const float* m, float* out) {
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t j = 0; j < C; ++j) out[r * C + j] = x[r * C + j] * m[j];
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int orc_num_threads(void) {
 #ifdef _OPENMP
