@@ -269,7 +269,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
     128x128 / 1x128 blocks), W4A8 at M=2048 (the decode step's packed INT4
     weights x per-token INT8 activations) and W4A16 at B=74/256, each timed
     alone."""
-    res = {"w8a8_m2048": {}, "w4a8_m2048": {}, "w4a16_large_batch": {}}
+    res = {"w8a8_m2048": {}, "w4a8_m2048": {}, "smoothquant_m2048": {}, "w4a16_large_batch": {}}
     M = 2048
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]
@@ -298,6 +298,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "kernel": kname}
             log(f"  w8a8 {name:8s} {tag:10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
                 f"act_quant {ms_q * 1e3:6.1f} us")
+        res["smoothquant_m2048"][name] = smoothquant(ops, torch, np, dev, xt, wt, x, w, graph_of, time_graph)
         # W4A8: the same activations as per-token INT8 codes, the packed weights
         a, a_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
         p = packs[name][0]
@@ -325,6 +326,49 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "kernel": ops.last_kernel()}
             log(f"  w4a16 {name:8s} B={B:3d} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s")
     return res
+
+
+def smoothquant(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph):
+    """The SmoothQuant fold on the INT8 prefill recipe (8 activation channels
+    x50): S from the column maxima of 256 calibration rows and of W (alpha =
+    1/2), activations quantized with 1/s in the quantizer's load, weights
+    folded with s.  Reports the INT8 W8A8 output error against the unquantized
+    product (relative L2 over 16 rows outside the calibration rows) without and
+    with the fold, for per-token and per-tensor activation scales, and the
+    quantizer time with and without the fused column factors."""
+    M = xt.shape[0]
+    x32 = (x_bits.astype(np.uint32) << 16).view(np.float32)           # BF16 -> binary32, exact
+    ax = np.abs(x32[:256]).max(axis=0)
+    aw = np.abs(w).max(axis=0)
+    ok = (ax > 0) & (aw > 0)
+    s = np.where(ok, np.sqrt(ax.astype(np.float64)) / np.sqrt(np.where(ok, aw, 1).astype(np.float64)), 1.0)
+    s = s.astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    sd, invd = torch.from_numpy(s).to(dev), torch.from_numpy(inv).to(dev)
+    rows = np.linspace(256, M - 1, 16).astype(np.int64)
+    exact = x32[rows].astype(np.float64) @ w.astype(np.float64).T
+    out = {}
+    for tag, ag in (("per_token", ops.GRAN_ROW), ("per_tensor", ops.GRAN_TENSOR)):
+        errs = {}
+        for fold in (False, True):
+            if fold:
+                a, a_s = ops.act_quant_int8_smooth(xt, invd, ag)
+                wq, w_s = ops.act_quant_int8_smooth(wt, sd, ops.GRAN_ROW)
+            else:
+                a, a_s = ops.act_quant_int8(xt, ag)
+                wq, w_s = ops.act_quant_int8(wt, ops.GRAN_ROW)
+            y = ops.gemm_w8a8(a, a_s, ag, wq, w_s, ops.GRAN_ROW, out_dtype=torch.float32)
+            yv = y[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+            errs["folded" if fold else "plain"] = float(np.linalg.norm(yv - exact) / np.linalg.norm(exact))
+        out[tag] = {k: round(v, 5) for k, v in errs.items()}
+    g0 = graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch)
+    g1 = graph_of(lambda: ops.act_quant_int8_smooth(xt, invd, ops.GRAN_ROW), torch)
+    out["act_quant_us"] = {"plain": round(time_graph(g0, 10, torch) * 1e3, 1),
+                           "folded": round(time_graph(g1, 10, torch) * 1e3, 1)}
+    log(f"  smoothquant rel-L2 err per-token {out['per_token']['plain']:.4f} -> {out['per_token']['folded']:.4f}, "
+        f"per-tensor {out['per_tensor']['plain']:.4f} -> {out['per_tensor']['folded']:.4f}; act_quant "
+        f"{out['act_quant_us']['plain']} -> {out['act_quant_us']['folded']} us")
+    return out
 
 
 def crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph):

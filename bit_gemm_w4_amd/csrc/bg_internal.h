@@ -36,9 +36,10 @@ const char* kname(const char* base, A... a) {
 const char* launch_w4_pack(const void* w, int dt, int64_t N, int64_t K, bool asym,
                     uint32_t* qweight, uint16_t* scales, uint8_t* zeros, hipStream_t s);
 
-// act_quant: out_fp8 selects E4M3 (else INT8); gran = bg_gran value.
+// act_quant: out_fp8 selects E4M3 (else INT8); gran = bg_gran value; col_mul
+// (C floats, or NULL) multiplies column j by col_mul[j] before quantizing.
 const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8,
-                      void* q, float* scales, hipStream_t s);
+                             void* q, float* scales, const float* col_mul, hipStream_t s);
 
 // W4A16 kernels (x_bf16: activations/output are BF16, else FP16).
 // The VALU GEMV stages up to 4 activation rows of length K in LDS.

@@ -182,8 +182,9 @@ BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
 }
 
 static bg_status act_quant(const char* name, bool fp8, const void* x, int x_dtype, int64_t rows, int64_t cols,
-                           int gran, void* q, float* scales, void* stream) {
+                           int gran, const float* col_mul, bool smooth, void* q, float* scales, void* stream) {
     if (!x || !q || !scales) return fail(BG_ERR_NULL, "act_quant: x, q and scales must be non-NULL");
+    if (smooth && !col_mul) return fail(BG_ERR_NULL, "act_quant: col_mul must be non-NULL");
     if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
         return fail(BG_ERR_DTYPE, "act_quant: x_dtype %lld is not F32/F16/BF16", x_dtype);
     if (gran < BG_GRAN_TENSOR || gran > BG_GRAN_BLOCK128)
@@ -193,20 +194,31 @@ static bg_status act_quant(const char* name, bool fp8, const void* x, int x_dtyp
         return fail(BG_ERR_SHAPE, "act_quant: cols=%lld must be a multiple of 128", cols);
     if (gran == BG_GRAN_BLOCK128 && rows % 128)
         return fail(BG_ERR_SHAPE, "act_quant: BLOCK128 needs rows %% 128 == 0 (rows=%lld)", rows);
-    if (!aligned16(x) || !aligned16(q) || !aligned16(scales))
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || (col_mul && !aligned16(col_mul)))
         return fail(BG_ERR_ALIGN, "act_quant: pointers must be 16-byte aligned");
-    note_kernel(bg::launch_act_quant(x, x_dtype, rows, cols, gran, fp8, q, scales, static_cast<hipStream_t>(stream)));
+    note_kernel(bg::launch_act_quant(x, x_dtype, rows, cols, gran, fp8, q, scales, smooth ? col_mul : nullptr,
+                                     static_cast<hipStream_t>(stream)));
     return launched(name);
 }
 
 BG_EXPORT bg_status act_quant_int8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran, int8_t* q,
                                    float* scales, void* stream) {
-    return act_quant("act_quant_int8", false, x, x_dtype, rows, cols, gran, q, scales, stream);
+    return act_quant("act_quant_int8", false, x, x_dtype, rows, cols, gran, nullptr, false, q, scales, stream);
 }
 
 BG_EXPORT bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran, uint8_t* q,
                                   float* scales, void* stream) {
-    return act_quant("act_quant_fp8", true, x, x_dtype, rows, cols, gran, q, scales, stream);
+    return act_quant("act_quant_fp8", true, x, x_dtype, rows, cols, gran, nullptr, false, q, scales, stream);
+}
+
+BG_EXPORT bg_status act_quant_int8_smooth(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                                          const float* col_mul, int8_t* q, float* scales, void* stream) {
+    return act_quant("act_quant_int8_smooth", false, x, x_dtype, rows, cols, gran, col_mul, true, q, scales, stream);
+}
+
+BG_EXPORT bg_status act_quant_fp8_smooth(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                                         const float* col_mul, uint8_t* q, float* scales, void* stream) {
+    return act_quant("act_quant_fp8_smooth", true, x, x_dtype, rows, cols, gran, col_mul, true, q, scales, stream);
 }
 
 BG_EXPORT int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype) {

@@ -14,6 +14,11 @@
 // the amax slot (no hipMemset, so the sequence is graph-capturable), the amax
 // kernel combines block maxima with an integer atomic max on the float bits
 // (valid because amax >= 0), and the quantize kernel reads the slot.
+//
+// CM (the SmoothQuant fold, §15: Y = (X S^-1)(W S)^T): every element is first
+// multiplied by its column's factor cm[j] (1/s_j for activations, s_j for the
+// weights folded offline) -- one binary32 multiplication, fused into the load,
+// so the smoothed tensor never goes back to HBM.
 #include "bg_device.h"
 #include "bg_internal.h"
 
@@ -49,6 +54,20 @@ __device__ __forceinline__ void quant_store8(const float v[8], float s, void* q,
     *reinterpret_cast<uint2*>(static_cast<uint8_t*>(q) + idx) = make_uint2(lo, hi);
 }
 
+// 8 consecutive elements (columns col .. col + 7) as floats, times their
+// column factors when CM.
+template <int DT, bool CM>
+__device__ __forceinline__ void load8(const void* x, int64_t idx, const float* __restrict__ cm, int64_t col,
+                                      float v[8]) {
+    load8_f32<DT>(x, idx, v);
+    if constexpr (CM) {
+        const float4 a = *reinterpret_cast<const float4*>(cm + col);
+        const float4 b = *reinterpret_cast<const float4*>(cm + col + 4);
+        v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+        v[4] *= b.x; v[5] *= b.y; v[6] *= b.z; v[7] *= b.w;
+    }
+}
+
 __device__ __forceinline__ float amax8(const float v[8]) {
     float a = 0.0f;
 #pragma unroll
@@ -71,9 +90,10 @@ __device__ __forceinline__ float block_max256(float a, float* red) {
 // registers and many rows resident per CU.
 constexpr int ROW_MAXIT = 8;
 
-template <int DT, bool FP8, int IT>
+template <int DT, bool FP8, bool CM, int IT>
 __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, int64_t C,
-                                                   void* __restrict__ q, float* __restrict__ scales) {
+                                                   void* __restrict__ q, float* __restrict__ scales,
+                                                   const float* __restrict__ cm) {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const int64_t nchunk = C >> 3;
@@ -83,7 +103,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, i
     for (int it = 0; it < IT; ++it) {
         const int64_t c = (int64_t)it * 256 + threadIdx.x;
         if (c < nchunk) {
-            load8_f32<DT>(x, r * C + c * 8, v[it]);
+            load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v[it]);
             a = __builtin_fmaxf(a, amax8(v[it]));
         }
     }
@@ -97,45 +117,48 @@ __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, i
 }
 
 // Rows longer than 256 * 8 * ROW_MAXIT: amax pass, then a second read.
-template <int DT, bool FP8>
+template <int DT, bool FP8, bool CM>
 __global__ __launch_bounds__(256) void k_quant_row_2pass(const void* __restrict__ x, int64_t C,
                                                          void* __restrict__ q,
-                                                         float* __restrict__ scales) {
+                                                         float* __restrict__ scales,
+                                                         const float* __restrict__ cm) {
     __shared__ float red[4];
     const int64_t r = blockIdx.x;
     const int64_t nchunk = C >> 3;
     float v[8];
     float a = 0.0f;
     for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
-        load8_f32<DT>(x, r * C + c * 8, v);
+        load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v);
         a = __builtin_fmaxf(a, amax8(v));
     }
     const float s = unit_scale<FP8>(block_max256(a, red));
     for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
-        load8_f32<DT>(x, r * C + c * 8, v);
+        load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v);
         quant_store8<FP8>(v, s, q, r * C + c * 8);
     }
     if (threadIdx.x == 0) scales[r] = s;
 }
 
 // ---- 1 x 128 groups: 16 consecutive lanes per group ----
-template <int DT, bool FP8>
+template <int DT, bool FP8, bool CM>
 __global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, int64_t total_chunks,
-                                                    void* __restrict__ q, float* __restrict__ scales) {
+                                                    void* __restrict__ q, float* __restrict__ scales,
+                                                    const float* __restrict__ cm, int64_t C) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= total_chunks) return;          // total_chunks is a multiple of 16
     float v[8];
-    load8_f32<DT>(x, t * 8, v);
+    load8<DT, CM>(x, t * 8, cm, CM ? (t % (C >> 3)) * 8 : 0, v);
     const float s = unit_scale<FP8>(wave_max<16>(amax8(v)));
     quant_store8<FP8>(v, s, q, t * 8);
     if ((t & 15) == 0) scales[t >> 4] = s;
 }
 
 // ---- 128 x 128 blocks: one workgroup per block ----
-template <int DT, bool FP8>
+template <int DT, bool FP8, bool CM>
 __global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__ x, int64_t C,
                                                         void* __restrict__ q,
-                                                        float* __restrict__ scales) {
+                                                        float* __restrict__ scales,
+                                                        const float* __restrict__ cm) {
     __shared__ float red[4];
     const int64_t nb_c = C >> 7;
     const int64_t rb = blockIdx.x / nb_c, cb = blockIdx.x - rb * nb_c;
@@ -145,7 +168,7 @@ __global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int64_t row = rb * 128 + it * 16 + lane_r;
-        load8_f32<DT>(x, row * C + cb * 128 + lane_c * 8, v[it]);
+        load8<DT, CM>(x, row * C + cb * 128 + lane_c * 8, cm, cb * 128 + lane_c * 8, v[it]);
         a = __builtin_fmaxf(a, amax8(v[it]));
     }
     const float s = unit_scale<FP8>(block_max256(a, red));
@@ -164,9 +187,10 @@ __global__ void k_clear_amax(float* __restrict__ scales) { scales[1] = 0.0f; }
 // thread and iteration so that several 16-byte loads are in flight at once.
 constexpr int TU = 4;
 
-template <int DT>
+template <int DT, bool CM>
 __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x, int64_t nchunk,
-                                                     float* __restrict__ scales) {
+                                                     float* __restrict__ scales, const float* __restrict__ cm,
+                                                     int64_t C) {
     __shared__ float red[4];
     float a = 0.0f;
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -174,7 +198,8 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x,
         float v[TU][8];
 #pragma unroll
         for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk) load8_f32<DT>(x, (c0 + u * stride) * 8, v[u]);
+            if (c0 + u * stride < nchunk)
+                load8<DT, CM>(x, (c0 + u * stride) * 8, cm, CM ? ((c0 + u * stride) % (C >> 3)) * 8 : 0, v[u]);
 #pragma unroll
         for (int u = 0; u < TU; ++u)
             if (c0 + u * stride < nchunk) a = __builtin_fmaxf(a, amax8(v[u]));
@@ -191,17 +216,19 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x,
     }
 }
 
-template <int DT, bool FP8>
+template <int DT, bool FP8, bool CM>
 __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x, int64_t nchunk,
                                                       void* __restrict__ q,
-                                                      float* __restrict__ scales) {
+                                                      float* __restrict__ scales,
+                                                      const float* __restrict__ cm, int64_t C) {
     const float s = unit_scale<FP8>(scales[1]);
     const int64_t stride = (int64_t)gridDim.x * 256;
     for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < nchunk; c0 += TU * stride) {
         float v[TU][8];
 #pragma unroll
         for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk) load8_f32<DT>(x, (c0 + u * stride) * 8, v[u]);
+            if (c0 + u * stride < nchunk)
+                load8<DT, CM>(x, (c0 + u * stride) * 8, cm, CM ? ((c0 + u * stride) % (C >> 3)) * 8 : 0, v[u]);
 #pragma unroll
         for (int u = 0; u < TU; ++u)
             if (c0 + u * stride < nchunk) quant_store8<FP8>(v[u], s, q, (c0 + u * stride) * 8);
@@ -215,57 +242,67 @@ static unsigned grid_for(int64_t nchunk) {
     return (unsigned)(b < 1 ? 1 : b);
 }
 
-template <int DT, bool FP8>
-static const char* launch_typed(const void* x, int64_t R, int64_t C, int gran, void* q, float* sc,
-                         hipStream_t s) {
+template <int DT, bool FP8, bool CM>
+static const char* launch_typed(const void* x, int64_t R, int64_t C, int gran, void* q, float* sc, const float* cm,
+                                hipStream_t s) {
     switch (gran) {
         case G_ROW:
             if (C <= 256 * 8 * ROW_MAXIT) {
                 const int64_t per = (C / 8 + 255) / 256;         // chunks per thread
                 if (per <= 1)
-                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 1>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, CM, 1>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc,
+                                       cm);
                 else if (per <= 2)
-                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 2>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, CM, 2>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc,
+                                       cm);
                 else if (per <= 4)
-                    hipLaunchKernelGGL((k_quant_row<DT, FP8, 4>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, CM, 4>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc,
+                                       cm);
                 else
-                    hipLaunchKernelGGL((k_quant_row<DT, FP8, ROW_MAXIT>), dim3((unsigned)R), dim3(256), 0, s, x, C,
-                                       q, sc);
-                return kname("k_quant_row", DT, FP8);
+                    hipLaunchKernelGGL((k_quant_row<DT, FP8, CM, ROW_MAXIT>), dim3((unsigned)R), dim3(256), 0, s, x,
+                                       C, q, sc, cm);
+                return kname("k_quant_row", DT, FP8, CM);
             }
-            hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc);
-            return kname("k_quant_row_2pass", DT, FP8);
+            hipLaunchKernelGGL((k_quant_row_2pass<DT, FP8, CM>), dim3((unsigned)R), dim3(256), 0, s, x, C, q, sc, cm);
+            return kname("k_quant_row_2pass", DT, FP8, CM);
         case G_ROW_G128: {
             const int64_t chunks = R * (C >> 3);
-            hipLaunchKernelGGL((k_quant_g128<DT, FP8>), dim3((unsigned)((chunks + 255) / 256)), dim3(256),
-                               0, s, x, chunks, q, sc);
-            return kname("k_quant_g128", DT, FP8);
+            hipLaunchKernelGGL((k_quant_g128<DT, FP8, CM>), dim3((unsigned)((chunks + 255) / 256)), dim3(256),
+                               0, s, x, chunks, q, sc, cm, C);
+            return kname("k_quant_g128", DT, FP8, CM);
         }
         case G_BLOCK128:
-            hipLaunchKernelGGL((k_quant_block128<DT, FP8>), dim3((unsigned)((R >> 7) * (C >> 7))), dim3(256),
-                               0, s, x, C, q, sc);
-            return kname("k_quant_block128", DT, FP8);
+            hipLaunchKernelGGL((k_quant_block128<DT, FP8, CM>), dim3((unsigned)((R >> 7) * (C >> 7))), dim3(256),
+                               0, s, x, C, q, sc, cm);
+            return kname("k_quant_block128", DT, FP8, CM);
         default: {
             const int64_t chunks = R * (C >> 3);
             hipLaunchKernelGGL(k_clear_amax, dim3(1), dim3(1), 0, s, sc);
-            hipLaunchKernelGGL((k_amax_tensor<DT>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks, sc);
-            hipLaunchKernelGGL((k_quant_tensor<DT, FP8>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks,
-                               q, sc);
-            return kname("k_quant_tensor", DT, FP8);
+            hipLaunchKernelGGL((k_amax_tensor<DT, CM>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks, sc, cm,
+                               C);
+            hipLaunchKernelGGL((k_quant_tensor<DT, FP8, CM>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks,
+                               q, sc, cm, C);
+            return kname("k_quant_tensor", DT, FP8, CM);
         }
     }
 }
 
+template <bool FP8, bool CM>
+static const char* launch_fp(const void* x, int dt, int64_t R, int64_t C, int gran, void* q, float* scales,
+                             const float* cm, hipStream_t s) {
+    if (dt == DT_F32) return launch_typed<DT_F32, FP8, CM>(x, R, C, gran, q, scales, cm, s);
+    if (dt == DT_F16) return launch_typed<DT_F16, FP8, CM>(x, R, C, gran, q, scales, cm, s);
+    return launch_typed<DT_BF16, FP8, CM>(x, R, C, gran, q, scales, cm, s);
+}
+
 const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gran, bool out_fp8, void* q,
-                             float* scales, hipStream_t s) {
-    if (out_fp8) {
-        if (dt == DT_F32) return launch_typed<DT_F32, true>(x, R, C, gran, q, scales, s);
-        if (dt == DT_F16) return launch_typed<DT_F16, true>(x, R, C, gran, q, scales, s);
-        return launch_typed<DT_BF16, true>(x, R, C, gran, q, scales, s);
+                             float* scales, const float* col_mul, hipStream_t s) {
+    if (col_mul) {
+        if (out_fp8) return launch_fp<true, true>(x, dt, R, C, gran, q, scales, col_mul, s);
+        return launch_fp<false, true>(x, dt, R, C, gran, q, scales, col_mul, s);
     }
-    if (dt == DT_F32) return launch_typed<DT_F32, false>(x, R, C, gran, q, scales, s);
-    if (dt == DT_F16) return launch_typed<DT_F16, false>(x, R, C, gran, q, scales, s);
-    return launch_typed<DT_BF16, false>(x, R, C, gran, q, scales, s);
+    if (out_fp8) return launch_fp<true, false>(x, dt, R, C, gran, q, scales, nullptr, s);
+    return launch_fp<false, false>(x, dt, R, C, gran, q, scales, nullptr, s);
 }
 
 }  // namespace bg

@@ -24,7 +24,8 @@ ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED, ALGO_SPLITK = 0, 1, 2, 3, 4
 PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
-    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8", "gemm_w8a8",
+    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
+    "act_quant_int8_smooth", "act_quant_fp8_smooth", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
     "gemm_w4a16_algo", "gemm_w8a8_algo",
     "bg_status_string", "bg_last_error",
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
             "gemm_w4a16_workspace_bytes": [I64, I64, I64, I],
             "act_quant_int8": [P, I, I64, I64, I, P, P, P],
             "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
+            "act_quant_int8_smooth": [P, I, I64, I64, I, P, P, P, P],
+            "act_quant_fp8_smooth": [P, I, I64, I64, I, P, P, P, P],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
             "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
             "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
@@ -202,14 +205,19 @@ def scale_shape(gran: int, rows: int, cols: int):
             GRAN_BLOCK128: (rows // 128, cols // 128)}[gran]
 
 
-def _act_quant(fn: str, x: torch.Tensor, gran: int, out_dtype: torch.dtype, stream=None):
+def _act_quant(fn: str, x: torch.Tensor, gran: int, out_dtype: torch.dtype, stream=None, col_mul=None):
     R, C = x.shape
     dt = _TORCH_DT.get(x.dtype)
     if dt is None:
         raise ValueError(f"{fn}: unsupported dtype {x.dtype}")
     q = torch.empty((R, C), dtype=out_dtype, device=x.device)
     s = torch.empty(scale_shape(gran, R, C), dtype=torch.float32, device=x.device)
-    _check(getattr(lib(), fn)(_ptr(x), dt, R, C, gran, _ptr(q), _ptr(s), _stream(stream)), fn)
+    if col_mul is None:
+        _check(getattr(lib(), fn)(_ptr(x), dt, R, C, gran, _ptr(q), _ptr(s), _stream(stream)), fn)
+    else:
+        if col_mul.dtype != torch.float32 or col_mul.numel() != C:
+            raise ValueError(f"{fn}: col_mul must be {C} float32 values")
+        _check(getattr(lib(), fn)(_ptr(x), dt, R, C, gran, _ptr(col_mul), _ptr(q), _ptr(s), _stream(stream)), fn)
     return q, s
 
 
@@ -221,6 +229,17 @@ def act_quant_int8(x: torch.Tensor, gran: int = GRAN_ROW, stream=None):
 def act_quant_fp8(x: torch.Tensor, gran: int = GRAN_ROW, stream=None):
     """-> (E4M3 bytes as uint8 [R][C], float32 scales in the layout of `gran`)."""
     return _act_quant("act_quant_fp8", x, gran, torch.uint8, stream)
+
+
+def act_quant_int8_smooth(x: torch.Tensor, col_mul: torch.Tensor, gran: int = GRAN_ROW, stream=None):
+    """INT8 codes and scales of X diag(col_mul) (the SmoothQuant fold: 1/s for
+    activations, s for the weights)."""
+    return _act_quant("act_quant_int8_smooth", x, gran, torch.int8, stream, col_mul)
+
+
+def act_quant_fp8_smooth(x: torch.Tensor, col_mul: torch.Tensor, gran: int = GRAN_ROW, stream=None):
+    """E4M3 codes and scales of X diag(col_mul)."""
+    return _act_quant("act_quant_fp8_smooth", x, gran, torch.uint8, stream, col_mul)
 
 
 _OUT_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32}

@@ -184,6 +184,23 @@ bg_status act_quant_fp8(const void* x, int x_dtype, int64_t rows, int64_t cols, 
                         uint8_t* q, float* scales, void* stream);
 
 /*
+ * act_quant_int8_smooth / act_quant_fp8_smooth -- the same quantizers applied
+ * to X diag(col_mul): element (r, j) is multiplied by col_mul[j] (one binary32
+ * multiplication, fused into the load) before the unit's amax and the codes.
+ * This is the online half of the SmoothQuant fold ([LPI] §15:
+ * Y = X W^T = (X S^-1)(W S)^T for a diagonal S over the input channels):
+ * activations pass col_mul = 1/s, and the weights are folded once with
+ * col_mul = s before their own quantization.  S comes from calibration
+ * statistics and a smoothing strength and is the caller's input.
+ *   col_mul  cols floats, 16-byte aligned device memory; BG_ERR_NULL if NULL.
+ * Other arguments, layouts and errors as act_quant_int8 / act_quant_fp8.
+ */
+bg_status act_quant_int8_smooth(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                                const float* col_mul, int8_t* q, float* scales, void* stream);
+bg_status act_quant_fp8_smooth(const void* x, int x_dtype, int64_t rows, int64_t cols, int gran,
+                               const float* col_mul, uint8_t* q, float* scales, void* stream);
+
+/*
  * gemm_w8a8 -- native INT8 or FP8 GEMM of quantized activations A [M][K] and
  * weights W [N][K] ([AIB] W8A8/FP8 section: no upcast, low-precision matrix
  * cores; [LPI] §9 FP8 GEMM contract, §22 INT32 / FP32 accumulators).

@@ -485,3 +485,55 @@ def test_w4a8_rejects(ops):
         ops.gemm_w4a8(a, s, ops.GRAN_ROW_G128, p)                       # granularity
     with pytest.raises(ValueError):
         ops.gemm_w4a8(a.float(), s, ops.GRAN_ROW, p)                    # dtype
+
+
+# ------------------------------------------------------- SmoothQuant fold ----
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("gran", [0, 1, 2, 3])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_quant_smooth_bitexact(ops, orc, fp8, gran, dtype):
+    """Codes and scales of X diag(m) bit-exact: the per-column factor is one
+    binary32 multiplication before the quantizer, on both sides."""
+    R, C = 256, 1152
+    w, x = synth.layer(R, 64, C, "f32", seed=50 + gran, x_outlier_cols=8)
+    rng = np.random.default_rng(51)
+    m = np.exp(rng.uniform(-3, 3, C)).astype(np.float32)
+    xd, x32 = as_f32(x, dtype)
+    fn = ops.act_quant_fp8_smooth if fp8 else ops.act_quant_int8_smooth
+    q, s = fn(xd, torch.from_numpy(m).cuda(), gran)
+    torch.cuda.synchronize()
+    oq = orc.act_quant_fp8 if fp8 else orc.act_quant_int8
+    qo, so = oq(orc.col_mul(x32, m), gran)
+    assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32))
+
+
+def test_smoothquant_w8a8_end_to_end(ops, orc):
+    """INT8 prefill recipe (8 activation channels x50): S from the column
+    maxima (alpha = 1/2), activations quantized with 1/s, weights folded with
+    s; codes bit-exact, the product within tolerance of the oracle's, and its
+    error against the unquantized product below the unsmoothed path's."""
+    M, N, K = 256, 512, 1024
+    w, x = synth.prefill_layer(M, N, K, seed=52)
+    x32 = orc.bits_to_f32(x, "bf16")
+    s = orc.smooth_scales(orc.col_amax(x32), orc.col_amax(w), 0.5)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    xt = dev_bits(x, "bf16")
+    wt = torch.from_numpy(w).cuda()
+    a, a_s = ops.act_quant_int8_smooth(xt, torch.from_numpy(inv).cuda(), ops.GRAN_ROW)
+    wq, w_s = ops.act_quant_int8_smooth(wt, torch.from_numpy(s).cuda(), ops.GRAN_ROW)
+    y = ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out_dtype=torch.float32)
+    a0, a0_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
+    w0, w0_s = ops.act_quant_int8(wt, ops.GRAN_ROW)
+    y0 = ops.gemm_w8a8(a0, a0_s, ops.GRAN_ROW, w0, w0_s, ops.GRAN_ROW, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ao, aso = orc.act_quant_int8(orc.col_mul(x32, inv), 1)
+    wo, wso = orc.act_quant_int8(orc.col_mul(w, s), 1)
+    assert np.array_equal(a.cpu().numpy(), ao) and np.array_equal(wq.cpu().numpy(), wo)
+    ref = orc.gemm_w8a8(ao, aso, 1, wo, wso, 1, False)
+    check_close(y.cpu().numpy().astype(np.float64), ref, orc, "smoothed w8a8")
+    exact = x32.astype(np.float64) @ w.astype(np.float64).T
+    err_s = orc.rel_l2(y.cpu().numpy(), exact)
+    err_0 = orc.rel_l2(y0.cpu().numpy(), exact)
+    assert err_s < 0.5 * err_0, (err_0, err_s)
