@@ -11,7 +11,8 @@ names the passage of the pages it follows in the C source:
 
 * [LPI] "Low-precision LLM inference: FP8/INT8/INT4/FP4 kernels and
   calibration (8/10)", blog.ruahverce.com -- §1 notation table and precision
-  manifest (W4A8), §2 eq. (1)-(2), §3 eq. (3), §15 SmoothQuant fold,
+  manifest (W4A8), §2 eq. (1)-(2), §3 eq. (3), §10 MX block formats, §15
+  SmoothQuant fold,
   §4 granularity, §5 effective bits, §7 FP8 formats, §8 FP8 scale recipes,
   §22 accumulator precision.
 * [AIB] "Quantization throughput by method: why W4A16 is overtaken by W8A8 as
@@ -79,6 +80,8 @@ def _load():
                 "orc_col_amax": [P, I64, I64, P],
                 "orc_smooth_scales": [P, P, I64, ctypes.c_double, P],
                 "orc_col_mul": [P, I64, I64, P, P],
+                "orc_quant_mxfp8": [P, I64, I64, P, P],
+                "orc_gemm_mxfp8": [P, P, P, P, I64, I64, I64, P],
                 "orc_num_threads": [],
             }
             for name, argtypes in sig.items():
@@ -320,6 +323,30 @@ def col_mul(x, m) -> np.ndarray:
     out = np.empty((R, C), np.float32)
     _load().orc_col_mul(_p(x), R, C, _p(m), _p(out))
     return out
+
+
+# ---------------------------------------------------------------- MXFP8 ----
+
+def quant_mxfp8(x):
+    """MXFP8 of binary32 x [R][C] (C % 32 == 0) -> (E4M3 bytes [R][C], E8M0
+    scale bytes [R][C/32])."""
+    x = _c(x, np.float32)
+    R, C = x.shape
+    assert C % 32 == 0
+    q = np.empty((R, C), np.uint8)
+    e = np.empty((R, C // 32), np.uint8)
+    _load().orc_quant_mxfp8(_p(x), R, C, _p(q), _p(e))
+    return q, e
+
+
+def gemm_mxfp8(a, ea, w, ew) -> np.ndarray:
+    """Exact MXFP8 GEMM in binary64: Y = (A X_a)(W X_w)^T."""
+    a, ea, w, ew = (_c(t, np.uint8) for t in (a, ea, w, ew))
+    M, K = a.shape
+    N = w.shape[0]
+    y = np.empty((M, N), np.float64)
+    _load().orc_gemm_mxfp8(_p(a), _p(ea), _p(w), _p(ew), M, N, K, _p(y))
+    return y
 
 
 def num_threads() -> int:

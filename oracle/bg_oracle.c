@@ -522,6 +522,58 @@ void orc_col_mul(const float* x, int64_t R, int64_t C, const float* m, float* ou
         for (int64_t j = 0; j < C; ++j) out[r * C + j] = x[r * C + j] * m[j];
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP8: microscaled E4M3.  [LPI] §10: the OCP MX specification treats a   */
+/* block of elements and its shared scale as one data format.  The block,    */
+/* scale type and conversion are the OCP MX v1.0 ones (the pages name the    */
+/* specification without restating it): 32 consecutive elements along K     */
+/* share an E8M0 scale X = 2^(E - 127); E = floor(log2(max |v|)) - 8 + 127   */
+/* (8 = the largest E4M3 exponent), clamped to 0..254, and every element is  */
+/* the saturating RNE E4M3 cast of v / X.  An all-zero block gets X = 1.     */
+/* Scales are stored [rows][cols/32].                                        */
+/* ------------------------------------------------------------------------ */
+
+void orc_quant_mxfp8(const float* x, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0) {
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t b = 0; b < C / 32; ++b) {
+            const float* v = x + r * C + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            int e = 127;
+            if (amax > 0.0f) {
+                e = ilogbf(amax) - 8 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            e8m0[r * (C / 32) + b] = (uint8_t)e;
+            for (int i = 0; i < 32; ++i) q[r * C + b * 32 + i] = orc_e4m3_encode(ldexpf(v[i], 127 - e));
+        }
+}
+
+/* Y[m,n] = sum_k (dec(a[m,k]) X_a[m,k/32]) (dec(w[n,k]) X_w[n,k/32]) in double
+ * (exact: every term is a product of two E4M3 values and powers of two). */
+void orc_gemm_mxfp8(const uint8_t* a, const uint8_t* ea, const uint8_t* w, const uint8_t* ew, int64_t M, int64_t N,
+                    int64_t K, double* y) {
+    double* ad = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k)
+            ad[m * K + k] = orc_e4m3_decode(a[m * K + k]) * ldexp(1.0, (int)ea[m * (K / 32) + k / 32] - 127);
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            wd[n * K + k] = orc_e4m3_decode(w[n * K + k]) * ldexp(1.0, (int)ew[n * (K / 32) + k / 32] - 127);
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += ad[m * K + k] * wd[n * K + k];
+            y[m * N + n] = acc;
+        }
+    free(ad);
+    free(wd);
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int orc_num_threads(void) {
 #ifdef _OPENMP
