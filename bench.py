@@ -310,6 +310,25 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
         res["w4a8_m2048"][name] = {"gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
                                    "frac": round(tf / peak, 4), "kernel": ops.last_kernel()}
         log(f"  w4a8 {name:8s} {ms * 1e3:8.1f} us {tf:7.1f} TOP/s ({tf / peak:.1%})")
+        if name in ("gate_up", "down"):
+            # MXFP8: E8M0 scales per 32 K elements, applied by the MFMA
+            a, ea = ops.act_quant_mxfp8(xt)
+            q, ew = ops.act_quant_mxfp8(wt)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            g = graph_of(lambda: ops.gemm_mxfp8(a, ea, q, ew, out=y), torch)
+            ms = time_graph(g, 10, torch)
+            kname = ops.last_kernel()
+            gq = graph_of(lambda: ops.act_quant_mxfp8(xt), torch)
+            ms_q = time_graph(gq, 10, torch)
+            tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+            peak = roofline.PEAK_TFLOPS["fp8"]
+            res["w8a8_m2048"][f"{name}/mxfp8"] = {
+                "gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac": round(tf / peak, 4),
+                "act_quant_us": round(ms_q * 1e3, 1),
+                "act_quant_gbps": round(roofline.act_quant_bytes(M, K) / (ms_q * 1e-3) / 1e9, 1),
+                "kernel": kname}
+            log(f"  w8a8 {name:8s} {'mxfp8':10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
+                f"act_quant {ms_q * 1e3:6.1f} us")
         del wt
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]

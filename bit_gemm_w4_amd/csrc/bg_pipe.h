@@ -81,6 +81,29 @@ __device__ __forceinline__ uint32_t ds_read4_after(uint32_t addr, const int4_t& 
     asm volatile("ds_read_b32 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
     return v;
 }
+__device__ __forceinline__ uint32_t ds_read4_after(uint32_t addr, const int8_t_v& a1, const int8_t_v& b1,
+                                                   const int8_t_v& a0, const int8_t_v& b0) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t ds_read1_after(uint32_t addr, const int8_t_v& a1, const int8_t_v& b1,
+                                                   const int8_t_v& a0, const int8_t_v& b0) {
+    uint32_t v;
+    asm volatile("ds_read_u8 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t ds_read1_after(uint32_t addr, const int4_t& a1, const int4_t& b1,
+                                                   const int4_t& a0, const int4_t& b0) {
+    uint32_t v;
+    asm volatile("ds_read_u8 %0, %1" : "=&v"(v) : "v"(addr), "v"(a1), "v"(b1), "v"(a0), "v"(b0) : "memory");
+    return v;
+}
+__device__ __forceinline__ uint32_t ds_read1(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_u8 %0, %1" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
 __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr) : "memory");

@@ -153,6 +153,41 @@ __global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, 
     if ((t & 15) == 0) scales[t >> 4] = s;
 }
 
+// ---- MXFP8: 32-element blocks along a row, 4 consecutive lanes per block ----
+// OCP MX: E8M0 scale 2^(e - 127), e = floor(log2 amax) - 8 + 127 (8 = the
+// largest E4M3 exponent) clamped to 0..254, 127 for an all-zero block; the
+// elements are the saturating RNE E4M3 casts of v * 2^(127 - e) (exact
+// power-of-two scaling).  Scales [rows][cols/32].
+template <int DT>
+__global__ __launch_bounds__(256) void k_quant_mx32(const void* __restrict__ x, int64_t total_chunks,
+                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= total_chunks) return;          // total_chunks is a multiple of 4: whole blocks retire together
+    float v[8];
+    load8_f32<DT>(x, t * 8, v);
+    const float amax = wave_max<4>(amax8(v));
+    int e = 127;
+    if (amax > 0.0f) {
+        e = ilogbf(amax) - 8 + 127;
+        e = e < 0 ? 0 : e > 254 ? 254 : e;
+    }
+    uint32_t lo = 0, hi = 0;
+    lo = e4m3x2(ldexpf(v[0], 127 - e), ldexpf(v[1], 127 - e)) | (e4m3x2(ldexpf(v[2], 127 - e), ldexpf(v[3], 127 - e)) << 16);
+    hi = e4m3x2(ldexpf(v[4], 127 - e), ldexpf(v[5], 127 - e)) | (e4m3x2(ldexpf(v[6], 127 - e), ldexpf(v[7], 127 - e)) << 16);
+    *reinterpret_cast<uint2*>(q + t * 8) = make_uint2(lo, hi);
+    if ((t & 3) == 0) e8m0[t >> 2] = (uint8_t)e;
+}
+
+const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0,
+                              hipStream_t s) {
+    const int64_t chunks = R * (C >> 3);
+    const dim3 grid((unsigned)((chunks + 255) / 256));
+    if (dt == DT_F32) hipLaunchKernelGGL((k_quant_mx32<DT_F32>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
+    else if (dt == DT_F16) hipLaunchKernelGGL((k_quant_mx32<DT_F16>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
+    else hipLaunchKernelGGL((k_quant_mx32<DT_BF16>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
+    return kname("k_quant_mx32", dt);
+}
+
 // ---- 128 x 128 blocks: one workgroup per block ----
 template <int DT, bool FP8, bool CM>
 __global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__ x, int64_t C,

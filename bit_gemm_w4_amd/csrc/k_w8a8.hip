@@ -19,7 +19,7 @@
 namespace bg {
 
 enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2, O_I32 = 5 };
-enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3 };
+enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4 };
 
 // ============================================================================
 // Large-M GEMM.  Block tile BM x BN; K advances in stages of 64 bytes (one LDS
@@ -49,9 +49,10 @@ __device__ __forceinline__ int gswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 template <int TM, int TN>
 struct Frags {
     int4_t a[TM][2], b[TN][2];                  // two 16-byte K chunks per 32-row fragment
+    uint32_t sa[TM], sb[TN];                    // MX: the lane's E8M0 byte of each fragment row
 };
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN>
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, bool MX = false>
 __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       int a_gran, const uint8_t* __restrict__ w,
                                                       const float* __restrict__ ws, int w_gran, int64_t M,
@@ -62,17 +63,25 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
     constexpr int STAGE_BYTES = ROWS * GK;
     constexpr int LOADS = ROWS / (16 * NW);                      // 1 KB wave-loads per wave per stage
+    // MX: E8M0 scales, 16 bytes per row per chunk of 8 stages, in a ring of 3
+    // chunks after the stage buffers; every stage also copies one eighth of a
+    // later chunk (one more copy per wave and stage)
+    static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8 variant");
+    constexpr int MX_CHUNK = ROWS * 16, MX_RING = MX ? 3 * MX_CHUNK : 0;
+    constexpr int LOADS_T = LOADS + (MX ? 1 : 0);
     // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
-    constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
-    constexpr int NB_MAX = BM * BN <= 128 * 128 ? 5 : 6;
+    constexpr int NB_FIT = (160 * 1024 - MX_RING) / STAGE_BYTES;
+    constexpr int NB_MAX = BM * BN <= 128 * 128 || BLOCK || MX ? 5 : 6;
     constexpr int NB = NB_FIT > NB_MAX ? NB_MAX : NB_FIT;
     static_assert(ROWS % (16 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
-    static_assert(NB >= 3 && (NB - 1) * LOADS + (BLOCK ? 4 * TM : 0) < 64, "stage count / vmcnt range");
+    static_assert(NB >= 3 && (NB - 1) * LOADS_T + 8 + (BLOCK ? 4 * TM : 0) < 64, "stage count / vmcnt range");
     static_assert(!BLOCK || NB == 5, "the block-scale load count in the stage waits assumes five buffers");
+    static_assert(!MX || NB <= 6, "the MX scale ring holds 3 chunks: at most 6 stages in flight");
     constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
     constexpr int EPI_BYTES = NW * WTM * EPI_PITCH;
-    constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
+    constexpr int RING_END = NB * STAGE_BYTES + MX_RING;
+    constexpr int LDS_BYTES = RING_END > EPI_BYTES ? RING_END : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -104,16 +113,51 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     }
     const int nkb = (int)(K / GK);
     const int kb0 = sl * spl, kb1 = kb0 + spl < nkb ? kb0 + spl : nkb;
+    // MX scale chunks: chunk c holds the 16 E8M0 bytes (K blocks 16c .. 16c+15,
+    // stages 8c .. 8c+7) of every A row, then of every W row, in slot c % 3.
+    // Piece p of a chunk (BM/8 A rows and BN/8 W rows) is copied by the first
+    // NW/2 waves (A) and the last NW/2 (W), rpa / rpw rows (lanes) each.
+    // Scales are [rows][K/32] bytes; K % 512 == 0, so chunks are whole.
+    const int64_t kb32 = K >> 5;
+    const int nchunk = (int)(K >> 9);
+    constexpr int RPA = MX ? BM / 8 / (NW / 2) : 1, RPW = MX ? BN / 8 / (NW / 2) : 1;
+    // (MX: as / ws point to the E8M0 bytes; otherwise the resources are empty)
+    const auto rsa = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint8_t*>(const_cast<float*>(as)) + (MX ? m0 * kb32 : 0), (short)0,
+        MX ? (int)(rows_a * kb32) : 0, 0x00020000);
+    const auto rsw = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint8_t*>(const_cast<float*>(ws)) + (MX ? n0 * kb32 : 0), (short)0,
+        MX ? (int)(rows_w * kb32) : 0, 0x00020000);
+    const bool mx_a = wave < NW / 2;
+    const int mx_w = mx_a ? wave : wave - NW / 2;
+    auto mx_piece = [&](int c, int p) {
+        if constexpr (MX) {
+            const int cc = c < nchunk - 1 ? c : nchunk - 1;      // past the end: repeat the last chunk's bytes
+            uint8_t* slot = lds + NB * STAGE_BYTES + (c % 3) * MX_CHUNK;
+            if (mx_a) {
+                const int r = p * (BM / 8) + mx_w * RPA;
+                if (lane < RPA) copy16_to_lds(rsa, slot + r * 16, (uint32_t)((r + lane) * kb32), cc * 16);
+            } else {
+                const int r = p * (BN / 8) + mx_w * RPW;
+                if (lane < RPW) copy16_to_lds(rsw, slot + (BM + r) * 16, (uint32_t)((r + lane) * kb32), cc * 16);
+            }
+        }
+    };
     // Stage kb goes to buffer kb % NB.  Stages past the end of K copy bytes of
     // later rows (zeros past the end of the buffer resource) into a free
-    // buffer that is never consumed.
+    // buffer that is never consumed.  With MX, copy LOADS of stage kb is
+    // piece kb % 8 of chunk kb / 8 + 1.
     auto issue_one = [&](int kb, int t) {
+        if (MX && t == LOADS) {
+            mx_piece(kb / 8 + 1, kb % 8);
+            return;
+        }
         const int j = wave * LOADS + t;
         copy16_to_lds(j < BM / 16 ? ra : rw, lds + (kb % NB) * STAGE_BYTES + j * 16 * GK, voff[t], kb * GK);
     };
     auto issue = [&](int kb) {
 #pragma unroll
-        for (int t = 0; t < LOADS; ++t) issue_one(kb, t);
+        for (int t = 0; t < LOADS_T; ++t) issue_one(kb, t);
     };
 
     // ---- fragment addresses: lane l reads chunks h and 2 + h of row l % 32 ----
@@ -126,8 +170,22 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     const uint32_t offa1 = (uint32_t)(ra0 * GK + (((2 + h) ^ gswz(ra0)) << 4));
     const uint32_t offb0 = (uint32_t)(rb0 * GK + ((h ^ gswz(rb0)) << 4));
     const uint32_t offb1 = (uint32_t)(rb0 * GK + (((2 + h) ^ gswz(rb0)) << 4));
-    // read number r of a stage (0 .. 2(TM+TN)-1): A fragments first, then W
-    auto read_one = [&](Frags<TM, TN>& f, uint32_t base, int r) {
+    // MX: stage kb's E8M0 bytes of a row are bytes 2kb % 16 (k 0..31 of the
+    // stage, lanes h = 0) and 2kb % 16 + 1 (k 32..63, h = 1) of its chunk row
+    const uint32_t mxa0 = (uint32_t)(ra0 * 16 + h), mxb0 = (uint32_t)(rb0 * 16 + h);
+    auto mx_base = [&](int kb) {
+        return lds0 + (uint32_t)(NB * STAGE_BYTES + ((kb >> 3) % 3) * MX_CHUNK + ((2 * kb) & 15));
+    };
+    constexpr int NFRAG = 2 * (TM + TN);
+    // read number r of a stage (0 .. NREAD-1): A fragments first, then W, then
+    // (MX) the scale dwords of the A and W fragment rows
+    auto read_one = [&](Frags<TM, TN>& f, uint32_t base, uint32_t mxb, int r) {
+        if (r >= NFRAG) {
+            const int i = r - NFRAG;
+            if (i < TM) f.sa[i] = ds_read1(mxb + mxa0 + (uint32_t)(i * 32 * 16));
+            else f.sb[i - TM] = ds_read1(mxb + mxb0 + (uint32_t)((i - TM) * 32 * 16));
+            return;
+        }
         const int frag = r >> 1, c = r & 1;
         if (frag < TM)
             f.a[frag][c] = ds_read16(base + (c ? offa1 : offa0) + (uint32_t)(frag * 32 * GK));
@@ -136,8 +194,14 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     };
     // the same, issued right after MFMAs whose operands must stay untouched
     using op_t = typename std::conditional<FP8, int8_t_v, int4_t>::type;
-    auto read_one_after = [&](Frags<TM, TN>& f, uint32_t base, int r, const op_t& a1, const op_t& b1,
+    auto read_one_after = [&](Frags<TM, TN>& f, uint32_t base, uint32_t mxb, int r, const op_t& a1, const op_t& b1,
                               const op_t& a0, const op_t& b0) {
+        if (r >= NFRAG) {
+            const int i = r - NFRAG;
+            if (i < TM) f.sa[i] = ds_read1_after(mxb + mxa0 + (uint32_t)(i * 32 * 16), a1, b1, a0, b0);
+            else f.sb[i - TM] = ds_read1_after(mxb + mxb0 + (uint32_t)((i - TM) * 32 * 16), a1, b1, a0, b0);
+            return;
+        }
         const int frag = r >> 1, c = r & 1;
         if (frag < TM)
             f.a[frag][c] = ds_read16_after(base + (c ? offa1 : offa0) + (uint32_t)(frag * 32 * GK), a1, b1, a0, b0);
@@ -152,6 +216,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         for (int i = 0; i < TM; ++i) settle(f.a[i][0]), settle(f.a[i][1]);
 #pragma unroll
         for (int j = 0; j < TN; ++j) settle(f.b[j][0]), settle(f.b[j][1]);
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) settle(f.sa[i]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) settle(f.sb[j]);
+        }
     };
 
     using acc_t = typename std::conditional<FP8, float16_t, int16_t_v>::type;
@@ -219,7 +289,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // the buffer of stage kb is free and receives stage kb+NB, and (b)
     // publishes stage kb+1, whose fragment reads are then spread between the
     // MFMAs of stage kb.
-    constexpr int NREAD = 2 * (TM + TN);
+    constexpr int NREAD = NFRAG + (MX ? TM + TN : 0);
     constexpr int NMFMA = FP8 ? TM * TN : 2 * TM * TN;
     constexpr int NSLOT = NMFMA - NMFMA / 4;
     auto step = [&](Frags<TM, TN>& cur, Frags<TM, TN>& nxt, int kb) {
@@ -227,9 +297,18 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         // this wave's copies of stage kb+1 landed: younger than them are the
         // copies of the NB-2 later stages and, with block scales, the scale
         // loads of the two closes among the last four steps (NB = 5)
-        wait_vmcnt<(NB - 2) * LOADS + (BLOCK ? 2 * TM : 0)>();
+        wait_vmcnt<(NB - 2) * LOADS_T + (BLOCK ? 2 * TM : 0)>();
         block_barrier();
-        const uint32_t nb_base = stage_base(kb + 1);
+        const uint32_t nb_base = stage_base(kb + 1), nb_mx = mx_base(kb + 1);
+        // MX: this stage's E8M0 bytes of the fragment rows, byte i of pka / j
+        // of pkb (the MFMA takes byte 0 of a constant shift of them)
+        uint32_t pka = 0, pkb = 0;
+        if constexpr (MX) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) pka |= cur.sa[i] << (8 * i);
+#pragma unroll
+            for (int j = 0; j < TN; ++j) pkb |= cur.sb[j] << (8 * j);
+        }
         // reads of stage kb+1 follow the first NSLOT MFMAs (NREAD/NSLOT per MFMA,
         // every read exactly once), so the last quarter of the MFMAs covers
         // their latency; the copies of stage kb+NB are spread over all MFMAs
@@ -244,7 +323,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                 i = t / TN, j = t % TN;
                 av = __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 bv = __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+                if constexpr (MX)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bv, av, acc[i][j], 0, 0, 0, (int)(pkb >> (8 * j)), 0, (int)(pka >> (8 * i)));
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
             } else {
                 const int half = t / (TM * TN);
                 i = (t % (TM * TN)) / TN, j = t % TN;
@@ -256,9 +339,9 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = t < NSLOT ? t * NREAD / NSLOT : NREAD; r < (t < NSLOT ? (t + 1) * NREAD / NSLOT : NREAD); ++r)
-                read_one_after(nxt, nb_base, r, av, bv, pa, pb);
+                read_one_after(nxt, nb_base, nb_mx, r, av, bv, pa, pb);
 #pragma unroll
-            for (int l = (t * LOADS + NMFMA - 1) / NMFMA; l < ((t + 1) * LOADS + NMFMA - 1) / NMFMA; ++l)
+            for (int l = (t * LOADS_T + NMFMA - 1) / NMFMA; l < ((t + 1) * LOADS_T + NMFMA - 1) / NMFMA; ++l)
                 issue_one(kb + NB, l);
             pa = av, pb = bv;
             __builtin_amdgcn_sched_barrier(0);
@@ -266,6 +349,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         if (BLOCK && (kb & 1)) close_block(kb);
     };
 
+    // MX: the whole first chunk, ahead of the first stages (their waits then
+    // cover it)
+#pragma unroll
+    for (int p = 0; p < 8; ++p) mx_piece(kb0 / 8, p);
 #pragma unroll
     for (int t = 0; t < NB; ++t) issue(kb0 + t);
     if constexpr (BLOCK) {
@@ -275,11 +362,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
         for (int r = 0; r < SCP; ++r) load_scales(sa_ring[r], sw_ring[r], kb0 / 2 + r);
     }
-    wait_vmcnt<(NB - 1) * LOADS + (BLOCK ? SCP * TM : 0)>();
+    wait_vmcnt<(NB - 1) * LOADS_T + (BLOCK ? SCP * TM : 0)>();
     block_barrier();
     Frags<TM, TN> f0, f1;
 #pragma unroll
-    for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(kb0), r);
+    for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(kb0), mx_base(kb0), r);
     for (int kb = kb0; kb < kb1; kb += 2) {                      // slices hold whole 128-byte K blocks
         step(f0, f1, kb);
         step(f1, f0, kb + 1);
@@ -326,7 +413,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int64_t m = mw + i * 32 + l32;
-        sa[i] = BLOCK || split ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
+        sa[i] = BLOCK || MX || split ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
     }
     uint8_t* stage = lds + wave * WTM * EPI_PITCH;
     const bool bf = odt == O_BF16;
@@ -337,7 +424,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         for (int q4 = 0; q4 < 4; ++q4) {
             const int64_t n = nw + j * 32 + 8 * q4 + 4 * h;
             float4 w4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-            if (!BLOCK && !split) {
+            if (!BLOCK && !MX && !split) {
                 if (w_gran == GT) w4 = make_float4(ws[0], ws[0], ws[0], ws[0]);
                 else w4 = n < N ? *reinterpret_cast<const float4*>(ws + n) : make_float4(0.f, 0.f, 0.f, 0.f);
             }
@@ -448,10 +535,10 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(const void* __restrict__ pa
     }
 }
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN>
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, bool MX = false>
 static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0, s,
+    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN, MX>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0, s,
                        static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
                        g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt, ws, c.S, c.spl);
     if (c.S > 1) {
@@ -461,7 +548,7 @@ static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipSt
                            static_cast<const void*>(ws), c.S, g.M, g.N, g.a_scales, g.a_gran, g.w_scales, g.w_gran,
                            scaled, g.y, g.out_dt);
     }
-    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN);
+    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN, MX);
 }
 
 // Tile choice for the large-M GEMM: estimated time = rounds of resident
@@ -478,12 +565,16 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     c.S = 1;
     c.spl = (int)(g.K / GK);
     const bool block = g.in_fp8 && g.a_gran == GR128;
+    const bool mx = g.a_gran == GMX32;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
     auto cost = [&](int64_t bm, int64_t bn, double round) { return (double)((tiles(bm, bn) + 255) / 256) * round; };
     if (block) c.bm = 128, c.bn = 128;
     else if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) c.bm = 256, c.bn = 256;
     else c.bm = 256, c.bn = 128;
-    if (!with_ws || tiles(c.bm, c.bn) > 128) return c;          // over half a round: no split
+    // MX: 256 x 128 tiles (the 8-wave 256 x 256 tile has no registers left for
+    // the scale bytes), 128 x 128 for M <= 128; no K split (whole scale chunks)
+    if (mx) c.bm = g.M <= 128 ? 128 : 256, c.bn = 128;
+    if (mx || !with_ws || tiles(c.bm, c.bn) > 128) return c;    // over half a round: no split
     const int64_t nk128 = g.K >> 7;
     const bool small_m = g.M <= 128;
     const int64_t bm = small_m ? 128 : c.bm, bn = small_m ? 128 : c.bn;
@@ -502,18 +593,21 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     return c;
 }
 
-template <bool FP8, bool BLOCK>
+template <bool FP8, bool BLOCK, bool MX = false>
 static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
-    if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2>(g, c, ws, s);
+    if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2, MX>(g, c, ws, s);
     if constexpr (!BLOCK) {
-        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4>(g, c, ws, s);
-        return gemm_cfg<FP8, false, 256, 128, 2>(g, c, ws, s);
+        if constexpr (!MX) {
+            if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4>(g, c, ws, s);
+        }
+        return gemm_cfg<FP8, false, 256, 128, 2, MX>(g, c, ws, s);
     }
     return nullptr;
 }
 
 const char* launch_w8a8_tiled(const W8A8Args& g, void* ws, hipStream_t s) {
     const W8Split c = w8a8_tiled_split(g, ws != nullptr);
+    if (g.a_gran == GMX32) return gemm_shape<true, false, true>(g, c, nullptr, s);
     if (g.in_fp8 && g.a_gran == GR128) return gemm_shape<true, true>(g, c, ws, s);
     if (g.in_fp8) return gemm_shape<true, false>(g, c, ws, s);
     return gemm_shape<false, false>(g, c, ws, s);

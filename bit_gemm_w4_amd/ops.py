@@ -25,7 +25,7 @@ PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
-    "act_quant_int8_smooth", "act_quant_fp8_smooth", "gemm_w8a8",
+    "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
     "gemm_w4a16_algo", "gemm_w8a8_algo",
     "bg_status_string", "bg_last_error",
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
             "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
             "act_quant_int8_smooth": [P, I, I64, I64, I, P, P, P, P],
             "act_quant_fp8_smooth": [P, I, I64, I64, I, P, P, P, P],
+            "act_quant_mxfp8": [P, I, I64, I64, P, P, P],
+            "gemm_mxfp8": [P, P, P, P, I64, I64, I64, P, I, P],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
             "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
             "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
@@ -243,6 +245,35 @@ def act_quant_fp8_smooth(x: torch.Tensor, col_mul: torch.Tensor, gran: int = GRA
 
 
 _OUT_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.int32: I32}
+
+
+def act_quant_mxfp8(x: torch.Tensor, stream=None):
+    """-> (E4M3 bytes as uint8 [R][C], E8M0 scale bytes uint8 [R][C/32])."""
+    R, C = x.shape
+    dt = _TORCH_DT.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"act_quant_mxfp8: unsupported dtype {x.dtype}")
+    q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    e = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().act_quant_mxfp8(_ptr(x), dt, R, C, _ptr(q), _ptr(e), _stream(stream)), "act_quant_mxfp8")
+    return q, e
+
+
+def gemm_mxfp8(a: torch.Tensor, a_e8m0: torch.Tensor, w: torch.Tensor, w_e8m0: torch.Tensor,
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = (A X_a)(W X_w)^T for MXFP8 operands (act_quant_mxfp8 outputs)."""
+    M, K = a.shape
+    N, K2 = w.shape
+    if K != K2:
+        raise ValueError(f"gemm_mxfp8: K mismatch {K} vs {K2}")
+    for t, rows in ((a_e8m0, M), (w_e8m0, N)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (rows, K // 32):
+            raise ValueError("gemm_mxfp8: scales must be uint8 [rows][K/32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(lib().gemm_mxfp8(_ptr(a), _ptr(a_e8m0), _ptr(w), _ptr(w_e8m0), M, N, K, _ptr(out), _OUT_DT[out.dtype],
+                            _stream(stream)), "gemm_mxfp8")
+    return out
 
 
 def gemm_w8a8_workspace_bytes(M: int, N: int, K: int, fp8: bool = False, a_gran: int = GRAN_ROW,

@@ -201,6 +201,35 @@ bg_status act_quant_fp8_smooth(const void* x, int x_dtype, int64_t rows, int64_t
                                const float* col_mul, uint8_t* q, float* scales, void* stream);
 
 /*
+ * act_quant_mxfp8 -- MXFP8 quantization ([LPI] §10: the OCP MX block format,
+ * a block of elements and its shared scale taken as one data format).  Each
+ * run of 32 consecutive elements of a row shares an E8M0 scale 2^(e - 127):
+ * e = floor(log2 amax) - 8 + 127 (8 = the largest E4M3 exponent), clamped to
+ * 0..254, 127 for an all-zero block; each element is the saturating RNE E4M3
+ * cast of v * 2^(127 - e) (OCP MX v1.0).
+ *   x      [rows][cols] F32, F16 or BF16; cols % 32 == 0
+ *   q      out E4M3 bytes [rows][cols]
+ *   e8m0   out scale bytes [rows][cols/32]
+ */
+bg_status act_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, void* stream);
+
+/*
+ * gemm_mxfp8 -- Y = (A X_a)(W X_w)^T for MXFP8 operands (act_quant_mxfp8 of
+ * the activations [M][K] and of the weights [N][K]) on gfx950's block-scaled
+ * FP8 matrix instruction: every MFMA takes the E8M0 scales of its 32-element
+ * K runs, so the block scaling costs no vector instructions; FP32
+ * accumulation, one RNE rounding to out_dtype.
+ *   a, a_e8m0   E4M3 [M][K], E8M0 [M][K/32]
+ *   w, w_e8m0   E4M3 [N][K], E8M0 [N][K/32]
+ *   y           out [M][N], BG_BF16, BG_F16 or BG_F32
+ * Requires K % 512 == 0, N % 16 == 0, M * K and N * K below 2^31, 16-byte
+ * aligned pointers.  No workspace.
+ */
+bg_status gemm_mxfp8(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, const uint8_t* w_e8m0,
+                     int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream);
+
+/*
  * gemm_w8a8 -- native INT8 or FP8 GEMM of quantized activations A [M][K] and
  * weights W [N][K] ([AIB] W8A8/FP8 section: no upcast, low-precision matrix
  * cores; [LPI] §9 FP8 GEMM contract, §22 INT32 / FP32 accumulators).

@@ -537,3 +537,60 @@ def test_smoothquant_w8a8_end_to_end(ops, orc):
     err_s = orc.rel_l2(y.cpu().numpy(), exact)
     err_0 = orc.rel_l2(y0.cpu().numpy(), exact)
     assert err_s < 0.5 * err_0, (err_0, err_s)
+
+
+# ----------------------------------------------------------------- MXFP8 ----
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_act_quant_mxfp8_bitexact(ops, orc, dtype):
+    R, C = 96, 1536
+    w, x = synth.layer(R, 16, C, "f32", seed=70, x_outlier_cols=8)
+    x[3, :32] = 0.0                                 # all-zero block: scale 1
+    x[4, 64:96] *= 1e-30                            # exponent clamp region
+    x[5, 96:128] = 448.0 * 2.0 ** np.arange(-16, 16)[:32]
+    xd, x32 = as_f32(x, dtype)
+    q, e = ops.act_quant_mxfp8(xd)
+    torch.cuda.synchronize()
+    qo, eo = orc.quant_mxfp8(x32)
+    assert np.array_equal(e.cpu().numpy(), eo)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def _mx_case(ops, orc, M, N, K, out=torch.bfloat16, rows=None, seed=0):
+    w, x = synth.prefill_layer(M, N, K, seed=seed)
+    a, ea = ops.act_quant_mxfp8(dev_bits(x, "bf16"))
+    q, ew = ops.act_quant_mxfp8(torch.from_numpy(w).cuda())
+    y = ops.gemm_mxfp8(a, ea, q, ew, out_dtype=out)
+    torch.cuda.synchronize()
+    ao, eao = orc.quant_mxfp8(orc.bits_to_f32(x, "bf16"))
+    qo, ewo = orc.quant_mxfp8(w)
+    assert np.array_equal(a.cpu().numpy(), ao) and np.array_equal(ea.cpu().numpy(), eao)
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(ew.cpu().numpy(), ewo)
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    ref = orc.gemm_mxfp8(ao[sel], eao[sel], qo, ewo)
+    check_close(y.float().cpu().numpy()[sel].astype(np.float64), ref, orc, f"mxfp8 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 272, 512), (100, 272, 1536), (129, 400, 1024), (300, 1040, 4608)])
+def test_gemm_mxfp8_small(ops, orc, M, N, K):
+    """128 x 128 tiles (M <= 128) and 256 x 128 tiles, ragged in M and N; 1 to 9
+    scale chunks of 8 stages (the three-slot ring wraps from 4 chunks on)."""
+    _mx_case(ops, orc, M, N, K, seed=M + K)
+
+
+@pytest.mark.parametrize("out", [torch.float16, torch.float32])
+def test_gemm_mxfp8_out_dtypes(ops, orc, out):
+    _mx_case(ops, orc, 257, 256, 1024, out=out, seed=71)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_gemm_mxfp8_full_shape_sampled(ops, orc, name):
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _mx_case(ops, orc, 2048, N, K, rows=[0, 255, 256, 1000, 2047], seed=72)
+
+
+def test_gemm_mxfp8_rejects(ops):
+    a = torch.zeros((4, 256), dtype=torch.uint8, device="cuda")
+    e = torch.zeros((4, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ops.BitGemmError):
+        ops.gemm_mxfp8(a, e, a, e)                                        # K % 512
