@@ -69,13 +69,14 @@ W4GemmSplit w4a16_gemm_split(int64_t M, int64_t N, int64_t K);
 const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s);
 
-// MXFP8 quantizer: E4M3 codes [R][C] and E8M0 scales [R][C/32] (C % 32 == 0).
+// MXFP8 quantizer: E4M3 codes [R][C] and E8M0 scales [C/32][R rounded up to
+// 16] (C % 32 == 0).
 const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0,
                               hipStream_t s);
 
 // W8A8: in_fp8 selects E4M3 x E4M3 (else INT8 x INT8); out_dt: 0 f32, 1 f16, 2 bf16, 5 i32.
 // a_gran = w_gran = 4 (MX32, FP8 only): a_scales / w_scales point to E8M0
-// bytes [rows][K/32], applied by the MFMA; K % 512 == 0, no K split.
+// bytes [K/32][rows rounded up to 16], applied by the MFMA; no K split.
 // block_scaled: a_gran = ROW_G128 and w_gran = BLOCK128 (FP8 only).
 struct W8A8Args {
     const void* a;

@@ -242,7 +242,7 @@ BG_EXPORT bg_status gemm_mxfp8(const uint8_t* a, const uint8_t* a_e8m0, const ui
         return fail(BG_ERR_DTYPE, "gemm_mxfp8: out_dtype %lld is not BF16/F16/F32", out_dtype);
     if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_mxfp8: M=%lld out of range", M);
     if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_mxfp8: N=%lld must be a multiple of 16", N);
-    if (K < 512 || K > kMaxDim || K % 512) return fail(BG_ERR_SHAPE, "gemm_mxfp8: K=%lld must be a multiple of 512", K);
+    if (K < 128 || K > kMaxDim || K % 128) return fail(BG_ERR_SHAPE, "gemm_mxfp8: K=%lld must be a multiple of 128", K);
     if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31))
         return fail(BG_ERR_SHAPE, "gemm_mxfp8: M*K and N*K must be below 2^31");
     if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(a_e8m0) || !aligned16(w_e8m0))

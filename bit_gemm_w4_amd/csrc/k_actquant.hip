@@ -157,10 +157,12 @@ __global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, 
 // OCP MX: E8M0 scale 2^(e - 127), e = floor(log2 amax) - 8 + 127 (8 = the
 // largest E4M3 exponent) clamped to 0..254, 127 for an all-zero block; the
 // elements are the saturating RNE E4M3 casts of v * 2^(127 - e) (exact
-// power-of-two scaling).  Scales [rows][cols/32].
+// power-of-two scaling).  Scales are K-block-major, [cols/32][rows rounded
+// up to 16], so one K block's scales of consecutive rows are contiguous.
 template <int DT>
 __global__ __launch_bounds__(256) void k_quant_mx32(const void* __restrict__ x, int64_t total_chunks,
-                                                    uint8_t* __restrict__ q, uint8_t* __restrict__ e8m0) {
+                                                    int64_t C, int64_t rpad, uint8_t* __restrict__ q,
+                                                    uint8_t* __restrict__ e8m0) {
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (t >= total_chunks) return;          // total_chunks is a multiple of 4: whole blocks retire together
     float v[8];
@@ -175,16 +177,22 @@ __global__ __launch_bounds__(256) void k_quant_mx32(const void* __restrict__ x, 
     lo = e4m3x2(ldexpf(v[0], 127 - e), ldexpf(v[1], 127 - e)) | (e4m3x2(ldexpf(v[2], 127 - e), ldexpf(v[3], 127 - e)) << 16);
     hi = e4m3x2(ldexpf(v[4], 127 - e), ldexpf(v[5], 127 - e)) | (e4m3x2(ldexpf(v[6], 127 - e), ldexpf(v[7], 127 - e)) << 16);
     *reinterpret_cast<uint2*>(q + t * 8) = make_uint2(lo, hi);
-    if ((t & 3) == 0) e8m0[t >> 2] = (uint8_t)e;
+    if ((t & 3) == 0) {
+        const int64_t row = t / (C >> 3), blk = (t - row * (C >> 3)) >> 2;
+        e8m0[blk * rpad + row] = (uint8_t)e;
+    }
 }
 
 const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0,
                               hipStream_t s) {
-    const int64_t chunks = R * (C >> 3);
+    const int64_t chunks = R * (C >> 3), rpad = (R + 15) & ~(int64_t)15;
     const dim3 grid((unsigned)((chunks + 255) / 256));
-    if (dt == DT_F32) hipLaunchKernelGGL((k_quant_mx32<DT_F32>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
-    else if (dt == DT_F16) hipLaunchKernelGGL((k_quant_mx32<DT_F16>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
-    else hipLaunchKernelGGL((k_quant_mx32<DT_BF16>), grid, dim3(256), 0, s, x, chunks, q, e8m0);
+    if (dt == DT_F32)
+        hipLaunchKernelGGL((k_quant_mx32<DT_F32>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
+    else if (dt == DT_F16)
+        hipLaunchKernelGGL((k_quant_mx32<DT_F16>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
+    else
+        hipLaunchKernelGGL((k_quant_mx32<DT_BF16>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
     return kname("k_quant_mx32", dt);
 }
 

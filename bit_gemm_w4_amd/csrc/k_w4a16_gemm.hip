@@ -124,10 +124,14 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     const bool meta_lane = lane < 8;
     const uint32_t voff_m = mrole < 2 ? (uint32_t)((4 * mrole + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
                                    : (uint32_t)(lane * (ngroups >> 1) * 16);
+    // Stages past the end of K repeat the last stage's bytes (metadata: the
+    // last group's) into free buffers and slots that are never consumed, so
+    // no copy leaves its tensor.
+    const int ks_last = (int)(2 * ngroups) - 1;
     auto copy_meta = [&](int ks) {
         // both stages of group g copy its metadata to slot g % 4 (the same bytes)
-        const int g = ks >> 1;
-        uint8_t* meta = lds + P_NB * P_STAGE + (g % P_MSLOTS) * P_META;
+        const int g = (ks < ks_last ? ks : ks_last) >> 1;
+        uint8_t* meta = lds + P_NB * P_STAGE + ((ks >> 1) % P_MSLOTS) * P_META;
         if (meta_lane) {
             if (mrole < 2) copy16_to_lds(rs, meta + mrole * 128, voff_m, g * 32);
             else copy16_to_lds(rz, meta + P_S, voff_m, (g >> 1) * 16);
@@ -136,10 +140,11 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     // copy number t (0 .. P_LOADS-1) of stage ks = half group
     auto issue_one = [&](int ks, int t) {
         uint8_t* buf = lds + (ks % P_NB) * P_STAGE;
+        const int kc = ks < ks_last ? ks : ks_last;
         if (t < A_LD) {
-            copy16_to_lds(ra, buf + (wave * A_LD + t) * 1024, voff_a[t], ks * PKS * 2);
+            copy16_to_lds(ra, buf + (wave * A_LD + t) * 1024, voff_a[t], kc * PKS * 2);
         } else if (t == A_LD && (NW == 4 || wave < 4)) {
-            copy16_to_lds(rw, buf + P_A + ww * 1024, voff_w, ks * 512);
+            copy16_to_lds(rw, buf + P_A + ww * 1024, voff_w, kc * 512);
         } else {
             copy_meta(ks);
         }

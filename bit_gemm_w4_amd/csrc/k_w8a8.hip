@@ -61,27 +61,27 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int NW = 2 * WN;                                   // waves
     constexpr int WTM = BM / 2, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
-    constexpr int STAGE_BYTES = ROWS * GK;
+    // MX: a stage also holds the E8M0 bytes of its two 32-wide K blocks: A
+    // block 2kb, A block 2kb+1 (BM bytes each), then the same for W (BN each)
+    constexpr int MXS = MX ? 2 * ROWS : 0;
+    constexpr int STAGE_BYTES = ROWS * GK + MXS;
     constexpr int LOADS = ROWS / (16 * NW);                      // 1 KB wave-loads per wave per stage
-    // MX: E8M0 scales, 16 bytes per row per chunk of 8 stages, in a ring of 3
-    // chunks after the stage buffers; every stage also copies one eighth of a
-    // later chunk (one more copy per wave and stage)
-    static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8 variant");
-    constexpr int MX_CHUNK = ROWS * 16, MX_RING = MX ? 3 * MX_CHUNK : 0;
+    // MX: every wave copies one of the stage's four scale runs (one more copy
+    // per wave and stage)
+    static_assert(!MX || (FP8 && !BLOCK && NW == 4), "MX scaling is an FP8 variant of the four-wave tiles");
     constexpr int LOADS_T = LOADS + (MX ? 1 : 0);
     // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
-    constexpr int NB_FIT = (160 * 1024 - MX_RING) / STAGE_BYTES;
-    constexpr int NB_MAX = BM * BN <= 128 * 128 || BLOCK || MX ? 5 : 6;
+    constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
+    constexpr int NB_MAX = BM * BN <= 128 * 128 || BLOCK ? 5 : 6;
     constexpr int NB = NB_FIT > NB_MAX ? NB_MAX : NB_FIT;
     static_assert(ROWS % (16 * NW) == 0 && WTM % 32 == 0 && WTN % 32 == 0, "tile shape");
     static_assert(!BLOCK || WTN <= 128, "one 128-column weight scale block per wave");
-    static_assert(NB >= 3 && (NB - 1) * LOADS_T + 8 + (BLOCK ? 4 * TM : 0) < 64, "stage count / vmcnt range");
+    static_assert(NB >= 3 && (NB - 1) * LOADS_T + (BLOCK ? 4 * TM : 0) < 64, "stage count / vmcnt range");
     static_assert(!BLOCK || NB == 5, "the block-scale load count in the stage waits assumes five buffers");
-    static_assert(!MX || NB <= 6, "the MX scale ring holds 3 chunks: at most 6 stages in flight");
+    static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
     constexpr int EPI_PITCH = WTN * 2 + 16;                      // bytes per staged output row (padded, 16-aligned)
     constexpr int EPI_BYTES = NW * WTM * EPI_PITCH;
-    constexpr int RING_END = NB * STAGE_BYTES + MX_RING;
-    constexpr int LDS_BYTES = RING_END > EPI_BYTES ? RING_END : EPI_BYTES;
+    constexpr int LDS_BYTES = NB * STAGE_BYTES > EPI_BYTES ? NB * STAGE_BYTES : EPI_BYTES;
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
 
@@ -113,47 +113,45 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     }
     const int nkb = (int)(K / GK);
     const int kb0 = sl * spl, kb1 = kb0 + spl < nkb ? kb0 + spl : nkb;
-    // MX scale chunks: chunk c holds the 16 E8M0 bytes (K blocks 16c .. 16c+15,
-    // stages 8c .. 8c+7) of every A row, then of every W row, in slot c % 3.
-    // Piece p of a chunk (BM/8 A rows and BN/8 W rows) is copied by the first
-    // NW/2 waves (A) and the last NW/2 (W), rpa / rpw rows (lanes) each.
-    // Scales are [rows][K/32] bytes; K % 512 == 0, so chunks are whole.
-    const int64_t kb32 = K >> 5;
-    const int nchunk = (int)(K >> 9);
-    constexpr int RPA = MX ? BM / 8 / (NW / 2) : 1, RPW = MX ? BN / 8 / (NW / 2) : 1;
-    // (MX: as / ws point to the E8M0 bytes; otherwise the resources are empty)
-    const auto rsa = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<uint8_t*>(const_cast<float*>(as)) + (MX ? m0 * kb32 : 0), (short)0,
-        MX ? (int)(rows_a * kb32) : 0, 0x00020000);
-    const auto rsw = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<uint8_t*>(const_cast<float*>(ws)) + (MX ? n0 * kb32 : 0), (short)0,
-        MX ? (int)(rows_w * kb32) : 0, 0x00020000);
-    const bool mx_a = wave < NW / 2;
-    const int mx_w = mx_a ? wave : wave - NW / 2;
-    auto mx_piece = [&](int c, int p) {
+    // MX scales are K-block-major, [K/32][rows padded to 16] bytes, so a K
+    // block's bytes for the tile's rows are one contiguous run.  The stage's
+    // scale area holds the runs A(2kb), A(2kb+1), W(2kb), W(2kb+1); wave w
+    // copies its bytes [256w, 256w + 256) with one 4-byte-per-lane copy, every
+    // lane active (each lane picks its run and row), and waves past the area
+    // repeat its last 256 bytes.  (as / ws point to the E8M0 bytes.)
+    constexpr int MX_AREA = 2 * ROWS;
+    static_assert(!MX || (MX_AREA % 256 == 0 && (2 * BM) % 256 == 0), "MX scale area in whole waves");
+    const int64_t mpad = (M + 15) & ~(int64_t)15, npad = (N + 15) & ~(int64_t)15;
+    const int mx_piece = 256 * wave < MX_AREA ? wave : MX_AREA / 256 - 1;
+    const int mx_pos = mx_piece * 256 + lane * 4;                 // byte of the scale area
+    const bool mx_a = mx_piece * 256 < 2 * BM;                    // wave-uniform
+    const int mx_run = mx_a ? mx_pos / BM : (mx_pos - 2 * BM) / BN;
+    const int mx_row = mx_a ? mx_pos % BM : (mx_pos - 2 * BM) % BN;
+    const int64_t mx_stride = mx_a ? mpad : npad;
+    const auto rsx = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint8_t*>(const_cast<float*>(mx_a ? as : ws)) + (MX ? (mx_a ? m0 : n0) : 0), (short)0,
+        MX ? (int)((K >> 5) * mx_stride - (mx_a ? m0 : n0)) : 0, 0x00020000);
+    const uint32_t mx_voff = (uint32_t)(mx_run * mx_stride + mx_row);
+    auto mx_copy = [&](int kb) {
         if constexpr (MX) {
-            const int cc = c < nchunk - 1 ? c : nchunk - 1;      // past the end: repeat the last chunk's bytes
-            uint8_t* slot = lds + NB * STAGE_BYTES + (c % 3) * MX_CHUNK;
-            if (mx_a) {
-                const int r = p * (BM / 8) + mx_w * RPA;
-                if (lane < RPA) copy16_to_lds(rsa, slot + r * 16, (uint32_t)((r + lane) * kb32), cc * 16);
-            } else {
-                const int r = p * (BN / 8) + mx_w * RPW;
-                if (lane < RPW) copy16_to_lds(rsw, slot + (BM + r) * 16, (uint32_t)((r + lane) * kb32), cc * 16);
-            }
+            const int kc = kb < nkb - 1 ? kb : nkb - 1;          // past the end: repeat the last stage's runs
+            // the whole offset per lane, so the range check covers it
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsx, (lds_ptr_t)(lds + (kb % NB) * STAGE_BYTES + ROWS * GK + mx_piece * 256), 4,
+                mx_voff + (uint32_t)(2 * kc * mx_stride), 0, 0, 0);
         }
     };
-    // Stage kb goes to buffer kb % NB.  Stages past the end of K copy bytes of
-    // later rows (zeros past the end of the buffer resource) into a free
-    // buffer that is never consumed.  With MX, copy LOADS of stage kb is
-    // piece kb % 8 of chunk kb / 8 + 1.
+    // Stage kb goes to buffer kb % NB.  Stages past the end of K repeat the
+    // last stage's bytes into a free buffer that is never consumed (so no copy
+    // leaves its tensor).  With MX, copy LOADS is the scale run.
     auto issue_one = [&](int kb, int t) {
         if (MX && t == LOADS) {
-            mx_piece(kb / 8 + 1, kb % 8);
+            mx_copy(kb);
             return;
         }
         const int j = wave * LOADS + t;
-        copy16_to_lds(j < BM / 16 ? ra : rw, lds + (kb % NB) * STAGE_BYTES + j * 16 * GK, voff[t], kb * GK);
+        const int kc = kb < nkb - 1 ? kb : nkb - 1;
+        copy16_to_lds(j < BM / 16 ? ra : rw, lds + (kb % NB) * STAGE_BYTES + j * 16 * GK, voff[t], kc * GK);
     };
     auto issue = [&](int kb) {
 #pragma unroll
@@ -170,20 +168,19 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     const uint32_t offa1 = (uint32_t)(ra0 * GK + (((2 + h) ^ gswz(ra0)) << 4));
     const uint32_t offb0 = (uint32_t)(rb0 * GK + ((h ^ gswz(rb0)) << 4));
     const uint32_t offb1 = (uint32_t)(rb0 * GK + (((2 + h) ^ gswz(rb0)) << 4));
-    // MX: stage kb's E8M0 bytes of a row are bytes 2kb % 16 (k 0..31 of the
-    // stage, lanes h = 0) and 2kb % 16 + 1 (k 32..63, h = 1) of its chunk row
-    const uint32_t mxa0 = (uint32_t)(ra0 * 16 + h), mxb0 = (uint32_t)(rb0 * 16 + h);
-    auto mx_base = [&](int kb) {
-        return lds0 + (uint32_t)(NB * STAGE_BYTES + ((kb >> 3) % 3) * MX_CHUNK + ((2 * kb) & 15));
-    };
+    // MX: the lane's scale byte of a fragment row: its K half h selects the
+    // run (block 2kb + h), the row its byte in the run
+    const uint32_t mxa0 = (uint32_t)(ROWS * GK + h * BM + ra0);
+    const uint32_t mxb0 = (uint32_t)(ROWS * GK + 2 * BM + h * BN + (rb0 - BM));
+    auto mx_base = [&](int kb) { return lds0 + (uint32_t)((kb % NB) * STAGE_BYTES); };
     constexpr int NFRAG = 2 * (TM + TN);
     // read number r of a stage (0 .. NREAD-1): A fragments first, then W, then
     // (MX) the scale dwords of the A and W fragment rows
     auto read_one = [&](Frags<TM, TN>& f, uint32_t base, uint32_t mxb, int r) {
         if (r >= NFRAG) {
             const int i = r - NFRAG;
-            if (i < TM) f.sa[i] = ds_read1(mxb + mxa0 + (uint32_t)(i * 32 * 16));
-            else f.sb[i - TM] = ds_read1(mxb + mxb0 + (uint32_t)((i - TM) * 32 * 16));
+            if (i < TM) f.sa[i] = ds_read1(mxb + mxa0 + (uint32_t)(i * 32));
+            else f.sb[i - TM] = ds_read1(mxb + mxb0 + (uint32_t)((i - TM) * 32));
             return;
         }
         const int frag = r >> 1, c = r & 1;
@@ -198,8 +195,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                               const op_t& a0, const op_t& b0) {
         if (r >= NFRAG) {
             const int i = r - NFRAG;
-            if (i < TM) f.sa[i] = ds_read1_after(mxb + mxa0 + (uint32_t)(i * 32 * 16), a1, b1, a0, b0);
-            else f.sb[i - TM] = ds_read1_after(mxb + mxb0 + (uint32_t)((i - TM) * 32 * 16), a1, b1, a0, b0);
+            if (i < TM) f.sa[i] = ds_read1_after(mxb + mxa0 + (uint32_t)(i * 32), a1, b1, a0, b0);
+            else f.sb[i - TM] = ds_read1_after(mxb + mxb0 + (uint32_t)((i - TM) * 32), a1, b1, a0, b0);
             return;
         }
         const int frag = r >> 1, c = r & 1;
@@ -349,10 +346,6 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         if (BLOCK && (kb & 1)) close_block(kb);
     };
 
-    // MX: the whole first chunk, ahead of the first stages (their waits then
-    // cover it)
-#pragma unroll
-    for (int p = 0; p < 8; ++p) mx_piece(kb0 / 8, p);
 #pragma unroll
     for (int t = 0; t < NB; ++t) issue(kb0 + t);
     if constexpr (BLOCK) {

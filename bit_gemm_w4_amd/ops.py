@@ -248,13 +248,14 @@ _OUT_DT = {torch.bfloat16: BF16, torch.float16: F16, torch.float32: F32, torch.i
 
 
 def act_quant_mxfp8(x: torch.Tensor, stream=None):
-    """-> (E4M3 bytes as uint8 [R][C], E8M0 scale bytes uint8 [R][C/32])."""
+    """-> (E4M3 bytes as uint8 [R][C], E8M0 scale bytes uint8 [C/32][R rounded
+    up to 16], K-block-major)."""
     R, C = x.shape
     dt = _TORCH_DT.get(x.dtype)
     if dt is None:
         raise ValueError(f"act_quant_mxfp8: unsupported dtype {x.dtype}")
     q = torch.empty((R, C), dtype=torch.uint8, device=x.device)
-    e = torch.empty((R, C // 32), dtype=torch.uint8, device=x.device)
+    e = torch.empty((C // 32, (R + 15) // 16 * 16), dtype=torch.uint8, device=x.device)
     _check(lib().act_quant_mxfp8(_ptr(x), dt, R, C, _ptr(q), _ptr(e), _stream(stream)), "act_quant_mxfp8")
     return q, e
 
@@ -267,8 +268,8 @@ def gemm_mxfp8(a: torch.Tensor, a_e8m0: torch.Tensor, w: torch.Tensor, w_e8m0: t
     if K != K2:
         raise ValueError(f"gemm_mxfp8: K mismatch {K} vs {K2}")
     for t, rows in ((a_e8m0, M), (w_e8m0, N)):
-        if t.dtype != torch.uint8 or tuple(t.shape) != (rows, K // 32):
-            raise ValueError("gemm_mxfp8: scales must be uint8 [rows][K/32]")
+        if t.dtype != torch.uint8 or tuple(t.shape) != (K // 32, (rows + 15) // 16 * 16):
+            raise ValueError("gemm_mxfp8: scales must be uint8 [K/32][rows rounded up to 16]")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _check(lib().gemm_mxfp8(_ptr(a), _ptr(a_e8m0), _ptr(w), _ptr(w_e8m0), M, N, K, _ptr(out), _OUT_DT[out.dtype],

@@ -209,7 +209,9 @@ bg_status act_quant_fp8_smooth(const void* x, int x_dtype, int64_t rows, int64_t
  * cast of v * 2^(127 - e) (OCP MX v1.0).
  *   x      [rows][cols] F32, F16 or BF16; cols % 32 == 0
  *   q      out E4M3 bytes [rows][cols]
- *   e8m0   out scale bytes [rows][cols/32]
+ *   e8m0   out scale bytes, K-block-major: [cols/32][rows rounded up to 16]
+ *          (scale of row r, block b at e8m0[b * rpad + r]; the padding bytes
+ *          are not written)
  */
 bg_status act_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* q,
                           uint8_t* e8m0, void* stream);
@@ -220,10 +222,10 @@ bg_status act_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols
  * FP8 matrix instruction: every MFMA takes the E8M0 scales of its 32-element
  * K runs, so the block scaling costs no vector instructions; FP32
  * accumulation, one RNE rounding to out_dtype.
- *   a, a_e8m0   E4M3 [M][K], E8M0 [M][K/32]
- *   w, w_e8m0   E4M3 [N][K], E8M0 [N][K/32]
+ *   a, a_e8m0   E4M3 [M][K], E8M0 [K/32][M rounded up to 16]
+ *   w, w_e8m0   E4M3 [N][K], E8M0 [K/32][N] (N % 16 == 0)
  *   y           out [M][N], BG_BF16, BG_F16 or BG_F32
- * Requires K % 512 == 0, N % 16 == 0, M * K and N * K below 2^31, 16-byte
+ * Requires K % 128 == 0, N % 16 == 0, M * K and N * K below 2^31, 16-byte
  * aligned pointers.  No workspace.
  */
 bg_status gemm_mxfp8(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, const uint8_t* w_e8m0,

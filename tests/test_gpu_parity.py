@@ -552,7 +552,7 @@ def test_act_quant_mxfp8_bitexact(ops, orc, dtype):
     q, e = ops.act_quant_mxfp8(xd)
     torch.cuda.synchronize()
     qo, eo = orc.quant_mxfp8(x32)
-    assert np.array_equal(e.cpu().numpy(), eo)
+    assert np.array_equal(e.cpu().numpy()[:, :R], eo.T)           # K-block-major, rows padded to 16
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
@@ -564,17 +564,17 @@ def _mx_case(ops, orc, M, N, K, out=torch.bfloat16, rows=None, seed=0):
     torch.cuda.synchronize()
     ao, eao = orc.quant_mxfp8(orc.bits_to_f32(x, "bf16"))
     qo, ewo = orc.quant_mxfp8(w)
-    assert np.array_equal(a.cpu().numpy(), ao) and np.array_equal(ea.cpu().numpy(), eao)
-    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(ew.cpu().numpy(), ewo)
+    assert np.array_equal(a.cpu().numpy(), ao) and np.array_equal(ea.cpu().numpy()[:, :M], eao.T)
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(ew.cpu().numpy()[:, :N], ewo.T)
     sel = np.arange(M) if rows is None else np.asarray(rows)
     ref = orc.gemm_mxfp8(ao[sel], eao[sel], qo, ewo)
     check_close(y.float().cpu().numpy()[sel].astype(np.float64), ref, orc, f"mxfp8 M={M} N={N} K={K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 272, 512), (100, 272, 1536), (129, 400, 1024), (300, 1040, 4608)])
+@pytest.mark.parametrize("M,N,K", [(1, 272, 128), (100, 272, 1536), (129, 400, 1024), (300, 1040, 4608)])
 def test_gemm_mxfp8_small(ops, orc, M, N, K):
-    """128 x 128 tiles (M <= 128) and 256 x 128 tiles, ragged in M and N; 1 to 9
-    scale chunks of 8 stages (the three-slot ring wraps from 4 chunks on)."""
+    """128 x 128 tiles (M <= 128) and 256 x 128 tiles, ragged in M and N, from
+    two stages of K up to 72."""
     _mx_case(ops, orc, M, N, K, seed=M + K)
 
 
@@ -590,7 +590,11 @@ def test_gemm_mxfp8_full_shape_sampled(ops, orc, name):
 
 
 def test_gemm_mxfp8_rejects(ops):
-    a = torch.zeros((4, 256), dtype=torch.uint8, device="cuda")
-    e = torch.zeros((4, 8), dtype=torch.uint8, device="cuda")
+    a = torch.zeros((16, 200), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        ops.gemm_mxfp8(a, torch.zeros((6, 16), dtype=torch.uint8, device="cuda"), a,
+                       torch.zeros((7, 16), dtype=torch.uint8, device="cuda"))      # scale shapes
+    e = torch.zeros((6, 16), dtype=torch.uint8, device="cuda")
+    b = torch.zeros((16, 192), dtype=torch.uint8, device="cuda")
     with pytest.raises(ops.BitGemmError):
-        ops.gemm_mxfp8(a, e, a, e)                                        # K % 512
+        ops.gemm_mxfp8(b, e, b, e)                                        # K % 128
