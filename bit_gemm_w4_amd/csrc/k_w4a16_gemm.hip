@@ -50,7 +50,7 @@ constexpr int P_W = (PBN / 16) * 512;               // 4 KB: half of each of 8 w
 constexpr int P_S = (PBN / 16) * 32;                // 256 B: FP16 scales of the group
 constexpr int P_Z = (PBN / 16) * 16;                // 128 B: zero-point bytes of the group pair
 constexpr int P_STAGE = P_A + P_W;
-constexpr int P_META = P_S + P_Z;                   // scales + zero bytes of one group
+constexpr int P_META = P_S + 2 * P_Z;               // scales + zero bytes of one group (zero bytes twice)
 constexpr int P_MSLOTS = 4;                         // group g's metadata lives in slot g % 4
 constexpr int P_NB = 4;
 }  // namespace
@@ -117,13 +117,15 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     // W: wave w < 4 copies the stage halves of weight tiles 2w, 2w + 1
     const int ww = wave & 3;
     const uint32_t voff_w = (uint32_t)((2 * ww + (lane >> 5)) * ngroups * 1024) + (uint32_t)((lane & 31) * 16);
-    // metadata role mrole: 0, 1 = scales of tiles 4 mrole .. +3 (32 bytes each),
-    // 2, 3 = zero bytes of the 8 tiles (16 each; two waves copy the same bytes);
-    // waves 0..3 with four waves, waves 4..7 with eight
-    const int mrole = wave & 3;
-    const bool meta_lane = lane < 8;
-    const uint32_t voff_m = mrole < 2 ? (uint32_t)((4 * mrole + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
-                                   : (uint32_t)(lane * (ngroups >> 1) * 16);
+    // metadata, 4 bytes per lane and every lane active (LDS copies narrower
+    // than 16 bytes put each lane's data in a 4-byte slot): even waves copy
+    // the group's 256 scale bytes (tile lane / 8, bytes 4 (lane % 8)), odd
+    // waves its 128 zero-point bytes (tile (lane % 32) / 4, bytes 4 (lane % 4)),
+    // lanes 32..63 the same bytes again into a spare 128; waves 0..3 with four
+    // waves, 4..7 with eight (pairs copy the same bytes to the same place)
+    const bool m_scales = (wave & 1) == 0;
+    const uint32_t voff_m = m_scales ? (uint32_t)((lane >> 3) * ngroups * 32 + (lane & 7) * 4)
+                                     : (uint32_t)(((lane & 31) >> 2) * (ngroups >> 1) * 16 + (lane & 3) * 4);
     // Stages past the end of K repeat the last stage's bytes (metadata: the
     // last group's) into free buffers and slots that are never consumed, so
     // no copy leaves its tensor.
@@ -132,10 +134,11 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
         // both stages of group g copy its metadata to slot g % 4 (the same bytes)
         const int g = (ks < ks_last ? ks : ks_last) >> 1;
         uint8_t* meta = lds + P_NB * P_STAGE + ((ks >> 1) % P_MSLOTS) * P_META;
-        if (meta_lane) {
-            if (mrole < 2) copy16_to_lds(rs, meta + mrole * 128, voff_m, g * 32);
-            else copy16_to_lds(rz, meta + P_S, voff_m, (g >> 1) * 16);
-        }
+        if (m_scales)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)meta, 4, voff_m + (uint32_t)(g * 32), 0, 0, 0);
+        else
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(meta + P_S), 4,
+                                                     voff_m + (uint32_t)((g >> 1) * 16), 0, 0, 0);
     };
     // copy number t (0 .. P_LOADS-1) of stage ks = half group
     auto issue_one = [&](int ks, int t) {

@@ -49,7 +49,7 @@ constexpr int Q_W = (QBN / 16) * 512;               // 4 KB: half of each of 8 w
 constexpr int Q_S = (QBN / 16) * 32;                // 256 B: FP16 scales of the group
 constexpr int Q_Z = (QBN / 16) * 16;                // 128 B: zero-point bytes of the group pair
 constexpr int Q_STAGE = Q_A + Q_W;
-constexpr int Q_META = Q_S + Q_Z;
+constexpr int Q_META = Q_S + 2 * Q_Z;               // scales + zero bytes of one group (zero bytes twice)
 constexpr int Q_MSLOTS = 4;                         // group g's metadata lives in slot g % 4
 constexpr int Q_NB = 6;
 constexpr int Q_WM = 4, Q_NW = 2 * Q_WM;            // waves: 4 x 2
@@ -135,13 +135,15 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
     // W: wave w < 4 copies the stage halves of weight tiles 2w, 2w + 1
     const int ww = wave & 3;
     const uint32_t voff_w = (uint32_t)((2 * ww + (lane >> 5)) * ngroups * 1024) + (uint32_t)((lane & 31) * 16);
-    // metadata (waves 4..7), role mrole: 0, 1 = scales of tiles 4 mrole .. +3
-    // (32 bytes each), 2, 3 = zero bytes of the 8 tiles (16 each; both copy
-    // the same bytes)
-    const int mrole = wave & 3;
-    const bool meta_lane = lane < 8;
-    const uint32_t voff_m = mrole < 2 ? (uint32_t)((4 * mrole + (lane >> 1)) * ngroups * 32 + (lane & 1) * 16)
-                                      : (uint32_t)(lane * (ngroups >> 1) * 16);
+    // metadata (waves 4..7), 4 bytes per lane and every lane active (LDS
+    // copies narrower than 16 bytes put each lane's data in a 4-byte slot):
+    // even waves copy the group's 256 scale bytes (tile lane / 8, bytes
+    // 4 (lane % 8)), odd waves its 128 zero-point bytes (tile (lane % 32) / 4,
+    // bytes 4 (lane % 4)), lanes 32..63 the same bytes again into a spare
+    // 128; the two pairs copy the same bytes to the same place
+    const bool m_scales = (wave & 1) == 0;
+    const uint32_t voff_m = m_scales ? (uint32_t)((lane >> 3) * ngroups * 32 + (lane & 7) * 4)
+                                     : (uint32_t)(((lane & 31) >> 2) * (ngroups >> 1) * 16 + (lane & 3) * 4);
     // Every step issues the same number of copies (the stage waits count
     // them); the stages past the end of the slice repeat its last stage's
     // bytes into a free buffer that is never consumed, so no copy leaves its
@@ -159,10 +161,11 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
             // bytes); past the end the slots of groups that never come
             const int g = kc >> 1;
             uint8_t* meta = lds + Q_NB * Q_STAGE + ((ks >> 1) % Q_MSLOTS) * Q_META;
-            if (meta_lane) {
-                if (mrole < 2) copy16_to_lds(rs, meta + mrole * 128, voff_m, g * 32);
-                else copy16_to_lds(rz, meta + Q_S, voff_m, (g >> 1) * 16);
-            }
+            if (m_scales)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)meta, 4, voff_m + (uint32_t)(g * 32), 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (lds_ptr_t)(meta + Q_S), 4,
+                                                         voff_m + (uint32_t)((g >> 1) * 16), 0, 0, 0);
         }
     };
     auto issue = [&](int ks) {
