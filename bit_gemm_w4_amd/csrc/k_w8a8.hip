@@ -68,7 +68,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int LOADS = ROWS / (16 * NW);                      // 1 KB wave-loads per wave per stage
     // MX: every wave copies one of the stage's four scale runs (one more copy
     // per wave and stage)
-    static_assert(!MX || (FP8 && !BLOCK && NW == 4), "MX scaling is an FP8 variant of the four-wave tiles");
+    static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8 variant");
     constexpr int LOADS_T = LOADS + (MX ? 1 : 0);
     // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
     constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
@@ -564,9 +564,8 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     if (block) c.bm = 128, c.bn = 128;
     else if (cost(256, 256, 75.0) <= cost(256, 128, 46.4)) c.bm = 256, c.bn = 256;
     else c.bm = 256, c.bn = 128;
-    // MX: 256 x 128 tiles (the 8-wave 256 x 256 tile has no registers left for
-    // the scale bytes), 128 x 128 for M <= 128; no K split (whole scale chunks)
-    if (mx) c.bm = g.M <= 128 ? 128 : 256, c.bn = 128;
+    // MX: the same tiles, 128 x 128 for M <= 128; no K split
+    if (mx && g.M <= 128) c.bm = 128, c.bn = 128;
     if (mx || !with_ws || tiles(c.bm, c.bn) > 128) return c;    // over half a round: no split
     const int64_t nk128 = g.K >> 7;
     const bool small_m = g.M <= 128;
@@ -590,9 +589,7 @@ template <bool FP8, bool BLOCK, bool MX = false>
 static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2, MX>(g, c, ws, s);
     if constexpr (!BLOCK) {
-        if constexpr (!MX) {
-            if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4>(g, c, ws, s);
-        }
+        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4, MX>(g, c, ws, s);
         return gemm_cfg<FP8, false, 256, 128, 2, MX>(g, c, ws, s);
     }
     return nullptr;

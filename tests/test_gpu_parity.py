@@ -578,6 +578,12 @@ def test_gemm_mxfp8_small(ops, orc, M, N, K):
     _mx_case(ops, orc, M, N, K, seed=M + K)
 
 
+def test_gemm_mxfp8_wide_tiles_ragged(ops, orc):
+    """256 x 256 tiles (132 of them: one round) with ragged M and N."""
+    _mx_case(ops, orc, 1000, 8208, 512, rows=[0, 255, 256, 511, 768, 999], seed=73)
+    assert "256, 256" in ops.last_kernel()
+
+
 @pytest.mark.parametrize("out", [torch.float16, torch.float32])
 def test_gemm_mxfp8_out_dtypes(ops, orc, out):
     _mx_case(ops, orc, 257, 256, 1024, out=out, seed=71)
