@@ -82,6 +82,10 @@ def _load():
                 "orc_col_mul": [P, I64, I64, P, P],
                 "orc_quant_mxfp8": [P, I64, I64, P, P],
                 "orc_gemm_mxfp8": [P, P, P, P, I64, I64, I64, P],
+                "orc_quant_mxfp4": [P, I64, I64, P, P],
+                "orc_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P],
+                "orc_e2m1_encode_n": [P, I64, P],
+                "orc_e2m1_decode_n": [P, I64, P],
                 "orc_num_threads": [],
             }
             for name, argtypes in sig.items():
@@ -346,6 +350,45 @@ def gemm_mxfp8(a, ea, w, ew) -> np.ndarray:
     N = w.shape[0]
     y = np.empty((M, N), np.float64)
     _load().orc_gemm_mxfp8(_p(a), _p(ea), _p(w), _p(ew), M, N, K, _p(y))
+    return y
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Saturating RNE E2M1 codes (0..15) of binary32 values."""
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().orc_e2m1_encode_n(_p(x), x.size, _p(out))
+    return out
+
+
+def e2m1_decode(c) -> np.ndarray:
+    """Values of E2M1 codes (the low nibble of each byte) in binary64."""
+    c = _c(c, np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().orc_e2m1_decode_n(_p(c), c.size, _p(out))
+    return out
+
+
+def quant_mxfp4(x):
+    """MXFP4 of binary32 x [R][C] (C % 32 == 0) -> (packed E2M1 bytes
+    [R][C/2], element 2i in the low nibble; E8M0 scale bytes [R][C/32])."""
+    x = _c(x, np.float32)
+    R, C = x.shape
+    assert C % 32 == 0
+    q = np.empty((R, C // 2), np.uint8)
+    e = np.empty((R, C // 32), np.uint8)
+    _load().orc_quant_mxfp4(_p(x), R, C, _p(q), _p(e))
+    return q, e
+
+
+def gemm_mxfp4(a, ea, w, ew) -> np.ndarray:
+    """Exact MXFP4 GEMM in binary64: Y = (A X_a)(W X_w)^T, A and W packed
+    [rows][K/2]."""
+    a, ea, w, ew = (_c(t, np.uint8) for t in (a, ea, w, ew))
+    M, K = a.shape[0], a.shape[1] * 2
+    N = w.shape[0]
+    y = np.empty((M, N), np.float64)
+    _load().orc_gemm_mxfp4(_p(a), _p(ea), _p(w), _p(ew), M, N, K, _p(y))
     return y
 
 

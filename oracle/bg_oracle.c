@@ -599,6 +599,116 @@ void orc_bf16_to_f32_n(const uint16_t* b, int64_t n, float* x) {
     for (int64_t i = 0; i < n; ++i) x[i] = orc_bf16_to_f32(b[i]);
 }
 
+/* ------------------------------------------------------------------------ */
+/* MXFP4: microscaled E2M1.  [LPI] §10: E2M1 is the usual FP4 element (1     */
+/* sign, 2 exponent, 1 mantissa bit), and the OCP MX specification makes a   */
+/* block of such elements with one shared scale a data format (MXFP4).  As   */
+/* for MXFP8, the block (32 consecutive elements along K), the E8M0 scale     */
+/* and the conversion are the OCP MX v1.0 ones: E = floor(log2(max |v|)) - 2 */
+/* + 127 (2 = the largest E2M1 exponent), clamped to 0..254, elements are    */
+/* the saturating RNE E2M1 cast of v / X, and an all-zero block gets X = 1.  */
+/* Two elements per byte, the even element in the low nibble.               */
+/* ------------------------------------------------------------------------ */
+
+/* E2M1: bias 1.  Exponent field 0 is subnormal (m * 0.5); otherwise         */
+/* 2^(e-1) * (1 + m/2).  Values 0, 0.5, 1, 1.5, 2, 3, 4, 6; no Inf or NaN.   */
+double orc_e2m1_decode(uint8_t c) {
+    int sign = (c >> 3) & 1;
+    int e = (c >> 1) & 3;
+    int m = c & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return sign ? -v : v;
+}
+
+/* Saturating round-to-nearest-even cast.  The quantum of the binade is     */
+/* 2^(e-1) with e = floor(log2 |v|) clamped to >= 0 (the subnormal quantum   */
+/* is 0.5); the magnitude is rint(|v| / quantum) * quantum, capped at 6.     */
+/* The sign is kept (a negative value that rounds to zero is -0).  NaN has   */
+/* no E2M1 code: it becomes a signed zero.                                   */
+uint8_t orc_e2m1_encode(float v) {
+    uint8_t sign = signbit(v) ? 8 : 0;
+    if (isnan(v)) return sign;
+    double a = fabs((double)v);
+    if (a >= 6.0) return sign | 7;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);
+    e -= 1;
+    if (e < 0) e = 0;
+    double quantum = ldexp(1.0, e - 1);
+    double r = rint(a / quantum) * quantum;
+    if (r > 6.0) r = 6.0;
+    if (r == 0.0) return sign;
+    if (r < 1.0) return sign | 1;                      /* the one subnormal, 0.5 */
+    int er;
+    frexp(r, &er);
+    er -= 1;
+    uint8_t mant = (uint8_t)((r / ldexp(1.0, er) - 1.0) * 2.0);
+    return sign | (uint8_t)((er + 1) << 1) | mant;
+}
+
+/* q: [R][C/2] bytes (element 2i in the low nibble of byte i of its row),
+ * e8m0: [R][C/32]. */
+void orc_quant_mxfp4(const float* x, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0) {
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t b = 0; b < C / 32; ++b) {
+            const float* v = x + r * C + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            int e = 127;
+            if (amax > 0.0f) {
+                e = ilogbf(amax) - 2 + 127;
+                if (e < 0) e = 0;
+                if (e > 254) e = 254;
+            }
+            e8m0[r * (C / 32) + b] = (uint8_t)e;
+            for (int i = 0; i < 32; i += 2) {
+                uint8_t lo = orc_e2m1_encode(ldexpf(v[i], 127 - e));
+                uint8_t hi = orc_e2m1_encode(ldexpf(v[i + 1], 127 - e));
+                q[r * (C / 2) + b * 16 + i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+}
+
+/* Y[m,n] = sum_k (dec(a[m,k]) X_a[m,k/32]) (dec(w[n,k]) X_w[n,k/32]) in double
+ * (exact: every term is a product of two E2M1 values and powers of two).
+ * a: [M][K/2], w: [N][K/2] packed as orc_quant_mxfp4 writes them. */
+void orc_gemm_mxfp4(const uint8_t* a, const uint8_t* ea, const uint8_t* w, const uint8_t* ew, int64_t M, int64_t N,
+                    int64_t K, double* y) {
+    double* ad = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = a[m * (K / 2) + k / 2];
+            uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            ad[m * K + k] = orc_e2m1_decode(code) * ldexp(1.0, (int)ea[m * (K / 32) + k / 32] - 127);
+        }
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = w[n * (K / 2) + k / 2];
+            uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            wd[n * K + k] = orc_e2m1_decode(code) * ldexp(1.0, (int)ew[n * (K / 32) + k / 32] - 127);
+        }
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k) acc += ad[m * K + k] * wd[n * K + k];
+            y[m * N + n] = acc;
+        }
+    free(ad);
+    free(wd);
+}
+
+void orc_e2m1_encode_n(const float* x, int64_t n, uint8_t* c) {
+    for (int64_t i = 0; i < n; ++i) c[i] = orc_e2m1_encode(x[i]);
+}
+
+void orc_e2m1_decode_n(const uint8_t* c, int64_t n, double* x) {
+    for (int64_t i = 0; i < n; ++i) x[i] = orc_e2m1_decode(c[i]);
+}
+
 void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* c) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) c[i] = orc_e4m3_encode(x[i]);

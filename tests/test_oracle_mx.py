@@ -1,4 +1,4 @@
-"""Pins for the oracle's MXFP8 format and GEMM (CPU only).
+"""Pins for the oracle's MXFP8 and MXFP4 formats and GEMMs (CPU only).
 
 "Low-precision LLM inference", §10: the OCP MX specification makes a block of
 elements and its shared scale one data format.  The oracle follows OCP MX
@@ -9,6 +9,15 @@ independent numpy/torch reading of that rule (frexp for the exponent, torch's
 E4M3 cast after clamping to +-448), closed forms, the element error bound,
 and the GEMM against numpy and against the (separately pinned) FP8 W8A8
 oracle at unit scales.
+
+MXFP4 (same section: E2M1 = 1 sign, 2 exponent, 1 mantissa bit, and MXFP4
+as the OCP MX block format of it): the same rule with 2 (the largest E2M1
+exponent) in place of 8 and saturating RNE E2M1 elements.  Pinned by the
+E2M1 value table of the format definition, a brute-force nearest-value
+search with ties to the even mantissa, an independent numpy reading of the
+block rule, closed forms, and the GEMM against numpy and against the MXFP8
+oracle (every E2M1 value is an E4M3 value, so the two GEMMs must agree bit
+for bit on the same scales).
 """
 import numpy as np
 import torch
@@ -81,3 +90,125 @@ def test_mxfp8_gemm_vs_numpy_and_fp8_oracle(orc):
     onesw = np.full((N, K // 32), 127, np.uint8)
     unit = np.ones(2, np.float32)
     assert np.array_equal(orc.gemm_mxfp8(a, ones, q, onesw), orc.gemm_w8a8(a, unit, 0, q, unit, 0, True))
+
+
+# ---- MXFP4 ----
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])     # magnitudes of codes 0..7
+
+
+def _nearest_e2m1(r):
+    """Code of the E2M1 value nearest to r (binary64), ties to the even
+    mantissa bit, magnitudes above 6 saturating: a brute-force search."""
+    r = np.asarray(r, np.float64)
+    a = np.minimum(np.abs(r), 6.0)
+    d = np.abs(a[..., None] - E2M1)                               # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    even = cand & ((np.arange(8) & 1) == 0)
+    pick = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    return (pick | np.where(np.signbit(r), 8, 0)).astype(np.uint8)
+
+
+def test_e2m1_value_table_and_round_trip(orc):
+    codes = np.arange(16, dtype=np.uint8)
+    v = orc.e2m1_decode(codes)
+    assert np.array_equal(np.abs(v[:8]), E2M1) and np.array_equal(v[8:], -E2M1)
+    assert np.signbit(v[8])                                      # code 8 is -0
+    assert np.array_equal(orc.e2m1_encode(v.astype(np.float32)), codes)
+
+
+def test_e2m1_encode_brute_force(orc):
+    grid = np.arange(-8 * 256, 8 * 256 + 1, dtype=np.float64) / 256.0   # every tie point lies on it
+    rng = np.random.default_rng(63)
+    extra = rng.standard_normal(20000) * np.exp(rng.uniform(-6, 4, 20000))
+    for v in (grid, extra):
+        v32 = v.astype(np.float32)
+        assert np.array_equal(orc.e2m1_encode(v32), _nearest_e2m1(v32.astype(np.float64)))
+    # the ties, one by one: to the even mantissa (codes 0, 2, 2, 4, 4, 6, 6)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    assert list(orc.e2m1_encode(ties)) == [0, 2, 2, 4, 4, 6, 6]
+    assert list(orc.e2m1_encode(-ties)) == [8, 10, 10, 12, 12, 14, 14]
+    assert list(orc.e2m1_encode(np.array([6.0, 7.0, 1e30, np.inf], np.float32))) == [7, 7, 7, 7]
+
+
+def _np_mx4(x):
+    R, C = x.shape
+    xb = x.reshape(R, C // 32, 32).astype(np.float32)
+    amax = np.abs(xb).max(axis=2)
+    _, ex = np.frexp(amax)
+    e = np.where(amax > 0, np.clip(ex - 1 - 2 + 127, 0, 254), 127).astype(np.int64)
+    scaled = (xb.astype(np.float64) * np.exp2(127 - e)[:, :, None]).astype(np.float32)
+    codes = _nearest_e2m1(scaled.astype(np.float64)).reshape(R, C)
+    q = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return q, e.astype(np.uint8)
+
+
+def test_mxfp4_quant_vs_independent_reading(orc):
+    w, x = synth.layer(64, 16, 1024, "f32", seed=64, x_outlier_cols=8)
+    x[3, :32] = 0.0                                # an all-zero block
+    x[4, 64:96] *= 1e-30                           # tiny values: exponent clamp region
+    x[5, 96:128] = 6.0 * 2.0 ** np.arange(-16, 16)[:32]
+    x[6, 128:160] = -x[6, 128:160]
+    q, e = orc.quant_mxfp4(x)
+    qn, en = _np_mx4(x)
+    assert q.shape == (64, 512) and e.shape == (64, 32)
+    assert np.array_equal(e, en)
+    assert np.array_equal(q, qn)
+    assert e[3, 0] == 127 and not q[3, :16].any()
+
+
+def test_mxfp4_closed_forms(orc):
+    x = np.zeros((4, 64), np.float32)
+    x[0, :32] = 6.0                                # amax 6: scale 1, every element code 7
+    x[1, :32] = 1.0                                # amax 2^0: scale 2^-2, elements 4.0 (code 6)
+    x[2, :32] = np.linspace(-1.0, 1.0, 32)
+    x[3, :32] = 2.0 ** 20 * 5.0                    # a block of ties at 5 X: to 4 X
+    q, e = orc.quant_mxfp4(x)
+    assert e[0, 0] == 127 and e[1, 0] == 125 and e[0, 1] == 127 and e[3, 0] == 127 + 20
+    assert np.all(q[0, :16] == 0x77) and np.all(q[1, :16] == 0x66) and np.all(q[3, :16] == 0x66)
+    assert not q[0, 16:].any()
+    # a block's largest magnitude always scales into [4, 8); elements are
+    # within half a quantum of v / X below 6, and saturate to 6 above it
+    rng = np.random.default_rng(65)
+    v = (rng.standard_normal((32, 256)) * np.exp(rng.uniform(-20, 20, (32, 1)))).astype(np.float32)
+    q, e = orc.quant_mxfp4(v)
+    codes = np.empty((32, 256), np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = q & 15, q >> 4
+    X = np.exp2(np.repeat(e.astype(np.int64), 32, axis=1) - 127)
+    r = np.abs(v) / X
+    dec = orc.e2m1_decode(codes)
+    quantum = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0))
+    ok = r <= 6.0
+    assert np.all(np.abs(np.abs(dec) - r)[ok] <= quantum[ok] / 2)
+    assert np.all(np.abs(dec[~ok]) == 6.0)
+    top = r.reshape(32, 8, 32).max(axis=2)
+    assert np.all((top >= 4) & (top < 8))
+
+
+def test_mxfp4_gemm_vs_numpy_and_mxfp8_oracle(orc):
+    M, N, K = 33, 48, 256
+    w, x = synth.layer(M, N, K, "f32", seed=66, x_outlier_cols=8)
+    a, ea = orc.quant_mxfp4(x)
+    q, ew = orc.quant_mxfp4(w)
+    assert a.shape == (M, K // 2) and q.shape == (N, K // 2)
+    y = orc.gemm_mxfp4(a, ea, q, ew)
+
+    def codes(p):
+        c = np.empty((p.shape[0], p.shape[1] * 2), np.uint8)
+        c[:, 0::2], c[:, 1::2] = p & 15, p >> 4
+        return c
+
+    def deq(p, e):
+        return orc.e2m1_decode(codes(p)) * np.exp2(np.repeat(e.astype(np.int64), 32, axis=1) - 127)
+
+    ref = deq(a, ea) @ deq(q, ew).T
+    assert orc.rel_l2(y, ref) <= 1e-14
+    # every E2M1 value is an E4M3 value: the same blocks as MXFP8 elements
+    a8 = orc.e4m3_encode(orc.e2m1_decode(codes(a)).astype(np.float32))
+    q8 = orc.e4m3_encode(orc.e2m1_decode(codes(q)).astype(np.float32))
+    assert np.array_equal(orc.gemm_mxfp8(a8, ea, q8, ew), y)
+    # and quantising the dequantised MXFP4 values again gives them back
+    a2, ea2 = orc.quant_mxfp4(deq(a, ea).astype(np.float32))
+    nz = ea != 127
+    assert np.array_equal(a2, a) and np.array_equal(ea2[nz], ea[nz])
