@@ -529,7 +529,8 @@ void orc_col_mul(const float* x, int64_t R, int64_t C, const float* m, float* ou
 /* specification without restating it): 32 consecutive elements along K     */
 /* share an E8M0 scale X = 2^(E - 127); E = floor(log2(max |v|)) - 8 + 127   */
 /* (8 = the largest E4M3 exponent), clamped to 0..254, and every element is  */
-/* the saturating RNE E4M3 cast of v / X.  An all-zero block gets X = 1.     */
+/* the saturating RNE E4M3 cast of v / X.  An all-zero block gets X = 1;    */
+/* a block holding an infinity gets E = 254 (log2 of it is infinite).       */
 /* Scales are stored [rows][cols/32].                                        */
 /* ------------------------------------------------------------------------ */
 
@@ -541,7 +542,8 @@ void orc_quant_mxfp8(const float* x, int64_t R, int64_t C, uint8_t* q, uint8_t* 
             for (int i = 0; i < 32; ++i)
                 if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
             int e = 127;
-            if (amax > 0.0f) {
+            if (isinf(amax)) e = 254;          /* floor(log2 inf) = inf: the clamp's top */
+            else if (amax > 0.0f) {
                 e = ilogbf(amax) - 8 + 127;
                 if (e < 0) e = 0;
                 if (e > 254) e = 254;
@@ -606,7 +608,8 @@ void orc_bf16_to_f32_n(const uint16_t* b, int64_t n, float* x) {
 /* for MXFP8, the block (32 consecutive elements along K), the E8M0 scale     */
 /* and the conversion are the OCP MX v1.0 ones: E = floor(log2(max |v|)) - 2 */
 /* + 127 (2 = the largest E2M1 exponent), clamped to 0..254, elements are    */
-/* the saturating RNE E2M1 cast of v / X, and an all-zero block gets X = 1.  */
+/* the saturating RNE E2M1 cast of v / X, an all-zero block gets X = 1 and  */
+/* a block holding an infinity E = 254.                                     */
 /* Two elements per byte, the even element in the low nibble.               */
 /* ------------------------------------------------------------------------ */
 
@@ -657,7 +660,8 @@ void orc_quant_mxfp4(const float* x, int64_t R, int64_t C, uint8_t* q, uint8_t* 
             for (int i = 0; i < 32; ++i)
                 if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
             int e = 127;
-            if (amax > 0.0f) {
+            if (isinf(amax)) e = 254;          /* floor(log2 inf) = inf: the clamp's top */
+            else if (amax > 0.0f) {
                 e = ilogbf(amax) - 2 + 127;
                 if (e < 0) e = 0;
                 if (e > 254) e = 254;

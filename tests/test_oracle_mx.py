@@ -212,3 +212,25 @@ def test_mxfp4_gemm_vs_numpy_and_mxfp8_oracle(orc):
     a2, ea2 = orc.quant_mxfp4(deq(a, ea).astype(np.float32))
     nz = ea != 127
     assert np.array_equal(a2, a) and np.array_equal(ea2[nz], ea[nz])
+
+
+def test_mx_infinite_block(orc):
+    """floor(log2 inf) is infinite, so a block holding an infinity takes the
+    top of the clamp, E = 254: the infinity saturates and the finite
+    elements scale to (signed) zero."""
+    x = np.zeros((2, 64), np.float32)
+    x[0, :32] = np.linspace(-3.0, 3.0, 32)
+    x[0, 5] = np.inf
+    x[1, 40] = -np.inf
+    x[1, 41] = 1e30
+    q8, e8 = orc.quant_mxfp8(x)
+    q4, e4 = orc.quant_mxfp4(x)
+    assert e8[0, 0] == 254 and e4[0, 0] == 254 and e8[1, 1] == 254 and e4[1, 1] == 254
+    assert e8[0, 1] == 127 and e4[1, 0] == 127
+    assert q8[0, 5] == 0x7E and q8[1, 40] == 0xFE
+    c4 = np.empty((2, 64), np.uint8)
+    c4[:, 0::2], c4[:, 1::2] = q4 & 15, q4 >> 4
+    assert c4[0, 5] == 7 and c4[1, 40] == 15
+    others = np.ones(32, bool)
+    others[5] = False
+    assert np.all(orc.e4m3_decode(q8[0, :32])[others] == 0) and np.all(orc.e2m1_decode(c4[0, :32])[others] == 0)
