@@ -329,6 +329,24 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "kernel": kname}
             log(f"  w8a8 {name:8s} {'mxfp8':10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
                 f"act_quant {ms_q * 1e3:6.1f} us")
+            # MXFP4: E2M1 elements in both operands, the same E8M0 blocks
+            a, ea = ops.act_quant_mxfp4(xt)
+            q, ew = ops.act_quant_mxfp4(wt)
+            g = graph_of(lambda: ops.gemm_mxfp4(a, ea, q, ew, out=y), torch)
+            ms = time_graph(g, 10, torch)
+            kname = ops.last_kernel()
+            gq = graph_of(lambda: ops.act_quant_mxfp4(xt), torch)
+            ms_q = time_graph(gq, 10, torch)
+            tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+            peak = roofline.PEAK_TFLOPS["fp4"]
+            qbytes = M * K * 2 + M * K // 2 + M * K // 32
+            res["w8a8_m2048"][f"{name}/mxfp4"] = {
+                "gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac": round(tf / peak, 4),
+                "act_quant_us": round(ms_q * 1e3, 1),
+                "act_quant_gbps": round(qbytes / (ms_q * 1e-3) / 1e9, 1),
+                "kernel": kname}
+            log(f"  w8a8 {name:8s} {'mxfp4':10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
+                f"act_quant {ms_q * 1e3:6.1f} us")
         del wt
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]

@@ -71,7 +71,7 @@ const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, 
 
 // MXFP8 quantizer: E4M3 codes [R][C] and E8M0 scales [C/32][R rounded up to
 // 16] (C % 32 == 0).
-const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0,
+const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, bool fp4, uint8_t* q, uint8_t* e8m0,
                               hipStream_t s);
 
 // W8A8: in_fp8 selects E4M3 x E4M3 (else INT8 x INT8); out_dt: 0 f32, 1 f16, 2 bf16, 5 i32.

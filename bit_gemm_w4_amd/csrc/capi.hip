@@ -25,6 +25,13 @@ bg_status fail(bg_status st, const char* fmt, long long a = 0, long long b = 0) 
     return st;
 }
 
+// The same, with the entry point's name in front.
+bg_status fail_in(const char* fn, bg_status st, const char* fmt, long long a = 0, long long b = 0) {
+    const int n = std::snprintf(g_last_error, sizeof(g_last_error), "%s: ", fn);
+    std::snprintf(g_last_error + n, sizeof(g_last_error) - n, fmt, a, b);
+    return st;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bg_status launched(const char* what) {
@@ -221,36 +228,62 @@ BG_EXPORT bg_status act_quant_fp8_smooth(const void* x, int x_dtype, int64_t row
     return act_quant("act_quant_fp8_smooth", true, x, x_dtype, rows, cols, gran, col_mul, true, q, scales, stream);
 }
 
+static bg_status act_quant_mx(const char* fn, bool fp4, const void* x, int x_dtype, int64_t rows, int64_t cols,
+                              uint8_t* q, uint8_t* e8m0, void* stream) {
+    if (!x || !q || !e8m0) return fail_in(fn, BG_ERR_NULL, "x, q and e8m0 must be non-NULL");
+    if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
+        return fail_in(fn, BG_ERR_DTYPE, "x_dtype %lld is not F32/F16/BF16", x_dtype);
+    if (rows < 1 || rows > kMaxRows) return fail_in(fn, BG_ERR_SHAPE, "rows=%lld out of range", rows);
+    if (cols < 32 || cols > kMaxDim || cols % 32)
+        return fail_in(fn, BG_ERR_SHAPE, "cols=%lld must be a multiple of 32", cols);
+    if (!aligned16(x) || !aligned16(q)) return fail_in(fn, BG_ERR_ALIGN, "x and q must be 16-byte aligned");
+    note_kernel(bg::launch_quant_mx32(x, x_dtype, rows, cols, fp4, q, e8m0, static_cast<hipStream_t>(stream)));
+    return launched(fn);
+}
+
 BG_EXPORT bg_status act_quant_mxfp8(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* q,
                                     uint8_t* e8m0, void* stream) {
-    if (!x || !q || !e8m0) return fail(BG_ERR_NULL, "act_quant_mxfp8: x, q and e8m0 must be non-NULL");
-    if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
-        return fail(BG_ERR_DTYPE, "act_quant_mxfp8: x_dtype %lld is not F32/F16/BF16", x_dtype);
-    if (rows < 1 || rows > kMaxRows) return fail(BG_ERR_SHAPE, "act_quant_mxfp8: rows=%lld out of range", rows);
-    if (cols < 32 || cols > kMaxDim || cols % 32)
-        return fail(BG_ERR_SHAPE, "act_quant_mxfp8: cols=%lld must be a multiple of 32", cols);
-    if (!aligned16(x) || !aligned16(q)) return fail(BG_ERR_ALIGN, "act_quant_mxfp8: x and q must be 16-byte aligned");
-    note_kernel(bg::launch_quant_mx32(x, x_dtype, rows, cols, q, e8m0, static_cast<hipStream_t>(stream)));
-    return launched("act_quant_mxfp8");
+    return act_quant_mx("act_quant_mxfp8", false, x, x_dtype, rows, cols, q, e8m0, stream);
+}
+
+BG_EXPORT bg_status act_quant_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                                    uint8_t* e8m0, void* stream) {
+    return act_quant_mx("act_quant_mxfp4", true, x, x_dtype, rows, cols, q, e8m0, stream);
+}
+
+// K granularity: one pair of 64-byte stages, i.e. 128 MXFP8 or 256 MXFP4 elements.
+static bg_status gemm_mx(const char* fn, bool fp4, const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w,
+                         const uint8_t* w_e8m0, int64_t M, int64_t N, int64_t K, void* y, int out_dtype,
+                         void* stream) {
+    if (!a || !a_e8m0 || !w || !w_e8m0 || !y)
+        return fail_in(fn, BG_ERR_NULL, "a, a_e8m0, w, w_e8m0 and y must be non-NULL");
+    if (out_dtype != BG_BF16 && out_dtype != BG_F16 && out_dtype != BG_F32)
+        return fail_in(fn, BG_ERR_DTYPE, "out_dtype %lld is not BF16/F16/F32", out_dtype);
+    const int64_t kq = fp4 ? 256 : 128;
+    const int64_t row_bytes = fp4 ? K / 2 : K;
+    if (M < 1 || M > kMaxM) return fail_in(fn, BG_ERR_SHAPE, "M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail_in(fn, BG_ERR_SHAPE, "N=%lld must be a multiple of 16", N);
+    if (K < kq || K > kMaxDim || K % kq)
+        return fail_in(fn, BG_ERR_SHAPE, "K=%lld must be a multiple of %lld", K, kq);
+    if (M * row_bytes >= (int64_t(1) << 31) || N * row_bytes >= (int64_t(1) << 31))
+        return fail_in(fn, BG_ERR_SHAPE, "the A and W operands must each be below 2^31 bytes");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(a_e8m0) || !aligned16(w_e8m0))
+        return fail_in(fn, BG_ERR_ALIGN, "pointers must be 16-byte aligned");
+    const int gran = fp4 ? 5 : 4;
+    bg::W8A8Args g{a, reinterpret_cast<const float*>(a_e8m0), gran, w, reinterpret_cast<const float*>(w_e8m0), gran,
+                   true, M, N, K, y, out_dtype};
+    note_kernel(bg::launch_w8a8_tiled(g, nullptr, static_cast<hipStream_t>(stream)));
+    return launched(fn);
 }
 
 BG_EXPORT bg_status gemm_mxfp8(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, const uint8_t* w_e8m0,
                                int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream) {
-    if (!a || !a_e8m0 || !w || !w_e8m0 || !y)
-        return fail(BG_ERR_NULL, "gemm_mxfp8: a, a_e8m0, w, w_e8m0 and y must be non-NULL");
-    if (out_dtype != BG_BF16 && out_dtype != BG_F16 && out_dtype != BG_F32)
-        return fail(BG_ERR_DTYPE, "gemm_mxfp8: out_dtype %lld is not BF16/F16/F32", out_dtype);
-    if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_mxfp8: M=%lld out of range", M);
-    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_mxfp8: N=%lld must be a multiple of 16", N);
-    if (K < 128 || K > kMaxDim || K % 128) return fail(BG_ERR_SHAPE, "gemm_mxfp8: K=%lld must be a multiple of 128", K);
-    if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31))
-        return fail(BG_ERR_SHAPE, "gemm_mxfp8: M*K and N*K must be below 2^31");
-    if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(a_e8m0) || !aligned16(w_e8m0))
-        return fail(BG_ERR_ALIGN, "gemm_mxfp8: pointers must be 16-byte aligned");
-    bg::W8A8Args g{a, reinterpret_cast<const float*>(a_e8m0), 4, w, reinterpret_cast<const float*>(w_e8m0), 4,
-                   true, M, N, K, y, out_dtype};
-    note_kernel(bg::launch_w8a8_tiled(g, nullptr, static_cast<hipStream_t>(stream)));
-    return launched("gemm_mxfp8");
+    return gemm_mx("gemm_mxfp8", false, a, a_e8m0, w, w_e8m0, M, N, K, y, out_dtype, stream);
+}
+
+BG_EXPORT bg_status gemm_mxfp4(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, const uint8_t* w_e8m0,
+                               int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream) {
+    return gemm_mx("gemm_mxfp4", true, a, a_e8m0, w, w_e8m0, M, N, K, y, out_dtype, stream);
 }
 
 BG_EXPORT int gemm_w8a8_algo(int64_t M, int64_t N, int64_t K, int in_dtype) {

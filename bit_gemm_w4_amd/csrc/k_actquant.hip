@@ -153,13 +153,29 @@ __global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, 
     if ((t & 15) == 0) scales[t >> 4] = s;
 }
 
-// ---- MXFP8: 32-element blocks along a row, 4 consecutive lanes per block ----
-// OCP MX: E8M0 scale 2^(e - 127), e = floor(log2 amax) - 8 + 127 (8 = the
-// largest E4M3 exponent) clamped to 0..254, 127 for an all-zero block; the
-// elements are the saturating RNE E4M3 casts of v * 2^(127 - e) (exact
-// power-of-two scaling).  Scales are K-block-major, [cols/32][rows rounded
-// up to 16], so one K block's scales of consecutive rows are contiguous.
-template <int DT>
+// ---- MXFP8 / MXFP4: 32-element blocks along a row, 4 consecutive lanes per block ----
+// OCP MX: E8M0 scale 2^(e - 127), e = floor(log2 amax) - emax + 127 (emax =
+// the largest element exponent: 8 for E4M3, 2 for E2M1) clamped to 0..254,
+// 127 for an all-zero block, 254 for a block holding an infinity; the
+// elements are the saturating RNE casts of
+// v * 2^(127 - e) (exact power-of-two scaling).  FP4 elements are packed two
+// per byte, the even element in the low nibble.  Scales are K-block-major,
+// [cols/32][rows rounded up to 16], so one K block's scales of consecutive
+// rows are contiguous.
+
+// E2M1 code of r: the magnitude code counts the rounding boundaries r passes
+// (the midpoints of 0, 0.5, 1, 1.5, 2, 3, 4, 6; a midpoint itself goes to
+// the neighbour with the even mantissa bit, so ">" where the lower neighbour
+// is even and ">=" where the upper one is), which also saturates at 6; the
+// sign bit is r's own, so values that round to zero keep it.
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+    const float a = __builtin_fabsf(r);
+    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return m | ((__float_as_uint(r) >> 28) & 8u);
+}
+
+template <int DT, bool FP4>
 __global__ __launch_bounds__(256) void k_quant_mx32(const void* __restrict__ x, int64_t total_chunks,
                                                     int64_t C, int64_t rpad, uint8_t* __restrict__ q,
                                                     uint8_t* __restrict__ e8m0) {
@@ -169,31 +185,46 @@ __global__ __launch_bounds__(256) void k_quant_mx32(const void* __restrict__ x, 
     load8_f32<DT>(x, t * 8, v);
     const float amax = wave_max<4>(amax8(v));
     int e = 127;
-    if (amax > 0.0f) {
-        e = ilogbf(amax) - 8 + 127;
+    if (__builtin_isinf(amax)) e = 254;     // floor(log2 inf) = inf: the clamp's top
+    else if (amax > 0.0f) {
+        e = ilogbf(amax) - (FP4 ? 2 : 8) + 127;
         e = e < 0 ? 0 : e > 254 ? 254 : e;
     }
-    uint32_t lo = 0, hi = 0;
-    lo = e4m3x2(ldexpf(v[0], 127 - e), ldexpf(v[1], 127 - e)) | (e4m3x2(ldexpf(v[2], 127 - e), ldexpf(v[3], 127 - e)) << 16);
-    hi = e4m3x2(ldexpf(v[4], 127 - e), ldexpf(v[5], 127 - e)) | (e4m3x2(ldexpf(v[6], 127 - e), ldexpf(v[7], 127 - e)) << 16);
-    *reinterpret_cast<uint2*>(q + t * 8) = make_uint2(lo, hi);
+    if constexpr (FP4) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) word |= e2m1_code(ldexpf(v[i], 127 - e)) << (4 * i);
+        *reinterpret_cast<uint32_t*>(q + t * 4) = word;
+    } else {
+        uint32_t lo = 0, hi = 0;
+        lo = e4m3x2(ldexpf(v[0], 127 - e), ldexpf(v[1], 127 - e)) | (e4m3x2(ldexpf(v[2], 127 - e), ldexpf(v[3], 127 - e)) << 16);
+        hi = e4m3x2(ldexpf(v[4], 127 - e), ldexpf(v[5], 127 - e)) | (e4m3x2(ldexpf(v[6], 127 - e), ldexpf(v[7], 127 - e)) << 16);
+        *reinterpret_cast<uint2*>(q + t * 8) = make_uint2(lo, hi);
+    }
     if ((t & 3) == 0) {
         const int64_t row = t / (C >> 3), blk = (t - row * (C >> 3)) >> 2;
         e8m0[blk * rpad + row] = (uint8_t)e;
     }
 }
 
-const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, uint8_t* q, uint8_t* e8m0,
-                              hipStream_t s) {
-    const int64_t chunks = R * (C >> 3), rpad = (R + 15) & ~(int64_t)15;
+template <bool FP4>
+static void quant_mx32(const void* x, int dt, int64_t chunks, int64_t C, int64_t rpad, uint8_t* q, uint8_t* e8m0,
+                       hipStream_t s) {
     const dim3 grid((unsigned)((chunks + 255) / 256));
     if (dt == DT_F32)
-        hipLaunchKernelGGL((k_quant_mx32<DT_F32>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
+        hipLaunchKernelGGL((k_quant_mx32<DT_F32, FP4>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
     else if (dt == DT_F16)
-        hipLaunchKernelGGL((k_quant_mx32<DT_F16>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
+        hipLaunchKernelGGL((k_quant_mx32<DT_F16, FP4>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
     else
-        hipLaunchKernelGGL((k_quant_mx32<DT_BF16>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
-    return kname("k_quant_mx32", dt);
+        hipLaunchKernelGGL((k_quant_mx32<DT_BF16, FP4>), grid, dim3(256), 0, s, x, chunks, C, rpad, q, e8m0);
+}
+
+const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, bool fp4, uint8_t* q, uint8_t* e8m0,
+                              hipStream_t s) {
+    const int64_t chunks = R * (C >> 3), rpad = (R + 15) & ~(int64_t)15;
+    if (fp4) quant_mx32<true>(x, dt, chunks, C, rpad, q, e8m0, s);
+    else quant_mx32<false>(x, dt, chunks, C, rpad, q, e8m0, s);
+    return kname("k_quant_mx32", dt, fp4);
 }
 
 // ---- 128 x 128 blocks: one workgroup per block ----

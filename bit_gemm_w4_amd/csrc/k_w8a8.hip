@@ -19,7 +19,7 @@
 namespace bg {
 
 enum { O_F32 = 0, O_F16 = 1, O_BF16 = 2, O_I32 = 5 };
-enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4 };
+enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4, GMX4 = 5 };
 
 // ============================================================================
 // Large-M GEMM.  Block tile BM x BN; K advances in stages of 64 bytes (one LDS
@@ -46,13 +46,16 @@ constexpr int GK = 64;                                           // K bytes per 
 
 __device__ __forceinline__ int gswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
-template <int TM, int TN>
+template <int TM, int TN, int MXR>
 struct Frags {
     int4_t a[TM][2], b[TN][2];                  // two 16-byte K chunks per 32-row fragment
-    uint32_t sa[TM], sb[TN];                    // MX: the lane's E8M0 byte of each fragment row
+    uint32_t sa[TM][MXR], sb[TN][MXR];          // MX: the lane's E8M0 byte(s) of each fragment row
 };
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN, bool MX = false>
+// MX: 0 = none, MX_F8 = MXFP8 operands, MX_F4 = MXFP4 operands
+enum { MX_F8 = 1, MX_F4 = 2 };
+
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0>
 __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       int a_gran, const uint8_t* __restrict__ w,
                                                       const float* __restrict__ ws, int w_gran, int64_t M,
@@ -61,15 +64,23 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int NW = 2 * WN;                                   // waves
     constexpr int WTM = BM / 2, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
-    // MX: a stage also holds the E8M0 bytes of its two 32-wide K blocks: A
-    // block 2kb, A block 2kb+1 (BM bytes each), then the same for W (BN each)
-    constexpr int MXS = MX ? 2 * ROWS : 0;
+    // MXFP4: a stage's 64 bytes of a row are 128 elements, two MFMA K steps
+    // of 64 (32 bytes each); MXFP8: 64 elements, one step
+    constexpr bool F4 = MX == MX_F4;
+    // MX: a stage also holds the E8M0 bytes of its RUNS 32-wide K blocks: A
+    // blocks RUNS kb .. RUNS kb + RUNS - 1 (BM bytes each), then the same for
+    // W (BN each)
+    constexpr int RUNS = F4 ? 4 : 2;
+    constexpr int MXR = F4 ? 2 : 1;                              // scale bytes per fragment row and stage
+    constexpr int MXS = MX ? RUNS * ROWS : 0;
     constexpr int STAGE_BYTES = ROWS * GK + MXS;
     constexpr int LOADS = ROWS / (16 * NW);                      // 1 KB wave-loads per wave per stage
-    // MX: every wave copies one of the stage's four scale runs (one more copy
-    // per wave and stage)
-    static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8 variant");
-    constexpr int LOADS_T = LOADS + (MX ? 1 : 0);
+    // MX: the scale area is copied 256 bytes per wave-copy, MXC copies per
+    // wave and stage
+    static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8-family variant");
+    constexpr int MX_AREA = RUNS * ROWS;
+    constexpr int MXC = MX ? (MX_AREA + 256 * NW - 1) / (256 * NW) : 0;
+    constexpr int LOADS_T = LOADS + MXC;
     // stage buffers: 128 x 128 keeps 5 (80 KB), so two blocks share a CU
     constexpr int NB_FIT = (160 * 1024) / STAGE_BYTES;
     constexpr int NB_MAX = BM * BN <= 128 * 128 || BLOCK ? 5 : 6;
@@ -99,54 +110,64 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     // ---- global -> LDS copies (rows past M or N read as zero) ----
+    const int64_t KB = F4 ? K >> 1 : K;                          // bytes per row
     const int64_t rows_a = M - m0 < BM ? M - m0 : BM, rows_w = N - n0 < BN ? N - n0 : BN;
-    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a + m0 * K), (short)0,
-                                                      (int)(rows_a * K), 0x00020000);
-    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + n0 * K), (short)0,
-                                                      (int)(rows_w * K), 0x00020000);
+    const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a + m0 * KB), (short)0,
+                                                      (int)(rows_a * KB), 0x00020000);
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + n0 * KB), (short)0,
+                                                      (int)(rows_w * KB), 0x00020000);
     uint32_t voff[LOADS];
 #pragma unroll
     for (int t = 0; t < LOADS; ++t) {
         const int j = wave * LOADS + t;                          // wave-load index in the stage
         const int r = (j < BM / 16 ? 16 * j : 16 * (j - BM / 16)) + (lane >> 2);
-        voff[t] = (uint32_t)(r * K) + (uint32_t)((((lane & 3) ^ gswz(r)) << 4));
+        voff[t] = (uint32_t)(r * KB) + (uint32_t)((((lane & 3) ^ gswz(r)) << 4));
     }
-    const int nkb = (int)(K / GK);
+    const int nkb = (int)(KB / GK);
     const int kb0 = sl * spl, kb1 = kb0 + spl < nkb ? kb0 + spl : nkb;
     // MX scales are K-block-major, [K/32][rows padded to 16] bytes, so a K
     // block's bytes for the tile's rows are one contiguous run.  The stage's
-    // scale area holds the runs A(2kb), A(2kb+1), W(2kb), W(2kb+1); wave w
-    // copies its bytes [256w, 256w + 256) with one 4-byte-per-lane copy, every
-    // lane active (each lane picks its run and row), and waves past the area
-    // repeat its last 256 bytes.  (as / ws point to the E8M0 bytes.)
-    constexpr int MX_AREA = 2 * ROWS;
-    static_assert(!MX || (MX_AREA % 256 == 0 && (2 * BM) % 256 == 0), "MX scale area in whole waves");
+    // scale area holds the runs A(RUNS kb + r), r < RUNS, then W's; wave-copy
+    // c of wave w moves the area's bytes [256 p, 256 p + 256), p = w + NW c,
+    // with one 4-byte-per-lane copy, every lane active (each lane picks its
+    // run and row), and copies past the area repeat its last 256 bytes.
+    // (as / ws point to the E8M0 bytes.)
+    static_assert(!MX || (MX_AREA % 256 == 0 && (RUNS * BM) % 256 == 0), "MX scale area in whole waves");
     const int64_t mpad = (M + 15) & ~(int64_t)15, npad = (N + 15) & ~(int64_t)15;
-    const int mx_piece = 256 * wave < MX_AREA ? wave : MX_AREA / 256 - 1;
-    const int mx_pos = mx_piece * 256 + lane * 4;                 // byte of the scale area
-    const bool mx_a = mx_piece * 256 < 2 * BM;                    // wave-uniform
-    const int mx_run = mx_a ? mx_pos / BM : (mx_pos - 2 * BM) / BN;
-    const int mx_row = mx_a ? mx_pos % BM : (mx_pos - 2 * BM) % BN;
-    const int64_t mx_stride = mx_a ? mpad : npad;
-    const auto rsx = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<uint8_t*>(const_cast<float*>(mx_a ? as : ws)) + (MX ? (mx_a ? m0 : n0) : 0), (short)0,
-        MX ? (int)((K >> 5) * mx_stride - (mx_a ? m0 : n0)) : 0, 0x00020000);
-    const uint32_t mx_voff = (uint32_t)(mx_run * mx_stride + mx_row);
-    auto mx_copy = [&](int kb) {
+    constexpr int MXC1 = MXC > 0 ? MXC : 1;
+    int mx_piece[MXC1];
+    uint32_t mx_voff[MXC1];
+    int64_t mx_stride[MXC1];
+    __amdgpu_buffer_rsrc_t rsx[MXC1];
+#pragma unroll
+    for (int c = 0; c < MXC1; ++c) {
+        const int p = wave + NW * c;
+        mx_piece[c] = 256 * p < MX_AREA ? p : MX_AREA / 256 - 1;
+        const int pos = mx_piece[c] * 256 + lane * 4;            // byte of the scale area
+        const bool on_a = mx_piece[c] * 256 < RUNS * BM;          // wave-uniform
+        const int run = on_a ? pos / BM : (pos - RUNS * BM) / BN;
+        const int row = on_a ? pos % BM : (pos - RUNS * BM) % BN;
+        mx_stride[c] = on_a ? mpad : npad;
+        rsx[c] = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<uint8_t*>(const_cast<float*>(on_a ? as : ws)) + (MX ? (on_a ? m0 : n0) : 0), (short)0,
+            MX ? (int)((K >> 5) * mx_stride[c] - (on_a ? m0 : n0)) : 0, 0x00020000);
+        mx_voff[c] = (uint32_t)(run * mx_stride[c] + row);
+    }
+    auto mx_copy = [&](int kb, int c) {
         if constexpr (MX) {
             const int kc = kb < nkb - 1 ? kb : nkb - 1;          // past the end: repeat the last stage's runs
             // the whole offset per lane, so the range check covers it
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsx, (lds_ptr_t)(lds + (kb % NB) * STAGE_BYTES + ROWS * GK + mx_piece * 256), 4,
-                mx_voff + (uint32_t)(2 * kc * mx_stride), 0, 0, 0);
+                rsx[c], (lds_ptr_t)(lds + (kb % NB) * STAGE_BYTES + ROWS * GK + mx_piece[c] * 256), 4,
+                mx_voff[c] + (uint32_t)(RUNS * kc * mx_stride[c]), 0, 0, 0);
         }
     };
     // Stage kb goes to buffer kb % NB.  Stages past the end of K repeat the
     // last stage's bytes into a free buffer that is never consumed (so no copy
-    // leaves its tensor).  With MX, copy LOADS is the scale run.
+    // leaves its tensor).  With MX, copies LOADS .. LOADS_T - 1 are the scale runs.
     auto issue_one = [&](int kb, int t) {
-        if (MX && t == LOADS) {
-            mx_copy(kb);
+        if (MX && t >= LOADS) {
+            mx_copy(kb, t - LOADS);
             return;
         }
         const int j = wave * LOADS + t;
@@ -168,19 +189,32 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     const uint32_t offa1 = (uint32_t)(ra0 * GK + (((2 + h) ^ gswz(ra0)) << 4));
     const uint32_t offb0 = (uint32_t)(rb0 * GK + ((h ^ gswz(rb0)) << 4));
     const uint32_t offb1 = (uint32_t)(rb0 * GK + (((2 + h) ^ gswz(rb0)) << 4));
-    // MX: the lane's scale byte of a fragment row: its K half h selects the
-    // run (block 2kb + h), the row its byte in the run
+    // MX: the lane's scale byte of a fragment row for MFMA step c of the
+    // stage: block 2c + h (MXFP8 has the one step c = 0), i.e. run 2c + h,
+    // and the row's byte in the run.  (The scaled MFMA takes the scale of K
+    // block b of a row from lane half b; an MXFP4 lane half holds exactly its
+    // block's 32 elements, an MXFP8 lane half the 16-byte chunks h and 2 + h,
+    // which the hardware reads as K block h.)
     const uint32_t mxa0 = (uint32_t)(ROWS * GK + h * BM + ra0);
-    const uint32_t mxb0 = (uint32_t)(ROWS * GK + 2 * BM + h * BN + (rb0 - BM));
+    const uint32_t mxb0 = (uint32_t)(ROWS * GK + RUNS * BM + h * BN + (rb0 - BM));
     auto mx_base = [&](int kb) { return lds0 + (uint32_t)((kb % NB) * STAGE_BYTES); };
     constexpr int NFRAG = 2 * (TM + TN);
+    using FragsT = Frags<TM, TN, MXR>;
     // read number r of a stage (0 .. NREAD-1): A fragments first, then W, then
-    // (MX) the scale dwords of the A and W fragment rows
-    auto read_one = [&](Frags<TM, TN>& f, uint32_t base, uint32_t mxb, int r) {
+    // (MX) the scale bytes of the A and W fragment rows, step by step
+    auto mx_addr = [&](uint32_t mxb, int i) {
+        const int c = i / (TM + TN), f = i % (TM + TN);
+        return f < TM ? mxb + mxa0 + (uint32_t)(c * 2 * BM + f * 32)
+                      : mxb + mxb0 + (uint32_t)(c * 2 * BN + (f - TM) * 32);
+    };
+    auto mx_slot = [&](FragsT& f, int i) -> uint32_t& {
+        const int c = i / (TM + TN), g = i % (TM + TN);
+        return g < TM ? f.sa[g][c] : f.sb[g - TM][c];
+    };
+    auto read_one = [&](FragsT& f, uint32_t base, uint32_t mxb, int r) {
         if (r >= NFRAG) {
             const int i = r - NFRAG;
-            if (i < TM) f.sa[i] = ds_read1(mxb + mxa0 + (uint32_t)(i * 32));
-            else f.sb[i - TM] = ds_read1(mxb + mxb0 + (uint32_t)((i - TM) * 32));
+            mx_slot(f, i) = ds_read1(mx_addr(mxb, i));
             return;
         }
         const int frag = r >> 1, c = r & 1;
@@ -190,13 +224,13 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
             f.b[frag - TM][c] = ds_read16(base + (c ? offb1 : offb0) + (uint32_t)((frag - TM) * 32 * GK));
     };
     // the same, issued right after MFMAs whose operands must stay untouched
-    using op_t = typename std::conditional<FP8, int8_t_v, int4_t>::type;
-    auto read_one_after = [&](Frags<TM, TN>& f, uint32_t base, uint32_t mxb, int r, const op_t& a1, const op_t& b1,
+    // (an MXFP4 operand is the fragment's 16 bytes: the MFMA reads 4 registers)
+    using op_t = typename std::conditional<FP8 && !F4, int8_t_v, int4_t>::type;
+    auto read_one_after = [&](FragsT& f, uint32_t base, uint32_t mxb, int r, const op_t& a1, const op_t& b1,
                               const op_t& a0, const op_t& b0) {
         if (r >= NFRAG) {
             const int i = r - NFRAG;
-            if (i < TM) f.sa[i] = ds_read1_after(mxb + mxa0 + (uint32_t)(i * 32), a1, b1, a0, b0);
-            else f.sb[i - TM] = ds_read1_after(mxb + mxb0 + (uint32_t)((i - TM) * 32), a1, b1, a0, b0);
+            mx_slot(f, i) = ds_read1_after(mx_addr(mxb, i), a1, b1, a0, b0);
             return;
         }
         const int frag = r >> 1, c = r & 1;
@@ -207,7 +241,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                 ds_read16_after(base + (c ? offb1 : offb0) + (uint32_t)((frag - TM) * 32 * GK), a1, b1, a0, b0);
     };
     auto stage_base = [&](int kb) { return lds0 + (uint32_t)((kb % NB) * STAGE_BYTES); };
-    auto settle_frags = [&](Frags<TM, TN>& f) {
+    auto settle_frags = [&](FragsT& f) {
         wait_lgkm0();
 #pragma unroll
         for (int i = 0; i < TM; ++i) settle(f.a[i][0]), settle(f.a[i][1]);
@@ -215,9 +249,12 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         for (int j = 0; j < TN; ++j) settle(f.b[j][0]), settle(f.b[j][1]);
         if constexpr (MX) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) settle(f.sa[i]);
+            for (int c = 0; c < MXR; ++c) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) settle(f.sb[j]);
+                for (int i = 0; i < TM; ++i) settle(f.sa[i][c]);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) settle(f.sb[j][c]);
+            }
         }
     };
 
@@ -286,10 +323,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // the buffer of stage kb is free and receives stage kb+NB, and (b)
     // publishes stage kb+1, whose fragment reads are then spread between the
     // MFMAs of stage kb.
-    constexpr int NREAD = NFRAG + (MX ? TM + TN : 0);
-    constexpr int NMFMA = FP8 ? TM * TN : 2 * TM * TN;
+    constexpr int NREAD = NFRAG + (MX ? MXR * (TM + TN) : 0);
+    constexpr int NMFMA = FP8 && !F4 ? TM * TN : 2 * TM * TN;
     constexpr int NSLOT = NMFMA - NMFMA / 4;
-    auto step = [&](Frags<TM, TN>& cur, Frags<TM, TN>& nxt, int kb) {
+    auto step = [&](FragsT& cur, FragsT& nxt, int kb) {
         settle_frags(cur);
         // this wave's copies of stage kb+1 landed: younger than them are the
         // copies of the NB-2 later stages and, with block scales, the scale
@@ -297,14 +334,19 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         wait_vmcnt<(NB - 2) * LOADS_T + (BLOCK ? 2 * TM : 0)>();
         block_barrier();
         const uint32_t nb_base = stage_base(kb + 1), nb_mx = mx_base(kb + 1);
-        // MX: this stage's E8M0 bytes of the fragment rows, byte i of pka / j
-        // of pkb (the MFMA takes byte 0 of a constant shift of them)
-        uint32_t pka = 0, pkb = 0;
-        if constexpr (MX) {
+        // MX: this stage's E8M0 bytes of the fragment rows for MFMA step c,
+        // byte i of pka[c] / j of pkb[c] (the MFMA takes byte 0 of a constant
+        // shift of them)
+        uint32_t pka[MXR], pkb[MXR];
 #pragma unroll
-            for (int i = 0; i < TM; ++i) pka |= cur.sa[i] << (8 * i);
+        for (int c = 0; c < MXR; ++c) {
+            pka[c] = 0, pkb[c] = 0;
+            if constexpr (MX) {
 #pragma unroll
-            for (int j = 0; j < TN; ++j) pkb |= cur.sb[j] << (8 * j);
+                for (int i = 0; i < TM; ++i) pka[c] |= cur.sa[i][c] << (8 * i);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) pkb[c] |= cur.sb[j][c] << (8 * j);
+            }
         }
         // reads of stage kb+1 follow the first NSLOT MFMAs (NREAD/NSLOT per MFMA,
         // every read exactly once), so the last quarter of the MFMAs covers
@@ -316,13 +358,22 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         for (int t = 0; t < NMFMA; ++t) {
             op_t av, bv;
             int i, j;
-            if constexpr (FP8) {
+            if constexpr (F4) {
+                const int half = t / (TM * TN);
+                i = (t % (TM * TN)) / TN, j = t % TN;
+                av = cur.a[i][half];
+                bv = cur.b[j][half];
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    __builtin_shufflevector(bv, bv, 0, 1, 2, 3, -1, -1, -1, -1),
+                    __builtin_shufflevector(av, av, 0, 1, 2, 3, -1, -1, -1, -1), acc[i][j], 4, 4, 0,
+                    (int)(pkb[half] >> (8 * j)), 0, (int)(pka[half] >> (8 * i)));
+            } else if constexpr (FP8) {
                 i = t / TN, j = t % TN;
                 av = __builtin_shufflevector(cur.a[i][0], cur.a[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 bv = __builtin_shufflevector(cur.b[j][0], cur.b[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
                 if constexpr (MX)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        bv, av, acc[i][j], 0, 0, 0, (int)(pkb >> (8 * j)), 0, (int)(pka >> (8 * i)));
+                        bv, av, acc[i][j], 0, 0, 0, (int)(pkb[0] >> (8 * j)), 0, (int)(pka[0] >> (8 * i)));
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
             } else {
@@ -357,7 +408,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     }
     wait_vmcnt<(NB - 1) * LOADS_T + (BLOCK ? SCP * TM : 0)>();
     block_barrier();
-    Frags<TM, TN> f0, f1;
+    FragsT f0, f1;
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(kb0), mx_base(kb0), r);
     for (int kb = kb0; kb < kb1; kb += 2) {                      // slices hold whole 128-byte K blocks
@@ -528,7 +579,7 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(const void* __restrict__ pa
     }
 }
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN, bool MX = false>
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0>
 static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
     hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN, MX>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0, s,
@@ -556,9 +607,9 @@ static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipSt
 W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     W8Split c{};
     c.S = 1;
-    c.spl = (int)(g.K / GK);
     const bool block = g.in_fp8 && g.a_gran == GR128;
-    const bool mx = g.a_gran == GMX32;
+    const bool mx = g.a_gran == GMX32 || g.a_gran == GMX4;
+    c.spl = (int)((g.a_gran == GMX4 ? g.K / 2 : g.K) / GK);
     auto tiles = [&](int64_t bm, int64_t bn) { return ((g.M + bm - 1) / bm) * ((g.N + bn - 1) / bn); };
     auto cost = [&](int64_t bm, int64_t bn, double round) { return (double)((tiles(bm, bn) + 255) / 256) * round; };
     if (block) c.bm = 128, c.bn = 128;
@@ -585,7 +636,7 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     return c;
 }
 
-template <bool FP8, bool BLOCK, bool MX = false>
+template <bool FP8, bool BLOCK, int MX = 0>
 static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2, MX>(g, c, ws, s);
     if constexpr (!BLOCK) {
@@ -597,7 +648,8 @@ static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hip
 
 const char* launch_w8a8_tiled(const W8A8Args& g, void* ws, hipStream_t s) {
     const W8Split c = w8a8_tiled_split(g, ws != nullptr);
-    if (g.a_gran == GMX32) return gemm_shape<true, false, true>(g, c, nullptr, s);
+    if (g.a_gran == GMX32) return gemm_shape<true, false, MX_F8>(g, c, nullptr, s);
+    if (g.a_gran == GMX4) return gemm_shape<true, false, MX_F4>(g, c, nullptr, s);
     if (g.in_fp8 && g.a_gran == GR128) return gemm_shape<true, true>(g, c, ws, s);
     if (g.in_fp8) return gemm_shape<true, false>(g, c, ws, s);
     return gemm_shape<false, false>(g, c, ws, s);

@@ -25,7 +25,7 @@ PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
-    "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "gemm_w8a8",
+    "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "act_quant_mxfp4", "gemm_mxfp4", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
     "gemm_w4a16_algo", "gemm_w8a8_algo",
     "bg_status_string", "bg_last_error",
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
             "act_quant_fp8_smooth": [P, I, I64, I64, I, P, P, P, P],
             "act_quant_mxfp8": [P, I, I64, I64, P, P, P],
             "gemm_mxfp8": [P, P, P, P, I64, I64, I64, P, I, P],
+            "act_quant_mxfp4": [P, I, I64, I64, P, P, P],
+            "gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I, P],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
             "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
             "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
@@ -274,6 +276,38 @@ def gemm_mxfp8(a: torch.Tensor, a_e8m0: torch.Tensor, w: torch.Tensor, w_e8m0: t
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _check(lib().gemm_mxfp8(_ptr(a), _ptr(a_e8m0), _ptr(w), _ptr(w_e8m0), M, N, K, _ptr(out), _OUT_DT[out.dtype],
                             _stream(stream)), "gemm_mxfp8")
+    return out
+
+
+def act_quant_mxfp4(x: torch.Tensor, stream=None):
+    """-> (packed E2M1 bytes uint8 [R][C/2], element 2i in the low nibble;
+    E8M0 scale bytes uint8 [C/32][R rounded up to 16], K-block-major)."""
+    R, C = x.shape
+    dt = _TORCH_DT.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"act_quant_mxfp4: unsupported dtype {x.dtype}")
+    q = torch.empty((R, C // 2), dtype=torch.uint8, device=x.device)
+    e = torch.empty((C // 32, (R + 15) // 16 * 16), dtype=torch.uint8, device=x.device)
+    _check(lib().act_quant_mxfp4(_ptr(x), dt, R, C, _ptr(q), _ptr(e), _stream(stream)), "act_quant_mxfp4")
+    return q, e
+
+
+def gemm_mxfp4(a: torch.Tensor, a_e8m0: torch.Tensor, w: torch.Tensor, w_e8m0: torch.Tensor,
+               out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = (A X_a)(W X_w)^T for MXFP4 operands (act_quant_mxfp4 outputs:
+    packed [rows][K/2] bytes)."""
+    M, KH = a.shape
+    N, KH2 = w.shape
+    if KH != KH2:
+        raise ValueError(f"gemm_mxfp4: K mismatch {2 * KH} vs {2 * KH2}")
+    K = 2 * KH
+    for t, rows in ((a_e8m0, M), (w_e8m0, N)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (K // 32, (rows + 15) // 16 * 16):
+            raise ValueError("gemm_mxfp4: scales must be uint8 [K/32][rows rounded up to 16]")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(lib().gemm_mxfp4(_ptr(a), _ptr(a_e8m0), _ptr(w), _ptr(w_e8m0), M, N, K, _ptr(out), _OUT_DT[out.dtype],
+                            _stream(stream)), "gemm_mxfp4")
     return out
 
 

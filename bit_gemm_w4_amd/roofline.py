@@ -15,7 +15,7 @@ from __future__ import annotations
 HBM_GBPS = 8000.0                 # HBM3E, GB/s
 PEAK_TFLOPS = {                    # dense matrix-core peaks
     "bf16": 2500.0, "f16": 2500.0, "fp8": 5000.0, "i8": 5000.0,
-    "f32": 157.3, "f64": 78.6,
+    "fp6": 10100.0, "fp4": 10100.0, "f32": 157.3, "f64": 78.6,
 }
 
 

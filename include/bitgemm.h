@@ -232,6 +232,37 @@ bg_status gemm_mxfp8(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, 
                      int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream);
 
 /*
+ * act_quant_mxfp4 -- MXFP4 quantization ([LPI] §10: E2M1 = 1 sign, 2
+ * exponent, 1 mantissa bit, and MXFP4 as the OCP MX block format of it).  As
+ * act_quant_mxfp8, with e = floor(log2 amax) - 2 + 127 (2 = the largest E2M1
+ * exponent) and each element the saturating RNE E2M1 cast of v * 2^(127 - e)
+ * (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives; a value that rounds
+ * to zero keeps its sign; NaN, which E2M1 cannot hold, becomes a signed zero).
+ *   x      [rows][cols] F32, F16 or BF16; cols % 32 == 0
+ *   q      out packed codes [rows][cols/2] bytes: element 2i in the low
+ *          nibble of byte i, element 2i + 1 in the high nibble
+ *   e8m0   out scale bytes, K-block-major: [cols/32][rows rounded up to 16]
+ *          (the padding bytes are not written)
+ */
+bg_status act_quant_mxfp4(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* q,
+                          uint8_t* e8m0, void* stream);
+
+/*
+ * gemm_mxfp4 -- Y = (A X_a)(W X_w)^T for MXFP4 operands (act_quant_mxfp4 of
+ * the activations [M][K] and of the weights [N][K]) on gfx950's block-scaled
+ * matrix instruction with both operands in E2M1: each MFMA takes the E8M0
+ * scales of its 32-element K blocks; FP32 accumulation, one RNE rounding to
+ * out_dtype.
+ *   a, a_e8m0   packed E2M1 [M][K/2], E8M0 [K/32][M rounded up to 16]
+ *   w, w_e8m0   packed E2M1 [N][K/2], E8M0 [K/32][N] (N % 16 == 0)
+ *   y           out [M][N], BG_BF16, BG_F16 or BG_F32
+ * Requires K % 256 == 0, N % 16 == 0, M * K / 2 and N * K / 2 below 2^31,
+ * 16-byte aligned pointers.  No workspace.
+ */
+bg_status gemm_mxfp4(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, const uint8_t* w_e8m0,
+                     int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream);
+
+/*
  * gemm_w8a8 -- native INT8 or FP8 GEMM of quantized activations A [M][K] and
  * weights W [N][K] ([AIB] W8A8/FP8 section: no upcast, low-precision matrix
  * cores; [LPI] §9 FP8 GEMM contract, §22 INT32 / FP32 accumulators).

@@ -604,3 +604,78 @@ def test_gemm_mxfp8_rejects(ops):
     b = torch.zeros((16, 192), dtype=torch.uint8, device="cuda")
     with pytest.raises(ops.BitGemmError):
         ops.gemm_mxfp8(b, e, b, e)                                        # K % 128
+
+
+# ---- MXFP4 (E2M1 elements, 32-element E8M0 blocks, both operands) ----
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_act_quant_mxfp4_bitexact(ops, orc, dtype):
+    R, C = 96, 1536
+    w, x = synth.layer(R, 16, C, "f32", seed=80, x_outlier_cols=8)
+    x[3, :32] = 0.0                                 # all-zero block: scale 1
+    x[4, 64:96] *= 1e-30                            # exponent clamp region
+    x[5, 96:128] = 6.0 * 2.0 ** np.arange(-16, 16)[:32]
+    # every rounding tie of E2M1 at scale 1 (block maximum 4), both signs, and
+    # small negatives that round to -0
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 4.0], np.float32)
+    x[6, 128:160] = np.concatenate([ties, -ties, np.full(8, -0.1, np.float32), ties * 0.5])
+    xd, x32 = as_f32(x, dtype)
+    q, e = ops.act_quant_mxfp4(xd)
+    torch.cuda.synchronize()
+    qo, eo = orc.quant_mxfp4(x32)
+    assert q.shape == (R, C // 2)
+    assert np.array_equal(e.cpu().numpy()[:, :R], eo.T)           # K-block-major, rows padded to 16
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def _mx4_case(ops, orc, M, N, K, out=torch.bfloat16, rows=None, seed=0):
+    w, x = synth.prefill_layer(M, N, K, seed=seed)
+    a, ea = ops.act_quant_mxfp4(dev_bits(x, "bf16"))
+    q, ew = ops.act_quant_mxfp4(torch.from_numpy(w).cuda())
+    y = ops.gemm_mxfp4(a, ea, q, ew, out_dtype=out)
+    torch.cuda.synchronize()
+    ao, eao = orc.quant_mxfp4(orc.bits_to_f32(x, "bf16"))
+    qo, ewo = orc.quant_mxfp4(w)
+    assert np.array_equal(a.cpu().numpy(), ao) and np.array_equal(ea.cpu().numpy()[:, :M], eao.T)
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(ew.cpu().numpy()[:, :N], ewo.T)
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    ref = orc.gemm_mxfp4(ao[sel], eao[sel], qo, ewo)
+    check_close(y.float().cpu().numpy()[sel].astype(np.float64), ref, orc, f"mxfp4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 272, 256), (100, 272, 1536), (129, 400, 1024), (300, 1040, 4608)])
+def test_gemm_mxfp4_small(ops, orc, M, N, K):
+    """128 x 128 tiles (M <= 128) and 256 x 128 tiles (whose scale area takes
+    two copies per wave), ragged in M and N, from one pair of stages of K up
+    to 18."""
+    _mx4_case(ops, orc, M, N, K, seed=M + K + 1)
+
+
+def test_gemm_mxfp4_wide_tiles_ragged(ops, orc):
+    """256 x 256 tiles (132 of them: one round) with ragged M and N."""
+    _mx4_case(ops, orc, 1000, 8208, 512, rows=[0, 255, 256, 511, 768, 999], seed=83)
+    assert "256, 256" in ops.last_kernel()
+
+
+@pytest.mark.parametrize("out", [torch.float16, torch.float32])
+def test_gemm_mxfp4_out_dtypes(ops, orc, out):
+    _mx4_case(ops, orc, 257, 256, 1024, out=out, seed=81)
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_gemm_mxfp4_full_shape_sampled(ops, orc, name):
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _mx4_case(ops, orc, 2048, N, K, rows=[0, 255, 256, 1000, 2047], seed=82)
+
+
+def test_gemm_mxfp4_rejects(ops):
+    a = torch.zeros((16, 128), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        ops.gemm_mxfp4(a, torch.zeros((8, 16), dtype=torch.uint8, device="cuda"), a,
+                       torch.zeros((7, 16), dtype=torch.uint8, device="cuda"))      # scale shapes
+    b = torch.zeros((16, 64), dtype=torch.uint8, device="cuda")                    # K = 128
+    e = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(ops.BitGemmError):
+        ops.gemm_mxfp4(b, e, b, e)                                        # K % 256
+    with pytest.raises(ops.BitGemmError):
+        ops.act_quant_mxfp4(torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda"))   # cols % 32
