@@ -83,6 +83,8 @@ def _load():
                 "orc_quant_mxfp8": [P, I64, I64, P, P],
                 "orc_gemm_mxfp8": [P, P, P, P, I64, I64, I64, P],
                 "orc_quant_mxfp4": [P, I64, I64, P, P],
+                "orc_outlier_channels": [P, I64, I64, ctypes.c_float, P],
+                "orc_gemm_w8a8_outlier": [P, P, P, P, P, P, I64, I64, I64, I64, P],
                 "orc_gemm_mxfp4": [P, P, P, P, I64, I64, I64, P],
                 "orc_e2m1_encode_n": [P, I64, P],
                 "orc_e2m1_decode_n": [P, I64, P],
@@ -91,7 +93,8 @@ def _load():
             for name, argtypes in sig.items():
                 fn = getattr(lib, name)
                 fn.argtypes = argtypes
-                fn.restype = ctypes.c_int if name in ("orc_gemm_i8_acc", "orc_num_threads") else None
+                fn.restype = (ctypes.c_int if name in ("orc_gemm_i8_acc", "orc_num_threads")
+                              else ctypes.c_int64 if name == "orc_outlier_channels" else None)
             _lib = lib
     return _lib
 
@@ -327,6 +330,42 @@ def col_mul(x, m) -> np.ndarray:
     out = np.empty((R, C), np.float32)
     _load().orc_col_mul(_p(x), R, C, _p(m), _p(out))
     return out
+
+
+# ------------------------------------------------------ LLM.int8() outliers ----
+
+def outlier_channels(x, tau: float) -> np.ndarray:
+    """Increasing int32 indices j with max_r |x[r, j]| >= tau (binary32 x)."""
+    x = _c(x, np.float32)
+    R, C = x.shape
+    idx = np.empty(C, np.int32)
+    n = _load().orc_outlier_channels(_p(x), R, C, float(tau), _p(idx))
+    return idx[:n].copy()
+
+
+def act_quant_int8_outlier(x, idx):
+    """Per-token INT8 of x with the columns idx set to zero: the column
+    multiplier with factors 0 on idx and 1 elsewhere, then per-token INT8."""
+    x = _c(x, np.float32)
+    mask = np.ones(x.shape[1], np.float32)
+    mask[np.asarray(idx, np.int64)] = 0.0
+    return act_quant_int8(col_mul(x, mask), GRAN_ROW)
+
+
+def gemm_w8a8_outlier(a, a_scales, w, w_scales, x, idx) -> np.ndarray:
+    """INT8 part plus the side path over the outlier columns, binary64."""
+    a = _c(a, np.int8)
+    w = _c(w, np.int8)
+    a_scales = _c(a_scales, np.float32)
+    w_scales = _c(w_scales, np.float32)
+    x = _c(x, np.float32)
+    idx = _c(idx, np.int32)
+    M, K = a.shape
+    N = w.shape[0]
+    y = np.empty((M, N), np.float64)
+    _load().orc_gemm_w8a8_outlier(_p(a), _p(a_scales), _p(w), _p(w_scales), _p(x), _p(idx), idx.size, M, N, K,
+                                  _p(y))
+    return y
 
 
 # ---------------------------------------------------------------- MXFP8 ----

@@ -713,6 +713,53 @@ void orc_e2m1_decode_n(const uint8_t* c, int64_t n, double* x) {
     for (int64_t i = 0; i < n; ++i) x[i] = orc_e2m1_decode(c[i]);
 }
 
+/* ------------------------------------------------------------------------ */
+/* LLM.int8() outlier side path.  [LPI] §16 (Mixed-precision Outlier Path): */
+/* outlier feature channels take a higher-precision path, the remaining      */
+/* channels the INT8 GEMM, and the two partial outputs are summed.  Readings */
+/* of what the section leaves open: an outlier channel is an input column j  */
+/* of X whose largest magnitude over the rows reaches a threshold tau; the   */
+/* common part is per-token INT8 of X with the outlier columns set to zero   */
+/* (the SmoothQuant column multiplier with factors 0 / 1) times the          */
+/* per-channel INT8 weight; the side path multiplies the unquantized         */
+/* activations of the outlier columns by the same stored weight columns,     */
+/* dequantized with their channel scale.                                     */
+/* ------------------------------------------------------------------------ */
+
+/* The outlier channels of x [R][C]: every j with max_r |x[r][j]| >= tau, in
+ * increasing order, into idx; returns how many. */
+int64_t orc_outlier_channels(const float* x, int64_t R, int64_t C, float tau, int32_t* idx) {
+    int64_t n = 0;
+    for (int64_t j = 0; j < C; ++j) {
+        float amax = 0.0f;
+        for (int64_t r = 0; r < R; ++r)
+            if (fabsf(x[r * C + j]) > amax) amax = fabsf(x[r * C + j]);
+        if (amax >= tau) idx[n++] = (int32_t)j;
+    }
+    return n;
+}
+
+/* Y[m,n] = s_a[m] s_w[n] sum_k a[m,k] w[n,k]                  (INT8 part)
+ *        + sum_{t < n_o} x[m, idx[t]] (s_w[n] w[n, idx[t]])    (side path)
+ * in binary64: a / s_a are the per-token codes and scales of x with the
+ * outlier columns zeroed (so those columns add nothing to the first sum),
+ * w / s_w the per-channel INT8 weight. */
+void orc_gemm_w8a8_outlier(const int8_t* a, const float* a_s, const int8_t* w, const float* w_s, const float* x,
+                           const int32_t* idx, int64_t n_o, int64_t M, int64_t N, int64_t K, double* y) {
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int64_t k = 0; k < K; ++k) acc += (int64_t)a[m * K + k] * (int64_t)w[n * K + k];
+            double side = 0.0;
+            for (int64_t t = 0; t < n_o; ++t) {
+                int64_t k = idx[t];
+                side += (double)x[m * K + k] * ((double)w_s[n] * (double)w[n * K + k]);
+            }
+            y[m * N + n] = (double)a_s[m] * (double)w_s[n] * (double)acc + side;
+        }
+}
+
 void orc_e4m3_encode_n(const float* x, int64_t n, uint8_t* c) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) c[i] = orc_e4m3_encode(x[i]);
