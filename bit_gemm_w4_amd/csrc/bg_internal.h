@@ -71,6 +71,12 @@ const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, 
 
 // MXFP8 quantizer: E4M3 codes [R][C] and E8M0 scales [C/32][R rounded up to
 // 16] (C % 32 == 0).
+// LLM.int8() outlier channels of x [R][C] (C % 8 == 0): idx / count, and the
+// 0 / 1 column multiplier (in ws) for the per-token quantizer.
+int64_t outlier_ws_bytes(int64_t R, int64_t C);
+const char* launch_outlier_detect(const void* x, int dt, int64_t R, int64_t C, float tau, float* ws, int32_t* idx,
+                                  int32_t* count, const float** mask_out, hipStream_t s);
+
 const char* launch_quant_mx32(const void* x, int dt, int64_t R, int64_t C, bool fp4, uint8_t* q, uint8_t* e8m0,
                               hipStream_t s);
 
@@ -89,6 +95,12 @@ struct W8A8Args {
     int64_t M, N, K;
     void* y;
     int out_dt;
+    // LLM.int8() side path (INT8 only, no K split): x [M][K] in ox_dt, the
+    // outlier columns oidx[0 .. *ocnt) (device memory)
+    const void* ox = nullptr;
+    int ox_dt = 0;
+    const int32_t* oidx = nullptr;
+    const int32_t* ocnt = nullptr;
 };
 // Large-M W8A8 tile shape and K split.  With a workspace (at least ws_bytes,
 // any contents) grids of less than one round split K into S slices of spl

@@ -363,6 +363,68 @@ BG_EXPORT bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran, 
                         stream);
 }
 
+// ---- LLM.int8() outlier side path ----
+
+BG_EXPORT int64_t act_quant_outlier_workspace_bytes(int64_t rows, int64_t cols) {
+    if (rows < 1 || rows > kMaxRows || cols < 128 || cols > kMaxDim || cols % 128) return 0;
+    return bg::outlier_ws_bytes(rows, cols);
+}
+
+BG_EXPORT bg_status act_quant_int8_outlier(const void* x, int x_dtype, int64_t rows, int64_t cols, float tau,
+                                           int8_t* q, float* scales, int32_t* idx, int32_t* count, void* workspace,
+                                           int64_t workspace_bytes, void* stream) {
+    const char* fn = "act_quant_int8_outlier";
+    if (!x || !q || !scales || !idx || !count || !workspace)
+        return fail_in(fn, BG_ERR_NULL, "x, q, scales, idx, count and workspace must be non-NULL");
+    if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
+        return fail_in(fn, BG_ERR_DTYPE, "x_dtype %lld is not F32/F16/BF16", x_dtype);
+    if (tau != tau) return fail_in(fn, BG_ERR_UNSUPPORTED, "tau is NaN");
+    if (rows < 1 || rows > kMaxRows) return fail_in(fn, BG_ERR_SHAPE, "rows=%lld out of range", rows);
+    if (cols < 128 || cols > kMaxDim || cols % 128)
+        return fail_in(fn, BG_ERR_SHAPE, "cols=%lld must be a multiple of 128", cols);
+    const int64_t need = bg::outlier_ws_bytes(rows, cols);
+    if (workspace_bytes < need)
+        return fail_in(fn, BG_ERR_WORKSPACE, "workspace of %lld bytes needed (got %lld)", need, workspace_bytes);
+    if (!aligned16(x) || !aligned16(q) || !aligned16(scales) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(idx) & 3u) || (reinterpret_cast<uintptr_t>(count) & 3u))
+        return fail_in(fn, BG_ERR_ALIGN, "x, q, scales and workspace must be 16-byte aligned, idx and count 4-byte");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const float* mask = nullptr;
+    bg::launch_outlier_detect(x, x_dtype, rows, cols, tau, static_cast<float*>(workspace), idx, count, &mask, s);
+    note_kernel(bg::launch_act_quant(x, x_dtype, rows, cols, BG_GRAN_ROW, false, q, scales, mask, s));
+    return launched(fn);
+}
+
+BG_EXPORT bg_status gemm_w8a8_outlier(const int8_t* a, const float* a_scales, const int8_t* w, const float* w_scales,
+                                      int w_gran, const void* x, int x_dtype, const int32_t* idx,
+                                      const int32_t* count, int64_t M, int64_t N, int64_t K, void* y, int out_dtype,
+                                      void* stream) {
+    const char* fn = "gemm_w8a8_outlier";
+    if (!a || !a_scales || !w || !w_scales || !x || !idx || !count || !y)
+        return fail_in(fn, BG_ERR_NULL, "a, a_scales, w, w_scales, x, idx, count and y must be non-NULL");
+    if (w_gran != BG_GRAN_TENSOR && w_gran != BG_GRAN_ROW)
+        return fail_in(fn, BG_ERR_UNSUPPORTED, "w_gran %lld is not TENSOR/ROW", w_gran);
+    if (x_dtype != BG_F32 && x_dtype != BG_F16 && x_dtype != BG_BF16)
+        return fail_in(fn, BG_ERR_DTYPE, "x_dtype %lld is not F32/F16/BF16", x_dtype);
+    if (out_dtype != BG_BF16 && out_dtype != BG_F16 && out_dtype != BG_F32)
+        return fail_in(fn, BG_ERR_DTYPE, "out_dtype %lld is not BF16/F16/F32", out_dtype);
+    if (M < 1 || M > kMaxM) return fail_in(fn, BG_ERR_SHAPE, "M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail_in(fn, BG_ERR_SHAPE, "N=%lld must be a multiple of 16", N);
+    if (K < 128 || K > 131072 || K % 128)
+        return fail_in(fn, BG_ERR_SHAPE, "K=%lld must be a multiple of 128 and at most 131072", K);
+    if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(a_scales) || !aligned16(w_scales) ||
+        (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u) ||
+        (reinterpret_cast<uintptr_t>(count) & 3u))
+        return fail_in(fn, BG_ERR_ALIGN, "a, w, y and the scales must be 16-byte aligned, x, idx and count 4-byte");
+    bg::W8A8Args g{a, a_scales, BG_GRAN_ROW, w, w_scales, w_gran, false, M, N, K, y, out_dtype};
+    g.ox = x;
+    g.ox_dt = x_dtype;
+    g.oidx = idx;
+    g.ocnt = count;
+    note_kernel(bg::launch_w8a8_tiled(g, nullptr, static_cast<hipStream_t>(stream)));
+    return launched(fn);
+}
+
 static bg_status w4a8_impl(const int8_t* a, const float* a_scales, int a_gran, int64_t M, int64_t K,
                            const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros, int64_t N, int group,
                            void* y, int out_dtype, void* ws, int64_t ws_bytes, bool with_ws, void* stream) {

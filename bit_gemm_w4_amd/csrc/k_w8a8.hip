@@ -55,12 +55,27 @@ struct Frags {
 // MX: 0 = none, MX_F8 = MXFP8 operands, MX_F4 = MXFP4 operands
 enum { MX_F8 = 1, MX_F4 = 2 };
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0>
+// One element of x [.][K] (F32 / F16 / BF16) as a float.
+__device__ __forceinline__ float load1_f32(const void* x, int dt, int64_t i) {
+    if (dt == DT_F32) return static_cast<const float*>(x)[i];
+    const uint32_t h = static_cast<const uint16_t*>(x)[i];
+    return dt == DT_BF16 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+// OL (INT8 only): the LLM.int8() side path.  The common columns of the
+// activations arrive as INT8 codes (outlier columns zero); after the K loop
+// the block adds, for each listed outlier column k, x[m][k] * w[n][k] from the
+// unquantized activations and the INT8 weight codes (the weight scale applies
+// to both parts in the epilogue).
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0, bool OL = false>
 __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                       int a_gran, const uint8_t* __restrict__ w,
                                                       const float* __restrict__ ws, int w_gran, int64_t M,
                                                       int64_t N, int64_t K, void* __restrict__ y, int out_dt,
-                                                      void* __restrict__ part, int S, int spl) {
+                                                      void* __restrict__ part, int S, int spl,
+                                                      const void* __restrict__ ox, int ox_dt,
+                                                      const int32_t* __restrict__ oidx,
+                                                      const int32_t* __restrict__ ocnt) {
     constexpr int NW = 2 * WN;                                   // waves
     constexpr int WTM = BM / 2, WTN = BN / WN, TM = WTM / 32, TN = WTN / 32;
     constexpr int ROWS = BM + BN;                                // LDS rows per stage
@@ -418,6 +433,86 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     wait_vmcnt<0>();                                             // no copy may land after the block exits
     wait_lgkm0();
 
+    // ---- side path (OL) ----
+    // acc becomes the float (acc * s_a[m]) in place, then gains
+    // sum_k x[m][k] w[n][k] over the outlier columns, taken in chunks of CH:
+    // the block copies the chunk's x (BM rows) and w (BN rows) values into the
+    // free stage buffers as floats, and every lane reads its rows' x and its
+    // columns' w (four consecutive columns per 16-byte read) from there.
+    // The count and the indices are clamped to [0, K] and [0, K) so a bad list
+    // never reads outside x or w.
+    if constexpr (OL) {
+        static_assert(!FP8 && !BLOCK && !MX, "the side path is an INT8 variant");
+        constexpr int CH = 64;
+        static_assert((BM + BN) * CH * 4 <= LDS_BYTES, "side-path chunk fits the stage buffers");
+        float* xo = reinterpret_cast<float*>(lds);               // [CH][BM]
+        float* wo = xo + CH * BM;                                 // [CH][BN]
+        const int64_t c_raw = *ocnt;
+        const int cnt = (int)(c_raw < 0 ? 0 : c_raw > K ? K : c_raw);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int64_t m = m0 + wm * WTM + i * 32 + l32;
+            const float s_a = a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = __float_as_int((float)acc[i][j][e] * s_a);
+        }
+        // The copies go 8 channels at a time: every thread first loads its
+        // XPT activation and WPT weight values of the 8 (all in flight
+        // together), then stores them, so a batch costs one memory round trip.
+        constexpr int NT = 128 * WN, XPT = 8 * BM / NT, WPT = 8 * BN / NT;
+        static_assert(8 * BM % NT == 0 && 8 * BN % NT == 0, "whole batches per thread");
+        auto col = [&](int i) -> int64_t { return oidx[i] < 0 ? 0 : oidx[i] >= K ? K - 1 : oidx[i]; };
+        for (int c0 = 0; c0 < cnt; c0 += CH) {
+            const int ch = cnt - c0 < CH ? cnt - c0 : CH;
+            block_barrier();                                     // stage buffers / previous chunk free
+            for (int b = 0; b < ch; b += 8) {
+                float xv[XPT], wv[WPT];
+#pragma unroll
+                for (int u = 0; u < XPT; ++u) {
+                    const int f = threadIdx.x + NT * u, t = b + f / BM, r = f % BM;
+                    xv[u] = t < ch && m0 + r < M ? load1_f32(ox, ox_dt, (m0 + r) * K + col(c0 + t)) : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < WPT; ++u) {
+                    const int f = threadIdx.x + NT * u, t = b + f / BN, c = f % BN;
+                    wv[u] = t < ch && n0 + c < N ? (float)(int8_t)w[(n0 + c) * K + col(c0 + t)] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < XPT; ++u) {
+                    const int f = threadIdx.x + NT * u, t = b + f / BM;
+                    if (t < ch) xo[(b * BM) + f] = xv[u];
+                }
+#pragma unroll
+                for (int u = 0; u < WPT; ++u) {
+                    const int f = threadIdx.x + NT * u, t = b + f / BN;
+                    if (t < ch) wo[(b * BN) + f] = wv[u];
+                }
+            }
+            block_barrier();
+            for (int t = 0; t < ch; ++t) {
+                float xv[TM];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) xv[i] = xo[t * BM + wm * WTM + i * 32 + l32];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const float4 w4 =
+                            *reinterpret_cast<const float4*>(wo + t * BN + wn * WTN + j * 32 + 8 * q4 + 4 * h);
+                        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                        for (int i = 0; i < TM; ++i)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[i][j][4 * q4 + r] =
+                                    __float_as_int(__int_as_float(acc[i][j][4 * q4 + r]) + xv[i] * wv[r]);
+                    }
+            }
+        }
+    }
+
     // ---- epilogue ----
     // The W fragment is the MFMA's first operand, so lane l, register e of
     // tile (i, j) holds output row m = 32i + l%32 and column
@@ -457,7 +552,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int64_t m = mw + i * 32 + l32;
-        sa[i] = BLOCK || MX || split ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
+        sa[i] = BLOCK || MX || OL || split ? 1.0f : a_gran == GT ? as[0] : (m < M ? as[m] : 0.0f);
     }
     uint8_t* stage = lds + wave * WTM * EPI_PITCH;
     const bool bf = odt == O_BF16;
@@ -484,6 +579,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if constexpr (BLOCK) v[r] = facc[i][j][4 * q4 + r];
+                    else if constexpr (OL) v[r] = __int_as_float(acc[i][j][4 * q4 + r]) * sw[q4][r];
                     else v[r] = ((float)acc[i][j][4 * q4 + r] * sa[i]) * sw[q4][r];
                 }
                 if (odt == O_F32) {
@@ -579,12 +675,13 @@ __global__ __launch_bounds__(256) void k_w8a8_reduce(const void* __restrict__ pa
     }
 }
 
-template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0>
+template <bool FP8, bool BLOCK, int BM, int BN, int WN, int MX = 0, bool OL = false>
 static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN, MX>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0, s,
-                       static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
-                       g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt, ws, c.S, c.spl);
+    hipLaunchKernelGGL((k_w8a8_gemm<FP8, BLOCK, BM, BN, WN, MX, OL>), dim3((unsigned)(tiles * c.S)), dim3(128 * WN), 0,
+                       s, static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran, static_cast<const uint8_t*>(g.w),
+                       g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt, ws, c.S, c.spl, g.ox, g.ox_dt, g.oidx,
+                       g.ocnt);
     if (c.S > 1) {
         const int64_t threads = g.M * g.N / 4;
         const bool scaled = !BLOCK && g.out_dt != O_I32;
@@ -592,7 +689,7 @@ static const char* gemm_cfg(const W8A8Args& g, const W8Split& c, void* ws, hipSt
                            static_cast<const void*>(ws), c.S, g.M, g.N, g.a_scales, g.a_gran, g.w_scales, g.w_gran,
                            scaled, g.y, g.out_dt);
     }
-    return kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN, MX);
+    return OL ? kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN, MX, OL) : kname("k_w8a8_gemm", FP8, BLOCK, BM, BN, WN, MX);
 }
 
 // Tile choice for the large-M GEMM: estimated time = rounds of resident
@@ -636,17 +733,18 @@ W8Split w8a8_tiled_split(const W8A8Args& g, bool with_ws) {
     return c;
 }
 
-template <bool FP8, bool BLOCK, int MX = 0>
+template <bool FP8, bool BLOCK, int MX = 0, bool OL = false>
 static const char* gemm_shape(const W8A8Args& g, const W8Split& c, void* ws, hipStream_t s) {
-    if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2, MX>(g, c, ws, s);
+    if (c.bm == 128) return gemm_cfg<FP8, BLOCK, 128, 128, 2, MX, OL>(g, c, ws, s);
     if constexpr (!BLOCK) {
-        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4, MX>(g, c, ws, s);
-        return gemm_cfg<FP8, false, 256, 128, 2, MX>(g, c, ws, s);
+        if (c.bn == 256) return gemm_cfg<FP8, false, 256, 256, 4, MX, OL>(g, c, ws, s);
+        return gemm_cfg<FP8, false, 256, 128, 2, MX, OL>(g, c, ws, s);
     }
     return nullptr;
 }
 
 const char* launch_w8a8_tiled(const W8A8Args& g, void* ws, hipStream_t s) {
+    if (g.oidx) return gemm_shape<false, false, 0, true>(g, w8a8_tiled_split(g, false), nullptr, s);
     const W8Split c = w8a8_tiled_split(g, ws != nullptr);
     if (g.a_gran == GMX32) return gemm_shape<true, false, MX_F8>(g, c, nullptr, s);
     if (g.a_gran == GMX4) return gemm_shape<true, false, MX_F4>(g, c, nullptr, s);

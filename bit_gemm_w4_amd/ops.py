@@ -25,7 +25,8 @@ PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
     "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
-    "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "act_quant_mxfp4", "gemm_mxfp4", "gemm_w8a8",
+    "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "act_quant_mxfp4", "gemm_mxfp4", "act_quant_int8_outlier", "act_quant_outlier_workspace_bytes",
+    "gemm_w8a8_outlier", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
     "gemm_w4a16_algo", "gemm_w8a8_algo",
     "bg_status_string", "bg_last_error",
@@ -68,6 +69,9 @@ def lib() -> ctypes.CDLL:
             "gemm_mxfp8": [P, P, P, P, I64, I64, I64, P, I, P],
             "act_quant_mxfp4": [P, I, I64, I64, P, P, P],
             "gemm_mxfp4": [P, P, P, P, I64, I64, I64, P, I, P],
+            "act_quant_int8_outlier": [P, I, I64, I64, ctypes.c_float, P, P, P, P, P, I64, P],
+            "gemm_w8a8_outlier": [P, P, P, P, I, P, I, P, P, I64, I64, I64, P, I, P],
+            "act_quant_outlier_workspace_bytes": [I64, I64],
             "gemm_w8a8": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P],
             "gemm_w8a8_ex": [P, P, I, P, P, I, I, I64, I64, I64, P, I, I, P],
             "gemm_w8a8_ws": [P, P, I, P, P, I, I, I64, I64, I64, P, I, P, I64, I, P],
@@ -308,6 +312,59 @@ def gemm_mxfp4(a: torch.Tensor, a_e8m0: torch.Tensor, w: torch.Tensor, w_e8m0: t
         out = torch.empty((M, N), dtype=out_dtype, device=a.device)
     _check(lib().gemm_mxfp4(_ptr(a), _ptr(a_e8m0), _ptr(w), _ptr(w_e8m0), M, N, K, _ptr(out), _OUT_DT[out.dtype],
                             _stream(stream)), "gemm_mxfp4")
+    return out
+
+
+def act_quant_outlier_workspace_bytes(rows: int, cols: int) -> int:
+    return int(lib().act_quant_outlier_workspace_bytes(rows, cols))
+
+
+def act_quant_int8_outlier(x: torch.Tensor, tau: float = 6.0, ws: torch.Tensor | None = None, stream=None):
+    """The LLM.int8() split of X: its outlier channels (columns whose largest
+    magnitude reaches tau) and the per-token INT8 codes of the other columns
+    (outlier columns quantize to 0).  -> (q int8 [R][C], scales f32 [R], idx
+    int32 [C] of which the first count entries are the outlier columns in
+    increasing order, count int32 [1]); idx and count stay on the device."""
+    R, C = x.shape
+    dt = _TORCH_DT.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"act_quant_int8_outlier: unsupported dtype {x.dtype}")
+    q = torch.empty((R, C), dtype=torch.int8, device=x.device)
+    sc = torch.empty((R,), dtype=torch.float32, device=x.device)
+    idx = torch.empty((C,), dtype=torch.int32, device=x.device)
+    cnt = torch.empty((1,), dtype=torch.int32, device=x.device)
+    if ws is None:
+        ws = workspace(max(act_quant_outlier_workspace_bytes(R, C), 16), x.device)
+    _check(lib().act_quant_int8_outlier(_ptr(x), dt, R, C, float(tau), _ptr(q), _ptr(sc), _ptr(idx), _ptr(cnt),
+                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "act_quant_int8_outlier")
+    return q, sc, idx, cnt
+
+
+def gemm_w8a8_outlier(a: torch.Tensor, a_scales: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor,
+                      w_gran: int, x: torch.Tensor, idx: torch.Tensor, count: torch.Tensor,
+                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """Y = s_a s_w (A W^T) + s_w (X_O W_O^T): the INT8 GEMM of the common
+    channels plus the side path over the outlier channels idx[:count] (the
+    act_quant_int8_outlier outputs), which multiplies the unquantized
+    activations x by the INT8 weight columns, fused into the GEMM."""
+    M, K = a.shape
+    N, K2 = w.shape
+    if K != K2 or tuple(x.shape) != (M, K):
+        raise ValueError(f"gemm_w8a8_outlier: shapes a {tuple(a.shape)}, w {tuple(w.shape)}, x {tuple(x.shape)}")
+    if a.dtype != torch.int8 or w.dtype != torch.int8:
+        raise ValueError("gemm_w8a8_outlier: a and w must be int8 codes")
+    if idx.dtype != torch.int32 or count.dtype != torch.int32 or idx.numel() < K:
+        raise ValueError("gemm_w8a8_outlier: idx must be int32 with room for K entries, count int32")
+    dt = _TORCH_DT.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"gemm_w8a8_outlier: unsupported dtype {x.dtype}")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _check(lib().gemm_w8a8_outlier(_ptr(a), _ptr(a_scales), _ptr(w), _ptr(w_scales), w_gran, _ptr(x), dt, _ptr(idx),
+                                   _ptr(count), M, N, K, _ptr(out), _OUT_DT[out.dtype], _stream(stream)),
+           "gemm_w8a8_outlier")
     return out
 
 

@@ -263,6 +263,57 @@ bg_status gemm_mxfp4(const uint8_t* a, const uint8_t* a_e8m0, const uint8_t* w, 
                      int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream);
 
 /*
+ * act_quant_int8_outlier -- the activation half of the LLM.int8() split ([LPI]
+ * §16, Mixed-precision Outlier Path: outlier feature channels go to a
+ * higher-precision side path, the rest to the INT8 GEMM).  An outlier channel
+ * is a column j of x whose largest magnitude over the rows is >= tau (NaN
+ * elements do not count).  The other columns are quantized per token as
+ * act_quant_int8 with BG_GRAN_ROW does, with the outlier columns set to zero
+ * first (they quantize to 0 and do not enter the row maxima).
+ *   x       [rows][cols] F32, F16 or BF16; cols % 128 == 0
+ *   tau     the threshold (not NaN; a negative tau makes every column an outlier)
+ *   q       out INT8 codes [rows][cols]
+ *   scales  out FP32 per-token scales [rows]
+ *   idx     out int32 [cols] (device): the outlier columns in increasing order
+ *           in idx[0 .. *count); the rest is not written
+ *   count   out int32 (device): how many
+ *   workspace, workspace_bytes  device scratch of at least
+ *           act_quant_outlier_workspace_bytes(rows, cols) bytes, any contents;
+ *           BG_ERR_WORKSPACE if smaller.
+ * The count stays on the device: nothing here synchronizes with the host.
+ */
+int64_t act_quant_outlier_workspace_bytes(int64_t rows, int64_t cols);
+bg_status act_quant_int8_outlier(const void* x, int x_dtype, int64_t rows, int64_t cols, float tau, int8_t* q,
+                                 float* scales, int32_t* idx, int32_t* count, void* workspace,
+                                 int64_t workspace_bytes, void* stream);
+
+/*
+ * gemm_w8a8_outlier -- the GEMM half of the LLM.int8() split ([LPI] §16: the
+ * two partial outputs are summed):
+ *   Y[m][n] = s_w[n] (s_a[m] sum_k a[m][k] w[n][k] + sum_{t < count} x[m][j_t] w[n][j_t]),
+ * j_t = idx[t]: the INT8 GEMM of the common channels (a from
+ * act_quant_int8_outlier, zero on the outlier columns) plus the side path,
+ * which multiplies the unquantized activations of the outlier columns by the
+ * INT8 weight codes of the same columns in FP32 (so with the channel scale
+ * s_w the weight's own dequantized values).  The side path is fused into the
+ * GEMM: after the K loop each block stages its rows' outlier activations and
+ * its columns' weight codes in LDS, 64 channels at a time, and adds them to
+ * the accumulators before the single rounding to out_dtype.
+ *   a, a_scales  INT8 [M][K], FP32 per-token scales [M]
+ *   w, w_scales  INT8 [N][K], FP32 scales: [N] (w_gran BG_GRAN_ROW) or one
+ *                (w_gran BG_GRAN_TENSOR)
+ *   x            [M][K] F32, F16 or BF16: the activations a was quantized from
+ *   idx, count   the outlier list (device); count is clamped to [0, K] and the
+ *                entries to [0, K), so a bad list never reads outside x or w
+ *   y            out [M][N], BG_BF16, BG_F16 or BG_F32
+ * Requires K % 128 == 0 and K <= 131072, N % 16 == 0, 16-byte aligned a, w,
+ * y and scales, 4-byte aligned x, idx and count.  No workspace, no K split.
+ */
+bg_status gemm_w8a8_outlier(const int8_t* a, const float* a_scales, const int8_t* w, const float* w_scales,
+                            int w_gran, const void* x, int x_dtype, const int32_t* idx, const int32_t* count,
+                            int64_t M, int64_t N, int64_t K, void* y, int out_dtype, void* stream);
+
+/*
  * gemm_w8a8 -- native INT8 or FP8 GEMM of quantized activations A [M][K] and
  * weights W [N][K] ([AIB] W8A8/FP8 section: no upcast, low-precision matrix
  * cores; [LPI] §9 FP8 GEMM contract, §22 INT32 / FP32 accumulators).

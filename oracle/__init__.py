@@ -353,7 +353,8 @@ def act_quant_int8_outlier(x, idx):
 
 
 def gemm_w8a8_outlier(a, a_scales, w, w_scales, x, idx) -> np.ndarray:
-    """INT8 part plus the side path over the outlier columns, binary64."""
+    """INT8 part plus the side path over the outlier columns, binary64
+    (per-token a_scales [M], per-channel w_scales [N])."""
     a = _c(a, np.int8)
     w = _c(w, np.int8)
     a_scales = _c(a_scales, np.float32)

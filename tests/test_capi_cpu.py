@@ -185,3 +185,11 @@ def test_auto_dispatch_thresholds(L):
     assert ws8(16, 4096, 4096, I8, 1, 0) == 0                   # o below M = 32: small-M kernel
     assert ws8(32, 4096, 4096, I8, 1, 0) == 32 * 4096 * 4 * (512 // 32 if 512 // 32 < 4 else 4)
     assert ws8(2048, 28672, 4096, I8, 1, 0) == 0                # full grid: no split
+
+
+def test_outlier_workspace_bytes(L):
+    # [min(rows, 128)][cols] row-slice column maxima plus the [cols] multiplier, FP32
+    assert L.act_quant_outlier_workspace_bytes(2048, 4096) == (128 * 4096 + 4096) * 4
+    assert L.act_quant_outlier_workspace_bytes(5, 128) == (5 * 128 + 128) * 4
+    assert L.act_quant_outlier_workspace_bytes(16, 100) == 0            # cols % 128
+    assert L.act_quant_outlier_workspace_bytes(0, 128) == 0

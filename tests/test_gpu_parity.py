@@ -679,3 +679,80 @@ def test_gemm_mxfp4_rejects(ops):
         ops.gemm_mxfp4(b, e, b, e)                                        # K % 256
     with pytest.raises(ops.BitGemmError):
         ops.act_quant_mxfp4(torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda"))   # cols % 32
+
+
+# ---- LLM.int8() outlier side path ----
+
+def _outlier_case(ops, orc, M, N, K, x_dtype="bf16", tau=6.0, n_out=8, w_gran=None, out=torch.bfloat16,
+                  rows=None, seed=0):
+    w, x = synth.layer(M, N, K, "f32", seed=seed, x_outlier_cols=n_out)
+    xd, x32 = as_f32(x, x_dtype)
+    g = ops.GRAN_ROW if w_gran is None else w_gran
+    wq, sw = orc.act_quant_int8(w, g)
+    q, sa, idx, cnt = ops.act_quant_int8_outlier(xd, tau)
+    wt, swt = torch.from_numpy(wq).cuda(), torch.from_numpy(sw).cuda()
+    y = ops.gemm_w8a8_outlier(q, sa, wt, swt, g, xd, idx, cnt, out_dtype=out)
+    torch.cuda.synchronize()
+    io = orc.outlier_channels(x32, tau)
+    qo, sao = orc.act_quant_int8_outlier(x32, io)
+    n = int(cnt.item())
+    assert n == len(io) and np.array_equal(idx.cpu().numpy()[:n], io), f"outlier list M={M} K={K}"
+    assert np.array_equal(q.cpu().numpy(), qo) and np.array_equal(sa.cpu().numpy(), sao)
+    sel = np.arange(M) if rows is None else np.asarray(rows)
+    sw_n = np.full(N, sw[0], np.float32) if g == ops.GRAN_TENSOR else sw       # the oracle takes [N]
+    ref = orc.gemm_w8a8_outlier(qo[sel], sao[sel], wq, sw_n, x32[sel], io)
+    check_close(y.float().cpu().numpy()[sel].astype(np.float64), ref, orc, f"outlier M={M} N={N} K={K}")
+    return n
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 272, 128), (100, 272, 1536), (129, 400, 1024), (300, 1040, 4608)])
+def test_outlier_small(ops, orc, M, N, K):
+    """128 x 128 and 256 x 128 tiles, ragged M and N, one to 36 stages of K."""
+    assert _outlier_case(ops, orc, M, N, K, seed=M + K + 2) >= 8 if M > 1 else True
+
+
+def test_outlier_wide_tiles_ragged(ops, orc):
+    _outlier_case(ops, orc, 1000, 8208, 512, rows=[0, 255, 256, 511, 768, 999], seed=95)
+    assert "256, 256" in ops.last_kernel()
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "f16"])
+def test_outlier_input_dtypes(ops, orc, x_dtype):
+    _outlier_case(ops, orc, 257, 256, 1024, x_dtype=x_dtype, seed=96)
+
+
+@pytest.mark.parametrize("out", [torch.float16, torch.float32])
+def test_outlier_out_dtypes_tensor_weight_scale(ops, orc, out):
+    _outlier_case(ops, orc, 200, 512, 768, w_gran=ops.GRAN_TENSOR, out=out, seed=97)
+
+
+def test_outlier_chunks_and_limits(ops, orc):
+    """150 outlier channels (three 64-channel chunks, the last ragged); tau above
+    every magnitude (no side path: plain per-token W8A8); tau below every
+    magnitude (every channel on the side path, the INT8 part all zero)."""
+    assert _outlier_case(ops, orc, 300, 528, 1024, n_out=150, seed=98) == 150
+    assert _outlier_case(ops, orc, 130, 272, 512, tau=1e9, seed=99) == 0
+    assert _outlier_case(ops, orc, 130, 272, 512, tau=-1.0, seed=100) == 512
+
+
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+def test_outlier_full_shape_sampled(ops, orc, name):
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _outlier_case(ops, orc, 2048, N, K, rows=[0, 255, 256, 1000, 2047], seed=101)
+
+
+def test_outlier_rejects(ops):
+    x = torch.zeros((16, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ops.BitGemmError):
+        ops.act_quant_int8_outlier(x, float("nan"))
+    with pytest.raises(ops.BitGemmError):
+        ops.act_quant_int8_outlier(x, 6.0, ws=torch.empty(16, dtype=torch.uint8, device="cuda"))   # too small
+    with pytest.raises(ops.BitGemmError):
+        ops.act_quant_int8_outlier(torch.zeros((16, 200), dtype=torch.bfloat16, device="cuda"))  # cols % 128
+    q, sa, idx, cnt = ops.act_quant_int8_outlier(x)
+    w = torch.zeros((32, 256), dtype=torch.int8, device="cuda")
+    sw = torch.ones(32, dtype=torch.float32, device="cuda")
+    with pytest.raises(ops.BitGemmError):
+        ops.gemm_w8a8_outlier(q, sa, w, sw, 7, x, idx, cnt)                                  # w_gran
+    with pytest.raises(ValueError):
+        ops.gemm_w8a8_outlier(q, sa, w, sw, ops.GRAN_ROW, x, idx[:100], cnt)                 # idx room
