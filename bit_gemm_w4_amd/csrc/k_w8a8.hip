@@ -412,6 +412,37 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         if (BLOCK && (kb & 1)) close_block(kb);
     };
 
+    // OL: the outlier count, and this thread's values of the first 8
+    // outlier channels (the first copy batch of the side path), are requested
+    // before the K loop, so their latency hides behind it.  A thread's copy
+    // elements in a batch lie in one channel per wave (BM and BN are
+    // multiples of 64), so the channel indices are wave-uniform scalar loads.
+    constexpr int OL_NT = 128 * WN, OL_XPT = OL ? 8 * BM / OL_NT : 1, OL_WPT = OL ? 8 * BN / OL_NT : 1;
+    [[maybe_unused]] int ol_cnt = 0;
+    [[maybe_unused]] float ol_x0[OL_XPT], ol_w0[OL_WPT];
+    auto ol_col = [&](int i) -> int64_t {
+        const int64_t c = oidx[i];
+        return c < 0 ? 0 : c >= K ? K - 1 : c;
+    };
+    auto ol_load = [&](int c0, int b, int ch, float (&xv)[OL_XPT], float (&wv)[OL_WPT]) {
+#pragma unroll
+        for (int u = 0; u < OL_XPT; ++u) {
+            const int f = threadIdx.x + OL_NT * u, r = f % BM;
+            const int t = __builtin_amdgcn_readfirstlane(b + f / BM);
+            xv[u] = t < ch && m0 + r < M ? load1_f32(ox, ox_dt, (m0 + r) * K + ol_col(c0 + t)) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < OL_WPT; ++u) {
+            const int f = threadIdx.x + OL_NT * u, c = f % BN;
+            const int t = __builtin_amdgcn_readfirstlane(b + f / BN);
+            wv[u] = t < ch && n0 + c < N ? (float)(int8_t)w[(n0 + c) * K + ol_col(c0 + t)] : 0.0f;
+        }
+    };
+    if constexpr (OL) {
+        const int64_t c_raw = *ocnt;
+        ol_cnt = (int)(c_raw < 0 ? 0 : c_raw > K ? K : c_raw);
+        ol_load(0, 0, ol_cnt < 64 ? ol_cnt : 64, ol_x0, ol_w0);
+    }
 #pragma unroll
     for (int t = 0; t < NB; ++t) issue(kb0 + t);
     if constexpr (BLOCK) {
@@ -435,20 +466,27 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 
     // ---- side path (OL) ----
     // acc becomes the float (acc * s_a[m]) in place, then gains
-    // sum_k x[m][k] w[n][k] over the outlier columns, taken in chunks of CH:
-    // the block copies the chunk's x (BM rows) and w (BN rows) values into the
-    // free stage buffers as floats, and every lane reads its rows' x and its
-    // columns' w (four consecutive columns per 16-byte read) from there.
-    // The count and the indices are clamped to [0, K] and [0, K) so a bad list
-    // never reads outside x or w.
+    // sum_k x[m][k] w[n][k] over the outlier columns on the BF16 matrix
+    // cores: an INT8 weight code is exact in BF16, and each activation is
+    // split into BF16 hi = RNE(x) and lo = RNE(x - hi), two MFMAs per K step
+    // (exact for BF16 inputs, where lo = 0, and for FP16 inputs, whose 11
+    // significant bits fit in hi and lo; an FP32 input keeps 16 of its 24,
+    // the rest below 2^-16 of its magnitude).  The channels go in chunks of
+    // CH: the block copies the chunk's values of its BM rows of x and BN rows
+    // of w into the free stage buffers as BF16 rows (PX / PW bytes apart;
+    // channels past the count up to a multiple of 16 are zero), 8 channels
+    // per batch with all of a thread's loads in flight together; then each
+    // tile (i, j) of the wave runs the chunk's K steps of v_mfma_f32_32x32x16
+    // with the W rows as the first operand and its own (float) acc as the
+    // accumulator.  The count and the indices are clamped to [0, K] and
+    // [0, K) so a bad list never reads outside x or w.
     if constexpr (OL) {
         static_assert(!FP8 && !BLOCK && !MX, "the side path is an INT8 variant");
-        constexpr int CH = 64;
-        static_assert((BM + BN) * CH * 4 <= LDS_BYTES, "side-path chunk fits the stage buffers");
-        float* xo = reinterpret_cast<float*>(lds);               // [CH][BM]
-        float* wo = xo + CH * BM;                                 // [CH][BN]
-        const int64_t c_raw = *ocnt;
-        const int cnt = (int)(c_raw < 0 ? 0 : c_raw > K ? K : c_raw);
+        constexpr int CH = 64, PX = 2 * CH * 2 + 16, PW = CH * 2 + 16;
+        static_assert(BM * PX + BN * PW <= LDS_BYTES, "side-path chunk fits the stage buffers");
+        uint8_t* xo = lds;                                        // [BM][PX]: hi plane, then lo plane
+        uint8_t* wo = lds + BM * PX;                              // [BN][PW]
+        const int cnt = ol_cnt;
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int64_t m = m0 + wm * WTM + i * 32 + l32;
@@ -458,58 +496,54 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[i][j][e] = __float_as_int((float)acc[i][j][e] * s_a);
         }
-        // The copies go 8 channels at a time: every thread first loads its
-        // XPT activation and WPT weight values of the 8 (all in flight
-        // together), then stores them, so a batch costs one memory round trip.
-        constexpr int NT = 128 * WN, XPT = 8 * BM / NT, WPT = 8 * BN / NT;
-        static_assert(8 * BM % NT == 0 && 8 * BN % NT == 0, "whole batches per thread");
-        auto col = [&](int i) -> int64_t { return oidx[i] < 0 ? 0 : oidx[i] >= K ? K - 1 : oidx[i]; };
+        constexpr int NT = OL_NT, XPT = OL_XPT, WPT = OL_WPT;
+        static_assert(8 * BM % NT == 0 && 8 * BN % NT == 0 && BM % 64 == 0 && BN % 64 == 0, "whole batches per thread");
         for (int c0 = 0; c0 < cnt; c0 += CH) {
-            const int ch = cnt - c0 < CH ? cnt - c0 : CH;
+            const int ch = cnt - c0 < CH ? cnt - c0 : CH, ch16 = (ch + 15) & ~15;
             block_barrier();                                     // stage buffers / previous chunk free
-            for (int b = 0; b < ch; b += 8) {
+            for (int b = 0; b < ch16; b += 8) {
                 float xv[XPT], wv[WPT];
+                if (c0 == 0 && b == 0) {
+#pragma unroll
+                    for (int u = 0; u < XPT; ++u) xv[u] = ol_x0[u];
+#pragma unroll
+                    for (int u = 0; u < WPT; ++u) wv[u] = ol_w0[u];
+                } else {
+                    ol_load(c0, b, ch, xv, wv);
+                }
 #pragma unroll
                 for (int u = 0; u < XPT; ++u) {
                     const int f = threadIdx.x + NT * u, t = b + f / BM, r = f % BM;
-                    xv[u] = t < ch && m0 + r < M ? load1_f32(ox, ox_dt, (m0 + r) * K + col(c0 + t)) : 0.0f;
+                    const uint16_t hi = f32_to_bf16(xv[u]);
+                    *reinterpret_cast<uint16_t*>(xo + r * PX + t * 2) = hi;
+                    *reinterpret_cast<uint16_t*>(xo + r * PX + CH * 2 + t * 2) = f32_to_bf16(xv[u] - bf16_to_f32(hi));
                 }
 #pragma unroll
                 for (int u = 0; u < WPT; ++u) {
                     const int f = threadIdx.x + NT * u, t = b + f / BN, c = f % BN;
-                    wv[u] = t < ch && n0 + c < N ? (float)(int8_t)w[(n0 + c) * K + col(c0 + t)] : 0.0f;
-                }
-#pragma unroll
-                for (int u = 0; u < XPT; ++u) {
-                    const int f = threadIdx.x + NT * u, t = b + f / BM;
-                    if (t < ch) xo[(b * BM) + f] = xv[u];
-                }
-#pragma unroll
-                for (int u = 0; u < WPT; ++u) {
-                    const int f = threadIdx.x + NT * u, t = b + f / BN;
-                    if (t < ch) wo[(b * BN) + f] = wv[u];
+                    *reinterpret_cast<uint16_t*>(wo + c * PW + t * 2) = f32_to_bf16(wv[u]);
                 }
             }
             block_barrier();
-            for (int t = 0; t < ch; ++t) {
-                float xv[TM];
+            // (plain LDS loads: the compiler sees these register writes and
+            // keeps them clear of the MFMAs still reading earlier operands)
 #pragma unroll
-                for (int i = 0; i < TM; ++i) xv[i] = xo[t * BM + wm * WTM + i * 32 + l32];
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const float4 w4 =
-                            *reinterpret_cast<const float4*>(wo + t * BN + wn * WTN + j * 32 + 8 * q4 + 4 * h);
-                        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                        for (int i = 0; i < TM; ++i)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc[i][j][4 * q4 + r] =
-                                    __float_as_int(__int_as_float(acc[i][j][4 * q4 + r]) + xv[i] * wv[r]);
+                for (int j = 0; j < TN; ++j) {
+                    float16_t c = __builtin_bit_cast(float16_t, acc[i][j]);
+                    const uint8_t* xrow = xo + (wm * WTM + i * 32 + l32) * PX + h * 16;
+                    const uint8_t* wrow = wo + (wn * WTN + j * 32 + l32) * PW + h * 16;
+                    for (int ks = 0; ks < ch16; ks += 16) {
+                        const bf168_t wb = __builtin_bit_cast(bf168_t, *reinterpret_cast<const int4_t*>(wrow + ks * 2));
+                        const bf168_t xa = __builtin_bit_cast(bf168_t, *reinterpret_cast<const int4_t*>(xrow + ks * 2));
+                        const bf168_t xl =
+                            __builtin_bit_cast(bf168_t, *reinterpret_cast<const int4_t*>(xrow + CH * 2 + ks * 2));
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, xa, c, 0, 0, 0);
+                        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wb, xl, c, 0, 0, 0);
                     }
-            }
+                    acc[i][j] = __builtin_bit_cast(acc_t, c);
+                }
         }
     }
 

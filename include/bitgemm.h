@@ -294,11 +294,14 @@ bg_status act_quant_int8_outlier(const void* x, int x_dtype, int64_t rows, int64
  * j_t = idx[t]: the INT8 GEMM of the common channels (a from
  * act_quant_int8_outlier, zero on the outlier columns) plus the side path,
  * which multiplies the unquantized activations of the outlier columns by the
- * INT8 weight codes of the same columns in FP32 (so with the channel scale
- * s_w the weight's own dequantized values).  The side path is fused into the
- * GEMM: after the K loop each block stages its rows' outlier activations and
- * its columns' weight codes in LDS, 64 channels at a time, and adds them to
- * the accumulators before the single rounding to out_dtype.
+ * INT8 weight codes of the same columns (so with the channel scale s_w the
+ * weight's own dequantized values), with FP32 accumulation.  The side path is
+ * fused into the GEMM and runs on the BF16 matrix instruction: after the K
+ * loop each block stages its rows' outlier activations (split into BF16 hi +
+ * lo: exact for BF16 and FP16 inputs, within 2^-16 relative for FP32) and its
+ * columns' weight codes (exact in BF16) in LDS, 64 channels at a time, and
+ * accumulates them into the FP32 accumulators before the single rounding to
+ * out_dtype.
  *   a, a_scales  INT8 [M][K], FP32 per-token scales [M]
  *   w, w_scales  INT8 [N][K], FP32 scales: [N] (w_gran BG_GRAN_ROW) or one
  *                (w_gran BG_GRAN_TENSOR)
