@@ -269,7 +269,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
     128x128 / 1x128 blocks), W4A8 at M=2048 (the decode step's packed INT4
     weights x per-token INT8 activations) and W4A16 at B=74/256, each timed
     alone."""
-    res = {"w8a8_m2048": {}, "w4a8_m2048": {}, "smoothquant_m2048": {}, "w4a16_large_batch": {}}
+    res = {"w8a8_m2048": {}, "w4a8_m2048": {}, "smoothquant_m2048": {}, "llm_int8_m2048": {}, "w4a16_large_batch": {}}
     M = 2048
     for name in LAYERS:
         K, N = synth.LLAMA3_8B_SHAPES[name]
@@ -299,6 +299,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             log(f"  w8a8 {name:8s} {tag:10s} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%}) "
                 f"act_quant {ms_q * 1e3:6.1f} us")
         res["smoothquant_m2048"][name] = smoothquant(ops, torch, np, dev, xt, wt, x, w, graph_of, time_graph)
+        res["llm_int8_m2048"][name] = llm_int8(ops, torch, np, dev, xt, wt, x, w, graph_of, time_graph)
         # W4A8: the same activations as per-token INT8 codes, the packed weights
         a, a_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
         p = packs[name][0]
@@ -405,6 +406,43 @@ def smoothquant(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph):
     log(f"  smoothquant rel-L2 err per-token {out['per_token']['plain']:.4f} -> {out['per_token']['folded']:.4f}, "
         f"per-tensor {out['per_tensor']['plain']:.4f} -> {out['per_tensor']['folded']:.4f}; act_quant "
         f"{out['act_quant_us']['plain']} -> {out['act_quant_us']['folded']} us")
+    return out
+
+
+def llm_int8(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph, tau=6.0):
+    """The LLM.int8() split on the INT8 prefill recipe (8 activation channels
+    x50): outlier channels with max |x| >= tau go to the side path, the rest
+    to per-token INT8 (per-channel INT8 weights).  Reports the output error
+    against the unquantized product (relative L2 over 16 rows) of plain
+    per-token W8A8 and of the split, the outlier count, and the times of
+    detection + quantization and of the GEMM with the fused side path against
+    plain per-token quantization and GEMM."""
+    M, N = xt.shape[0], wt.shape[0]
+    x32 = (x_bits.astype(np.uint32) << 16).view(np.float32)           # BF16 -> binary32, exact
+    rows = np.linspace(0, M - 1, 16).astype(np.int64)
+    exact = x32[rows].astype(np.float64) @ w.astype(np.float64).T
+    ridx = torch.from_numpy(rows).to(dev)
+    wq, w_s = ops.act_quant_int8(wt, ops.GRAN_ROW)
+    a, a_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
+    y0 = ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out_dtype=torch.float32)
+    q, sa, idx, cnt = ops.act_quant_int8_outlier(xt, tau)
+    y1 = ops.gemm_w8a8_outlier(q, sa, wq, w_s, ops.GRAN_ROW, xt, idx, cnt, out_dtype=torch.float32)
+    e0 = float(np.linalg.norm(y0[ridx].double().cpu().numpy() - exact) / np.linalg.norm(exact))
+    e1 = float(np.linalg.norm(y1[ridx].double().cpu().numpy() - exact) / np.linalg.norm(exact))
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t = {}
+    t["plain_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch), 10, torch)
+    t["plain_gemm_us"] = time_graph(graph_of(
+        lambda: ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out=y), torch), 10, torch)
+    t["detect_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8_outlier(xt, tau), torch), 10, torch)
+    t["gemm_side_us"] = time_graph(graph_of(
+        lambda: ops.gemm_w8a8_outlier(q, sa, wq, w_s, ops.GRAN_ROW, xt, idx, cnt, out=y), torch), 10, torch)
+    kname = ops.last_kernel()
+    out = {"tau": tau, "outlier_channels": int(cnt.item()), "err_plain": round(e0, 5), "err_split": round(e1, 5)}
+    out.update({k: round(v * 1e3, 1) for k, v in t.items()})
+    out["kernel"] = kname
+    log(f"  llm.int8 {out['outlier_channels']} ch: rel-L2 err {e0:.4f} -> {e1:.4f}; quant {out['plain_quant_us']} -> "
+        f"{out['detect_quant_us']} us, gemm {out['plain_gemm_us']} -> {out['gemm_side_us']} us")
     return out
 
 
