@@ -1,9 +1,12 @@
-// k_w8a8.hip -- native INT8 / FP8-E4M3 GEMM (gemm_w8a8).
+// k_w8a8.hip -- native INT8 / FP8-E4M3 GEMM (gemm_w8a8) and its variants:
+// MXFP8 / MXFP4 (gemm_mxfp8, gemm_mxfp4) and the LLM.int8() side path
+// (gemm_w8a8_outlier).
 //
 // "Quantization throughput by method" (hrletsgo.me), W8A8/FP8 section: weights
 // and activations both in 8 bits, the GEMM runs on the low-precision matrix
 // cores with no upcast.  "Low-precision LLM inference" §8 (scale recipe and
-// 128-wide block scaling), §14 (W8A8), §22 (INT32 / FP32 accumulators).
+// 128-wide block scaling), §10 (MX block formats), §14 (W8A8), §16 (outlier
+// side path), §22 (INT32 / FP32 accumulators).
 //
 // Y = A W^T, A [M][K], W [N][K], both K-contiguous.  This file holds the
 // large-M kernel (32x32 MFMA tiles, multi-stage LDS pipeline, below); the
@@ -36,8 +39,10 @@ enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4, GMX4 = 5 };
 // and memory waits overlap the other's MFMAs); each owns a (BM/2) x (BN/WN)
 // tile of 32x32 MFMA tiles:
 // v_mfma_i32_32x32x32_i8 (lane l supplies 16 bytes of row l%32: chunk l/32
-// in the first half of the stage, 2 + l/32 in the second) or
-// v_mfma_f32_32x32x64_f8f6f4 (32 bytes: both chunks).  The W fragment is the
+// in the first half of the stage, 2 + l/32 in the second),
+// v_mfma_f32_32x32x64_f8f6f4 with E4M3 operands (32 bytes: both chunks) or,
+// for MXFP4, with E2M1 operands (16 bytes, one chunk per K step of 64
+// elements, two steps per stage).  The W fragment is the
 // first operand, so output lane l, register e holds row l%32 of the A tile
 // and column 8(e/4) + 4(l/32) + e%4 of the W tile.
 // Block order: grouped_tile (XCD-aware, bands of 8 row tiles).
