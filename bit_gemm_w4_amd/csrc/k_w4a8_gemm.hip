@@ -19,7 +19,7 @@
 // Block tile 256 rows of A x 128 output columns (8 weight tiles), 8 waves
 // (4 x 2, two per SIMD) of 64 x 64 = 2 x 2 MFMA tiles.  K advances in stages
 // of 64 (half a group); each stage buffer holds
-//   A: 256 rows x 64 bytes, 16-byte chunks swizzled by bits 1..4 of the row,
+//   A: 256 rows x 64 bytes, 16-byte chunks swizzled by bits 0..3 of the row,
 //   W: the matching halves (512 bytes) of the 8 weight tiles,
 // copied by buffer_load ... lds; six buffers: while stage ks + 1 is read,
 // stages ks + 2 .. ks + 6 are in flight (the buffer of stage ks is refilled as
@@ -56,9 +56,11 @@ constexpr int Q_WM = 4, Q_NW = 2 * Q_WM;            // waves: 4 x 2
 
 enum { QO_F32 = 0, QO_F16 = 1, QO_BF16 = 2 };
 
-// 16-byte chunk swizzle of a 64-byte LDS row: the 8 rows one ds_read_b128
-// phase touches land on distinct banks.
-__device__ __forceinline__ int qswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 16-byte chunk swizzle of a 64-byte LDS row: the fragment reads (32
+// consecutive rows, chunk 2s + h) hit the LDS without bank conflicts --
+// measured with the bank-conflict counter on that pattern, where
+// ((r >> 1) ^ (r >> 3)) & 3 spent half of the LDS cycles in conflicts.
+__device__ __forceinline__ int qswz(int r) { return (r ^ (r >> 2)) & 3; }
 
 // The 16 signed bytes u - z of two packed words (k in order), z folded into
 // zc = 0x80808080 - z * 0x01010101.

@@ -33,8 +33,11 @@ enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4, GMX4 = 5 };
 // buffer_load_dwordx4 ... lds (no trip through VGPRs): lane i of a wave writes
 // bytes [16i, 16i+16) of a 1 KB LDS run = 16 rows x 64 bytes, so the 16-byte
 // chunk swizzle is applied on the global side (lane i fetches chunk
-// (i & 3) ^ swz(row)).  swz(r) = ((r >> 1) ^ (r >> 3)) & 3 keeps the 8 or 16
-// rows read together by one ds_read_b128 phase on distinct banks.
+// (i & 3) ^ swz(row)).  swz(r) = (r ^ (r >> 2)) & 3: the fragment reads
+// (lane l: row base + l % 32, chunk (l / 32) ^ swz or (2 + l / 32) ^ swz)
+// then hit the LDS without bank conflicts -- measured with the bank-conflict
+// counter on that exact pattern, where ((r >> 1) ^ (r >> 3)) & 3 spent half
+// of the LDS cycles in conflicts.
 // 2 x WN waves (WN = 2: one wave per SIMD; WN = 4: two, so one wave's LDS
 // and memory waits overlap the other's MFMAs); each owns a (BM/2) x (BN/WN)
 // tile of 32x32 MFMA tiles:
@@ -49,7 +52,7 @@ enum { GT = 0, GR = 1, GR128 = 2, GB128 = 3, GMX32 = 4, GMX4 = 5 };
 // ============================================================================
 constexpr int GK = 64;                                           // K bytes per stage
 
-__device__ __forceinline__ int gswz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int gswz(int r) { return (r ^ (r >> 2)) & 3; }
 
 template <int TM, int TN, int MXR>
 struct Frags {
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 
     // ---- fragment addresses: lane l reads chunks h and 2 + h of row l % 32 ----
     // (the same K chunks for A and W, so matching k meet in the MFMA).  The
-    // swizzle of row r depends on bits 1..4 of r only, so fragments 32 rows
+    // swizzle of row r depends on bits 0..3 of r only, so fragments 32 rows
     // apart differ by a constant 2 KB.
     const uint32_t lds0 = lds_addr(lds);
     const int ra0 = wm * WTM + l32, rb0 = BM + wn * WTN + l32;
