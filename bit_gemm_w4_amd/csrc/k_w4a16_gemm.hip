@@ -19,7 +19,7 @@
 // Block tile 256 (rows of X) x 128 (output columns = 8 weight tiles), WM x 2
 // waves, each (256 / WM) x 64 of v_mfma_f32_32x32x16 tiles.  K advances in
 // stages of 64 (half a group); each stage buffer holds
-//   A: 256 rows x 128 bytes, 16-byte chunks XOR-swizzled by (row & 7),
+//   A: 256 rows x 128 bytes, 16-byte chunks XOR-swizzled by xswz(row),
 //   W: the matching halves (512 bytes) of the 8 weight tiles,
 // all copied by buffer_load ... lds; four buffers: while stage ks + 1 is read,
 // stages ks + 2 .. ks + 4 are in flight (the buffer of stage ks is refilled as
@@ -41,6 +41,13 @@
 #include "bg_w4.h"
 
 namespace bg {
+
+// 16-byte chunk swizzle of a 128-byte activation row in LDS.  It depends on
+// bits 0..4 of the row only (fragments 32 rows apart share it), and with it
+// the fragment reads (32 consecutive rows, chunk c ^ xswz) hit the LDS
+// without bank conflicts -- measured with the bank-conflict counter on that
+// read pattern, where row & 7 spent half of the LDS cycles in conflicts.
+__device__ __forceinline__ int xswz(int r) { return (r ^ (r >> 2)) & 7; }
 
 namespace {
 constexpr int PBM = 256, PBN = 128;                 // block tile
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
     for (int t = 0; t < A_LD; ++t) {
         const int j = wave * A_LD + t;                           // 1 KB run = 8 rows
         const int r = 8 * j + (lane >> 3);
-        voff_a[t] = (uint32_t)(r * K * 2) + (uint32_t)((((lane & 7) ^ (r & 7)) << 4));
+        voff_a[t] = (uint32_t)(r * K * 2) + (uint32_t)((((lane & 7) ^ xswz(r)) << 4));
     }
     // W: wave w < 4 copies the stage halves of weight tiles 2w, 2w + 1
     const int ww = wave & 3;
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         const int c = 4 * (s >> 1) + 2 * h + (s & 1);
-        offa[s] = (uint32_t)((wm * WTM + l32) * 128 + ((c ^ (l32 & 7)) << 4));
+        offa[s] = (uint32_t)((wm * WTM + l32) * 128 + ((c ^ xswz(l32)) << 4));
     }
     // W: weight tile wn*4 + 2j + l32/16, slot (16 (s/2) + l32 % 16), words 2h, 2h+1
     const uint32_t offw = (uint32_t)(P_A + (wn * 4 + (l32 >> 4)) * 512 + (l32 & 15) * 16 + 8 * h);
