@@ -82,8 +82,8 @@ def time_graph(g, reps, torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: every GPU box here has one, so --gpus must be 1 "
-              "(the path shards column-parallel across GPUs with no exchange; see the design notes)",
+        print("bench.py measures a single GPU, so --gpus must be 1 (the path would shard column-parallel "
+              "across GPUs, each owning a slice of the output channels, with no exchange between them)",
               file=sys.stderr)
         sys.exit(2)
 
