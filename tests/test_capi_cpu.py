@@ -108,10 +108,12 @@ def test_gemm_w4a16_workspace(L):
     need = L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 0)
     assert need > 0 and need % 16 == 0
     assert L.gemm_w4a16_workspace_bytes(16, 4096, 14336, 3) == 0            # tiled: none
-    # AUTO with a workspace: split-K from M = 8 on wide or deep layers, from
+    # AUTO with a workspace: split-K from M = 8 on deep layers, M = 9 on wide ones, from
     # M = 17 on N > 4096, from M = 24 everywhere; the small-M kernel otherwise
-    assert L.gemm_w4a16_workspace_bytes(7, 28672, 4096, 0) == 0
-    assert L.gemm_w4a16_workspace_bytes(8, 28672, 4096, 0) > 0
+    assert L.gemm_w4a16_workspace_bytes(8, 28672, 4096, 0) == 0
+    assert L.gemm_w4a16_workspace_bytes(9, 28672, 4096, 0) > 0
+    assert L.gemm_w4a16_workspace_bytes(7, 4096, 14336, 0) == 0
+    assert L.gemm_w4a16_workspace_bytes(8, 4096, 14336, 0) > 0
     assert L.gemm_w4a16_workspace_bytes(16, 6144, 4096, 0) == 0
     assert L.gemm_w4a16_workspace_bytes(17, 6144, 4096, 0) > 0
     assert L.gemm_w4a16_workspace_bytes(23, 4096, 4096, 0) == 0
