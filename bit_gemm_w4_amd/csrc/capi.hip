@@ -48,6 +48,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 24;   // N, act_quant rows
 constexpr int64_t kMaxDim = int64_t(1) << 20;    // K, cols
 constexpr int64_t kMaxM = int64_t(65535) * 16;   // GEMM M: grid.y stays below 65536
 constexpr int64_t kMaxGemvM = 256;               // explicit GEMV requests
+constexpr int64_t kI8MaxKExcl = int64_t(1) << 17; // INT8 K bound: K * 2^14 < 2^31
 
 // W4A16: small-M MFMA kernel up to kW4SkinnyMax rows, tiled MFMA kernel beyond;
 // the VALU GEMV is selected explicitly only (BG_ALGO_GEMV).
@@ -312,8 +313,10 @@ static bg_status w8a8_impl(const void* a, const float* a_scales, int a_gran, con
     if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w8a8: M=%lld out of range", M);
     if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w8a8: N=%lld must be a multiple of 16", N);
     if (K < 128 || K > kMaxDim || K % 128) return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld must be a multiple of 128", K);
-    if (in_dtype == BG_I8 && K > 131072)
-        return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld too long for exact INT32 accumulation", K);
+    // |acc| <= K * 128 * 128 must stay below 2^31: K <= 130944 (K = 131072
+    // with every code at -128 would reach exactly 2^31 and wrap)
+    if (in_dtype == BG_I8 && K >= kI8MaxKExcl)
+        return fail(BG_ERR_SHAPE, "gemm_w8a8: K=%lld too long for exact INT32 accumulation (K < 131072)", K);
     if (block && N % 128) return fail(BG_ERR_SHAPE, "gemm_w8a8: BLOCK128 weights need N %% 128 == 0 (N=%lld)", N);
     if (!aligned16(a) || !aligned16(w) || !aligned16(y) || (a_scales && !aligned16(a_scales)) ||
         (w_scales && !aligned16(w_scales)) || (ws && !aligned16(ws)))
@@ -412,8 +415,8 @@ BG_EXPORT bg_status gemm_w8a8_outlier(const int8_t* a, const float* a_scales, co
         return fail_in(fn, BG_ERR_DTYPE, "out_dtype %lld is not BF16/F16/F32", out_dtype);
     if (M < 1 || M > kMaxM) return fail_in(fn, BG_ERR_SHAPE, "M=%lld out of range", M);
     if (N < 16 || N > kMaxRows || N % 16) return fail_in(fn, BG_ERR_SHAPE, "N=%lld must be a multiple of 16", N);
-    if (K < 128 || K > 131072 || K % 128)
-        return fail_in(fn, BG_ERR_SHAPE, "K=%lld must be a multiple of 128 and at most 131072", K);
+    if (K < 128 || K >= kI8MaxKExcl || K % 128)
+        return fail_in(fn, BG_ERR_SHAPE, "K=%lld must be a multiple of 128 and below 131072", K);
     if (!aligned16(a) || !aligned16(w) || !aligned16(y) || !aligned16(a_scales) || !aligned16(w_scales) ||
         (reinterpret_cast<uintptr_t>(x) & 3u) || (reinterpret_cast<uintptr_t>(idx) & 3u) ||
         (reinterpret_cast<uintptr_t>(count) & 3u))

@@ -309,7 +309,7 @@ bg_status act_quant_int8_outlier(const void* x, int x_dtype, int64_t rows, int64
  *   idx, count   the outlier list (device); count is clamped to [0, K] and the
  *                entries to [0, K), so a bad list never reads outside x or w
  *   y            out [M][N], BG_BF16, BG_F16 or BG_F32
- * Requires K % 128 == 0 and K <= 131072, N % 16 == 0, 16-byte aligned a, w,
+ * Requires K % 128 == 0 and K < 131072, N % 16 == 0, 16-byte aligned a, w,
  * y and scales, 4-byte aligned x, idx and count.  No workspace, no K split.
  */
 bg_status gemm_w8a8_outlier(const int8_t* a, const float* a_scales, const int8_t* w, const float* w_scales,
@@ -331,8 +331,9 @@ bg_status gemm_w8a8_outlier(const int8_t* a, const float* a_scales, const int8_t
  *   out_dtype BG_BF16, BG_F16 or BG_F32 (round-to-nearest-even); BG_I32
  *            (in_dtype BG_I8 only) writes the raw INT32 accumulators
  *   y        out [M][N] of out_dtype
- * Requires 1 <= M <= 1048560, N % 16 == 0, K % 128 == 0, K <= 131072 for BG_I8
- * (so |acc| <= K * 128 * 128 < 2^31); BLOCK128 needs N % 128 == 0.
+ * Requires 1 <= M <= 1048560, N % 16 == 0, K % 128 == 0, K < 131072 (at most
+ * 130944) for BG_I8, so |acc| <= K * 128 * 128 < 2^31 even with every code at
+ * -128; BLOCK128 needs N % 128 == 0.
  */
 bg_status gemm_w8a8(const void* a, const float* a_scales, int a_gran,
                     const void* w, const float* w_scales, int w_gran,

@@ -157,6 +157,8 @@ def test_gemm_w8a8_validation(L):
     assert f(P, P, R, P, Q, R, I8, 4, 24, 128, P, BF16, 0, None) == E_SHAPE     # N % 16
     assert f(P, P, R, P, Q, R, I8, 4, 16, 192, P, BF16, 0, None) == E_SHAPE     # K % 128
     assert f(P, P, R, P, Q, R, I8, 4, 16, 131072 + 128, P, BF16, 0, None) == E_SHAPE
+    # K = 131072 with every code at -128 would sum to exactly 2^31: rejected
+    assert f(P, P, R, P, Q, R, I8, 4, 16, 131072, P, BF16, 0, None) == E_SHAPE
     assert f(P, P, R, P, Q, R, I8, 4, 16, 128, P + 1, BF16, 0, None) == E_ALIGN
     assert f(P, P, R, P, Q, R, I8, 4, 16, 128, P, BF16, 5, None) == E_UNSUP     # algo
 
@@ -195,3 +197,15 @@ def test_outlier_workspace_bytes(L):
     assert L.act_quant_outlier_workspace_bytes(5, 128) == (5 * 128 + 128) * 4
     assert L.act_quant_outlier_workspace_bytes(16, 100) == 0            # cols % 128
     assert L.act_quant_outlier_workspace_bytes(0, 128) == 0
+
+
+def test_outlier_gemm_int8_k_bound(L):
+    # the INT8 part accumulates K products of at most 128 * 128 in INT32: K = 131072
+    # could reach 2^31, so the largest K accepted is 130944
+    f = L.gemm_w8a8_outlier
+    P = 1 << 20
+    R = 1
+    assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 131072, P, BF16, None) == E_SHAPE
+    assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 131072 + 128, P, BF16, None) == E_SHAPE
+    assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 192, P, BF16, None) == E_SHAPE    # K % 128
+    assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 130944, P + 4, BF16, None) == E_ALIGN   # K passes
