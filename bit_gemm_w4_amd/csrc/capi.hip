@@ -3,8 +3,10 @@
 // §31 fallback_policy) and kernel dispatch by M ("small batch and large
 // prefill get different kernels", §24).  Validation touches no HIP API, so
 // a rejected call never reaches the device.
+#include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/bitgemm.h"
 #include "bg_internal.h"
@@ -189,6 +191,85 @@ BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
                                const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
                                void* stream) {
     return gemm_w4a16_ex(x, x_dtype, M, K, qweight, scales, zeros, N, group, y, BG_ALGO_AUTO, stream);
+}
+
+// ---- gemm_w4a16_noalloc: split-K partials in a static device array ----
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc).  `scratch` lives in the code
+// object: every GPU that runs the library holds its own copy, at its own
+// address, until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol); it uses the
+// device address hipGetSymbolAddress returns, looked up once per device with
+// that device current.
+static __device__ __align__(256) uint8_t scratch[BG_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+bg_status hip_fail(const char* what, hipError_t e) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "gemm_w4a16_noalloc: %s: %s", what, hipGetErrorString(e));
+    return BG_ERR_HIP;
+}
+
+// Device address of `scratch` on the device `stream` runs on, which must be
+// the current device.
+bg_status scratch_address(void* stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail("hipGetDevice", e);
+    if (dev < 0 || dev >= kMaxDevices) return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16_noalloc: device %lld out of range", dev);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) return hip_fail("hipStreamGetDevice", e);
+        if (sdev != dev)
+            return fail(BG_ERR_UNSUPPORTED, "gemm_w4a16_noalloc: the stream is on device %lld, the current device is %lld",
+                        sdev, dev);
+    }
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) return hip_fail("hipGetSymbolAddress(scratch)", e);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BG_OK;
+}
+
+}  // namespace
+
+BG_EXPORT bg_status gemm_w4a16_noalloc(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
+                                       const uint16_t* scales, const uint8_t* zeros, int64_t N, int group, void* y,
+                                       void* stream) {
+    // the shape checks of gemm_w4a16 come first, so the size asked of the
+    // scratch is only computed for an eligible call
+    if (!x || !qweight || !scales || !y) return fail(BG_ERR_NULL, "gemm_w4a16: x, qweight, scales and y must be non-NULL");
+    if (M < 1 || M > kMaxM) return fail(BG_ERR_SHAPE, "gemm_w4a16: M=%lld out of range", M);
+    if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w4a16: N=%lld must be a multiple of 16", N);
+    if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a16: K=%lld must be a multiple of 256", K);
+    const int algo = w4_auto_algo_ws(M, N, K);
+    const int64_t need = algo != BG_ALGO_SPLITK ? 0
+                         : M > kW4SkinnyMax     ? bg::w4a16_gemm_split(M, N, K).ws_bytes
+                                                : bg::w4a16_splitk_workspace(M, N, K);
+    if (need > BG_NOALLOC_SCRATCH_BYTES)
+        return fail(BG_ERR_WORKSPACE,
+                    "gemm_w4a16_noalloc: this shape needs %lld bytes of scratch; the static scratch holds %lld "
+                    "(use gemm_w4a16_ws with a larger workspace)",
+                    need, (long long)BG_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0) {
+        const bg_status st = scratch_address(stream, &ws);
+        if (st != BG_OK) return st;
+    }
+    return w4a16_impl(x, x_dtype, M, K, qweight, scales, zeros, N, group, y, ws, need, true, algo, stream);
 }
 
 static bg_status act_quant(const char* name, bool fp8, const void* x, int x_dtype, int64_t rows, int64_t cols,

@@ -24,7 +24,7 @@ ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED, ALGO_SPLITK = 0, 1, 2, 3, 4
 PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
-    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
+    "w4_pack", "gemm_w4a16", "gemm_w4a16_ex", "gemm_w4a16_ws", "gemm_w4a16_noalloc", "gemm_w4a16_workspace_bytes", "act_quant_int8", "act_quant_fp8",
     "act_quant_int8_smooth", "act_quant_fp8_smooth", "act_quant_mxfp8", "gemm_mxfp8", "act_quant_mxfp4", "gemm_mxfp4", "act_quant_int8_outlier", "act_quant_outlier_workspace_bytes",
     "gemm_w8a8_outlier", "gemm_w8a8",
     "gemm_w8a8_ex", "gemm_w8a8_ws", "gemm_w8a8_workspace_bytes", "gemm_w4a8", "gemm_w4a8_ws", "gemm_w4a8_workspace_bytes",
@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "gemm_w4a16": [P, I, I64, I64, P, P, P, I64, I, P, P],
             "gemm_w4a16_ex": [P, I, I64, I64, P, P, P, I64, I, P, I, P],
             "gemm_w4a16_ws": [P, I, I64, I64, P, P, P, I64, I, P, P, I64, I, P],
+            "gemm_w4a16_noalloc": [P, I, I64, I64, P, P, P, I64, I, P, P],
             "gemm_w4a16_workspace_bytes": [I64, I64, I64, I],
             "act_quant_int8": [P, I, I64, I64, I, P, P, P],
             "act_quant_fp8": [P, I, I64, I64, I, P, P, P],
@@ -199,6 +200,27 @@ def gemm_w4a16(x: torch.Tensor, packed: PackedW4, out: torch.Tensor | None = Non
     _check(L.gemm_w4a16_ws(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales), _ptr(packed.zeros),
                            packed.N, packed.group, _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(), algo,
                            _stream(stream)), "gemm_w4a16")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # BG_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_w4a16_noalloc(x: torch.Tensor, packed: PackedW4, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Y = X W^T through gemm_w4a16_noalloc: the split-K partials go to the
+    library's static per-device scratch, so the call allocates nothing (the
+    caller supplies `out`).  Calls on one GPU must not overlap in time."""
+    M, K = x.shape
+    if K != packed.K:
+        raise ValueError(f"gemm_w4a16_noalloc: x has K={K}, weights K={packed.K}")
+    dt = _TORCH_DT.get(x.dtype)
+    if dt not in (F16, BF16):
+        raise ValueError(f"gemm_w4a16_noalloc: activations must be float16/bfloat16, got {x.dtype}")
+    if out.shape != (M, packed.N) or out.dtype != x.dtype:
+        raise ValueError(f"gemm_w4a16_noalloc: out must be [{M}, {packed.N}] of {x.dtype}")
+    _check(lib().gemm_w4a16_noalloc(_ptr(x), dt, M, K, _ptr(packed.qweight), _ptr(packed.scales),
+                                    _ptr(packed.zeros), packed.N, packed.group, _ptr(out), _stream(stream)),
+           "gemm_w4a16_noalloc")
     return out
 
 

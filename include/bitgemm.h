@@ -154,6 +154,33 @@ bg_status gemm_w4a16_ws(const void* x, int x_dtype, int64_t M, int64_t K,
 int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo);
 
 /*
+ * gemm_w4a16_noalloc -- gemm_w4a16_ws with BG_ALGO_AUTO for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The split-K partials go to a
+ * static device array of BG_NOALLOC_SCRATCH_BYTES inside the library instead
+ * of a caller workspace; every GPU the library runs on holds its own copy
+ * until the process ends.  Its address is looked up (hipGetSymbolAddress)
+ * on the first call on each device; after that a call enqueues exactly the
+ * kernels gemm_w4a16_ws enqueues for the same shape, so results are bit for
+ * bit the same.  The call allocates and frees nothing.
+ *
+ *   arguments, layouts and results as gemm_w4a16; `stream` must belong to
+ *   the current device (BG_ERR_UNSUPPORTED otherwise).
+ * Errors as gemm_w4a16_ws, plus BG_ERR_WORKSPACE when the shape needs more
+ * than BG_NOALLOC_SCRATCH_BYTES (gemm_w4a16_workspace_bytes(M, N, K,
+ * BG_ALGO_AUTO) tells the size in advance), and BG_ERR_HIP if the address
+ * lookup fails.
+ * All calls on one GPU share its scratch array: calls that overlap in time on
+ * the same GPU (different streams, or different host threads without
+ * ordering) race and give wrong results.  The array needs no clearing: each
+ * call writes every partial it later reads.
+ */
+#define BG_NOALLOC_SCRATCH_BYTES (32LL << 20)
+bg_status gemm_w4a16_noalloc(const void* x, int x_dtype, int64_t M, int64_t K,
+                             const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
+                             int64_t N, int group, void* y, void* stream);
+
+/*
  * act_quant_int8 -- dynamic symmetric INT8 quantization of a [rows][cols]
  * tensor: per unit of granularity `gran`, s = amax/127 (binary32; s = 1 for an
  * all-zero unit) and q = clamp(round(x/s), -128, 127), round half to even.

@@ -209,3 +209,18 @@ def test_outlier_gemm_int8_k_bound(L):
     assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 131072 + 128, P, BF16, None) == E_SHAPE
     assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 192, P, BF16, None) == E_SHAPE    # K % 128
     assert f(P, P, P, P, R, P, BF16, P, P, 4, 16, 130944, P + 4, BF16, None) == E_ALIGN   # K passes
+
+
+def test_noalloc_rejects_before_touching_the_device(L):
+    # shapes whose split-K partials exceed the static scratch are refused on
+    # the host, with the size in the message; so are the usual shape errors
+    f = L.gemm_w4a16_noalloc
+    P = 1 << 20
+    limit = 32 << 20
+    assert L.gemm_w4a16_workspace_bytes(64, 28672, 4096, 0) > limit
+    assert f(P, BF16, 64, 4096, P, P, P, 28672, 128, P, None) == E_WS
+    assert b"scratch" in L.bg_last_error()
+    assert f(None, BF16, 16, 4096, P, P, P, 4096, 128, P, None) == E_NULL
+    assert f(P, BF16, 0, 4096, P, P, P, 4096, 128, P, None) == E_SHAPE
+    assert f(P, BF16, 16, 4096 + 128, P, P, P, 4096, 128, P, None) == E_SHAPE
+    assert f(P, BF16, 16, 4096, P, P, P, 4100, 128, P, None) == E_SHAPE
