@@ -756,3 +756,54 @@ def test_outlier_rejects(ops):
         ops.gemm_w8a8_outlier(q, sa, w, sw, 7, x, idx, cnt)                                  # w_gran
     with pytest.raises(ValueError):
         ops.gemm_w8a8_outlier(q, sa, w, sw, ops.GRAN_ROW, x, idx[:100], cnt)                 # idx room
+
+
+# ---- the launch configurations the benchmark times, at full size ----
+# Grids of many rounds (thousands of blocks) on the projection shapes, with
+# output rows sampled in the first, a middle and the last row tile of every
+# size (the oracle computes only those rows; the per-tensor FP8 scale still
+# comes from the oracle's amax over the whole activation tensor).
+
+def _sample_rows(M, tile=256):
+    rows = {0, 1, M // 2, M - 1}
+    if M > tile:
+        rows |= {tile - 1, tile, M - tile, M - tile - 1}
+    return sorted(r for r in rows if 0 <= r < M)
+
+
+@pytest.mark.parametrize("name,M", [("gate_up", 2048), ("down", 4096), ("qkv", 1024), ("o", 512)])
+def test_w4a16_prefill_multiround(ops, orc, name, M):
+    """The large-M W4A16 path (AUTO with the cached workspace, as the
+    benchmark's crossover and prefill rows run it) on grids of many rounds:
+    gate_up at M = 2048 is 1,792 tiles of 256 x 128."""
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _w4a16_case(ops, orc, M, N, K, "bf16", True, 0, seed=11, rows=_sample_rows(M))
+
+
+@pytest.mark.parametrize("M", [512, 2048, 8192])
+@pytest.mark.parametrize("name", ["gate_up", "down"])
+@pytest.mark.parametrize("variant", ["tensor", "block"])
+def test_w8a8_fp8_config_sizes(ops, orc, name, variant, M):
+    """FP8 E4M3 W8A8 at every M of the FP8 prefill workload, (a) per-tensor and
+    (b) 128 x 128 weight blocks with 1 x 128 activation groups."""
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    a_gran, w_gran = (0, 0) if variant == "tensor" else (2, 3)
+    _w8a8_case(ops, orc, M, N, K, True, a_gran, w_gran, 0, rows=_sample_rows(M), seed=M)
+
+
+@pytest.mark.parametrize("M", [512, 4096])
+@pytest.mark.parametrize("path", ["w4a16", "int8", "fp8", "w4a8"])
+def test_crossover_points(ops, orc, path, M):
+    """Large-batch points of the crossover sweep on the down projection
+    (K = 14336, N = 4096), each path through the dispatch the sweep times."""
+    K, N = synth.LLAMA3_8B_SHAPES["down"]
+    rows = _sample_rows(M)
+    if path == "w4a16":
+        _w4a16_case(ops, orc, M, N, K, "bf16", True, 0, seed=21, rows=rows)
+    elif path == "int8":
+        _w8a8_case(ops, orc, M, N, K, False, 1, 1, 0, out_dtype=torch.int32, rows=rows, seed=22)
+        _w8a8_case(ops, orc, M, N, K, False, 1, 1, 0, rows=rows, seed=22)
+    elif path == "fp8":
+        _w8a8_case(ops, orc, M, N, K, True, 0, 0, 0, rows=rows, seed=23)
+    else:
+        _w4a8_case(ops, orc, M, N, K, True, 1, rows=rows, seed=24)
