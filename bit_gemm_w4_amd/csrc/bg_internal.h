@@ -44,6 +44,9 @@ const char* launch_act_quant(const void* x, int dt, int64_t R, int64_t C, int gr
 // W4A16 kernels (x_bf16: activations/output are BF16, else FP16).
 // The VALU GEMV stages up to 4 activation rows of length K in LDS.
 bool w4a16_gemv_supported(int64_t M, int64_t K);
+// The small-M kernels stage the block's group scales and zero-points in LDS
+// for all of K: they take K up to this bound (larger K goes to the tiled kernel).
+constexpr int64_t kW4DecodeMaxK = 65536;
 const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                        const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s);
 const char* launch_w4a16_skinny(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,

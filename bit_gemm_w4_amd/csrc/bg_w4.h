@@ -54,6 +54,40 @@ __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t D[4]) {
     D[3] = and_or(w >> 12, 0x000F000Fu, m);
 }
 
+// The 16 pairs of a lane's 16-byte slot: D[kk][p] = pair p of word kk.  The
+// three nibble shifts run on word pairs as 64-bit shifts (one instruction
+// for two words; the bits a shift moves across the word boundary land above
+// bit 19 and are masked off).  The shift is inline assembly only because the
+// compiler splits 64-bit shifts whose halves are used separately; its
+// result feeds and_or (VALU), never an MFMA directly.
+__device__ __forceinline__ uint64_t shr64(uint64_t v, int sh) {
+    uint64_t r;
+    if (sh == 4) asm("v_lshrrev_b64 %0, 4, %1" : "=v"(r) : "v"(v));
+    else if (sh == 8) asm("v_lshrrev_b64 %0, 8, %1" : "=v"(r) : "v"(v));
+    else asm("v_lshrrev_b64 %0, 12, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void dequant_tile(const uint4& w, uint32_t D[4][4]) {
+    constexpr uint32_t m = W4Magic<BF16>::bits;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = wd[2 * h], hi = wd[2 * h + 1];
+        const uint64_t v = ((uint64_t)hi << 32) | lo;
+        const uint64_t v4 = shr64(v, 4), v8 = shr64(v, 8), v12 = shr64(v, 12);
+        D[2 * h][0] = and_or(lo, 0x000F000Fu, m);
+        D[2 * h][1] = and_or((uint32_t)v4, 0x000F000Fu, m);
+        D[2 * h][2] = and_or((uint32_t)v8, 0x000F000Fu, m);
+        D[2 * h][3] = and_or((uint32_t)v12, 0x000F000Fu, m);
+        D[2 * h + 1][0] = and_or(hi, 0x000F000Fu, m);
+        D[2 * h + 1][1] = and_or((uint32_t)(v4 >> 32), 0x000F000Fu, m);
+        D[2 * h + 1][2] = and_or((uint32_t)(v8 >> 32), 0x000F000Fu, m);
+        D[2 * h + 1][3] = and_or((uint32_t)(v12 >> 32), 0x000F000Fu, m);
+    }
+}
+
 // Difference of two FP16 pairs (one v_pk_add_f16 with negation).
 __device__ __forceinline__ uint32_t sub_h2(uint32_t a, uint32_t b) {
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, a) - __builtin_bit_cast(half2_t, b));

@@ -58,7 +58,8 @@ constexpr int64_t kW4GemvMax = 0;
 constexpr int64_t kW4SkinnyMax = 64;
 constexpr int64_t kW8SkinnyMax = 32;
 
-int w4_auto_algo(int64_t M) {
+int w4_auto_algo(int64_t M, int64_t K) {
+    if (K > bg::kW4DecodeMaxK) return BG_ALGO_TILED;
     if (M <= kW4GemvMax) return BG_ALGO_GEMV;
     if (M <= kW4SkinnyMax) return BG_ALGO_SKINNY;
     return BG_ALGO_TILED;
@@ -99,7 +100,8 @@ int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
     // (measured: gate_up at M = 8 is 5 % faster unsplit, from M = 12 split;
     // down, K = 14336, is faster split at every M >= 8)
     const bool split = (M >= 8 && K >= 8192) || (M > 8 && N >= 16384) || (M > 16 && N > 4096) || M >= 24;
-    return split ? BG_ALGO_SPLITK : BG_ALGO_SKINNY;
+    if (split) return BG_ALGO_SPLITK;
+    return K > bg::kW4DecodeMaxK ? BG_ALGO_TILED : BG_ALGO_SKINNY;
 }
 
 }  // namespace
@@ -123,8 +125,8 @@ BG_EXPORT bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, in
 }
 
 BG_EXPORT int gemm_w4a16_algo(int64_t M, int64_t N, int64_t K, int x_dtype) {
-    (void)N; (void)K; (void)x_dtype;
-    return w4_auto_algo(M);
+    (void)N; (void)x_dtype;
+    return w4_auto_algo(M, K);
 }
 
 static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
@@ -140,9 +142,11 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
     if (!aligned16(x) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) || (zeros && !aligned16(zeros)) ||
         (ws && !aligned16(ws)))
         return fail(BG_ERR_ALIGN, "gemm_w4a16: pointers must be 16-byte aligned");
-    if (algo == BG_ALGO_AUTO) algo = with_ws ? w4_auto_algo_ws(M, N, K) : w4_auto_algo(M);
+    if (algo == BG_ALGO_AUTO) algo = with_ws ? w4_auto_algo_ws(M, N, K) : w4_auto_algo(M, K);
     if (algo == BG_ALGO_GEMV && (M > kMaxGemvM || !bg::w4a16_gemv_supported(M, K)))
-        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 20000 (M=%lld, K=%lld)", M, K);
+        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 16640 (M=%lld, K=%lld)", M, K);
+    if (algo == BG_ALGO_SKINNY && K > bg::kW4DecodeMaxK)
+        return fail(BG_ERR_SHAPE, "gemm_w4a16: the small-M kernel takes K <= 65536 (K=%lld)", K);
     if (algo == BG_ALGO_SPLITK) {
         if (!with_ws) return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernels need gemm_w4a16_ws");
         const int64_t need =

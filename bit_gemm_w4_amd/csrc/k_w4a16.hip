@@ -52,9 +52,18 @@ namespace bg {
 // after group g is consumed.  The vector-memory counter retires loads in issue
 // order, so consuming group g waits only for g's own loads.
 //
+// Group scales and zero-points: each wave copies those of its own groups
+// (32 bytes of scales and the 16 zero-point bytes per tile and group) into a
+// wave-private LDS area with a few 16-byte loads before its first weight
+// stage, so the stream of global loads is the 1 KB weight tiles alone (a
+// tiny scattered scale and zero-point request per tile and group measured
+// about 7 % of the call on the widest layer).  No block barrier waits for
+// these copies: a wave reads only what its own lanes wrote, and the in-order
+// memory counter has released them before the wave's first weight stage.
+//
 // XLDS: the block first copies its activation rows (all of K) into LDS and the
 // activation operand is read from there (ds_read, a separate counter), so a
-// stage holds only 16 bytes of weights plus scale/zero per tile and the
+// stage holds only the 16 bytes of weights per tile and lane and the
 // pipeline runs deep.  Without XLDS the activation fragments travel in the
 // stage registers and the pipeline is shallower.  Rows >= M only ever feed
 // output rows >= M (MFMA row i reads only operand row i), so lanes for such
@@ -63,8 +72,6 @@ template <int TM, int TN, bool XLDS>
 struct DecStage {
     uint4 w[TN];
     uint4 a[XLDS ? 1 : TM][XLDS ? 1 : 4];
-    uint32_t s[TN];
-    uint32_t z[TN];
 };
 
 template <bool BF16, int TM, int TN, int NW, bool XLDS, int VROWS>
@@ -72,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
                                                           const uint32_t* __restrict__ qw,
                                                           const uint16_t* __restrict__ sc,
                                                           const uint8_t* __restrict__ zr, int64_t N,
-                                                          uint16_t* __restrict__ y) {
+                                                          uint16_t* __restrict__ y, uint64_t rcp) {
     constexpr bool VALU = VROWS > 0;
     static_assert(!VALU || (XLDS && TM == 1), "the VALU product reads activations from LDS");
     // groups in flight per wave: 4 for two-tile blocks; 3 for one-tile blocks,
@@ -101,7 +108,14 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     const int64_t rows = (M - m0) < BAND ? (M - m0) : BAND;           // real rows of this block
     const int64_t xstride = K + 8;                                    // LDS row pitch in halves
     const int64_t x_bytes = XLDS ? rows * xstride * 2 : 0;
-    float* sxt = reinterpret_cast<float*>(dyn_lds + x_bytes);         // VALU: Sx[row][group]
+    // LDS: [per wave: its groups' scales and zero bytes][X rows][VALU: Sx table]
+    // A (group i of the wave, tile j) record is 48 bytes: 16 FP16 scales, then
+    // the 16 zero-point bytes of the group pair.
+    const bool has_z = zr != nullptr;
+    const int nmax = (ngroups + NW - 1) / NW;                         // most groups of any wave
+    uint8_t* wsz = dyn_lds + wave * nmax * TN * 48;                   // this wave's records
+    uint8_t* x_l = dyn_lds + NW * nmax * TN * 48;
+    float* sxt = reinterpret_cast<float*>(x_l + x_bytes);             // VALU: Sx[row][group]
 
     // Buffer descriptors over this block's tiles: per-lane offsets live in
     // VGPRs, the group offset is wave-uniform (scalar unit), and reads past the
@@ -111,7 +125,6 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
                                                       (int)(my_tiles * ngroups * 1024), 0x00020000);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc + t0 * ngroups * 16), (short)0,
                                                       (int)(my_tiles * ngroups * 32), 0x00020000);
-    const bool has_z = zr != nullptr;
     const auto rz = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(has_z ? zr + t0 * (ngroups >> 1) * 16 : zr),
                                                       (short)0, has_z ? (int)(my_tiles * (ngroups >> 1) * 16) : 0,
                                                       0x00020000);
@@ -132,12 +145,9 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     auto issue = [&](DecStage<TM, TN, XLDS>& st, int i) {
         const int g = (i < i_last ? i : i_last) * NW + wave;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int j = 0; j < TN; ++j)
             st.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                     rw, lane * 16, (j * ngroups + g) * 1024, 0));
-            st.s[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, l16 * 2, (j * ngroups + g) * 32, 0);
-            st.z[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, (j * (ngroups >> 1) + (g >> 1)) * 16, 0);
-        }
         if constexpr (!XLDS) {
 #pragma unroll
             for (int ii = 0; ii < TM; ++ii)
@@ -149,10 +159,35 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
         }
     };
 
+    // This wave's scale and zero records: 16 records per pass of 64 lanes,
+    // lane = 4 * record + part (parts 0 and 1: the two 16-byte halves of the
+    // scales; part 2: the zero bytes; part 3 idle).
+    const int nrec = n_mine * TN;
+    auto sz_issue = [&](int r0, uint4& v) {
+        const int rec = r0 + (lane >> 2), part = lane & 3;
+        const int i = rec / TN, j = rec - i * TN;
+        const int g = i * NW + wave;
+        if (rec < nrec && part < 2)
+            v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (j * ngroups + g) * 32 + part * 16,
+                                                                                 0, 0));
+        else if (rec < nrec && part == 2 && has_z)
+            v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rz, (j * (ngroups >> 1) + (g >> 1)) * 16, 0, 0));
+    };
+    auto sz_store = [&](int r0, const uint4& v) {
+        const int rec = r0 + (lane >> 2), part = lane & 3;
+        if (rec < nrec && part < 3) *reinterpret_cast<uint4*>(wsz + rec * 48 + part * 16) = v;
+    };
+    uint4 szv = uint4{0, 0, 0, 0};
+    sz_issue(0, szv);
+
     // XLDS: rows [m0, m0 + rows) of X are copied into LDS in 16-byte chunks,
     // XB per thread in flight together (one memory round trip per batch).  The
     // first batch is requested before the weight stages, so that the
-    // in-order memory counter releases it first.
+    // in-order memory counter releases it first.  Chunk c is row c / cpr,
+    // found by a multiply with rcp = ceil(2^40 / cpr) (computed on the host):
+    // exact for c < 2^21 and cpr <= 2^17, which K <= 2^20 and at most 16
+    // rows guarantee.
     const int cpr = (int)(K >> 3);                                     // chunks per row
     const int total = XLDS ? (int)rows * cpr : 0;
     auto x_load = [&](uint4 (&v)[XB], int c0) {
@@ -167,8 +202,8 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
         for (int u = 0; u < XB; ++u) {
             const int c = c0 + u * NW * 64;
             if (c < total) {
-                const int r = c / cpr, kc = c - r * cpr;
-                *reinterpret_cast<uint4*>(dyn_lds + ((int64_t)r * xstride + kc * 8) * 2) = v[u];
+                const int r = (int)(((uint64_t)c * rcp) >> 40), kc = c - r * cpr;
+                *reinterpret_cast<uint4*>(x_l + ((int64_t)r * xstride + kc * 8) * 2) = v[u];
             }
         }
     };
@@ -179,6 +214,10 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue(stage[s], s);
 
+    // X first (it is shared by the block, and usually cache-resident), then
+    // this wave's own records: only the block barrier waits for the X copy,
+    // and each wave waits for its scale load alone, which the memory counter
+    // returns before the wave's first weight stage
     if constexpr (XLDS) {
         x_store(xv0, threadIdx.x);
         for (int c0 = threadIdx.x + XB * NW * 64; c0 < total; c0 += XB * NW * 64) {
@@ -187,17 +226,23 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
             x_store(v, c0);
         }
         __syncthreads();
-        if constexpr (VALU) {
-            // Sx[row][g]: sum of the 128 activations of each group
-            for (int64_t e = threadIdx.x; e < rows * ngroups; e += NW * 64) {
-                const int64_t r = e / ngroups, g = e - r * ngroups;
-                const uint32_t* p = reinterpret_cast<const uint32_t*>(dyn_lds + (r * xstride + g * 128) * 2);
-                float sum = 0.0f;
-                for (int k2 = 0; k2 < 64; ++k2) sum = dot2<BF16>(p[k2], ONE2, sum);
-                sxt[e] = sum;
-            }
-            __syncthreads();
+    }
+    sz_store(0, szv);
+    for (int r0 = 16; r0 < nrec; r0 += 16) {
+        uint4 v = uint4{0, 0, 0, 0};
+        sz_issue(r0, v);
+        sz_store(r0, v);
+    }
+    if constexpr (VALU) {
+        // Sx[row][g]: sum of the 128 activations of each group
+        for (int64_t e = threadIdx.x; e < rows * ngroups; e += NW * 64) {
+            const int64_t r = e / ngroups, g = e - r * ngroups;
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(x_l + (r * xstride + g * 128) * 2);
+            float sum = 0.0f;
+            for (int k2 = 0; k2 < 64; ++k2) sum = dot2<BF16>(p[k2], ONE2, sum);
+            sxt[e] = sum;
         }
+        __syncthreads();
     }
 
     float4_t acc[VALU ? 1 : TM][TN];
@@ -210,25 +255,23 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
         for (int b = 0; b < (VALU ? VROWS : 1); ++b) vacc[j][b] = 0.0f;
     }
 
-    auto consume = [&](const DecStage<TM, TN, XLDS>& st, int g) {
+    auto consume = [&](const DecStage<TM, TN, XLDS>& st, int i) {
+        const int g = i * NW + wave;
         float scale[TN], corr[TN];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            scale[j] = f16_to_f32(st.s[j] & 0xFFFFu);
-            corr[j] = MV + (float)(has_z ? (st.z[j] >> (4 * (g & 1))) & 0xF : 8u);
+            const uint8_t* rec = wsz + (i * TN + j) * 48;
+            scale[j] = f16_to_f32(*reinterpret_cast<const uint16_t*>(rec + l16 * 2));
+            corr[j] = MV + (float)(has_z ? (rec[32 + l16] >> (4 * (g & 1))) & 0xF : 8u);
         }
         if constexpr (VALU) {
             uint32_t D[TN][4][4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const uint32_t wd[4] = {st.w[j].x, st.w[j].y, st.w[j].z, st.w[j].w};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) dequant_word<BF16>(wd[kk], D[j][kk]);
-            }
+            for (int j = 0; j < TN; ++j) dequant_tile<BF16>(st.w[j], D[j]);
 #pragma unroll
             for (int b = 0; b < VROWS; ++b) {
                 if (b >= rows) break;
-                const uint8_t* xr = dyn_lds + (b * xstride + (int64_t)g * 128 + q * 32) * 2;
+                const uint8_t* xr = x_l + (b * xstride + (int64_t)g * 128 + q * 32) * 2;
                 uint4 xv[4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) xv[kk] = *reinterpret_cast<const uint4*>(xr + kk * 16);
@@ -255,19 +298,21 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
 #pragma unroll
                 for (int j = 0; j < TN; ++j) part[i][j] = float4_t{0, 0, 0, 0};
             }
+            uint32_t D[TN][4][4];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) dequant_tile<BF16>(st.w[j], D[j]);
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 uint32_t bfrag[TN][4];
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const uint32_t w = kk == 0 ? st.w[j].x : kk == 1 ? st.w[j].y : kk == 2 ? st.w[j].z : st.w[j].w;
-                    dequant_word<BF16>(w, bfrag[j]);
-                }
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) bfrag[j][r] = D[j][kk][r];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     uint4 av;
                     if constexpr (XLDS)
-                        av = *reinterpret_cast<const uint4*>(dyn_lds +
+                        av = *reinterpret_cast<const uint4*>(x_l +
                                                              (arow[i] * xstride + (int64_t)g * 128 + q * 32 + kk * 8) * 2);
                     else
                         av = st.a[i][kk];
@@ -289,13 +334,13 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     for (int i = 0; i < n_mine; i += STAGES) {
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) {
-            if (i + s < n_mine) consume(stage[s], (i + s) * NW + wave);
+            if (i + s < n_mine) consume(stage[s], i + s);
             issue(stage[s], i + s + STAGES);
         }
     }
 
-    // ---- sum the NW partial tiles through LDS (reusing the activation space) ----
-    if constexpr (XLDS) __syncthreads();
+    // ---- sum the NW partial tiles through LDS (reusing the staging space) ----
+    __syncthreads();
     if constexpr (VALU) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -562,11 +607,16 @@ static void allow_lds(Kern kernel, size_t bytes) {
                                   (int)bytes);
 }
 
-// LDS bytes of the decode kernel: staged activation rows (+ Sx table for the
-// VALU product) or the cross-wave reduction buffer, whichever is larger.
-static int64_t decode_lds(int tile_floats, int NW, bool xlds, bool valu, int64_t rows, int64_t K) {
+// LDS bytes of the decode kernel: the block's scales and zero bytes, then the
+// staged activation rows (+ Sx table for the VALU product), or the
+// cross-wave reduction buffer, whichever is larger.
+static int64_t decode_scale_lds(int TN, int NW, int64_t K) {
+    return (int64_t)NW * (((K >> 7) + NW - 1) / NW) * TN * 48;
+}
+static int64_t decode_lds(int tile_floats, int NW, int TN, bool xlds, bool valu, int64_t rows, int64_t K) {
     const int64_t red = (int64_t)NW * tile_floats * 4;
-    const int64_t xb = xlds ? rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) : 0;
+    const int64_t xb = decode_scale_lds(TN, NW, K) +
+                       (xlds ? rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) : 0);
     return red > xb ? red : xb;
 }
 
@@ -577,11 +627,13 @@ static const char* decode_cfg(const void* x, int64_t M, int64_t K, const uint32_
     constexpr int TILE_FLOATS = VROWS > 0 ? TN * VROWS * 64 : TM * TN * 4 * 64;
     dim3 grid((unsigned)(((N >> 4) + TN - 1) / TN), (unsigned)((M + BAND - 1) / BAND));
     const int64_t rows = M < BAND ? M : BAND;
-    const size_t lds = (size_t)decode_lds(TILE_FLOATS, NW, XLDS, VROWS > 0, rows, K);
+    const size_t lds = (size_t)decode_lds(TILE_FLOATS, NW, TN, XLDS, VROWS > 0, rows, K);
     auto kern = k_w4a16_decode<BF16, TM, TN, NW, XLDS, VROWS>;
     allow_lds(kern, lds);
+    const uint64_t cpr = (uint64_t)(K >> 3);
+    const uint64_t rcp = ((uint64_t(1) << 40) + cpr - 1) / cpr;
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, static_cast<const uint16_t*>(x), M, K, qw, sc, zr, N,
-                       static_cast<uint16_t*>(y));
+                       static_cast<uint16_t*>(y), rcp);
     return kname("k_w4a16_decode", BF16, TM, TN, NW, XLDS, VROWS);
 }
 
@@ -608,8 +660,9 @@ static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t
     return decode_cfg<BF16, TM, TN, 1, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
 }
 
+// (TN = 4 tiles, 16 waves: the largest scale area of any configuration)
 static bool xlds_fits(int64_t rows, int64_t K, bool valu) {
-    return rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
+    return decode_scale_lds(4, 16, K) + rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
 }
 
 // Two weight tiles per block on wide layers, and from M = 9 on N > 4096 (the

@@ -108,7 +108,10 @@ bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, i
  *   qweight, scales, zeros   as produced by w4_pack (zeros NULL = symmetric)
  *   y        out [M][N] of x_dtype
  * Requires 1 <= M <= 1048560, N % 16 == 0, K % 256 == 0, group == 128
- * (BG_ALGO_GEMV: M <= 256).  Small M runs the bandwidth-bound decode kernels, large M the LDS-tiled
+ * (BG_ALGO_GEMV: M <= 256 and K <= 16640; BG_ALGO_SKINNY: K <= 65536, as
+ * the small-M kernels hold a block's group scales and zero-points for all of
+ * K in LDS; BG_ALGO_AUTO sends larger K to the tiled kernel).  Small M runs
+ * the bandwidth-bound decode kernels, large M the LDS-tiled
  * MFMA kernel ([LPI] §24: small batch and large prefill use different kernels).
  */
 bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K,
