@@ -68,24 +68,26 @@ __device__ __forceinline__ uint64_t shr64(uint64_t v, int sh) {
     return r;
 }
 
+// Words lo, hi (consecutive in a slot) -> their four pairs each.
+template <bool BF16>
+__device__ __forceinline__ void dequant_pair(uint32_t lo, uint32_t hi, uint32_t Dlo[4], uint32_t Dhi[4]) {
+    constexpr uint32_t m = W4Magic<BF16>::bits;
+    const uint64_t v = ((uint64_t)hi << 32) | lo;
+    const uint64_t v4 = shr64(v, 4), v8 = shr64(v, 8), v12 = shr64(v, 12);
+    Dlo[0] = and_or(lo, 0x000F000Fu, m);
+    Dlo[1] = and_or((uint32_t)v4, 0x000F000Fu, m);
+    Dlo[2] = and_or((uint32_t)v8, 0x000F000Fu, m);
+    Dlo[3] = and_or((uint32_t)v12, 0x000F000Fu, m);
+    Dhi[0] = and_or(hi, 0x000F000Fu, m);
+    Dhi[1] = and_or((uint32_t)(v4 >> 32), 0x000F000Fu, m);
+    Dhi[2] = and_or((uint32_t)(v8 >> 32), 0x000F000Fu, m);
+    Dhi[3] = and_or((uint32_t)(v12 >> 32), 0x000F000Fu, m);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void dequant_tile(const uint4& w, uint32_t D[4][4]) {
-    constexpr uint32_t m = W4Magic<BF16>::bits;
-    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t lo = wd[2 * h], hi = wd[2 * h + 1];
-        const uint64_t v = ((uint64_t)hi << 32) | lo;
-        const uint64_t v4 = shr64(v, 4), v8 = shr64(v, 8), v12 = shr64(v, 12);
-        D[2 * h][0] = and_or(lo, 0x000F000Fu, m);
-        D[2 * h][1] = and_or((uint32_t)v4, 0x000F000Fu, m);
-        D[2 * h][2] = and_or((uint32_t)v8, 0x000F000Fu, m);
-        D[2 * h][3] = and_or((uint32_t)v12, 0x000F000Fu, m);
-        D[2 * h + 1][0] = and_or(hi, 0x000F000Fu, m);
-        D[2 * h + 1][1] = and_or((uint32_t)(v4 >> 32), 0x000F000Fu, m);
-        D[2 * h + 1][2] = and_or((uint32_t)(v8 >> 32), 0x000F000Fu, m);
-        D[2 * h + 1][3] = and_or((uint32_t)(v12 >> 32), 0x000F000Fu, m);
-    }
+    dequant_pair<BF16>(w.x, w.y, D[0], D[1]);
+    dequant_pair<BF16>(w.z, w.w, D[2], D[3]);
 }
 
 // Difference of two FP16 pairs (one v_pk_add_f16 with negation).

@@ -97,9 +97,10 @@ int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
 // tiles do not fill the device.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
     if (M > kW4SkinnyMax) return bg::w4a16_gemm_split(M, N, K).S > 1 ? BG_ALGO_SPLITK : BG_ALGO_TILED;
-    // (measured: gate_up at M = 8 is 5 % faster unsplit, from M = 12 split;
-    // down, K = 14336, is faster split at every M >= 8)
-    const bool split = (M >= 8 && K >= 8192) || (M > 8 && N >= 16384) || (M > 16 && N > 4096) || M >= 24;
+    // (measured: down, K = 14336, is faster split at every M >= 8; gate_up,
+    // N = 28672, is faster unsplit through M = 16 -- 19.2-19.8 us against
+    // 20.6-21.7 -- since the small-M kernel deals its tiles in one round)
+    const bool split = (M >= 8 && K >= 8192) || (M > 16 && N > 4096) || M >= 24;
     if (split) return BG_ALGO_SPLITK;
     return K > bg::kW4DecodeMaxK ? BG_ALGO_TILED : BG_ALGO_SKINNY;
 }
@@ -144,7 +145,7 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
         return fail(BG_ERR_ALIGN, "gemm_w4a16: pointers must be 16-byte aligned");
     if (algo == BG_ALGO_AUTO) algo = with_ws ? w4_auto_algo_ws(M, N, K) : w4_auto_algo(M, K);
     if (algo == BG_ALGO_GEMV && (M > kMaxGemvM || !bg::w4a16_gemv_supported(M, K)))
-        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 16640 (M=%lld, K=%lld)", M, K);
+        return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 18432 (M=%lld, K=%lld)", M, K);
     if (algo == BG_ALGO_SKINNY && K > bg::kW4DecodeMaxK)
         return fail(BG_ERR_SHAPE, "gemm_w4a16: the small-M kernel takes K <= 65536 (K=%lld)", K);
     if (algo == BG_ALGO_SPLITK) {

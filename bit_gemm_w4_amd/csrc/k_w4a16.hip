@@ -85,7 +85,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     // groups in flight per wave: 4 for two-tile blocks; 3 for one-tile blocks,
     // whose fewer registers per wave keep more waves resident (o / down /
     // qkv at B = 1..4: 4-7 % faster per call than with 4)
-    constexpr int STAGES = XLDS ? (TN == 1 ? 3 : 4) : 3;
+    constexpr int STAGES = XLDS ? (TN == 1 ? 3 : TN <= 2 ? 4 : 2) : 3;
     constexpr int XB = 8;                                              // X staging batch
     constexpr int BAND = VALU ? VROWS : 16 * TM;                       // activation rows per block
     constexpr float MV = W4Magic<BF16>::value;
@@ -298,16 +298,22 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
 #pragma unroll
                 for (int j = 0; j < TN; ++j) part[i][j] = float4_t{0, 0, 0, 0};
             }
-            uint32_t D[TN][4][4];
-#pragma unroll
-            for (int j = 0; j < TN; ++j) dequant_tile<BF16>(st.w[j], D[j]);
+            // one word pair (two K steps) of every tile at a time: 8 registers
+            // of dequantized operands per tile in flight
+            uint32_t D[TN][2][4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
+                if ((kk & 1) == 0) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        dequant_pair<BF16>(kk == 0 ? st.w[j].x : st.w[j].z, kk == 0 ? st.w[j].y : st.w[j].w, D[j][0],
+                                           D[j][1]);
+                }
                 uint32_t bfrag[TN][4];
 #pragma unroll
                 for (int j = 0; j < TN; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) bfrag[j][r] = D[j][kk][r];
+                    for (int r = 0; r < 4; ++r) bfrag[j][r] = D[j][kk & 1][r];
 #pragma unroll
                 for (int i = 0; i < TM; ++i) {
                     uint4 av;
@@ -660,21 +666,32 @@ static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t
     return decode_cfg<BF16, TM, TN, 1, XLDS, VROWS>(x, M, K, qw, sc, zr, N, y, s);
 }
 
-// (TN = 4 tiles, 16 waves: the largest scale area of any configuration)
-static bool xlds_fits(int64_t rows, int64_t K, bool valu) {
-    return decode_scale_lds(4, 16, K) + rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
+// (tn_max tiles and 16 waves: at least the scale area of any configuration
+// the caller may pick)
+static bool xlds_fits(int64_t rows, int64_t K, bool valu, int tn_max) {
+    return decode_scale_lds(tn_max, 16, K) + rows * (K + 8) * 2 + (valu ? rows * (K >> 7) * 4 : 0) <= kLdsMax;
 }
 
 // Two weight tiles per block on wide layers, and from M = 9 on N > 4096 (the
-// activation rows a block stages are then shared by twice the weight bytes),
-// four on wide layers from M = 9; one otherwise (more blocks for short layers).
+// activation rows a block stages are then shared by twice the weight bytes);
+// one otherwise (more blocks for short layers).  When the staged rows take
+// more than half the LDS, a CU holds one block: the tiles are then dealt so
+// that the grid is one round of at most 256 blocks (7 tiles per block on a
+// 28672-wide layer instead of 1.75 rounds of 4).
 template <bool BF16>
 static const char* decode_dt(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                              const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     const bool wide = N >= 16384 || (M > 8 && N > 4096);
     if (M <= 16) {
-        if (xlds_fits(M, K, false)) {
-            if (N >= 16384 && M > 8) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+        if (xlds_fits(M, K, false, 8)) {
+            if (M * (K + 8) * 2 > 80 * 1024) {
+                const int64_t per = ((N >> 4) + 255) / 256;               // tiles per block for one round
+                if (per > 7) return decode_nw<BF16, 1, 8, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+                if (per > 4) return decode_nw<BF16, 1, 7, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+                if (per > 2) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+                if (per > 1) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+                return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+            }
             if (wide) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
         }
@@ -708,7 +725,7 @@ static const char* gemv_dt(const void* x, int64_t M, int64_t K, const uint32_t* 
     return decode_nw<BF16, 1, 1, true, 4>(x, M, K, qw, sc, zr, N, y, s);
 }
 
-bool w4a16_gemv_supported(int64_t M, int64_t K) { return xlds_fits(M < 4 ? M : 4, K, true); }
+bool w4a16_gemv_supported(int64_t M, int64_t K) { return xlds_fits(M < 4 ? M : 4, K, true, 2); }
 
 const char* launch_w4a16_gemv(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, hipStream_t s) {

@@ -108,7 +108,7 @@ bg_status w4_pack(const void* w, int w_dtype, int64_t N, int64_t K, int group, i
  *   qweight, scales, zeros   as produced by w4_pack (zeros NULL = symmetric)
  *   y        out [M][N] of x_dtype
  * Requires 1 <= M <= 1048560, N % 16 == 0, K % 256 == 0, group == 128
- * (BG_ALGO_GEMV: M <= 256 and K <= 16640; BG_ALGO_SKINNY: K <= 65536, as
+ * (BG_ALGO_GEMV: M <= 256 and K <= 18432; BG_ALGO_SKINNY: K <= 65536, as
  * the small-M kernels hold a block's group scales and zero-points for all of
  * K in LDS; BG_ALGO_AUTO sends larger K to the tiled kernel).  Small M runs
  * the bandwidth-bound decode kernels, large M the LDS-tiled
@@ -128,7 +128,7 @@ bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
  * enables the split-K kernels (BG_ALGO_SPLITK):
  *   M <= 64  the small-M split-K kernel.  BG_ALGO_AUTO picks it for M from 8
  *            to 64 where it measured faster than BG_ALGO_SKINNY: M >= 8 with
- *            N >= 16384 or K >= 8192, M >= 17 with N > 4096, or M >= 24.
+ *            K >= 8192, M >= 17 with N > 4096, or M >= 24.
  *            Splitting K across workgroups lets each workgroup reuse its
  *            activations across 16 weight tiles.
  *   M > 64   the large-M kernel with K split into S slices of whole groups

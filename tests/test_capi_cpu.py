@@ -111,7 +111,8 @@ def test_gemm_w4a16_workspace(L):
     # AUTO with a workspace: split-K from M = 8 on deep layers, M = 9 on wide ones, from
     # M = 17 on N > 4096, from M = 24 everywhere; the small-M kernel otherwise
     assert L.gemm_w4a16_workspace_bytes(8, 28672, 4096, 0) == 0
-    assert L.gemm_w4a16_workspace_bytes(9, 28672, 4096, 0) > 0
+    assert L.gemm_w4a16_workspace_bytes(16, 28672, 4096, 0) == 0       # wide layer: one-round small-M
+    assert L.gemm_w4a16_workspace_bytes(17, 28672, 4096, 0) > 0
     assert L.gemm_w4a16_workspace_bytes(7, 4096, 14336, 0) == 0
     assert L.gemm_w4a16_workspace_bytes(8, 4096, 14336, 0) > 0
     assert L.gemm_w4a16_workspace_bytes(16, 6144, 4096, 0) == 0

@@ -45,7 +45,7 @@ def _prepare(ops, M, N, K, x_dtype, asym, seed):
 @pytest.mark.parametrize("first,second", [
     ((32, 4096, 14336), (16, 1024, 8192)),      # small-M split-K, then a smaller split-K call
     ((130, 1040, 2048), (65, 272, 2048)),       # large-M kernel with K split, then smaller
-    ((16, 28672, 4096), (9, 16400, 4096)),      # the wide decode layer at B = 16, then B = 9
+    ((24, 28672, 4096), (17, 16400, 4096)),     # the wide layer at B = 24, then B = 17 (ragged)
 ])
 @pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
 def test_noalloc_matches_workspace_entry(ops, orc, first, second, x_dtype, asym):
