@@ -69,6 +69,15 @@ struct W4GemmSplit {
     int64_t ws_bytes;       // S * M * N * 4 when S > 1, else 0
 };
 W4GemmSplit w4a16_gemm_split(int64_t M, int64_t N, int64_t K);
+// Sum of S FP32 partial outputs ws[S][M][N] in slice order -> y (BF16 or FP16).
+void launch_w4a16_gemm_reduce(bool bf16, const float* ws, int S, int64_t M, int64_t N, void* y, hipStream_t s);
+// Mid-batch kernel (k_w4a16_mid.hip, 17 <= M <= 128 intended; any M works):
+// one wide N slab per block, the activation group staged once per block.
+// With a workspace (ws non-NULL, at least w4a16_mid_workspace(M, N, K)
+// bytes, any contents) K is split when one slice does not fill the device.
+int64_t w4a16_mid_workspace(int64_t M, int64_t N, int64_t K);
+const char* launch_w4a16_mid(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
+                             const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s);
 const char* launch_w4a16_gemm(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s);
 

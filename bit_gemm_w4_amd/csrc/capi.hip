@@ -88,6 +88,13 @@ int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
     return w8_auto_algo(M, N, K);
 }
 
+// Workspace bytes of a W4A16 kernel choice (0: none).
+int64_t w4_ws_need(int algo, int64_t M, int64_t N, int64_t K) {
+    if (algo == BG_ALGO_MID) return bg::w4a16_mid_workspace(M, N, K);
+    if (algo != BG_ALGO_SPLITK) return 0;
+    return M > kW4SkinnyMax ? bg::w4a16_gemm_split(M, N, K).ws_bytes : bg::w4a16_splitk_workspace(M, N, K);
+}
+
 // With a workspace, small M runs split-K where the small-M kernel's per-block
 // re-staging of the activation rows costs more than split-K's cross-block
 // reduction: from the measured crossovers (graph-replayed, cold weights) on
@@ -96,6 +103,11 @@ int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
 // Past the small-M range, split-K (of the large-M kernel) while its output
 // tiles do not fill the device.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
+    // mid-batch kernel: measured faster than the split small-M and the tiled
+    // kernels on the projection shapes from M = 32 on the 28672-wide layer
+    // and from M = 64 on the others, through M = 128 (the tiled kernel wins
+    // again at M = 256)
+    if (M <= 128 && (M >= 64 || (M >= 32 && N >= 16384))) return BG_ALGO_MID;
     if (M > kW4SkinnyMax) return bg::w4a16_gemm_split(M, N, K).S > 1 ? BG_ALGO_SPLITK : BG_ALGO_TILED;
     // (measured: down, K = 14336, is faster split at every M >= 8; gate_up,
     // N = 28672, is faster unsplit through M = 16 -- 19.2-19.8 us against
@@ -148,10 +160,10 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
         return fail(BG_ERR_SHAPE, "gemm_w4a16: the GEMV kernel takes M <= 256 and K <= 18432 (M=%lld, K=%lld)", M, K);
     if (algo == BG_ALGO_SKINNY && K > bg::kW4DecodeMaxK)
         return fail(BG_ERR_SHAPE, "gemm_w4a16: the small-M kernel takes K <= 65536 (K=%lld)", K);
-    if (algo == BG_ALGO_SPLITK) {
-        if (!with_ws) return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernels need gemm_w4a16_ws");
-        const int64_t need =
-            M > kW4SkinnyMax ? bg::w4a16_gemm_split(M, N, K).ws_bytes : bg::w4a16_splitk_workspace(M, N, K);
+    if (algo == BG_ALGO_SPLITK && !with_ws)
+        return fail(BG_ERR_WORKSPACE, "gemm_w4a16: the split-K kernels need gemm_w4a16_ws");
+    if (with_ws && (algo == BG_ALGO_SPLITK || algo == BG_ALGO_MID)) {
+        const int64_t need = w4_ws_need(algo, M, N, K);
         if (need > 0 && (!ws || ws_bytes < need))
             return fail(BG_ERR_WORKSPACE, "gemm_w4a16: workspace of %lld bytes needed (got %lld)", need, ws ? ws_bytes : 0);
     }
@@ -161,6 +173,9 @@ static bg_status w4a16_impl(const void* x, int x_dtype, int64_t M, int64_t K, co
         case BG_ALGO_GEMV: note_kernel(bg::launch_w4a16_gemv(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_SKINNY: note_kernel(bg::launch_w4a16_skinny(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
         case BG_ALGO_TILED: note_kernel(bg::launch_w4a16_tiled(x, bf16, M, K, qweight, scales, zeros, N, y, s)); break;
+        case BG_ALGO_MID:
+            note_kernel(bg::launch_w4a16_mid(x, bf16, M, K, qweight, scales, zeros, N, y, with_ws ? ws : nullptr, s));
+            break;
         case BG_ALGO_SPLITK:
             if (M > kW4SkinnyMax)
                 note_kernel(bg::launch_w4a16_gemm(x, bf16, M, K, qweight, scales, zeros, N, y, ws, s));
@@ -188,8 +203,7 @@ BG_EXPORT bg_status gemm_w4a16_ws(const void* x, int x_dtype, int64_t M, int64_t
 BG_EXPORT int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo) {
     if (M < 1 || M > kMaxM || N < 16 || N % 16 || K < 256 || K % 256) return 0;
     if (algo == BG_ALGO_AUTO) algo = w4_auto_algo_ws(M, N, K);
-    if (algo != BG_ALGO_SPLITK) return 0;
-    return M > kW4SkinnyMax ? bg::w4a16_gemm_split(M, N, K).ws_bytes : bg::w4a16_splitk_workspace(M, N, K);
+    return w4_ws_need(algo, M, N, K);
 }
 
 BG_EXPORT bg_status gemm_w4a16(const void* x, int x_dtype, int64_t M, int64_t K, const uint32_t* qweight,
@@ -261,9 +275,7 @@ BG_EXPORT bg_status gemm_w4a16_noalloc(const void* x, int x_dtype, int64_t M, in
     if (N < 16 || N > kMaxRows || N % 16) return fail(BG_ERR_SHAPE, "gemm_w4a16: N=%lld must be a multiple of 16", N);
     if (K < 256 || K > kMaxDim || K % 256) return fail(BG_ERR_SHAPE, "gemm_w4a16: K=%lld must be a multiple of 256", K);
     const int algo = w4_auto_algo_ws(M, N, K);
-    const int64_t need = algo != BG_ALGO_SPLITK ? 0
-                         : M > kW4SkinnyMax     ? bg::w4a16_gemm_split(M, N, K).ws_bytes
-                                                : bg::w4a16_splitk_workspace(M, N, K);
+    const int64_t need = w4_ws_need(algo, M, N, K);
     if (need > BG_NOALLOC_SCRATCH_BYTES)
         return fail(BG_ERR_WORKSPACE,
                     "gemm_w4a16_noalloc: this shape needs %lld bytes of scratch; the static scratch holds %lld "

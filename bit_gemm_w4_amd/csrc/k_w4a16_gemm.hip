@@ -465,6 +465,16 @@ __global__ __launch_bounds__(256) void k_w4a16_gemm_reduce(const float* __restri
     *reinterpret_cast<uint4*>(y + e) = o;
 }
 
+void launch_w4a16_gemm_reduce(bool bf16, const float* ws, int S, int64_t M, int64_t N, void* y, hipStream_t s) {
+    const int64_t threads = M * N / 8;
+    if (bf16)
+        hipLaunchKernelGGL((k_w4a16_gemm_reduce<true>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ws,
+                           S, M, N, static_cast<uint16_t*>(y));
+    else
+        hipLaunchKernelGGL((k_w4a16_gemm_reduce<false>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, ws,
+                           S, M, N, static_cast<uint16_t*>(y));
+}
+
 // K slices for the large-M kernel: while its tiles do not fill one round (one
 // block per CU), split K into whole groups, at least 4 per slice.
 W4GemmSplit w4a16_gemm_split(int64_t M, int64_t N, int64_t K) {

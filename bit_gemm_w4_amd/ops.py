@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libbitgemm.so")
 # enums of include/bitgemm.h
 F32, F16, BF16, I8, FP8_E4M3, I32 = 0, 1, 2, 3, 4, 5
 GRAN_TENSOR, GRAN_ROW, GRAN_ROW_G128, GRAN_BLOCK128 = 0, 1, 2, 3
-ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED, ALGO_SPLITK = 0, 1, 2, 3, 4
+ALGO_AUTO, ALGO_GEMV, ALGO_SKINNY, ALGO_TILED, ALGO_SPLITK, ALGO_MID = 0, 1, 2, 3, 4, 5
 PACK_FORMAT_VERSION = 1
 
 EXPORTS = (
@@ -203,7 +203,7 @@ def gemm_w4a16(x: torch.Tensor, packed: PackedW4, out: torch.Tensor | None = Non
     return out
 
 
-NOALLOC_SCRATCH_BYTES = 32 << 20   # BG_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 16 << 20   # BG_NOALLOC_SCRATCH_BYTES
 
 
 def gemm_w4a16_noalloc(x: torch.Tensor, packed: PackedW4, out: torch.Tensor, stream=None) -> torch.Tensor:

@@ -64,7 +64,9 @@ typedef enum bg_algo {
     BG_ALGO_GEMV = 1,      /* W4A16 small-M: VALU dot products, wave reductions    */
     BG_ALGO_SKINNY = 2,    /* small-M on MFMA (M padded to the MFMA tile)          */
     BG_ALGO_TILED = 3,     /* large-M LDS-tiled MFMA GEMM                          */
-    BG_ALGO_SPLITK = 4     /* W4A16: K split over blocks, needs a workspace        */
+    BG_ALGO_SPLITK = 4,    /* W4A16: K split over blocks, needs a workspace        */
+    BG_ALGO_MID = 5        /* W4A16 mid-size M: wide N slab per block, activation
+                              groups staged once per block; K split with a workspace */
 } bg_algo;
 
 /*
@@ -178,7 +180,7 @@ int64_t gemm_w4a16_workspace_bytes(int64_t M, int64_t N, int64_t K, int algo);
  * ordering) race and give wrong results.  The array needs no clearing: each
  * call writes every partial it later reads.
  */
-#define BG_NOALLOC_SCRATCH_BYTES (32LL << 20)
+#define BG_NOALLOC_SCRATCH_BYTES (16LL << 20)
 bg_status gemm_w4a16_noalloc(const void* x, int x_dtype, int64_t M, int64_t K,
                              const uint32_t* qweight, const uint16_t* scales, const uint8_t* zeros,
                              int64_t N, int group, void* y, void* stream);

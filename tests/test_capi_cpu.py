@@ -217,9 +217,9 @@ def test_noalloc_rejects_before_touching_the_device(L):
     # the host, with the size in the message; so are the usual shape errors
     f = L.gemm_w4a16_noalloc
     P = 1 << 20
-    limit = 32 << 20
-    assert L.gemm_w4a16_workspace_bytes(64, 28672, 4096, 0) > limit
-    assert f(P, BF16, 64, 4096, P, P, P, 28672, 128, P, None) == E_WS
+    limit = 16 << 20
+    assert L.gemm_w4a16_workspace_bytes(256, 4096, 14336, 0) > limit      # down at M = 256: K split in 8
+    assert f(P, BF16, 256, 14336, P, P, P, 4096, 128, P, None) == E_WS
     assert b"scratch" in L.bg_last_error()
     assert f(None, BF16, 16, 4096, P, P, P, 4096, 128, P, None) == E_NULL
     assert f(P, BF16, 0, 4096, P, P, P, 4096, 128, P, None) == E_SHAPE

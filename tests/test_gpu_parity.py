@@ -143,6 +143,22 @@ def test_w4a16_splitk_large_m(ops, orc, x_dtype, asym, M):
     _w4a16_case(ops, orc, M, N, K, x_dtype, asym, 4, seed=M)
 
 
+@pytest.mark.parametrize("ws", [None, False], ids=["split", "nosplit"])
+@pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
+@pytest.mark.parametrize("M", [1, 17, 33, 74, 100, 128, 129, 200])
+def test_w4a16_mid(ops, orc, x_dtype, asym, M, ws):
+    """Mid-batch kernel: bands of up to 96 rows (ragged), 65 weight tiles
+    (ragged last block of 16 or 32 tiles), 16 groups, K split with a workspace."""
+    _w4a16_case(ops, orc, M, 1040, 2048, x_dtype, asym, ops.ALGO_MID, seed=M + 7, ws=ws)
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+@pytest.mark.parametrize("B", [24, 74, 128])
+def test_w4a16_mid_llama_shapes(ops, orc, name, B):
+    K, N = synth.LLAMA3_8B_SHAPES[name]
+    _w4a16_case(ops, orc, B, N, K, "bf16", True, ops.ALGO_MID, seed=3, rows=[0, 1, B // 2, B - 2, B - 1])
+
+
 def test_w4a16_qwen_layer(ops, orc):
     """1024x1024 layer, batch 1, FP16 activations, symmetric INT4 (full compare)."""
     w, x = synth.qwen_layer(seed=0)

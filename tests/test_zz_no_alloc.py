@@ -61,7 +61,7 @@ def test_noalloc_matches_workspace_entry(ops, orc, first, second, x_dtype, asym)
         y = torch.full((M, N), float("nan"), dtype=_bits(x[:1], x_dtype).dtype, device="cuda")
         ops.gemm_w4a16_noalloc(_bits(x, x_dtype), p, y)
         kern = ops.last_kernel()
-        assert "splitk" in kern or "gemm" in kern, kern
+        assert any(k in kern for k in ("splitk", "gemm", "mid")), kern
         outs.append(y)
     torch.cuda.synchronize()
     for (M, N, K, w, x, p), y in zip(cases, outs):
@@ -90,7 +90,7 @@ def test_noalloc_without_split(ops, orc):
 
 
 def test_noalloc_rejects_oversized_scratch(ops):
-    M, N, K = 64, 28672, 4096
+    M, N, K = 256, 4096, 14336
     assert ops.gemm_w4a16_workspace_bytes(M, N, K, 0) > ops.NOALLOC_SCRATCH_BYTES
     p = ops.w4_pack(torch.zeros((N, K), dtype=torch.float32, device="cuda"), 128, True)
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
