@@ -42,8 +42,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
@@ -65,18 +65,30 @@ def graph_of(fn, torch):
     return g
 
 
-def time_graph(g, reps, torch):
-    """Average milliseconds per replay of g, HIP events on the replay stream."""
-    g.replay()
-    torch.cuda.synchronize()
+def time_graph(g, reps, torch, trials=5, warm_ms=20.0, trial_ms=2.0):
+    """Milliseconds per replay of g, HIP events on the replay stream: replays
+    for about warm_ms first (the clocks ramp up from idle), then the median of
+    `trials` runs of at least `reps` replays and at least trial_ms each."""
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()
     e0.record()
-    for _ in range(reps):
-        g.replay()
+    g.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    one = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(min(5000, int(warm_ms / one) + 2)):
+        g.replay()
+    n = max(reps, min(5000, int(trial_ms / one) + 1))
+    ts = []
+    for _ in range(trials):
+        e0.record()
+        for _ in range(n):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / n)
+    return sorted(ts)[len(ts) // 2]
 
 
 def main():
@@ -195,6 +207,10 @@ def main():
     if not args.no_secondary:
         out["secondary"] = secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
         out["secondary"]["crossover_down"] = crossover(ops, synth, roofline, torch, np, dev, graph_of, time_graph)
+        out["secondary"]["qwen_1024_b1"] = qwen_single(ops, synth, roofline, torch, np, dev, graph_of, time_graph)
+        out["secondary"]["w8a8_decode"] = w8a8_decode(ops, synth, roofline, torch, np, dev, graph_of, time_graph)
+        out["secondary"]["fp8_prefill_m"] = fp8_sizes(ops, synth, roofline, torch, np, dev, graph_of, time_graph)
+        out["secondary"]["tensor_metrics"] = tensor_metrics(ops, synth, torch, np, dev, packs)
 
     # ----------------------------------------------------- cpu baseline ----
     if not args.no_cpu_baseline:
@@ -233,11 +249,12 @@ def library_digest() -> str:
 
 
 def call_kernels(ops, main: str, M: int, N: int, K: int) -> str:
-    """The kernels one gemm_w4a16 call enqueues, joined by " + ": the split-K
-    paths add a fixed-order reduction kernel when they split K."""
+    """The kernels one gemm_w4a16 call enqueues, joined by " + ": the split-K,
+    tiled and mid-batch paths add a fixed-order reduction kernel when they
+    split K."""
     if ops.gemm_w4a16_workspace_bytes(M, N, K) > 0 and "k_w4a16_splitk<" in main:
         return main + " + " + main.replace("k_w4a16_splitk<", "k_w4a16_splitk_reduce<")
-    if ops.gemm_w4a16_workspace_bytes(M, N, K) > 0 and "k_w4a16_gemm<" in main:
+    if ops.gemm_w4a16_workspace_bytes(M, N, K) > 0 and ("k_w4a16_gemm<" in main or "k_w4a16_mid<" in main):
         return main + " + " + "k_w4a16_gemm_reduce<" + main.split("<", 1)[1].split(",")[0] + ">"
     return main
 
@@ -288,7 +305,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             ms = time_graph(g, 10, torch)
             kname = ops.last_kernel()
             gq = graph_of(lambda: quant(xt, ag), torch)
-            ms_q = time_graph(gq, 10, torch)
+            ms_q = time_graph(gq, 200, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp8" if fp8 else "i8"]
             res["w8a8_m2048"][f"{name}/{tag}"] = {
@@ -320,7 +337,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             ms = time_graph(g, 10, torch)
             kname = ops.last_kernel()
             gq = graph_of(lambda: ops.act_quant_mxfp8(xt), torch)
-            ms_q = time_graph(gq, 10, torch)
+            ms_q = time_graph(gq, 200, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp8"]
             res["w8a8_m2048"][f"{name}/mxfp8"] = {
@@ -337,7 +354,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             ms = time_graph(g, 10, torch)
             kname = ops.last_kernel()
             gq = graph_of(lambda: ops.act_quant_mxfp4(xt), torch)
-            ms_q = time_graph(gq, 10, torch)
+            ms_q = time_graph(gq, 200, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp4"]
             qbytes = M * K * 2 + M * K // 2 + M * K // 32
@@ -363,6 +380,173 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
                 "us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4),
                 "kernel": ops.last_kernel()}
             log(f"  w4a16 {name:8s} B={B:3d} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s")
+    return res
+
+
+def qwen_single(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
+    """The single Qwen3-0.6B-sized linear (K = N = 1024, B = 1, FP16
+    activations, symmetric INT4 G=128, FP16 output), rotated over copies that
+    exceed the 256 MB last-level cache.  0.54 MB per call: at 8 TB/s that is
+    0.07 us, far below the cost of a kernel launch, so the call is bound by
+    launch latency and the fraction of the HBM roofline is reported as such."""
+    w, x = synth.qwen_layer(seed=0)
+    p0 = ops.w4_pack(torch.from_numpy(w).to(dev), 128, False)
+    n = -(-(320 << 20) // p0.nbytes)
+    cps = [p0] + [ops.PackedW4(p0.qweight.clone(), p0.scales.clone(), None, 1024, 1024) for _ in range(n - 1)]
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.float16).to(dev)
+    y = torch.empty((1, 1024), dtype=torch.float16, device=dev)
+    g = graph_of(lambda: [ops.gemm_w4a16(xt, c, out=y) for c in cps], torch)
+    ms = time_graph(g, 20, torch) / len(cps)
+    byts = roofline.w4a16_bytes(1, 1024, 1024, asym=False)
+    gbps = byts / (ms * 1e-3) / 1e9
+    log(f"  qwen 1024x1024 B=1 fp16 sym: {ms * 1e3:.2f} us {gbps:.0f} GB/s ({gbps / roofline.HBM_GBPS:.1%}, launch-bound)")
+    return {"us": round(ms * 1e3, 2), "bytes": byts, "gbps": round(gbps, 1),
+            "frac": round(gbps / roofline.HBM_GBPS, 4), "bound": "launch latency (0.07 us of HBM time at 8 TB/s)",
+            "kernel": ops.last_kernel()}
+
+
+def w8a8_decode(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
+    """W8A8 at decode batches B = 1, 4, 16 on the four projection shapes:
+    INT8 (per-token x per-channel) and FP8 (per-tensor), the GEMM alone and
+    with the activation quantization it needs, weights rotated over copies
+    that exceed the last-level cache.  GB/s = the GEMM call's algorithmic
+    bytes (8-bit weights and activations, scales, BF16 output) over its time."""
+    res = {}
+    for name in LAYERS:
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        w = synth.weights(N, K, seed=0)
+        wd = torch.from_numpy(w).to(dev)
+        n = max(2, -(-(320 << 20) // (N * K)))
+        q8, s8 = ops.act_quant_int8(wd, ops.GRAN_ROW)
+        qf, sf = ops.act_quant_fp8(wd, ops.GRAN_TENSOR)
+        i8 = [(q8, s8)] + [(q8.clone(), s8.clone()) for _ in range(n - 1)]
+        f8 = [(qf, sf)] + [(qf.clone(), sf.clone()) for _ in range(n - 1)]
+        del wd
+        for B in BATCHES:
+            x = torch.from_numpy(synth.activations(B, K, "bf16", seed=B).view(np.int16)).view(torch.bfloat16).to(dev)
+            y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+            for tag, fp8, gran, wl in (("int8", False, ops.GRAN_ROW, i8), ("fp8", True, ops.GRAN_TENSOR, f8)):
+                quant = ops.act_quant_fp8 if fp8 else ops.act_quant_int8
+                a, a_s = quant(x, gran)
+                g = graph_of(lambda: [ops.gemm_w8a8(a, a_s, gran, c[0], c[1], gran, out=y) for c in wl], torch)
+                ms = time_graph(g, 20, torch) / len(wl)
+                kname = ops.last_kernel()
+                def with_q():
+                    for c in wl:
+                        aa, ss = quant(x, gran)
+                        ops.gemm_w8a8(aa, ss, gran, c[0], c[1], gran, out=y)
+                ms_q = time_graph(graph_of(with_q, torch), 20, torch) / len(wl)
+                byts = roofline.w8a8_bytes(B, N, K, w_scales=1 if fp8 else None)
+                gbps = byts / (ms * 1e-3) / 1e9
+                res[f"{name}/{tag}@B{B}"] = {"gemm_us": round(ms * 1e3, 2), "gbps": round(gbps, 1),
+                                             "frac": round(gbps / roofline.HBM_GBPS, 4),
+                                             "with_act_quant_us": round(ms_q * 1e3, 2), "kernel": kname}
+                log(f"  w8a8 decode {name:8s} {tag:4s} B={B:2d} {ms * 1e3:7.2f} us {gbps:6.0f} GB/s "
+                    f"({gbps / roofline.HBM_GBPS:.1%}); with act_quant {ms_q * 1e3:7.2f} us  {kname}")
+        del i8, f8
+    return res
+
+
+def fp8_sizes(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
+    """FP8 E4M3 W8A8 at the other prefill sizes of the FP8 workload, M = 512
+    and 8192 (M = 2048 is with the other prefill rows), on gate_up and down:
+    (a) per-tensor scales, (b) 128 x 128 weight blocks with 1 x 128 activation
+    groups."""
+    res = {}
+    for name in ("gate_up", "down"):
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        w = synth.weights(N, K, seed=0)
+        wt = torch.from_numpy(w).to(dev)
+        for M in (512, 8192):
+            x = synth.activations(M, K, "bf16", seed=M, n_outlier_cols=8)
+            xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for tag, ag, wg in (("tensor", 0, 0), ("block", 2, 3)):
+                a, a_s = ops.act_quant_fp8(xt, ag)
+                wq, w_s = ops.act_quant_fp8(wt, wg)
+                g = graph_of(lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y), torch)
+                ms = time_graph(g, 10, torch)
+                tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
+                peak = roofline.PEAK_TFLOPS["fp8"]
+                res[f"{name}/fp8_{tag}@M{M}"] = {"gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                                                 "frac": round(tf / peak, 4), "kernel": ops.last_kernel()}
+                log(f"  fp8 {name:8s} {tag:6s} M={M:5d} {ms * 1e3:8.1f} us {tf:7.1f} TFLOP/s ({tf / peak:.1%})")
+            del xt, y
+        del wt
+    return res
+
+
+def w4_codes(qweight, scales, zeros, np):
+    """4-bit codes [N][K] and dequantized weights (u - z) * s of the tiled
+    w4_pack layout, read back on the host: 16 channels x 128-wide group per
+    tile; column n, offset c in the group sits in slot 16 * (c / 32) + n % 16,
+    word (c % 32) / 8; of the 8 codes of a word, even k fill the low half-word
+    and odd k the high one, lowest k in the lowest nibble."""
+    T, G = qweight.shape[0], qweight.shape[1]
+    N, K = 16 * T, 128 * G
+    shifts = np.array([0, 16, 4, 20, 8, 24, 12, 28], dtype=np.uint32)
+    qw = qweight.view(np.uint32).reshape(T, G, 4, 16, 4)
+    u = ((qw[..., None] >> shifts) & 0xF).transpose(0, 3, 1, 2, 4, 5).reshape(N, K)
+    sc = np.asarray(scales).view(np.float16).astype(np.float64).transpose(0, 2, 1).reshape(N, G)
+    if zeros is None:
+        z = np.full((N, G), 8.0)
+    else:
+        zb = zeros.transpose(0, 2, 1).reshape(N, G // 2)
+        z = np.stack([zb & 0xF, zb >> 4], axis=-1).reshape(N, G).astype(np.float64)
+    return u, (u - np.repeat(z, 128, axis=1)) * np.repeat(sc, 128, axis=1)
+
+
+def tensor_metrics(ops, synth, torch, np, dev, packs, rows=2048):
+    """Tensor-level quantization metrics of the benchmark's quantized tensors
+    (host-side analysis of the codes the kernels produced): saturation ratio
+    (share of codes at the format's extreme magnitude), code utilisation
+    (distinct codes used / codes of the format), MSE and cosine similarity of
+    the dequantized tensor against the original.  INT8 / FP8 activations
+    (per token; 8 channels x50) of the gate_up prefill layer at M = 2048 and
+    its weights (per channel, per tensor), and the packed INT4 weights of the
+    four decode layers; each tensor is quantized whole and its first `rows`
+    rows are analysed."""
+    def stats(orig, deq, codes, n_codes, extreme):
+        o = orig.astype(np.float64).ravel()
+        d = deq.astype(np.float64).ravel()
+        cos = float(o @ d / (np.linalg.norm(o) * np.linalg.norm(d) + 1e-300))
+        return {"saturation": round(float(np.mean(extreme)), 6),
+                "code_utilisation": round(len(np.unique(codes)) / n_codes, 4),
+                "mse": float(np.mean((o - d) ** 2)), "cosine": round(cos, 7)}
+
+    def e4m3_value(b):
+        b = b.astype(np.int64)
+        e, m = (b >> 3) & 0xF, (b & 7).astype(np.float64)
+        v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * 2.0 ** (e - 7.0))
+        return np.where(b & 0x80, -v, v)
+
+    res = {}
+    K, N = synth.LLAMA3_8B_SHAPES["gate_up"]
+    w, x = synth.prefill_layer(2048, N, K, seed=0)
+    x32 = (x.astype(np.uint32) << 16).view(np.float32)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(w).to(dev)
+    cases = (("act_per_token", xt, x32, ops.GRAN_ROW, ("int8", "fp8")),
+             ("weight_per_channel", wt, w, ops.GRAN_ROW, ("int8", "fp8")),
+             ("weight_per_tensor", wt, w, ops.GRAN_TENSOR, ("fp8",)))
+    for tag, t, t32, gran, fmts in cases:
+        for fmt in fmts:
+            q, s = (ops.act_quant_fp8 if fmt == "fp8" else ops.act_quant_int8)(t, gran)
+            qn = q[:rows].cpu().view(torch.uint8 if fmt == "fp8" else torch.int8).numpy()
+            sn = s.cpu().numpy().astype(np.float64)
+            scale = sn[:rows, None] if gran == ops.GRAN_ROW else sn[0]
+            if fmt == "fp8":
+                res[f"{tag}/{fmt}"] = stats(t32[:rows], e4m3_value(qn) * scale, qn, 254, (qn & 0x7F) == 0x7E)
+            else:
+                res[f"{tag}/{fmt}"] = stats(t32[:rows], qn * scale, qn, 255, np.abs(qn.astype(np.int64)) >= 127)
+    del xt, wt
+    for name in LAYERS:
+        Kd, Nd = synth.LLAMA3_8B_SHAPES[name]
+        wd = synth.decode_layer(1, Nd, Kd, seed=0)[0][:rows]
+        p, T = packs[name][0], rows // 16
+        u, deq = w4_codes(p.qweight[:T].cpu().numpy(), p.scales[:T].cpu().numpy(), p.zeros[:T].cpu().numpy(), np)
+        res[f"w4_{name}"] = stats(wd, deq, u, 16, (u == 0) | (u == 15))
+    log("  tensor metrics: " + ", ".join(f"{k} sat {v['saturation']:.4f} cos {v['cosine']:.5f}" for k, v in res.items()))
     return res
 
 
@@ -401,8 +585,8 @@ def smoothquant(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph):
         out[tag] = {k: round(v, 5) for k, v in errs.items()}
     g0 = graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch)
     g1 = graph_of(lambda: ops.act_quant_int8_smooth(xt, invd, ops.GRAN_ROW), torch)
-    out["act_quant_us"] = {"plain": round(time_graph(g0, 10, torch) * 1e3, 1),
-                           "folded": round(time_graph(g1, 10, torch) * 1e3, 1)}
+    out["act_quant_us"] = {"plain": round(time_graph(g0, 200, torch) * 1e3, 1),
+                           "folded": round(time_graph(g1, 200, torch) * 1e3, 1)}
     log(f"  smoothquant rel-L2 err per-token {out['per_token']['plain']:.4f} -> {out['per_token']['folded']:.4f}, "
         f"per-tensor {out['per_tensor']['plain']:.4f} -> {out['per_tensor']['folded']:.4f}; act_quant "
         f"{out['act_quant_us']['plain']} -> {out['act_quant_us']['folded']} us")
@@ -431,10 +615,10 @@ def llm_int8(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph, tau=6
     e1 = float(np.linalg.norm(y1[ridx].double().cpu().numpy() - exact) / np.linalg.norm(exact))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     t = {}
-    t["plain_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch), 10, torch)
+    t["plain_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch), 200, torch)
     t["plain_gemm_us"] = time_graph(graph_of(
         lambda: ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out=y), torch), 10, torch)
-    t["detect_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8_outlier(xt, tau), torch), 10, torch)
+    t["detect_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8_outlier(xt, tau), torch), 200, torch)
     t["gemm_side_us"] = time_graph(graph_of(
         lambda: ops.gemm_w8a8_outlier(q, sa, wq, w_s, ops.GRAN_ROW, xt, idx, cnt, out=y), torch), 10, torch)
     kname = ops.last_kernel()

@@ -51,3 +51,9 @@ def gemm_flops(M: int, N: int, K: int) -> float:
 def act_quant_bytes(R: int, C: int, in_bytes: int = 2, n_scales: int | None = None) -> int:
     """Read the tensor once, write one byte per element plus FP32 scales."""
     return R * C * in_bytes + R * C + 4 * (R if n_scales is None else n_scales)
+
+
+def w8a8_bytes(M: int, N: int, K: int, out_bytes: int = 2, w_scales: int | None = None) -> int:
+    """Algorithmic HBM bytes of one W8A8 GEMM call: 8-bit weights and
+    activations, FP32 scales (per channel and per token unless given), output."""
+    return N * K + M * K + 4 * (N if w_scales is None else w_scales) + 4 * M + M * N * out_bytes

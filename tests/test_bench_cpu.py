@@ -46,3 +46,18 @@ def test_committed_traffic_summary_has_the_decode_kernels():
     assert any(n.startswith("k_w4a16_decode<") for n in names)
     assert all(len(l.strip().strip("|").split("|")) == 7 for l in rows)
     assert "FETCH_SIZE" in text and "WRITE_SIZE" in text and "Calibration" in text
+
+
+def test_w4_codes_reads_the_packed_layout_like_the_oracle():
+    """The benchmark's host-side reader of packed weights (used for its
+    tensor-level metrics) against the oracle's unpack and dequantization."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((48, 512)) * 0.02).astype(np.float32)
+    for asym in (False, True):
+        qw, sc, z = oracle.w4_pack(w, 128, asym)
+        u, deq = bench.w4_codes(qw, sc, z, np)
+        u_ref, _, _ = oracle.w4_unpack(qw, sc, z, 48, 512)
+        assert np.array_equal(u, u_ref)
+        assert np.array_equal(deq, oracle.w4_dequant(qw, sc, z, 48, 512))
