@@ -15,7 +15,7 @@ from dataclasses import dataclass
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbitgemm.so")
+LIB_PATH = os.environ.get("BG_LIB_PATH") or os.path.join(_PKG, "libbitgemm.so")
 
 # enums of include/bitgemm.h
 F32, F16, BF16, I8, FP8_E4M3, I32 = 0, 1, 2, 3, 4, 5

@@ -31,7 +31,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "bg_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# BG_ORACLE_LIB: an already built copy of bg_oracle.c to load instead (the
+# sanitizer test builds one with -fsanitize=address,undefined)
+_LIB_OVERRIDE = os.environ.get("BG_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -45,6 +48,8 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
 
 def build(force: bool = False) -> str:
     """Compile bg_oracle.c into liboracle.so with gcc (no GPU involved)."""
+    if _LIB_OVERRIDE:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
