@@ -25,6 +25,12 @@ typedef int int16_t_v __attribute__((ext_vector_type(16)));
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
+// A buffer-load offset beyond the range of every buffer resource the kernels
+// build (each well below 1 GiB, offsets included): such a load returns zeros
+// without a memory access.  Software pipelines issue it for the stages past
+// a wave's last unit of work.
+constexpr int kBufOOB = 0x40000000;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)h);

@@ -67,10 +67,12 @@ int w4_auto_algo(int64_t M, int64_t K) {
 
 // W8A8: the small-M kernel streams the weights once per band of up to 64
 // rows; the tiled kernel is flat in M until its 256 x 128 tiles fill the
-// device. Measured on the 8B projection shapes: the tiled grid wins once it
-// has >= 128 tiles (from M = 1) or M > 128, or M > 64 with a short K; the
-// small-M kernel wins below that.
+// device. Measured on the 8B projection shapes: through M = 16 the small-M
+// kernel (activations staged in LDS) wins on every shape, by 1.3-1.5x on the
+// 28672-wide layer; above that the tiled grid wins once it has >= 128 tiles
+// or M > 128, or M > 64 with a short K.
 int w8_auto_algo(int64_t M, int64_t N, int64_t K) {
+    if (M <= 16) return BG_ALGO_SKINNY;
     const int64_t tiles = ((M + 255) / 256) * ((N + 127) / 128);
     if (tiles >= 128 || M > 128) return BG_ALGO_TILED;
     if (M <= kW8SkinnyMax) return BG_ALGO_SKINNY;
@@ -78,12 +80,15 @@ int w8_auto_algo(int64_t M, int64_t N, int64_t K) {
     return BG_ALGO_TILED;
 }
 
-// W8A8 with a workspace: the large-M kernel with K split wherever it measured
-// faster than the small-M kernel on the projection shapes (N >= 6144 at any
-// M; K >= 8192 from M = 4; otherwise from M = 32), else the choice above.
+// W8A8 with a workspace: the small-M kernel through M = 16, and through
+// M = 32 on layers up to 4096 x 8192; beyond that the large-M kernel with K
+// split wherever it measured faster than the small-M kernel on the
+// projection shapes (N >= 6144, or K >= 8192, or M >= 32), else the choice
+// above.
 int w8_auto_algo_ws(int64_t M, int64_t N, int64_t K, int in_dtype, int a_gran) {
+    if (M <= 16 || (M <= 32 && N <= 4096 && K <= 8192)) return BG_ALGO_SKINNY;
     bg::W8A8Args g{nullptr, nullptr, a_gran, nullptr, nullptr, 0, in_dtype == BG_FP8_E4M3, M, N, K, nullptr, BG_BF16};
-    const bool fits = N >= 6144 || (K >= 8192 && M >= 4) || M >= 32;
+    const bool fits = N >= 6144 || K >= 8192 || M >= 32;
     if (fits && bg::w8a8_tiled_split(g, true).S > 1) return BG_ALGO_TILED;
     return w8_auto_algo(M, N, K);
 }

@@ -104,7 +104,6 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     // wave w takes groups w, w + NW, w + 2 NW, ...: at any moment the waves of
     // a block read neighbouring 1 KB tiles, i.e. one contiguous stretch of HBM
     const int n_mine = ngroups > wave ? (ngroups - wave + NW - 1) / NW : 0;
-    const int i_last = n_mine > 0 ? n_mine - 1 : 0;
     const int64_t rows = (M - m0) < BAND ? (M - m0) : BAND;           // real rows of this block
     const int64_t xstride = K + 8;                                    // LDS row pitch in halves
     const int64_t x_bytes = XLDS ? rows * xstride * 2 : 0;
@@ -140,14 +139,16 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
     }
     const uint32_t ones[4] = {ONE2, ONE2, ONE2, ONE2};
 
-    // Every stage issues the same loads (the group index is clamped to the
-    // wave's last group), so the compiler can wait for exactly one stage.
+    // Every stage issues the same loads, so the compiler can wait for exactly
+    // one stage.  Past the wave's last group the loads address beyond the
+    // buffer's range (kBufOOB): they return zeros without a memory access.
     auto issue = [&](DecStage<TM, TN, XLDS>& st, int i) {
-        const int g = (i < i_last ? i : i_last) * NW + wave;
+        const bool real = i < n_mine;
+        const int g = i * NW + wave;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             st.w[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                    rw, lane * 16, (j * ngroups + g) * 1024, 0));
+                                                    rw, lane * 16, real ? (j * ngroups + g) * 1024 : kBufOOB, 0));
         if constexpr (!XLDS) {
 #pragma unroll
             for (int ii = 0; ii < TM; ++ii)
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
                 for (int kk = 0; kk < 4; ++kk)
                     st.a[ii][kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                  rx, (int)(arow[ii] * K * 2) + q * 64 + kk * 16,
-                                                                 g * 256, 0));
+                                                                 real ? g * 256 : kBufOOB, 0));
         }
     };
 
@@ -461,10 +462,10 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
                                                       (int)(((int64_t)(rows - 1) * K + ng * 128) * 2), 0x00020000);
 
     auto issue = [&](SpkStage& st, int i) {
-        const int gl = i < ng - 1 ? i : ng - 1;
-        st.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, gl * 1024, 0));
-        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, l16 * 2, gl * 32, 0);
-        st.z = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, (((g0 + gl) >> 1) - zb0) * 16, 0);
+        const bool real = i < ng;                     // else: out of range, zeros, no memory access
+        st.w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, real ? i * 1024 : kBufOOB, 0));
+        st.s = __builtin_amdgcn_raw_buffer_load_b16(rs, l16 * 2, real ? i * 32 : kBufOOB, 0);
+        st.z = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, real ? (((g0 + i) >> 1) - zb0) * 16 : kBufOOB, 0);
     };
     SpkStage stage[STAGES];
 #pragma unroll

@@ -6,12 +6,23 @@
 // §8 (scale granularities, 128-wide blocks), §14 (W8A8), §22 (INT32 / FP32
 // accumulators).
 //
-// A block owns 16 output columns and a band of 16*TM activation rows for the
-// whole of K; its 4, 8 or 16 waves take the 128-wide K blocks round-robin, so the
-// block streams its 16 weight rows front to back while every wave has its
-// own loads in flight.  Each lane loads 32 bytes of K per weight row and per
-// activation row and K block (16-byte buffer loads, software-pipelined
-// STAGES deep, issued unconditionally so the in-order counter never drains).
+// A block owns 16*TN output columns (TN weight tiles of 16 rows) and a band
+// of 16*TM activation rows for the whole of K; its 4, 8 or 16 waves take the
+// 128-wide K blocks round-robin, so the block streams its weight rows front
+// to back while every wave has its own loads in flight.  Each lane loads 32
+// bytes of K per weight row and K block (16-byte buffer loads, software-
+// pipelined STAGES deep, issued unconditionally so the in-order counter never
+// drains; past the wave's last K block they address beyond the buffer and
+// return zeros without a memory access).  Loads of 16 rows x 64 bytes stream
+// as fast as contiguous ones on this device (measured: the same bytes in 16 x
+// 64-byte row pieces or in 1 KB runs of one row, within 2 %).
+//
+// XL (M <= 16, when the rows fit): the block first copies its activation rows
+// (all of K) into LDS, and the activation operand is read from there, so a
+// stage holds weights only (deeper pipeline, no per-lane activation loads
+// that repeat a row 16 times at small M).  Otherwise the activation fragments
+// are loaded with the weights.
+//
 // The partial tiles of the waves are added in LDS in wave order (fixed
 // order: deterministic), then scaled and written.
 //
@@ -22,7 +33,7 @@
 // holds row 4(l/16) + e and column l % 16.  Rows past M read row M-1 and are
 // never written.  With 128x128 weight blocks and 1x128 activation groups
 // (FP8), each K block's product is scaled by s_a[m][kb] * s_w[n/128][kb] and
-// added in FP32.
+// added in FP32 (16*TN divides 128, so a block's tiles share one weight block).
 #include <type_traits>
 
 #include "bg_device.h"
@@ -33,44 +44,53 @@ namespace bg {
 namespace {
 enum { DO_F32 = 0, DO_F16 = 1, DO_BF16 = 2, DO_I32 = 5 };
 enum { DG_T = 0, DG_R = 1, DG_R128 = 2, DG_B128 = 3 };
-// Stages in flight per wave for NW waves per block and a 16*TM-row band:
-// deeper when fewer waves share a CU's registers (1024 threads leave 128
-// VGPRs per lane, 512 threads 256).
-template <int NW, int TM>
+// Stages in flight per wave for NW waves per block, a 16*TM-row band and TN
+// tiles: deeper when fewer waves share a CU's registers (1024 threads leave
+// 128 VGPRs per lane, 512 threads 256) and when the activations are in LDS.
+template <int NW, int TM, int TN, bool XL>
 struct DecCfg {
-    static constexpr int STAGES = NW == 4 ? (TM == 4 ? 4 : 8) : NW == 8 ? (TM == 4 ? 3 : 4) : (TM == 1 ? 4 : 2);
+    static constexpr int STAGES = XL ? 4 : NW == 4 ? (TM == 4 ? 4 : 8) : NW == 8 ? (TM == 4 ? 3 : 4) : (TM == 1 ? 4 : 2);
 };
 }  // namespace
 
-template <int TM>
+template <int TM, int TN, bool XL>
 struct W8Stage {
-    uint4 w[2];
-    uint4 a[TM][2];
+    uint4 w[TN][2];
+    uint4 a[XL ? 1 : TM][2];
     float sc[TM][4];                    // block-scaled FP8: s_a * s_w per row, this K block
 };
 
-template <bool FP8, bool BLOCK, int TM, int DNW>
+template <bool FP8, bool BLOCK, int TM, int TN, int DNW, bool XL>
 __global__ __launch_bounds__(DNW * 64) void k_w8a8_decode(const uint8_t* __restrict__ a, const float* __restrict__ as,
                                                           int a_gran, const uint8_t* __restrict__ w,
                                                           const float* __restrict__ ws, int w_gran, int64_t M,
                                                           int64_t N, int64_t K, void* __restrict__ y, int out_dt) {
+    static_assert(!XL || TM == 1, "LDS-staged activations: one 16-row band");
+    static_assert(128 % (16 * TN) == 0, "a block's tiles lie in one 128-wide weight block");
     using acc_t = typename std::conditional<FP8, float4_t, int4_t>::type;
-    constexpr int DSTAGES = DecCfg<DNW, TM>::STAGES;
+    constexpr int DSTAGES = DecCfg<DNW, TM, TN, XL>::STAGES;
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, q = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * TN;
     const int64_t m0 = (int64_t)blockIdx.y * 16 * TM;
     const int nkb = (int)(K >> 7);
     const int c0 = FP8 ? 2 * q : q, c1 = FP8 ? 2 * q + 1 : 4 + q;   // 16-byte K chunks of a K block
 
-    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + n0 * K), (short)0,
-                                                      (int)((N - n0 < 16 ? N - n0 : 16) * K), 0x00020000);
+    // weight rows past N (last block) read zeros
+    const int64_t wrows = N - n0 < 16 * TN ? N - n0 : 16 * TN;
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(w + n0 * K), (short)0, (int)(wrows * K),
+                                                      0x00020000);
     const int64_t rows_here = M - m0 < 16 * TM ? M - m0 : 16 * TM;
     const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a + m0 * K), (short)0,
                                                       (int)(rows_here * K), 0x00020000);
-    const uint32_t vw0 = (uint32_t)(l16 * K + c0 * 16), vw1 = (uint32_t)(l16 * K + c1 * 16);
+    uint32_t vw0[TN], vw1[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        vw0[j] = (uint32_t)((16 * j + l16) * K + c0 * 16);
+        vw1[j] = (uint32_t)((16 * j + l16) * K + c1 * 16);
+    }
     uint32_t va0[TM], va1[TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -78,19 +98,26 @@ __global__ __launch_bounds__(DNW * 64) void k_w8a8_decode(const uint8_t* __restr
         va0[i] = (uint32_t)(r * K + c0 * 16);
         va1[i] = (uint32_t)(r * K + c1 * 16);
     }
-    // block-scaled FP8: the rows of this lane's output (first operand = activations)
+    // block-scaled FP8: the weight block of this block's columns
     const int64_t nb = n0 >> 7;
+    const int64_t pitch = K + 16;                                 // LDS row pitch: rows 4 banks apart
 
-    auto issue = [&](W8Stage<TM>& st, int j) {
-        int kb = wave + j * DNW;
-        kb = kb < nkb ? kb : nkb - 1;                            // past the end: reload the last block
-        const int soff = kb * 128;
-        st.w[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw0, soff, 0));
-        st.w[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw1, soff, 0));
+    auto issue = [&](W8Stage<TM, TN, XL>& st, int jj) {
+        int kb = wave + jj * DNW;
+        const bool real = kb < nkb;
+        kb = real ? kb : nkb - 1;
+        const int soff = real ? kb * 128 : kBufOOB;              // past the end: zeros, no memory access
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            st.a[i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, va0[i], soff, 0));
-            st.a[i][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, va1[i], soff, 0));
+        for (int j = 0; j < TN; ++j) {
+            st.w[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw0[j], soff, 0));
+            st.w[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, vw1[j], soff, 0));
+        }
+        if constexpr (!XL) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                st.a[i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, va0[i], soff, 0));
+                st.a[i][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, va1[i], soff, 0));
+            }
         }
         if constexpr (BLOCK) {
             const float sw = ws[nb * nkb + kb];
@@ -104,58 +131,114 @@ __global__ __launch_bounds__(DNW * 64) void k_w8a8_decode(const uint8_t* __restr
         }
     };
 
-    acc_t acc[TM];
+    // XL: the first batch of activation chunks is requested before the weight
+    // stages, so that the in-order counter returns it first
+    constexpr int XB = 4;
+    const int cpr = (int)(K >> 4);                                // 16-byte chunks per row
+    const int xtotal = XL ? (int)rows_here * cpr : 0;
+    uint4 xv[XB];
+    auto x_load = [&](uint4 (&v)[XB], int cb) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) acc[i] = acc_t{};
-    auto consume = [&](const W8Stage<TM>& st) {
+        for (int u = 0; u < XB; ++u) {
+            const int c = cb + u * DNW * 64;
+            if (c < xtotal) v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, c * 16, 0, 0));
+        }
+    };
+    auto x_store = [&](const uint4 (&v)[XB], int cb) {
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            const int c = cb + u * DNW * 64;
+            if (c < xtotal) {
+                const int r = c / cpr, kc = c - r * cpr;
+                *reinterpret_cast<uint4*>(dyn_lds + r * pitch + kc * 16) = v[u];
+            }
+        }
+    };
+    if constexpr (XL) x_load(xv, threadIdx.x);
+
+    W8Stage<TM, TN, XL> stage[DSTAGES];
+#pragma unroll
+    for (int j = 0; j < DSTAGES; ++j) issue(stage[j], j);
+
+    if constexpr (XL) {
+        x_store(xv, threadIdx.x);
+        for (int cb = threadIdx.x + XB * DNW * 64; cb < xtotal; cb += XB * DNW * 64) {
+            uint4 v[XB];
+            x_load(v, cb);
+            x_store(v, cb);
+        }
+        __syncthreads();
+    }
+    const int arow = l16 < rows_here ? l16 : (int)rows_here - 1;
+
+    acc_t acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = acc_t{};
+    auto consume = [&](const W8Stage<TM, TN, XL>& st, int kb) {
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            if constexpr (FP8) {
-                const int8_t_v av = {(int)st.a[i][0].x, (int)st.a[i][0].y, (int)st.a[i][0].z, (int)st.a[i][0].w,
-                                     (int)st.a[i][1].x, (int)st.a[i][1].y, (int)st.a[i][1].z, (int)st.a[i][1].w};
-                const int8_t_v wv = {(int)st.w[0].x, (int)st.w[0].y, (int)st.w[0].z, (int)st.w[0].w,
-                                     (int)st.w[1].x, (int)st.w[1].y, (int)st.w[1].z, (int)st.w[1].w};
-                if constexpr (BLOCK) {
-                    const float4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, wv, float4_t{0, 0, 0, 0},
-                                                                                       0, 0, 0, 0, 0, 0);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[i][e] += p[e] * st.sc[i][e];
-                } else {
-                    acc[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, wv, acc[i], 0, 0, 0, 0, 0, 0);
-                }
+            uint4 a0, a1;
+            if constexpr (XL) {
+                const uint8_t* ap = dyn_lds + arow * pitch + kb * 128;
+                a0 = *reinterpret_cast<const uint4*>(ap + c0 * 16);
+                a1 = *reinterpret_cast<const uint4*>(ap + c1 * 16);
             } else {
+                a0 = st.a[i][0];
+                a1 = st.a[i][1];
+            }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int4_t av = {(int)st.a[i][h].x, (int)st.a[i][h].y, (int)st.a[i][h].z, (int)st.a[i][h].w};
-                    const int4_t wv = {(int)st.w[h].x, (int)st.w[h].y, (int)st.w[h].z, (int)st.w[h].w};
-                    acc[i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, wv, acc[i], 0, 0, 0);
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (FP8) {
+                    const int8_t_v av = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                                         (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const int8_t_v wv = {(int)st.w[j][0].x, (int)st.w[j][0].y, (int)st.w[j][0].z, (int)st.w[j][0].w,
+                                         (int)st.w[j][1].x, (int)st.w[j][1].y, (int)st.w[j][1].z, (int)st.w[j][1].w};
+                    if constexpr (BLOCK) {
+                        const float4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            av, wv, float4_t{0, 0, 0, 0}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][j][e] += p[e] * st.sc[i][e];
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, wv, acc[i][j], 0, 0, 0, 0,
+                                                                                      0, 0);
+                    }
+                } else {
+                    const int4_t av0 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
+                    const int4_t wv0 = {(int)st.w[j][0].x, (int)st.w[j][0].y, (int)st.w[j][0].z, (int)st.w[j][0].w};
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av0, wv0, acc[i][j], 0, 0, 0);
+                    const int4_t av1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+                    const int4_t wv1 = {(int)st.w[j][1].x, (int)st.w[j][1].y, (int)st.w[j][1].z, (int)st.w[j][1].w};
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av1, wv1, acc[i][j], 0, 0, 0);
                 }
             }
         }
     };
 
     const int nmine = (nkb - wave + DNW - 1) / DNW;              // K blocks of this wave (may be 0)
-    W8Stage<TM> stage[DSTAGES];
-#pragma unroll
-    for (int j = 0; j < DSTAGES; ++j) issue(stage[j], j);
     for (int j = 0; j < nmine; j += DSTAGES) {
 #pragma unroll
         for (int u = 0; u < DSTAGES; ++u) {
-            if (j + u < nmine) consume(stage[u]);
+            if (j + u < nmine) consume(stage[u], wave + (j + u) * DNW);
             issue(stage[u], j + u + DSTAGES);
         }
     }
 
     // ---- fixed-order sum of the waves' partial tiles ----
-    acc_t* red = reinterpret_cast<acc_t*>(dyn_lds);              // [DNW][TM][64]
+    if constexpr (XL) __syncthreads();                            // the staged rows are dead
+    acc_t* red = reinterpret_cast<acc_t*>(dyn_lds);              // [DNW][TM * TN][64]
 #pragma unroll
-    for (int i = 0; i < TM; ++i) red[(wave * TM + i) * 64 + lane] = acc[i];
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) red[((wave * TM + i) * TN + j) * 64 + lane] = acc[i][j];
     __syncthreads();
-    // wave v finishes band rows 16i of tiles i with i % DNW == v (TM <= DNW): one wave per band
-    for (int i = wave; i < TM; i += DNW) {
-        acc_t v = red[(0 * TM + i) * 64 + lane];
-        for (int v2 = 1; v2 < DNW; ++v2) v += red[(v2 * TM + i) * 64 + lane];
-        const int64_t n = n0 + l16;
+    // wave v finishes the (band, tile) pairs u = v, v + DNW, ...
+    for (int u = wave; u < TM * TN; u += DNW) {
+        const int i = u / TN, j = u - i * TN;
+        acc_t v = red[u * 64 + lane];
+        for (int v2 = 1; v2 < DNW; ++v2) v += red[(v2 * TM * TN + u) * 64 + lane];
+        const int64_t n = n0 + 16 * j + l16;
         if (n >= N) continue;
         float sw = 1.0f;
         if (!BLOCK && out_dt != DO_I32) sw = w_gran == DG_T ? ws[0] : ws[n];
@@ -182,29 +265,52 @@ __global__ __launch_bounds__(DNW * 64) void k_w8a8_decode(const uint8_t* __restr
     }
 }
 
-template <bool FP8, bool BLOCK, int TM, int NW>
+template <bool FP8, bool BLOCK, int TM, int TN, int NW, bool XL>
 static const char* decode_cfg(const W8A8Args& g, hipStream_t s) {
-    const dim3 grid((unsigned)((g.N + 15) / 16), (unsigned)((g.M + 16 * TM - 1) / (16 * TM)));
-    const size_t lds = (size_t)NW * TM * 64 * 16;
-    auto kern = k_w8a8_decode<FP8, BLOCK, TM, NW>;
+    const dim3 grid((unsigned)(((g.N + 15) / 16 + TN - 1) / TN), (unsigned)((g.M + 16 * TM - 1) / (16 * TM)));
+    size_t lds = (size_t)NW * TM * TN * 64 * 16;
+    if (XL) {
+        const size_t xb = (size_t)(g.M < 16 ? g.M : 16) * (g.K + 16);
+        lds = xb > lds ? xb : lds;
+    }
+    auto kern = k_w8a8_decode<FP8, BLOCK, TM, TN, NW, XL>;
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, static_cast<const uint8_t*>(g.a), g.a_scales, g.a_gran,
                        static_cast<const uint8_t*>(g.w), g.w_scales, g.w_gran, g.M, g.N, g.K, g.y, g.out_dt);
-    return kname("k_w8a8_decode", FP8, BLOCK, TM, NW);
+    return kname("k_w8a8_decode", FP8, BLOCK, TM, TN, NW, XL);
+}
+
+// Activation rows staged in LDS (M <= 16) while they take at most 144 KB
+// (K <= 9200 at M = 16, K <= 14336 through M = 10): measured on the
+// projection shapes, one tile per
+// block with 8 waves unless the grid would not fill the device evenly -- two
+// tiles with 4 waves for 256 < N/16 < 1024 (qkv: 192 blocks beat 384), four
+// tiles with 4 waves on wide layers from M = 5 on (the staged rows are then
+// shared by four tiles).
+bool w8_decode_xl(int64_t M, int64_t K) { return M <= 16 && (M < 16 ? M : 16) * (K + 16) <= 144 * 1024; }
+
+template <bool FP8, bool BLOCK>
+static const char* decode_xl(const W8A8Args& g, hipStream_t s) {
+    const int64_t tiles = (g.N + 15) / 16;
+    if (tiles >= 1024 && g.M > 4) return decode_cfg<FP8, BLOCK, 1, 4, 4, true>(g, s);
+    if (tiles > 256 && tiles < 1024) return decode_cfg<FP8, BLOCK, 1, 2, 4, true>(g, s);
+    return decode_cfg<FP8, BLOCK, 1, 1, 8, true>(g, s);
 }
 
 // Waves per block: as many as keep at least 4 K blocks per wave, and no more
 // than needed for about 4096 waves in the grid.
 template <bool FP8, bool BLOCK, int TM>
 static const char* decode_nw(const W8A8Args& g, hipStream_t s) {
+    if constexpr (TM == 1)
+        if (w8_decode_xl(g.M, g.K)) return decode_xl<FP8, BLOCK>(g, s);
     const int64_t blocks = ((g.N + 15) / 16) * ((g.M + 16 * TM - 1) / (16 * TM));
     const int64_t nkb = g.K >> 7;
     if constexpr (TM < 4)                                         // (a 64-row band needs the registers of 8 waves)
-        if (nkb >= 64 && blocks * 8 < 4096) return decode_cfg<FP8, BLOCK, TM, 16>(g, s);
-    if (nkb >= 32 && blocks * 4 < 4096) return decode_cfg<FP8, BLOCK, TM, 8>(g, s);
-    return decode_cfg<FP8, BLOCK, TM, 4>(g, s);
+        if (nkb >= 64 && blocks * 8 < 4096) return decode_cfg<FP8, BLOCK, TM, 1, 16, false>(g, s);
+    if (nkb >= 32 && blocks * 4 < 4096) return decode_cfg<FP8, BLOCK, TM, 1, 8, false>(g, s);
+    return decode_cfg<FP8, BLOCK, TM, 1, 4, false>(g, s);
 }
 
 template <int TM>

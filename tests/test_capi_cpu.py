@@ -172,23 +172,27 @@ def test_auto_dispatch_thresholds(L):
     seen = {L.gemm_w4a16_algo(m, 4096, 4096, BF16) for m in range(1, 300)}
     assert seen == {SKINNY, TILED}
     assert GEMV not in seen        # the VALU GEMV is reachable through gemm_w4a16_ex only
-    # W8A8: small-M kernel at decode sizes, tiled once the 256 x 128 tiles fill the device
-    for n, k in ((6144, 4096), (4096, 4096), (4096, 14336)):
+    # W8A8: small-M kernel at decode sizes (through M = 16 on every shape),
+    # tiled once the 256 x 128 tiles fill the device
+    for n, k in ((6144, 4096), (4096, 4096), (4096, 14336), (28672, 4096)):
         assert L.gemm_w8a8_algo(1, n, k, I8) == SKINNY
         assert L.gemm_w8a8_algo(8, n, k, FP8) == SKINNY
+        assert L.gemm_w8a8_algo(16, n, k, I8) == SKINNY
         assert L.gemm_w8a8_algo(129, n, k, I8) == TILED
-    assert L.gemm_w8a8_algo(1, 28672, 4096, I8) == TILED       # 224 tiles already
-    assert L.gemm_w8a8_algo(16, 28672, 4096, I8) == TILED
+    assert L.gemm_w8a8_algo(17, 28672, 4096, I8) == TILED      # 224 tiles already
     assert L.gemm_w8a8_algo(32, 4096, 14336, I8) == SKINNY
     assert L.gemm_w8a8_algo(128, 4096, 14336, I8) == SKINNY    # 32 tiles, long K
     assert L.gemm_w8a8_algo(128, 4096, 4096, I8) == TILED      # 32 tiles, short K
     # with a workspace: the split large-M kernel where it measured faster
     ws8 = L.gemm_w8a8_workspace_bytes
-    assert ws8(1, 6144, 4096, I8, 1, 0) > 0                     # qkv: any M
-    assert ws8(1, 4096, 14336, I8, 1, 0) == 0                   # down at M = 1: small-M kernel
-    assert ws8(4, 4096, 14336, FP8, 0, 0) > 0                   # down from M = 4
-    assert ws8(16, 4096, 4096, I8, 1, 0) == 0                   # o below M = 32: small-M kernel
-    assert ws8(32, 4096, 4096, I8, 1, 0) == 32 * 4096 * 4 * (512 // 32 if 512 // 32 < 4 else 4)
+    for n, k in ((6144, 4096), (4096, 4096), (4096, 14336), (28672, 4096)):
+        assert ws8(1, n, k, I8, 1, 0) == 0                      # small-M kernel through M = 16
+        assert ws8(16, n, k, FP8, 0, 0) == 0
+    assert ws8(17, 6144, 4096, I8, 1, 0) > 0                    # qkv above M = 16: split large-M
+    assert ws8(17, 4096, 14336, FP8, 0, 0) > 0                  # down above M = 16
+    assert ws8(24, 4096, 4096, I8, 1, 0) == 0                   # o through M = 32: small-M kernel
+    assert ws8(32, 4096, 4096, I8, 1, 0) == 0
+    assert ws8(48, 4096, 4096, I8, 1, 0) == 48 * 4096 * 4 * 4            # above: split large-M, S = 4
     assert ws8(2048, 28672, 4096, I8, 1, 0) == 0                # full grid: no split
 
 

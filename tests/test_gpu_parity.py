@@ -330,6 +330,31 @@ def test_w8a8_small(ops, orc, algo, M, fp8, a_gran, w_gran, out):
     _w8a8_case(ops, orc, M, 256, 384, fp8, a_gran, w_gran, algo, out_dtype=out, seed=M)
 
 
+# The small-M kernel with the activation rows in LDS deals 1, 2 or 4 weight
+# tiles to a block (2 for 256 < N/16 < 1024, 4 from N/16 = 1024 at M > 4); N
+# here leaves the last block with fewer tiles.  K = 14336 puts M = 10 inside
+# and M = 11 outside the LDS limit of the staged rows.
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("N", [6416, 16480])
+@pytest.mark.parametrize("fp8,a_gran,w_gran,out", [
+    (False, 1, 1, torch.int32), (False, 1, 1, torch.bfloat16), (True, 0, 0, torch.float16),
+    (True, 1, 1, torch.float32)])
+def test_w8a8_decode_multi_tile(ops, orc, M, N, fp8, a_gran, w_gran, out):
+    _w8a8_case(ops, orc, M, N, 384, fp8, a_gran, w_gran, 2, out_dtype=out, seed=M + N)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("N", [6272, 16640])
+def test_w8a8_decode_multi_tile_fp8_blocks(ops, orc, M, N):
+    _w8a8_case(ops, orc, M, N, 512, True, 2, 3, 2, seed=M + N)
+
+
+@pytest.mark.parametrize("M", [10, 11])
+@pytest.mark.parametrize("fp8,a_gran,w_gran", [(False, 1, 1), (True, 0, 0), (True, 2, 3)])
+def test_w8a8_decode_staging_limit(ops, orc, M, fp8, a_gran, w_gran):
+    _w8a8_case(ops, orc, M, 256, 14336, fp8, a_gran, w_gran, 2, seed=M)
+
+
 @pytest.mark.parametrize("fp8,a_gran,w_gran,out", [
     (False, 1, 1, torch.float32), (False, 0, 1, torch.float16), (False, 1, 1, torch.int32),
     (True, 1, 0, torch.float32), (True, 0, 0, torch.float16)])
