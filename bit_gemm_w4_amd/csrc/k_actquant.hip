@@ -28,23 +28,56 @@ namespace bg {
 
 enum { G_TENSOR = 0, G_ROW = 1, G_ROW_G128 = 2, G_BLOCK128 = 3 };
 
+// The scale of a unit and what its quotients v / s need: the codes are the
+// roundings of the correctly rounded binary32 quotient.  Rather than one
+// IEEE division per element (a long instruction sequence on this device), a
+// unit computes r = RN(1/s) once and each element takes Markstein's
+// correction of q0 = RN(v r): with the exact remainder e = v - q0 s (one
+// fma), RN(q0 + e r) is the correctly rounded quotient, since r is within
+// half an ulp of 1/s and q0 within one ulp of v/s (P. Markstein, IBM J. Res.
+// Dev. 34(1), 1990; the theorem holds without overflow or underflow).  Units
+// whose scale lies outside [2^-100, 2^100] (r could overflow, or the
+// remainder underflow) divide instead.
+struct QScale {
+    float s, r;
+    bool mk;
+};
+
 template <bool FP8>
-__device__ __forceinline__ float unit_scale(float amax) {
+__device__ __forceinline__ QScale unit_scale(float amax) {
     float s = amax / (FP8 ? 448.0f : 127.0f);
-    return s == 0.0f ? 1.0f : s;
+    s = s == 0.0f ? 1.0f : s;
+    return QScale{s, 1.0f / s, s >= 0x1p-100f && s <= 0x1p100f};
 }
 
-// Quantize 8 values with scale s and store 8 bytes at q[idx].
+__device__ __forceinline__ void quotients8(const float v[8], const QScale& u, float d[8]) {
+    if (u.mk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q0 = v[i] * u.r;
+            // (the sign is v's, as in v / s: -0 and quotients that round to
+            // zero stay negative)
+            d[i] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q0, u.s, v[i]), u.r, q0), v[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d[i] = v[i] / u.s;
+    }
+}
+
+// Quantize 8 values with the unit's scale and store 8 bytes at q[idx].
 template <bool FP8>
-__device__ __forceinline__ void quant_store8(const float v[8], float s, void* q, int64_t idx) {
+__device__ __forceinline__ void quant_store8(const float v[8], const QScale& u, void* q, int64_t idx) {
+    float d[8];
+    quotients8(v, u, d);
     uint32_t lo = 0, hi = 0;
     if constexpr (FP8) {
-        lo = e4m3x2(v[0] / s, v[1] / s) | (e4m3x2(v[2] / s, v[3] / s) << 16);
-        hi = e4m3x2(v[4] / s, v[5] / s) | (e4m3x2(v[6] / s, v[7] / s) << 16);
+        lo = e4m3x2(d[0], d[1]) | (e4m3x2(d[2], d[3]) << 16);
+        hi = e4m3x2(d[4], d[5]) | (e4m3x2(d[6], d[7]) << 16);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float r = __builtin_rintf(v[i] / s);
+            float r = __builtin_rintf(d[i]);
             r = __builtin_fminf(__builtin_fmaxf(r, -128.0f), 127.0f);
             const uint32_t b = (uint32_t)((int)r & 0xFF);
             if (i < 4) lo |= b << (8 * i);
@@ -90,30 +123,68 @@ __device__ __forceinline__ float block_max256(float a, float* red) {
 // registers and many rows resident per CU.
 constexpr int ROW_MAXIT = 8;
 
+// The chunk at byte offset off of the row behind buffer resource rs as 8
+// floats (16 bytes of F16 / BF16 or 32 of F32), times the 8 column factors at
+// byte offset coff of rc when CM.  Offset kBufOOB reads zeros, so a thread
+// can issue all its chunks unconditionally and keep them in flight together.
+template <int DT, bool CM>
+__device__ __forceinline__ void load8_buf(__amdgpu_buffer_rsrc_t rs, int off, __amdgpu_buffer_rsrc_t rc, int coff,
+                                          float v[8]) {
+    if constexpr (DT == DT_F32) {
+        const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 16, 0));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+        const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (DT == DT_BF16) {
+                v[2 * i] = __uint_as_float(u[i] << 16);
+                v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+            } else {
+                v[2 * i] = f16_to_f32(u[i] & 0xFFFFu);
+                v[2 * i + 1] = f16_to_f32(u[i] >> 16);
+            }
+        }
+    }
+    if constexpr (CM) {
+        const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff, 0, 0));
+        const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rc, coff, 16, 0));
+        v[0] *= a.x; v[1] *= a.y; v[2] *= a.z; v[3] *= a.w;
+        v[4] *= b.x; v[5] *= b.y; v[6] *= b.z; v[7] *= b.w;
+    }
+}
+
 template <int DT, bool FP8, bool CM, int IT>
 __global__ __launch_bounds__(256) void k_quant_row(const void* __restrict__ x, int64_t C,
                                                    void* __restrict__ q, float* __restrict__ scales,
                                                    const float* __restrict__ cm) {
     __shared__ float red[4];
+    constexpr int EB = DT == DT_F32 ? 4 : 2;
     const int64_t r = blockIdx.x;
-    const int64_t nchunk = C >> 3;
+    const int nchunk = (int)(C >> 3);
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(x) + r * C * EB), (short)0, (int)(C * EB), 0x00020000);
+    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(cm), (short)0, CM ? (int)(C * 4) : 0,
+                                                      0x00020000);
     float v[IT][8];
     float a = 0.0f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-        const int64_t c = (int64_t)it * 256 + threadIdx.x;
-        if (c < nchunk) {
-            load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v[it]);
-            a = __builtin_fmaxf(a, amax8(v[it]));
-        }
+        const int c = it * 256 + (int)threadIdx.x;
+        load8_buf<DT, CM>(rs, c < nchunk ? c * 8 * EB : kBufOOB, rc, c < nchunk ? c * 32 : kBufOOB, v[it]);
     }
-    const float s = unit_scale<FP8>(block_max256(a, red));
+#pragma unroll
+    for (int it = 0; it < IT; ++it) a = __builtin_fmaxf(a, amax8(v[it]));     // out-of-range chunks are 0
+    const QScale u = unit_scale<FP8>(block_max256(a, red));
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int64_t c = (int64_t)it * 256 + threadIdx.x;
-        if (c < nchunk) quant_store8<FP8>(v[it], s, q, r * C + c * 8);
+        if (c < nchunk) quant_store8<FP8>(v[it], u, q, r * C + c * 8);
     }
-    if (threadIdx.x == 0) scales[r] = s;
+    if (threadIdx.x == 0) scales[r] = u.s;
 }
 
 // Rows longer than 256 * 8 * ROW_MAXIT: amax pass, then a second read.
@@ -131,12 +202,12 @@ __global__ __launch_bounds__(256) void k_quant_row_2pass(const void* __restrict_
         load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v);
         a = __builtin_fmaxf(a, amax8(v));
     }
-    const float s = unit_scale<FP8>(block_max256(a, red));
+    const QScale u = unit_scale<FP8>(block_max256(a, red));
     for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
         load8<DT, CM>(x, r * C + c * 8, cm, c * 8, v);
-        quant_store8<FP8>(v, s, q, r * C + c * 8);
+        quant_store8<FP8>(v, u, q, r * C + c * 8);
     }
-    if (threadIdx.x == 0) scales[r] = s;
+    if (threadIdx.x == 0) scales[r] = u.s;
 }
 
 // ---- 1 x 128 groups: 16 consecutive lanes per group ----
@@ -148,9 +219,9 @@ __global__ __launch_bounds__(256) void k_quant_g128(const void* __restrict__ x, 
     if (t >= total_chunks) return;          // total_chunks is a multiple of 16
     float v[8];
     load8<DT, CM>(x, t * 8, cm, CM ? (t % (C >> 3)) * 8 : 0, v);
-    const float s = unit_scale<FP8>(wave_max<16>(amax8(v)));
-    quant_store8<FP8>(v, s, q, t * 8);
-    if ((t & 15) == 0) scales[t >> 4] = s;
+    const QScale u = unit_scale<FP8>(wave_max<16>(amax8(v)));
+    quant_store8<FP8>(v, u, q, t * 8);
+    if ((t & 15) == 0) scales[t >> 4] = u.s;
 }
 
 // ---- MXFP8 / MXFP4: 32-element blocks along a row, 4 consecutive lanes per block ----
@@ -245,21 +316,47 @@ __global__ __launch_bounds__(256) void k_quant_block128(const void* __restrict__
         load8<DT, CM>(x, row * C + cb * 128 + lane_c * 8, cm, cb * 128 + lane_c * 8, v[it]);
         a = __builtin_fmaxf(a, amax8(v[it]));
     }
-    const float s = unit_scale<FP8>(block_max256(a, red));
+    const QScale u = unit_scale<FP8>(block_max256(a, red));
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int64_t row = rb * 128 + it * 16 + lane_r;
-        quant_store8<FP8>(v[it], s, q, row * C + cb * 128 + lane_c * 8);
+        quant_store8<FP8>(v[it], u, q, row * C + cb * 128 + lane_c * 8);
     }
-    if (threadIdx.x == 0) scales[blockIdx.x] = s;
+    if (threadIdx.x == 0) scales[blockIdx.x] = u.s;
 }
 
 // ---- whole tensor ----
 __global__ void k_clear_amax(float* __restrict__ scales) { scales[1] = 0.0f; }
 
-// Grid-stride passes over the whole tensor, TU chunks of 8 elements per
-// thread and iteration so that several 16-byte loads are in flight at once.
-constexpr int TU = 4;
+// Both passes walk the tensor in tiles of TU * 256 chunks (8 elements each),
+// tile t = blockIdx.x, + gridDim.x, ...; a thread issues its TU chunks of a
+// tile unconditionally (buffer loads; chunks past the end read zeros), so
+// they are in flight together.  The amax pass runs at most one block per CU
+// with 8 chunks per thread: every block ends in an atomic on the one amax
+// slot, and those serialize (measured: 1024 blocks' atomics cost 12 us on a
+// 2048 x 4096 tensor, 256 blocks' about 3 us).
+constexpr int TU = 4, TU_AMAX = 8;
+constexpr unsigned AMAX_GRID = 256;
+
+template <int DT, bool CM, int TUN>
+__device__ __forceinline__ void load_tile(const void* x, const float* cm, int64_t nchunk, int64_t C, int64_t t,
+                                          float (&v)[TUN][8]) {
+    constexpr int EB = DT == DT_F32 ? 4 : 2;
+    constexpr int64_t TILE_CHUNKS = TUN * 256;
+    const int64_t c0 = t * TILE_CHUNKS;
+    const int64_t n = nchunk - c0 < TILE_CHUNKS ? nchunk - c0 : TILE_CHUNKS;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(x) + c0 * 8 * EB), (short)0, (int)(n * 8 * EB), 0x00020000);
+    const auto rc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(cm), (short)0, CM ? (int)(C * 4) : 0,
+                                                      0x00020000);
+#pragma unroll
+    for (int u = 0; u < TUN; ++u) {
+        const int i = u * 256 + (int)threadIdx.x;
+        // column of the chunk's first element (rows are whole chunks: C % 8 == 0)
+        const int col = CM ? (int)(((c0 + i) % (C >> 3)) * 8) : 0;
+        load8_buf<DT, CM>(rs, i < n ? i * 8 * EB : kBufOOB, rc, i < n ? col * 4 : kBufOOB, v[u]);
+    }
+}
 
 template <int DT, bool CM>
 __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x, int64_t nchunk,
@@ -267,16 +364,12 @@ __global__ __launch_bounds__(256) void k_amax_tensor(const void* __restrict__ x,
                                                      int64_t C) {
     __shared__ float red[4];
     float a = 0.0f;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < nchunk; c0 += TU * stride) {
-        float v[TU][8];
+    const int64_t tiles = (nchunk + TU_AMAX * 256 - 1) / (TU_AMAX * 256);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        float v[TU_AMAX][8];
+        load_tile<DT, CM, TU_AMAX>(x, cm, nchunk, C, t, v);
 #pragma unroll
-        for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk)
-                load8<DT, CM>(x, (c0 + u * stride) * 8, cm, CM ? ((c0 + u * stride) % (C >> 3)) * 8 : 0, v[u]);
-#pragma unroll
-        for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk) a = __builtin_fmaxf(a, amax8(v[u]));
+        for (int u = 0; u < TU_AMAX; ++u) a = __builtin_fmaxf(a, amax8(v[u]));
     }
     a = block_max256(a, red);
     // Only blocks that would raise the running maximum take the atomic (all
@@ -295,24 +388,23 @@ __global__ __launch_bounds__(256) void k_quant_tensor(const void* __restrict__ x
                                                       void* __restrict__ q,
                                                       float* __restrict__ scales,
                                                       const float* __restrict__ cm, int64_t C) {
-    const float s = unit_scale<FP8>(scales[1]);
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t c0 = (int64_t)blockIdx.x * 256 + threadIdx.x; c0 < nchunk; c0 += TU * stride) {
+    const QScale us = unit_scale<FP8>(scales[1]);
+    const int64_t tiles = (nchunk + TU * 256 - 1) / (TU * 256);
+    for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
         float v[TU][8];
+        load_tile<DT, CM, TU>(x, cm, nchunk, C, t, v);
 #pragma unroll
-        for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk)
-                load8<DT, CM>(x, (c0 + u * stride) * 8, cm, CM ? ((c0 + u * stride) % (C >> 3)) * 8 : 0, v[u]);
-#pragma unroll
-        for (int u = 0; u < TU; ++u)
-            if (c0 + u * stride < nchunk) quant_store8<FP8>(v[u], s, q, (c0 + u * stride) * 8);
+        for (int u = 0; u < TU; ++u) {
+            const int64_t c = t * TU * 256 + u * 256 + threadIdx.x;
+            if (c < nchunk) quant_store8<FP8>(v[u], us, q, c * 8);
+        }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) scales[0] = us.s;
 }
 
-static unsigned grid_for(int64_t nchunk) {
-    int64_t b = (nchunk + 256 * TU - 1) / (256 * TU);
-    if (b > 256 * 8) b = 256 * 8;          // grid-stride beyond 8 blocks per CU
+static unsigned grid_for(int64_t nchunk, int tu, unsigned cap) {
+    int64_t b = (nchunk + tu * 256 - 1) / (tu * 256);
+    if (b > cap) b = cap;                  // tile-stride beyond the cap
     return (unsigned)(b < 1 ? 1 : b);
 }
 
@@ -352,10 +444,10 @@ static const char* launch_typed(const void* x, int64_t R, int64_t C, int gran, v
         default: {
             const int64_t chunks = R * (C >> 3);
             hipLaunchKernelGGL(k_clear_amax, dim3(1), dim3(1), 0, s, sc);
-            hipLaunchKernelGGL((k_amax_tensor<DT, CM>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks, sc, cm,
-                               C);
-            hipLaunchKernelGGL((k_quant_tensor<DT, FP8, CM>), dim3(grid_for(chunks)), dim3(256), 0, s, x, chunks,
-                               q, sc, cm, C);
+            hipLaunchKernelGGL((k_amax_tensor<DT, CM>), dim3(grid_for(chunks, TU_AMAX, AMAX_GRID)), dim3(256), 0, s, x,
+                               chunks, sc, cm, C);
+            hipLaunchKernelGGL((k_quant_tensor<DT, FP8, CM>), dim3(grid_for(chunks, TU, 256 * 8)), dim3(256), 0, s,
+                               x, chunks, q, sc, cm, C);
             return kname("k_quant_tensor", DT, FP8, CM);
         }
     }

@@ -261,6 +261,44 @@ def test_act_quant_full_shapes(ops, orc, fp8, gran, rows, cols, dtype):
     assert np.array_equal(q.cpu().numpy().view(np.uint8), qo.view(np.uint8))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_act_quant_quotient_rounding(ops, orc, fp8):
+    """Random per-row scales, and quotients v / s within two ulps of the INT8
+    half-integers or the E4M3 midpoints: the codes are those of the correctly
+    rounded binary32 quotient (the oracle divides).  Rows 0-3 have scales
+    outside [2^-100, 2^100] (amax 1e-36, 3e-38, 1e37, 3e38)."""
+    from pins import _e4m3_finite_table
+    rng = np.random.default_rng(11 + fp8)
+    R, C = 512, 1024
+    qmax = np.float32(448.0 if fp8 else 127.0)
+    if fp8:
+        vals, _ = _e4m3_finite_table()
+        vals = vals[vals >= 0]
+        bnd = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    else:
+        bnd = (np.arange(127, dtype=np.float32) + np.float32(0.5))
+    amax = (np.float32(2.0) ** rng.uniform(-20, 20, R).astype(np.float32) *
+            rng.uniform(1, 2, R).astype(np.float32)).astype(np.float32)
+    amax[:4] = np.array([1e-36, 3e-38, 1e37, 3e38], np.float32)
+    s = (amax / qmax).astype(np.float32)
+    b = bnd[rng.integers(0, bnd.size, (R, C - 1))]
+    v = (b * s[:, None]).astype(np.float32)
+    for k in range(2):
+        up = rng.random((R, C - 1)) < 0.3
+        dn = rng.random((R, C - 1)) < 0.3
+        v = np.where(up, np.nextafter(v, np.float32(np.inf)), v)
+        v = np.where(dn, np.nextafter(v, np.float32(-np.inf)), v)
+    v = np.minimum(v, amax[:, None])
+    v = np.where(rng.random((R, C - 1)) < 0.5, -v, v).astype(np.float32)
+    x = np.concatenate([amax[:, None], v], axis=1)
+    q, sc = (ops.act_quant_fp8 if fp8 else ops.act_quant_int8)(torch.from_numpy(x).cuda(), 1)
+    qo, so = (orc.act_quant_fp8 if fp8 else orc.act_quant_int8)(x, 1)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), so.view(np.uint32))
+    qv, qov = q.cpu().numpy().view(np.uint8), qo.view(np.uint8)
+    bad = np.argwhere(qv != qov)
+    assert bad.size == 0, (bad[:5], x[tuple(bad[0])] if bad.size else None)
+
+
 def test_fp8_encoder_rounding(ops, orc):
     """Every row holds 448 (so its scale is exactly 1) and then values around
     every E4M3 rounding boundary: the codes are the device encoder's cast."""
