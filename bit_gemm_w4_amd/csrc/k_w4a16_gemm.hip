@@ -380,7 +380,10 @@ __global__ __launch_bounds__(128 * WM, 1) void k_w4a16_gemm(const uint16_t* __re
         step(f1, f0, ks + 1, false);
     }
     wait_vmcnt<0>();
-    wait_lgkm0();
+    // the last step read the (unused) stage after the slice into f0: those
+    // registers stay allocated until the reads have landed, or a value the
+    // compiler put there (the group close, the epilogue) would be overwritten
+    settle_frags(f0);
     const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;
     if (S > 1) {
         // FP32 partial tile of slice sl -> ws[sl][M][N] (k_w4a16_gemm_reduce adds

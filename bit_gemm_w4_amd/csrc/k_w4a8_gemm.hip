@@ -317,7 +317,10 @@ __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __rest
         step(f1, f0, ks + 1, false);
     }
     wait_vmcnt<0>();                                             // no copy may land after the block exits
-    wait_lgkm0();
+    // the last step read the (unused) stage after the slice into f0: those
+    // registers stay allocated until the reads have landed, or a value the
+    // compiler put there (the group close, the epilogue) would be overwritten
+    settle_frags(f0);
 
     // ---- epilogue: row scale s_a, then the output type ----
     const int64_t mw = m0 + wm * WTM, nw = n0 + wn * WTN;

@@ -470,7 +470,10 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
         step(f1, f0, kb + 1);
     }
     wait_vmcnt<0>();                                             // no copy may land after the block exits
-    wait_lgkm0();
+    // the last step read the (unused) stage after the slice into f0: those
+    // registers stay allocated until the reads have landed, or a value the
+    // compiler put there (a close, the epilogue) would be overwritten
+    settle_frags(f0);
 
     // ---- side path (OL) ----
     // acc becomes the float (acc * s_a[m]) in place, then gains
