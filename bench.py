@@ -93,6 +93,19 @@ def time_graph(g, reps, torch, trials=5, warm_ms=20.0, trial_ms=2.0):
     return sorted(ts)[len(ts) // 2]
 
 
+def per_call(fns, reps, torch):
+    """Milliseconds per call of the calls in fns, captured together in one
+    graph: a graph holding one short call would time the graph launch."""
+    g = graph_of(lambda: [f() for f in fns], torch)
+    return time_graph(g, reps, torch) / len(fns)
+
+
+def rotated(t, min_bytes=320 << 20):
+    """t and enough copies of it that they do not all fit the 256 MB MALL."""
+    n = max(1, -(-min_bytes // (t.numel() * t.element_size())))
+    return [t] + [t.clone() for _ in range(n - 1)]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -349,6 +362,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
         w, x = synth.prefill_layer(M, N, K, seed=0)
         xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
         wt = torch.from_numpy(w).to(dev)
+        xrot = rotated(xt)                              # quantizer timings read X from HBM
         variants = [("int8_row", False, 1, 1)]
         if name in ("gate_up", "down"):
             variants += [("fp8_tensor", True, 0, 0), ("fp8_block", True, 2, 3)]
@@ -357,11 +371,9 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             a, a_s = quant(xt, ag)
             wq, w_s = quant(wt, wg)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            g = graph_of(lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y), torch)
-            ms = time_graph(g, 10, torch)
+            ms = per_call([lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y)] * 4, 10, torch)
             kname = ops.last_kernel()
-            gq = graph_of(lambda: quant(xt, ag), torch)
-            ms_q = time_graph(gq, 200, torch)
+            ms_q = per_call([lambda x=x: quant(x, ag) for x in xrot], 20, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp8" if fp8 else "i8"]
             res["w8a8_m2048"][f"{name}/{tag}"] = {
@@ -377,8 +389,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
         a, a_s = ops.act_quant_int8(xt, ops.GRAN_ROW)
         p = packs[name][0]
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        g = graph_of(lambda: ops.gemm_w4a8(a, a_s, ops.GRAN_ROW, p, out=y), torch)
-        ms = time_graph(g, 10, torch)
+        ms = per_call([lambda: ops.gemm_w4a8(a, a_s, ops.GRAN_ROW, p, out=y)] * 4, 10, torch)
         tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
         peak = roofline.PEAK_TFLOPS["i8"]
         res["w4a8_m2048"][name] = {"gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
@@ -389,11 +400,9 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             a, ea = ops.act_quant_mxfp8(xt)
             q, ew = ops.act_quant_mxfp8(wt)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            g = graph_of(lambda: ops.gemm_mxfp8(a, ea, q, ew, out=y), torch)
-            ms = time_graph(g, 10, torch)
+            ms = per_call([lambda: ops.gemm_mxfp8(a, ea, q, ew, out=y)] * 4, 10, torch)
             kname = ops.last_kernel()
-            gq = graph_of(lambda: ops.act_quant_mxfp8(xt), torch)
-            ms_q = time_graph(gq, 200, torch)
+            ms_q = per_call([lambda x=x: ops.act_quant_mxfp8(x) for x in xrot], 20, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp8"]
             res["w8a8_m2048"][f"{name}/mxfp8"] = {
@@ -406,11 +415,9 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             # MXFP4: E2M1 elements in both operands, the same E8M0 blocks
             a, ea = ops.act_quant_mxfp4(xt)
             q, ew = ops.act_quant_mxfp4(wt)
-            g = graph_of(lambda: ops.gemm_mxfp4(a, ea, q, ew, out=y), torch)
-            ms = time_graph(g, 10, torch)
+            ms = per_call([lambda: ops.gemm_mxfp4(a, ea, q, ew, out=y)] * 4, 10, torch)
             kname = ops.last_kernel()
-            gq = graph_of(lambda: ops.act_quant_mxfp4(xt), torch)
-            ms_q = time_graph(gq, 200, torch)
+            ms_q = per_call([lambda x=x: ops.act_quant_mxfp4(x) for x in xrot], 20, torch)
             tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
             peak = roofline.PEAK_TFLOPS["fp4"]
             qbytes = M * K * 2 + M * K // 2 + M * K // 32
@@ -428,9 +435,7 @@ def secondary(ops, synth, roofline, torch, np, dev, packs, graph_of, time_graph)
             x = synth.activations(B, K, "bf16", seed=1)
             xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
             y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
-            p = packs[name][0]
-            g = graph_of(lambda: ops.gemm_w4a16(xt, p, out=y), torch)
-            ms = time_graph(g, 10, torch)
+            ms = per_call([lambda p=p: ops.gemm_w4a16(xt, p, out=y) for p in packs[name]], 10, torch)
             tf = roofline.gemm_flops(B, N, K) / (ms * 1e-3) / 1e12
             res["w4a16_large_batch"][f"{name}@B{B}"] = {
                 "us": round(ms * 1e3, 1), "tflops": round(tf, 1), "frac_bf16_peak": round(tf / 2500.0, 4),
@@ -520,8 +525,7 @@ def fp8_sizes(ops, synth, roofline, torch, np, dev, graph_of, time_graph):
             for tag, ag, wg in (("tensor", 0, 0), ("block", 2, 3)):
                 a, a_s = ops.act_quant_fp8(xt, ag)
                 wq, w_s = ops.act_quant_fp8(wt, wg)
-                g = graph_of(lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y), torch)
-                ms = time_graph(g, 10, torch)
+                ms = per_call([lambda: ops.gemm_w8a8(a, a_s, ag, wq, w_s, wg, out=y)] * 2, 10, torch)
                 tf = roofline.gemm_flops(M, N, K) / (ms * 1e-3) / 1e12
                 peak = roofline.PEAK_TFLOPS["fp8"]
                 res[f"{name}/fp8_{tag}@M{M}"] = {"gemm_us": round(ms * 1e3, 1), "tflops": round(tf, 1),
@@ -639,10 +643,10 @@ def smoothquant(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph):
             yv = y[torch.from_numpy(rows).to(dev)].double().cpu().numpy()
             errs["folded" if fold else "plain"] = float(np.linalg.norm(yv - exact) / np.linalg.norm(exact))
         out[tag] = {k: round(v, 5) for k, v in errs.items()}
-    g0 = graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch)
-    g1 = graph_of(lambda: ops.act_quant_int8_smooth(xt, invd, ops.GRAN_ROW), torch)
-    out["act_quant_us"] = {"plain": round(time_graph(g0, 200, torch) * 1e3, 1),
-                           "folded": round(time_graph(g1, 200, torch) * 1e3, 1)}
+    xr = rotated(xt)
+    t0 = per_call([lambda x=x: ops.act_quant_int8(x, ops.GRAN_ROW) for x in xr], 20, torch)
+    t1 = per_call([lambda x=x: ops.act_quant_int8_smooth(x, invd, ops.GRAN_ROW) for x in xr], 20, torch)
+    out["act_quant_us"] = {"plain": round(t0 * 1e3, 1), "folded": round(t1 * 1e3, 1)}
     log(f"  smoothquant rel-L2 err per-token {out['per_token']['plain']:.4f} -> {out['per_token']['folded']:.4f}, "
         f"per-tensor {out['per_tensor']['plain']:.4f} -> {out['per_tensor']['folded']:.4f}; act_quant "
         f"{out['act_quant_us']['plain']} -> {out['act_quant_us']['folded']} us")
@@ -671,12 +675,13 @@ def llm_int8(ops, torch, np, dev, xt, wt, x_bits, w, graph_of, time_graph, tau=6
     e1 = float(np.linalg.norm(y1[ridx].double().cpu().numpy() - exact) / np.linalg.norm(exact))
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     t = {}
-    t["plain_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8(xt, ops.GRAN_ROW), torch), 200, torch)
-    t["plain_gemm_us"] = time_graph(graph_of(
-        lambda: ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out=y), torch), 10, torch)
-    t["detect_quant_us"] = time_graph(graph_of(lambda: ops.act_quant_int8_outlier(xt, tau), torch), 200, torch)
-    t["gemm_side_us"] = time_graph(graph_of(
-        lambda: ops.gemm_w8a8_outlier(q, sa, wq, w_s, ops.GRAN_ROW, xt, idx, cnt, out=y), torch), 10, torch)
+    xr = rotated(xt)
+    t["plain_quant_us"] = per_call([lambda x=x: ops.act_quant_int8(x, ops.GRAN_ROW) for x in xr], 20, torch)
+    t["plain_gemm_us"] = per_call(
+        [lambda: ops.gemm_w8a8(a, a_s, ops.GRAN_ROW, wq, w_s, ops.GRAN_ROW, out=y)] * 4, 10, torch)
+    t["detect_quant_us"] = per_call([lambda x=x: ops.act_quant_int8_outlier(x, tau) for x in xr], 20, torch)
+    t["gemm_side_us"] = per_call(
+        [lambda: ops.gemm_w8a8_outlier(q, sa, wq, w_s, ops.GRAN_ROW, xt, idx, cnt, out=y)] * 4, 10, torch)
     kname = ops.last_kernel()
     out = {"tau": tau, "outlier_channels": int(cnt.item()), "err_plain": round(e0, 5), "err_split": round(e1, 5)}
     out.update({k: round(v * 1e3, 1) for k, v in t.items()})

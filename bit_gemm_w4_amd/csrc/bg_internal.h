@@ -132,6 +132,11 @@ const char* launch_w8a8_skinny(const W8A8Args& args, hipStream_t s);
 // contents) K is split into S slices when the output tiles do not fill the
 // device; a second kernel on the same stream sums the FP32 partials.
 W4GemmSplit w4a8_gemm_split(int64_t M, int64_t N, int64_t K);
+// W4A8 at M <= 16 (k_w4a8_decode): whether the activation rows and the
+// waves' scale records fit its LDS budget, and the launch (no workspace).
+bool w4a8_decode_fits(int64_t M, int64_t N, int64_t K);
+const char* launch_w4a8_decode(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
+                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, hipStream_t s);
 const char* launch_w4a8_gemm(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, void* ws,
                              hipStream_t s);

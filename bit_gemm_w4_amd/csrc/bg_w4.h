@@ -1,4 +1,4 @@
-// bg_w4.h -- INT4 weight helpers shared by the W4A16 kernels (device only).
+// bg_w4.h -- INT4 weight helpers shared by the W4A16 and W4A8 kernels (device only).
 //
 // A nibble u OR-ed into the mantissa of the constant MV (BF16 128.0, FP16
 // 1024.0: the binade where one ulp is 1) is the exact 16-bit value MV + u.
@@ -110,6 +110,24 @@ __device__ __forceinline__ float4_t mfma16(const uint32_t a[4], const uint32_t b
 template <bool BF16>
 __device__ __forceinline__ uint16_t to_out(float v) {
     return BF16 ? f32_to_bf16(v) : f32_to_f16(v);
+}
+
+// The 16 signed bytes u - z of two packed words (k in order), z folded into
+// zc = 0x80808080 - z * 0x01010101: (u + 0x80 - z) per byte never carries,
+// and flipping bit 7 makes it the two's complement of u - z.  A word holds
+// its even k in the low nibbles and its odd k in the high ones; two byte
+// permutes put them back in k order.
+__device__ __forceinline__ int4_t w4_to_i8(uint2 wp, uint32_t zc) {
+    uint32_t d[4];
+    const uint32_t w2[2] = {wp.x, wp.y};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const uint32_t lo = w2[p] & 0x0F0F0F0Fu;            // bytes: k0 k4 k1 k5
+        const uint32_t hi = (w2[p] >> 4) & 0x0F0F0F0Fu;     // bytes: k2 k6 k3 k7
+        d[2 * p] = (__builtin_amdgcn_perm(hi, lo, 0x06040200u) + zc) ^ 0x80808080u;      // k0 k1 k2 k3
+        d[2 * p + 1] = (__builtin_amdgcn_perm(hi, lo, 0x07050301u) + zc) ^ 0x80808080u;  // k4 k5 k6 k7
+    }
+    return int4_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
 }
 
 }  // namespace bg

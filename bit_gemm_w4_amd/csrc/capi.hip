@@ -550,6 +550,11 @@ static bg_status w4a8_impl(const int8_t* a, const float* a_scales, int a_gran, i
     if (!aligned16(a) || !aligned16(a_scales) || !aligned16(qweight) || !aligned16(scales) || !aligned16(y) ||
         (zeros && !aligned16(zeros)) || (ws && !aligned16(ws)))
         return fail(BG_ERR_ALIGN, "gemm_w4a8: pointers must be 16-byte aligned");
+    if (bg::w4a8_decode_fits(M, N, K)) {
+        note_kernel(bg::launch_w4a8_decode(a, a_scales, a_gran == BG_GRAN_ROW, M, K, qweight, scales, zeros, N, y,
+                                           out_dtype, static_cast<hipStream_t>(stream)));
+        return launched("gemm_w4a8");
+    }
     void* use_ws = nullptr;
     if (with_ws) {
         const int64_t need = bg::w4a8_gemm_split(M, N, K).ws_bytes;
@@ -582,6 +587,7 @@ BG_EXPORT bg_status gemm_w4a8_ws(const int8_t* a, const float* a_scales, int a_g
 
 BG_EXPORT int64_t gemm_w4a8_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || M > kMaxM || N < 16 || N > kMaxRows || N % 16 || K < 256 || K > kMaxDim || K % 256) return 0;
+    if (bg::w4a8_decode_fits(M, N, K)) return 0;
     return bg::w4a8_gemm_split(M, N, K).ws_bytes;
 }
 

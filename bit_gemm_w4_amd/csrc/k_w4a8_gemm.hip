@@ -38,6 +38,7 @@
 #include "bg_device.h"
 #include "bg_internal.h"
 #include "bg_pipe.h"
+#include "bg_w4.h"
 
 namespace bg {
 
@@ -62,20 +63,6 @@ enum { QO_F32 = 0, QO_F16 = 1, QO_BF16 = 2 };
 // ((r >> 1) ^ (r >> 3)) & 3 spent half of the LDS cycles in conflicts.
 __device__ __forceinline__ int qswz(int r) { return (r ^ (r >> 2)) & 3; }
 
-// The 16 signed bytes u - z of two packed words (k in order), z folded into
-// zc = 0x80808080 - z * 0x01010101.
-__device__ __forceinline__ int4_t w4_to_i8(uint2 wp, uint32_t zc) {
-    uint32_t d[4];
-    const uint32_t w2[2] = {wp.x, wp.y};
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const uint32_t lo = w2[p] & 0x0F0F0F0Fu;            // bytes: k0 k4 k1 k5
-        const uint32_t hi = (w2[p] >> 4) & 0x0F0F0F0Fu;     // bytes: k2 k6 k3 k7
-        d[2 * p] = (__builtin_amdgcn_perm(hi, lo, 0x06040200u) + zc) ^ 0x80808080u;      // k0 k1 k2 k3
-        d[2 * p + 1] = (__builtin_amdgcn_perm(hi, lo, 0x07050301u) + zc) ^ 0x80808080u;  // k4 k5 k6 k7
-    }
-    return int4_t{(int)d[0], (int)d[1], (int)d[2], (int)d[3]};
-}
 }  // namespace
 
 __global__ __launch_bounds__(64 * Q_NW, 1) void k_w4a8_gemm(const int8_t* __restrict__ a,
