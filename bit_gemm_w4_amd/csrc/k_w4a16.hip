@@ -645,14 +645,19 @@ static const char* decode_cfg(const void* x, int64_t M, int64_t K, const uint32_
 }
 
 // Waves per block: enough blocks x waves to keep ~16 waves per CU resident
-// (at least 4), never more waves than K has groups.
+// (at least 4), never more waves than K has groups -- ~8 for a single
+// staged row (measured at B = 1: down 7.7 us with 8 waves per block against
+// 8.3 with 16, qkv 6.0 with 4 against 6.15 with 8, o equal; at B = 4 the
+// extra waves pay off again on down) and for blocks of four or more tiles
+// (gate_up at B = 4: 15.0 us with 4 waves, 16.6 with 8).
 template <bool BF16, int TM, int TN, bool XLDS, int VROWS>
 static const char* decode_nw(const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                              const uint8_t* zr, int64_t N, void* y, hipStream_t s) {
     constexpr int BAND = VROWS > 0 ? VROWS : 16 * TM;
     const int64_t blocks = (((N >> 4) + TN - 1) / TN) * ((M + BAND - 1) / BAND);
     const int64_t ngroups = K >> 7;
-    int64_t want = (4096 + blocks - 1) / blocks;
+    const int64_t waves_per_device = XLDS && TM == 1 && VROWS == 0 && (M == 1 || TN >= 4) ? 2048 : 4096;
+    int64_t want = (waves_per_device + blocks - 1) / blocks;
     if (want > ngroups) want = ngroups;
     // 16 waves per block caps a thread at 128 VGPRs: only the light variants
     constexpr bool fits16 = VROWS > 0 ? (VROWS == 1 && TN == 1) : (TM * TN == 1 || (XLDS && TM * TN == 2));
@@ -693,6 +698,9 @@ static const char* decode_dt(const void* x, int64_t M, int64_t K, const uint32_t
                 if (per > 1) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
                 return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             }
+            // (four tiles per block on the widest layers through M = 4: gate_up
+            // 14.7 / 15.0 us at B = 1 / 4 against 15.5 / 15.6 with two)
+            if (N >= 16384 && M <= 4) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             if (wide) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
         }
