@@ -28,11 +28,15 @@ FLAGS = [
 ]
 
 
-# Per-source extra flags.  The decode kernels keep MFMA results in VGPRs:
-# their accumulators are read by VALU code after every group, and the
-# AGPR form adds a v_accvgpr_read per value (measured 2 % on the widest layer).
+# Per-source extra flags.  Kernels whose MFMA accumulators are read by VALU
+# code inside the K loop keep MFMA results in VGPRs: the AGPR form adds a
+# v_accvgpr_read per value (the W4A16 decode kernels: 2 % on the widest
+# layer; the block-scaled FP8 GEMM, which scales and adds its accumulators
+# every 128-wide K block: 6-10 % at M = 2048; the other W8A8 tile kernels
+# in the same file measured unchanged).
 FILE_FLAGS = {
     "k_w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_w8a8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
