@@ -1,5 +1,6 @@
 // k_w4a8_decode.hip -- W4A8 at small M (decode): Y = (A s_a) W^T with A the
-// INT8 activation codes of at most 16 rows and W in the packed INT4 format.
+// INT8 activation codes of at most 32 rows (one or two 16-row bands, TM) and
+// W in the packed INT4 format.
 //
 // "Low-precision LLM inference" §1 (W4A8: INT4 weights, INT8 activations,
 // INT32/FP32 accumulation), §14 (per-token activation scales), §26 (decode
@@ -38,14 +39,14 @@ namespace bg {
 namespace {
 enum { WO_F32 = 0, WO_F16 = 1, WO_BF16 = 2 };
 
-template <int TN, bool XL>
+template <int TM, int TN, bool XL>
 struct Q8Stage {
     uint4 w[TN];
-    uint4 a[XL ? 1 : 2];
+    uint4 a[XL ? 1 : TM][2];
 };
 }  // namespace
 
-template <int TN, int NW, bool XL>
+template <int TM, int TN, int NW, bool XL>
 __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restrict__ a, const float* __restrict__ as,
                                                          int a_row, int64_t M, int64_t K,
                                                          const uint32_t* __restrict__ qw,
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
                                                          void* __restrict__ y, int out_dt, uint64_t rcp) {
     constexpr int STAGES = TN == 1 ? 4 : TN == 2 ? 3 : 2;
     static_assert(XL || TN <= 2, "activation fragments in the stages: at most two tiles");
+    static_assert(TM == 1 || TN <= 4, "two bands: at most four tiles");
     constexpr int XB = 4;                                              // activation chunks per batch
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
 
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
     const int64_t t0 = (int64_t)blockIdx.x * TN;
     const int ngroups = (int)(K >> 7);
     const int n_mine = ngroups > wave ? (ngroups - wave + NW - 1) / NW : 0;
-    const int rows = M < 16 ? (int)M : 16;
+    const int rows = M < 16 * TM ? (int)M : 16 * TM;
     const int64_t pitch = K + 16;                                      // LDS row pitch: rows 4 banks apart
     const bool has_z = zr != nullptr;
     // LDS: [per wave: its groups' scale and zero records][activation rows]
@@ -82,8 +84,10 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
                                                       0x00020000);
     const auto ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(a), (short)0, (int)(rows * K), 0x00020000);
 
-    const int arow = l16 < rows ? l16 : rows - 1;                     // rows past M: row M - 1, never written
-    auto issue = [&](Q8Stage<TN, XL>& st, int i) {
+    int arow[TM];                                                     // rows past M: row M - 1, never written
+#pragma unroll
+    for (int i = 0; i < TM; ++i) arow[i] = 16 * i + l16 < rows ? 16 * i + l16 : rows - 1;
+    auto issue = [&](Q8Stage<TM, TN, XL>& st, int i) {
         const bool real = i < n_mine;
         const int g = i * NW + wave;
 #pragma unroll
@@ -92,10 +96,12 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
                                                     rw, lane * 16, real ? (j * ngroups + g) * 1024 : kBufOOB, 0));
         if constexpr (!XL) {
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                st.a[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                         ra, (int)(arow * K) + q * 32 + s2 * 16,
-                                                         real ? g * 128 : kBufOOB, 0));
+            for (int b = 0; b < TM; ++b)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                    st.a[b][s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                ra, (int)(arow[b] * K) + q * 32 + s2 * 16,
+                                                                real ? g * 128 : kBufOOB, 0));
         }
     };
 
@@ -146,7 +152,7 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
     uint4 xv0[XB];
     x_load(xv0, threadIdx.x);
 
-    Q8Stage<TN, XL> stage[STAGES];
+    Q8Stage<TM, TN, XL> stage[STAGES];
 #pragma unroll
     for (int s = 0; s < STAGES; ++s) issue(stage[s], s);
 
@@ -164,34 +170,45 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
         sz_store(r0, v);
     }
 
-    float4_t acc[TN];
+    float4_t acc[TM][TN];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) acc[j] = float4_t{0, 0, 0, 0};
+    for (int b = 0; b < TM; ++b)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[b][j] = float4_t{0, 0, 0, 0};
 
-    auto consume = [&](const Q8Stage<TN, XL>& st, int i) {
+    auto consume = [&](const Q8Stage<TM, TN, XL>& st, int i) {
         const int g = i * NW + wave;
-        uint4 x0, x1;
-        if constexpr (XL) {
-            const uint8_t* xr = x_l + (int64_t)arow * pitch + (int64_t)g * 128 + q * 32;
-            x0 = *reinterpret_cast<const uint4*>(xr);
-            x1 = *reinterpret_cast<const uint4*>(xr + 16);
-        } else {
-            x0 = st.a[0];
-            x1 = st.a[1];
+        int4_t a0[TM], a1[TM];
+#pragma unroll
+        for (int b = 0; b < TM; ++b) {
+            uint4 x0, x1;
+            if constexpr (XL) {
+                const uint8_t* xr = x_l + (int64_t)arow[b] * pitch + (int64_t)g * 128 + q * 32;
+                x0 = *reinterpret_cast<const uint4*>(xr);
+                x1 = *reinterpret_cast<const uint4*>(xr + 16);
+            } else {
+                x0 = st.a[b][0];
+                x1 = st.a[b][1];
+            }
+            a0[b] = int4_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+            a1[b] = int4_t{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
         }
-        const int4_t a0 = int4_t{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-        const int4_t a1 = int4_t{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const uint8_t* rec = wsz + (i * TN + j) * 48;
             const float s_w = f16_to_f32(*reinterpret_cast<const uint16_t*>(rec + l16 * 2));
             const uint32_t z = has_z ? (rec[32 + l16] >> (4 * (g & 1))) & 0xFu : 8u;
             const uint32_t zc = 0x80808080u - z * 0x01010101u;
-            int4_t t = int4_t{0, 0, 0, 0};
-            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, w4_to_i8(make_uint2(st.w[j].x, st.w[j].y), zc), t, 0, 0, 0);
-            t = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, w4_to_i8(make_uint2(st.w[j].z, st.w[j].w), zc), t, 0, 0, 0);
+            const int4_t w0 = w4_to_i8(make_uint2(st.w[j].x, st.w[j].y), zc);
+            const int4_t w1 = w4_to_i8(make_uint2(st.w[j].z, st.w[j].w), zc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j][e] += s_w * (float)t[e];
+            for (int b = 0; b < TM; ++b) {
+                int4_t t = int4_t{0, 0, 0, 0};
+                t = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0[b], w0, t, 0, 0, 0);
+                t = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1[b], w1, t, 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[b][j][e] += s_w * (float)t[e];
+            }
         }
     };
 
@@ -205,18 +222,21 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
 
     // ---- sum the NW partial tiles in wave order through LDS ----
     __syncthreads();
-    float* red = reinterpret_cast<float*>(dyn_lds);                   // [NW][TN][4][64]
+    float* red = reinterpret_cast<float*>(dyn_lds);                   // [NW][TM][TN][4][64]
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int b = 0; b < TM; ++b)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red[((wave * TN + j) * 4 + e) * 64 + lane] = acc[j][e];
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[(((wave * TM + b) * TN + j) * 4 + e) * 64 + lane] = acc[b][j][e];
     __syncthreads();
-    for (int t = threadIdx.x; t < TN * 4 * 64; t += NW * 64) {
+    for (int t = threadIdx.x; t < TM * TN * 256; t += NW * 64) {
         float v = 0.0f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) v += red[w * TN * 256 + t];
-        const int ln = t & 63, e = (t >> 6) & 3, j = t >> 8;
-        const int64_t m = 4 * (ln >> 4) + e;
+        for (int w = 0; w < NW; ++w) v += red[w * TM * TN * 256 + t];
+        const int ln = t & 63, e = (t >> 6) & 3, bj = t >> 8;
+        const int b = bj / TN, j = bj - b * TN;
+        const int64_t m = 16 * b + 4 * (ln >> 4) + e;
         const int64_t n = (t0 + j) * 16 + (ln & 15);
         if (m >= M || n >= N) continue;
         const float f = v * (a_row ? as[m] : as[0]);
@@ -231,72 +251,91 @@ constexpr int64_t kW4A8DecodeLds = 144 * 1024;
 
 // LDS bytes: the waves' records and (XL) the activation rows, or the
 // reduction buffer, whichever is larger.
-static int64_t w4a8_decode_lds(int TN, int NW, bool xl, int64_t M, int64_t K) {
-    const int64_t rows = M < 16 ? M : 16;
+static int64_t w4a8_decode_lds(int TM, int TN, int NW, bool xl, int64_t M, int64_t K) {
+    const int64_t rows = M < 16 * TM ? M : 16 * TM;
     const int64_t xb = (int64_t)NW * (((K >> 7) + NW - 1) / NW) * TN * 48 + (xl ? rows * (K + 16) : 0);
-    const int64_t red = (int64_t)NW * TN * 256 * 4;
+    const int64_t red = (int64_t)NW * TM * TN * 256 * 4;
     return xb > red ? xb : red;
 }
 
-// Tiles per block: two on wide layers (N >= 16384); when the staged rows take
-// more than 80 KB (a CU then holds one block) the tiles are dealt so the grid
-// is about one round of 256 blocks.  Without room for the rows (XL false) at
-// most two.  Waves per block: about 16 per CU resident, never more than K
-// has groups, at most 8 with four or more tiles (registers).
+// Bands: one up to 16 rows, two up to 32.  Tiles per block: two on wide
+// layers (N >= 16384); when the staged rows take more than 80 KB (a CU then
+// holds one block) the tiles are dealt so the grid is about one round of 256
+// blocks (at most four with two bands).  Without room for the rows (XL
+// false) at most two.  Waves per block: about 16 per CU resident, never more
+// than K has groups, at most 8 with four or more tiles (registers).
 struct Q8Cfg {
-    int TN, NW;
+    int TM, TN, NW;
     bool xl;
 };
 static Q8Cfg w4a8_decode_cfg(int64_t M, int64_t N, int64_t K) {
-    const int64_t rows = M < 16 ? M : 16, ntiles = N >> 4, ngroups = K >> 7;
+    const int TM = M <= 16 ? 1 : 2;
+    const int64_t rows = M < 16 * TM ? M : 16 * TM, ntiles = N >> 4, ngroups = K >> 7;
     int TN = N >= 16384 ? 2 : 1;
     bool xl = true;
     if (rows * (K + 16) > 80 * 1024) {
         const int64_t per = (ntiles + 255) / 256;
         TN = per > 4 ? 8 : per > 2 ? 4 : per > 1 ? 2 : 1;
+        if (TM == 2 && TN > 4) TN = 4;
     }
     for (;;) {
         const int64_t blocks = (ntiles + TN - 1) / TN;
         int64_t want = (4096 + blocks - 1) / blocks;
         if (want > ngroups) want = ngroups;
         int NW = want >= 16 ? 16 : want >= 8 ? 8 : 4;
-        if (TN >= 4 && NW > 8) NW = 8;
-        if (!xl || w4a8_decode_lds(TN, NW, true, M, K) <= kW4A8DecodeLds) return Q8Cfg{TN, NW, xl};
+        if ((TN >= 4 || TM * TN >= 4) && NW > 8) NW = 8;
+        if (!xl || w4a8_decode_lds(TM, TN, NW, true, M, K) <= kW4A8DecodeLds) return Q8Cfg{TM, TN, NW, xl};
         xl = false;                                  // the rows do not fit: fragments in the stages
         TN = N >= 16384 ? 2 : 1;
     }
 }
 
 bool w4a8_decode_fits(int64_t M, int64_t N, int64_t K) {
-    if (M > 16) return false;
+    if (M > 32) return false;
     const Q8Cfg c = w4a8_decode_cfg(M, N, K);
-    return w4a8_decode_lds(c.TN, c.NW, c.xl, M, K) <= kW4A8DecodeLds;
+    return w4a8_decode_lds(c.TM, c.TN, c.NW, c.xl, M, K) <= kW4A8DecodeLds;
 }
 
-template <int TN, int NW, bool XL>
+template <int TM, int TN, int NW, bool XL>
 static const char* decode_cfg(const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K, const uint32_t* qw,
                               const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt, hipStream_t s) {
     const dim3 grid((unsigned)(((N >> 4) + TN - 1) / TN));
-    const size_t lds = (size_t)w4a8_decode_lds(TN, NW, XL, M, K);
-    auto kern = k_w4a8_decode<TN, NW, XL>;
+    const size_t lds = (size_t)w4a8_decode_lds(TM, TN, NW, XL, M, K);
+    auto kern = k_w4a8_decode<TM, TN, NW, XL>;
     if (lds > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
     const uint64_t cpr = (uint64_t)(K >> 4);
     const uint64_t rcp = ((uint64_t(1) << 40) + cpr - 1) / cpr;
     hipLaunchKernelGGL(kern, grid, dim3(NW * 64), lds, s, a, as, (int)a_row, M, K, qw, sc, zr, N, y, out_dt, rcp);
-    return kname("k_w4a8_decode", TN, NW, XL);
+    return kname("k_w4a8_decode", TM, TN, NW, XL);
 }
 
-template <int TN, bool XL>
+template <int TM, int TN, bool XL>
 static const char* decode_nw(int NW, const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K,
                              const uint32_t* qw, const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, int out_dt,
                              hipStream_t s) {
-    if constexpr (TN < 4) {
-        if (NW == 16) return decode_cfg<TN, 16, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    if constexpr (TN < 4 && TM * TN < 4) {
+        if (NW == 16) return decode_cfg<TM, TN, 16, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
     }
-    if (NW >= 8) return decode_cfg<TN, 8, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-    return decode_cfg<TN, 4, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    if (NW >= 8) return decode_cfg<TM, TN, 8, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    return decode_cfg<TM, TN, 4, XL>(a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+}
+
+template <int TM>
+static const char* decode_tn(const Q8Cfg& c, const int8_t* a, const float* as, bool a_row, int64_t M, int64_t K,
+                             const uint32_t* qw, const uint16_t* sc, const uint8_t* zr, int64_t N, void* y,
+                             int out_dt, hipStream_t s) {
+    if (!c.xl) {
+        if (c.TN == 2) return decode_nw<TM, 2, false>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+        return decode_nw<TM, 1, false>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    }
+    if constexpr (TM == 1) {
+        if (c.TN == 8) return decode_nw<TM, 8, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    }
+    if (c.TN >= 4) return decode_nw<TM, 4, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    if (c.TN == 2) return decode_nw<TM, 2, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    return decode_nw<TM, 1, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
 }
 
 // Requires w4a8_decode_fits(M, N, K).
@@ -304,16 +343,8 @@ const char* launch_w4a8_decode(const int8_t* a, const float* as, bool a_row, int
                                const uint32_t* qw, const uint16_t* sc, const uint8_t* zr, int64_t N, void* y,
                                int out_dt, hipStream_t s) {
     const Q8Cfg c = w4a8_decode_cfg(M, N, K);
-    if (!c.xl) {
-        if (c.TN == 2) return decode_nw<2, false>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-        return decode_nw<1, false>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-    }
-    switch (c.TN) {
-        case 8: return decode_nw<8, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-        case 4: return decode_nw<4, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-        case 2: return decode_nw<2, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-        default: return decode_nw<1, true>(c.NW, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
-    }
+    if (c.TM == 2) return decode_tn<2>(c, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
+    return decode_tn<1>(c, a, as, a_row, M, K, qw, sc, zr, N, y, out_dt, s);
 }
 
 }  // namespace bg

@@ -430,7 +430,7 @@ int64_t gemm_w8a8_workspace_bytes(int64_t M, int64_t N, int64_t K, int in_dtype,
  *   y, out_dtype         out [M][N], BG_BF16, BG_F16 or BG_F32
  *                        (round-to-nearest-even)
  * Requires 1 <= M, N % 16 == 0, K % 256 == 0, M * K < 2^31, 16-byte aligned
- * pointers.  M <= 16 runs the small-M kernel, which streams the packed
+ * pointers.  M <= 32 runs the small-M kernel, which streams the packed
  * weight tiles once ([LPI] §26: decode is bound by the weight bytes) and
  * needs no workspace; larger M the 256 x 128-tile kernel.  Both compute the
  * same exact group sums and close them in the same order, up to FP32
@@ -441,7 +441,7 @@ bg_status gemm_w4a8(const int8_t* a, const float* a_scales, int a_gran, int64_t 
                     int64_t N, int group, void* y, int out_dtype, void* stream);
 
 /*
- * gemm_w4a8_ws -- gemm_w4a8 with a caller-provided device workspace: for M > 16,
+ * gemm_w4a8_ws -- gemm_w4a8 with a caller-provided device workspace: for M > 32,
  * while the output tiles do not fill one round of the device (fewer than 256), K is
  * split into S = min(256 / tiles, groups / 4) slices of whole groups; each
  * slice writes its FP32 partial (row scale applied) to the workspace and a

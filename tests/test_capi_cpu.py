@@ -99,13 +99,13 @@ def test_gemm_w4a8_workspace(L):
     assert L.gemm_w4a8_workspace_bytes(2048, 4096, 14336) == 0                       # 256 tiles
     assert L.gemm_w4a8_workspace_bytes(16, 1024, 512) == 0                           # 4 groups
     assert L.gemm_w4a8_workspace_bytes(16, 1000, 512) == 0                           # N % 16
-    # M <= 16 runs the small-M kernel (no workspace), above it the split large-M kernel
+    # M <= 32 runs the small-M kernel (no workspace), above it the split large-M kernel
     for n, k in ((6144, 4096), (4096, 4096), (28672, 4096), (4096, 14336)):
-        assert L.gemm_w4a8_workspace_bytes(16, n, k) == 0
-        assert L.gemm_w4a8_workspace_bytes(1, n, k) == 0
-    assert L.gemm_w4a8_workspace_bytes(17, 4096, 14336) > 0
+        for m in (1, 16, 17, 32):
+            assert L.gemm_w4a8_workspace_bytes(m, n, k) == 0
+    assert L.gemm_w4a8_workspace_bytes(33, 4096, 14336) > 0
     f = L.gemm_w4a8_ws
-    assert f(P, P, 1, 17, 14336, P, Q, None, 4096, 128, P, BF16, None, 0, None) == E_WS
+    assert f(P, P, 1, 33, 14336, P, Q, None, 4096, 128, P, BF16, None, 0, None) == E_WS
 
 
 def test_gemm_w4a16_workspace(L):

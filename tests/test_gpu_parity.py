@@ -526,24 +526,25 @@ def _w4a8_case(ops, orc, M, N, K, asym, a_gran, out_dtype=torch.bfloat16, rows=N
 
 
 @pytest.mark.parametrize("ws", [None, False], ids=["split", "nosplit"])
-@pytest.mark.parametrize("M", [1, 17, 130, 300])
+@pytest.mark.parametrize("M", [1, 33, 130, 300])
 @pytest.mark.parametrize("asym,a_gran", [(True, 1), (False, 1), (True, 0)])
 def test_w4a8_small(ops, orc, M, asym, a_gran, ws):
     # 1040 columns: 8 full 128-column tiles and a 16-column tail; 16 groups,
-    # split into 4 slices of 4 when a workspace is given (M > 16: M = 1 runs
+    # split into 4 slices of 4 when a workspace is given (M > 32: M = 1 runs
     # the small-M kernel, which needs none)
     if ws is None:
-        assert ops.gemm_w4a8_workspace_bytes(M, 1040, 2048) == (0 if M <= 16 else 4 * M * 1040 * 4)
+        assert ops.gemm_w4a8_workspace_bytes(M, 1040, 2048) == (0 if M <= 32 else 4 * M * 1040 * 4)
     _w4a8_case(ops, orc, M, 1040, 2048, asym, a_gran, seed=M, ws=ws)
 
 
-# The small-M W4A8 kernel: 1, 2, 4 or 8 tiles per block (two on N >= 16384;
-# one round of blocks once the staged rows exceed 48 KB), ragged tile
-# counts, every output type, symmetric and asymmetric weights, per-token and
-# per-tensor activation scales; K = 14336 with 8 rows is inside its LDS
-# budget for the staged rows, with 16 rows outside (the activation fragments
-# then travel with the weight loads).
-@pytest.mark.parametrize("M", [1, 5, 16])
+# The small-M W4A8 kernel: one 16-row band up to M = 16, two up to 32; 1, 2,
+# 4 or 8 tiles per block (two on N >= 16384; one round of blocks once the
+# staged rows exceed 80 KB), ragged tile counts, every output type,
+# symmetric and asymmetric weights, per-token and per-tensor activation
+# scales; K = 14336 with 8 rows is inside its LDS budget for the staged
+# rows, with 16 and more rows outside (the activation fragments then travel
+# with the weight loads).
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 32])
 @pytest.mark.parametrize("N,K", [(1040, 2048), (6160, 4096), (16400, 4096), (28672, 4096)])
 @pytest.mark.parametrize("asym,a_gran,out", [(True, 1, torch.bfloat16), (False, 0, torch.float16),
                                               (True, 0, torch.float32)])
@@ -554,7 +555,7 @@ def test_w4a8_decode(ops, orc, M, N, K, asym, a_gran, out):
     assert ops.last_kernel().startswith("k_w4a8_decode<")
 
 
-@pytest.mark.parametrize("M", [8, 16])
+@pytest.mark.parametrize("M", [8, 16, 24])
 def test_w4a8_decode_staging_limit(ops, orc, M):
     K, N = synth.LLAMA3_8B_SHAPES["down"]
     _w4a8_case(ops, orc, M, N, K, True, 1, seed=M)
