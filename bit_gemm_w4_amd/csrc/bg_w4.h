@@ -54,36 +54,18 @@ __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t D[4]) {
     D[3] = and_or(w >> 12, 0x000F000Fu, m);
 }
 
-// The 16 pairs of a lane's 16-byte slot: D[kk][p] = pair p of word kk.  The
-// three nibble shifts run on word pairs as 64-bit shifts (one instruction
-// for two words; the bits a shift moves across the word boundary land above
-// bit 19 and are masked off).  The shift is inline assembly only because the
-// compiler splits 64-bit shifts whose halves are used separately; its
-// result feeds and_or (VALU), never an MFMA directly.
-__device__ __forceinline__ uint64_t shr64(uint64_t v, int sh) {
-    uint64_t r;
-    if (sh == 4) asm("v_lshrrev_b64 %0, 4, %1" : "=v"(r) : "v"(v));
-    else if (sh == 8) asm("v_lshrrev_b64 %0, 8, %1" : "=v"(r) : "v"(v));
-    else asm("v_lshrrev_b64 %0, 12, %1" : "=v"(r) : "v"(v));
-    return r;
-}
-
-// Words lo, hi (consecutive in a slot) -> their four pairs each.
+// Words lo, hi (consecutive in a slot) -> their four pairs each.  Plain
+// shifts the compiler sees: it keeps the wait states around the matrix
+// cores (an MFMA reads its accumulator input and writes its result several
+// cycles after issue), which it cannot do for a VALU instruction hidden in
+// inline assembly.
 template <bool BF16>
 __device__ __forceinline__ void dequant_pair(uint32_t lo, uint32_t hi, uint32_t Dlo[4], uint32_t Dhi[4]) {
-    constexpr uint32_t m = W4Magic<BF16>::bits;
-    const uint64_t v = ((uint64_t)hi << 32) | lo;
-    const uint64_t v4 = shr64(v, 4), v8 = shr64(v, 8), v12 = shr64(v, 12);
-    Dlo[0] = and_or(lo, 0x000F000Fu, m);
-    Dlo[1] = and_or((uint32_t)v4, 0x000F000Fu, m);
-    Dlo[2] = and_or((uint32_t)v8, 0x000F000Fu, m);
-    Dlo[3] = and_or((uint32_t)v12, 0x000F000Fu, m);
-    Dhi[0] = and_or(hi, 0x000F000Fu, m);
-    Dhi[1] = and_or((uint32_t)(v4 >> 32), 0x000F000Fu, m);
-    Dhi[2] = and_or((uint32_t)(v8 >> 32), 0x000F000Fu, m);
-    Dhi[3] = and_or((uint32_t)(v12 >> 32), 0x000F000Fu, m);
+    dequant_word<BF16>(lo, Dlo);
+    dequant_word<BF16>(hi, Dhi);
 }
 
+// The 16 pairs of a lane's 16-byte slot: D[kk][p] = pair p of word kk.
 template <bool BF16>
 __device__ __forceinline__ void dequant_tile(const uint4& w, uint32_t D[4][4]) {
     dequant_pair<BF16>(w.x, w.y, D[0], D[1]);

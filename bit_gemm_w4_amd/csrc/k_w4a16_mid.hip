@@ -9,31 +9,31 @@
 // and scales into the tile, dequantization in registers, one output write),
 // §22 (FP32 accumulation).
 //
-// Block: WM x WN waves over a band of 16*TMW*WM activation rows and
-// 16*TNW*WN output columns (TNW weight tiles of 16 columns per wave), for its
-// range of K.  All waves work on the same 128-wide group at a time: the
-// group's activation rows are staged in LDS once per block (a double-buffered
-// ring, one barrier per group), while each wave streams its own weight tiles
-// straight from memory into registers, STAGES groups ahead (the WM waves of a
-// column range read the same tiles: the second read is a cache hit).  Every
-// activation fragment a wave reads from LDS feeds TNW = 4 tiles of MFMAs, so
-// the LDS traffic stays below what the matrix cores consume (one tile per
-// fragment would make the kernel LDS-bound at half the MFMA rate), and every
-// weight tile is dequantized by WM <= 2 waves -- the 256-row prefill tile
-// dequantizes each one four times and pads a 74-row batch to 256.
+// Block: WM x WN waves over a band of 16*TMW*WM activation rows and 64*WN
+// output columns (4 weight tiles of 16 columns per wave), for its range of K.
+// All waves step through the 128-wide groups together, one barrier per
+// group.  A group's activation rows go from memory straight into LDS
+// (buffer_load ... lds, no registers) in a ring of three buffers, 16-byte
+// chunks XOR-swizzled by row so the fragment reads are free of bank
+// conflicts; each wave reads all its fragments of the group at once, then
+// copies the group after next into the ring.  Each wave streams its own
+// weight tiles straight from memory into registers, two groups ahead (the
+// WM waves of a column range read the same tiles: the second read is a
+// cache hit).  Every activation fragment feeds 4 tiles of MFMAs (LDS traffic
+// well below what the matrix cores consume) and every weight tile is
+// dequantized by WM <= 2 waves for up to 48 rows each.
 //
-// Dequantization and exactness as in the decode kernels: the MFMA consumes
-// the exact 16-bit values MV + u (v_bitop3 on the packed nibbles), and per
-// group the zero-point and MV are removed with (MV + z) * Sx before the FP16
-// scale multiplies the FP32 group sum.  Sx (sum of a row's 128 activations of
-// the group) is computed while the group is staged: the 16 lanes that copy a
-// row's 16-byte chunks add their 8 values and combine them in a fixed xor
-// tree, so the result does not depend on timing.  BF16: the removal is one
-// more MFMA per row tile and weight tile and group, on the matrix cores
-// instead of the vector ALU (which bounds this kernel): Sx is split exactly
-// into three BF16 parts (8 + 8 + 8 significant bits), staged as K slots 0..2
-// of the first lane quarter, against -(MV + z) (exact in BF16) in the weight
-// operand.  FP16 keeps the FP32 correction (an FP16 part could overflow).
+// Exactness as in the decode kernels: the MFMA consumes the exact 16-bit
+// values MV + u (v_bitop3 on the packed nibbles) and the group's FP32 sum
+// P = sum_k x (MV + u) is scaled by the group's FP16 scale s and added to the
+// FP32 accumulator.  The zero point and MV come off as
+// -s (MV + z) Sx, Sx = sum_k x of the row over the group: Sx is an MFMA of a
+// row of ones against the activation fragment (the fragment as the second
+// operand leaves Sx of row r in the lanes of output column r), and four
+// groups' products are added by one FP32 MFMA (16x16x4, k = the four
+// groups: lane q of a row holds Sx of group 4t + q, lane q of a column
+// -s (MV + z) of the same group).  No vector-ALU work per row beyond the one
+// scale multiply-add per group, for BF16 and FP16 alike.
 //
 // K split: with a workspace the K range is cut into S slices of whole groups
 // when the blocks of one slice do not fill the device; slice sl writes FP32
@@ -41,13 +41,15 @@
 // them in slice order on the same stream.
 #include "bg_device.h"
 #include "bg_internal.h"
+#include "bg_pipe.h"
 #include "bg_w4.h"
 
 namespace bg {
 
 namespace {
-constexpr int MID_STAGES = 2;
-constexpr int XPITCH = 128 + 8;         // LDS row pitch of a staged group, in 16-bit elements
+constexpr int MID_XS = 3;               // LDS ring of staged activation groups
+constexpr int MID_WST = 2;              // weight stages in registers
+constexpr int MID_TNW = 4;              // weight tiles per wave
 }  // namespace
 
 template <int TNW>
@@ -57,28 +59,24 @@ struct MidStage {
     uint32_t z[TNW];
 };
 
-template <bool BF16, int TMW, int TNW, int WM, int WN>
+template <bool BF16, int TMW, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                        const uint32_t* __restrict__ qw, const uint16_t* __restrict__ sc,
                                                        const uint8_t* __restrict__ zr, int64_t N,
                                                        uint16_t* __restrict__ y, float* __restrict__ ws, int gs) {
-    constexpr int NW = WM * WN;
+    constexpr int TNW = MID_TNW, NW = WM * WN;
     constexpr int BM = 16 * TMW * WM;
-    constexpr int NT = NW * 64;
-    constexpr int CHUNKS = BM * 16;                                   // 16-byte chunks of a staged group
-    constexpr int CPT = (CHUNKS + NT - 1) / NT;                       // chunks per thread
-    constexpr int XBUF = BM * XPITCH * 2;                             // bytes of one staged group
+    constexpr int NCOPY = BM / 4;                                     // 1 KB copies (4 rows) per staged group
+    constexpr int LX = (NCOPY + NW - 1) / NW;                         // copies per wave per group
+    constexpr int LW = 3 * TNW;                                       // weight loads per lane per group
+    constexpr int XB = BM * 256;                                      // bytes of one staged group
     constexpr float MV = W4Magic<BF16>::value;
     constexpr uint32_t ONE2 = W4Magic<BF16>::ones;
-    static_assert(NT % 64 == 0 && (CHUNKS % 16) == 0, "a row's 16 chunks sit in 16 consecutive lanes");
+    static_assert(LX + 2 * LW < 64, "vmcnt is a 6-bit field");
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
-    uint16_t* xbuf = reinterpret_cast<uint16_t*>(dyn_lds);                       // [2][BM][XPITCH]
-    float* sxbuf = reinterpret_cast<float*>(dyn_lds + 2 * XBUF);                 // FP16: [2][BM]
-    uint2* sxpart = reinterpret_cast<uint2*>(dyn_lds + 2 * XBUF);                // BF16: [2][BM] 3 parts
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l16 = lane & 15, q = lane >> 4;
     const int ntiles = (int)(N >> 4);
     const int ngroups = (int)(K >> 7);
@@ -92,8 +90,8 @@ __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __re
     const int t0 = (blockIdx.x * WN + wn) * TNW;                       // this wave's first tile
     const int my_tiles = t0 >= ntiles ? 0 : (ntiles - t0 < TNW ? ntiles - t0 : TNW);
 
-    // weights, scales, zero bytes of this wave's tiles, K range of the slice;
-    // reads past the wave's tiles (ragged N) return 0
+    // weights, scales, zero bytes of this wave's tiles; reads past the
+    // wave's tiles (ragged N) return 0
     const bool has_z = zr != nullptr;
     const int tt = my_tiles > 0 ? t0 : 0;
     const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw + (int64_t)tt * ngroups * 256), (short)0,
@@ -103,12 +101,13 @@ __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __re
     const auto rz = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(has_z ? zr + (int64_t)tt * (ngroups >> 1) * 16 : zr), (short)0,
         has_z ? my_tiles * (ngroups >> 1) * 16 : 0, 0x00020000);
-    // activation rows of the band (rows past M read row M - 1: they only feed
-    // output rows that are never written)
     const auto rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + m0 * K), (short)0,
                                                       (int)((int64_t)rows * K * 2), 0x00020000);
 
-    auto issue = [&](MidStage<TNW>& st, int i) {
+    // group i of the slice: past its last group every load repeats that
+    // group (in bounds, never consumed), so each wave issues the same loads
+    // at every step and the waits below count them exactly
+    auto w_issue = [&](MidStage<TNW>& st, int i) {
         const int g = g0 + (i < ng - 1 ? i : ng - 1);
 #pragma unroll
         for (int j = 0; j < TNW; ++j) {
@@ -118,167 +117,136 @@ __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __re
             st.z[j] = __builtin_amdgcn_raw_buffer_load_b8(rz, l16, (j * (ngroups >> 1) + (g >> 1)) * 16, 0);
         }
     };
-
-    // staging of group i of the slice: chunk c = tid + u * NT is row c / 16,
-    // 16-byte part c % 16 (8 consecutive k).  Every thread issues all CPT
-    // loads (past the last chunk it reloads that chunk, and past the slice's
-    // last group that group): unconditional loads keep the compiler's count
-    // of loads in flight exact, so each wait covers exactly the loads it needs.
-    uint4 xr[CPT];
-    int xoff[CPT];
+    // copy c of a group fills LDS rows 4c .. 4c + 3 of its buffer (1 KB):
+    // lane l writes row 4c + l / 16, 16-byte slot l % 16, which holds chunk
+    // (l % 16) ^ (row % 16) of the row.  Rows past M copy row M - 1 (they
+    // only feed output rows that are never written); a wave with fewer than
+    // LX copies of its own repeats the last one (same bytes, same place).
+    int xoff[LX];
+    uint32_t xdst[LX];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        int c = tid + u * NT;
-        c = c < CHUNKS ? c : CHUNKS - 1;
-        int r = c >> 4;
-        r = r < rows ? r : rows - 1;
-        xoff[u] = r * (int)K * 2 + (c & 15) * 16;
+    for (int u = 0; u < LX; ++u) {
+        const int c = (u * NW + wave) < NCOPY ? u * NW + wave : NCOPY - 1;
+        const int r = 4 * c + (lane >> 4);
+        const int rr = r < rows ? r : rows - 1;
+        xoff[u] = rr * (int)K * 2 + (((lane & 15) ^ (r & 15)) << 4);
+        xdst[u] = (uint32_t)c * 1024;
     }
-    auto x_load = [&](int i) {
+    auto x_issue = [&](int i) {
         const int g = g0 + (i < ng - 1 ? i : ng - 1);
+        uint8_t* buf = dyn_lds + (i % MID_XS) * XB;
 #pragma unroll
-        for (int u = 0; u < CPT; ++u)
-            xr[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[u], g * 256, 0));
-    };
-    auto x_store = [&](int buf) {
-        uint16_t* xb = xbuf + buf * (BM * XPITCH);
-        float* sxb = sxbuf + buf * BM;
-#pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            const int c = tid + u * NT;
-            // sum of this lane's 8 values, then the 16 lanes of the row in a
-            // fixed xor tree (every lane of a row is in the same wave)
-            float s = dot2<BF16>(xr[u].x, ONE2, 0.0f);
-            s = dot2<BF16>(xr[u].y, ONE2, s);
-            s = dot2<BF16>(xr[u].z, ONE2, s);
-            s = dot2<BF16>(xr[u].w, ONE2, s);
-            s += __shfl_xor(s, 8, 64);
-            s += __shfl_xor(s, 4, 64);
-            s += __shfl_xor(s, 2, 64);
-            s += __shfl_xor(s, 1, 64);
-            if (c < CHUNKS) {
-                *reinterpret_cast<uint4*>(xb + (c >> 4) * XPITCH + (c & 15) * 8) = xr[u];
-                if ((c & 15) == 0) {
-                    if constexpr (BF16) {
-                        // s = hi + mid + lo exactly: each residual is exact in FP32
-                        // and the last one has at most 8 significant bits
-                        const uint32_t hi = f32_to_bf16(s);
-                        const float r1 = s - bf16_to_f32(hi);
-                        const uint32_t mid = f32_to_bf16(r1);
-                        const uint32_t lo = f32_to_bf16(r1 - bf16_to_f32(mid));
-                        sxpart[buf * BM + (c >> 4)] = uint2{hi | (mid << 16), lo};
-                    } else {
-                        sxb[c >> 4] = s;
-                    }
-                }
-            }
-        }
+        for (int u = 0; u < LX; ++u) copy16_to_lds(rx, buf + xdst[u], xoff[u], g * 256);
     };
 
-    MidStage<TNW> stage[MID_STAGES];
-    x_load(0);
-    x_store(0);
-    x_load(1);
-#pragma unroll
-    for (int s = 0; s < MID_STAGES; ++s) issue(stage[s], s);
-    __syncthreads();
+    // fragment (ii, kk) of lane (l16, q): row rw0 + 16 ii + l16, chunk 4q + kk
+    // (k = 32q + 8kk .. + 7 of the group), at slot (4q + kk) ^ l16
+    const uint8_t* xrow = dyn_lds + (rw0 + l16) * 256;
+    const int sw0 = ((4 * q) ^ l16) << 4;
 
     float4_t acc[TMW][TNW];
 #pragma unroll
-    for (int i = 0; i < TMW; ++i)
+    for (int ii = 0; ii < TMW; ++ii)
 #pragma unroll
-        for (int j = 0; j < TNW; ++j) acc[i][j] = float4_t{0, 0, 0, 0};
+        for (int j = 0; j < TNW; ++j) acc[ii][j] = float4_t{0, 0, 0, 0};
+    float sel[TMW], bsel[TNW];                                        // correction operands of the current four groups
+#pragma unroll
+    for (int ii = 0; ii < TMW; ++ii) sel[ii] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) bsel[j] = 0.0f;
+    const uint32_t ones[4] = {ONE2, ONE2, ONE2, ONE2};
 
     auto consume = [&](const MidStage<TNW>& st, int i) {
         const int g = g0 + i;
-        const uint16_t* xb = xbuf + (i & 1) * (BM * XPITCH);
-        const float* sxb = sxbuf + (i & 1) * BM;
-        float scale[TNW], corr[TNW];
-#pragma unroll
-        for (int j = 0; j < TNW; ++j) {
-            scale[j] = f16_to_f32(st.s[j] & 0xFFFFu);
-            corr[j] = MV + (float)(has_z ? (st.z[j] >> (4 * (g & 1))) & 0xF : 8u);
-        }
-        float4_t part[TMW][TNW];
+        uint32_t xf[TMW][4][4];
+        const uint8_t* xb = xrow + (i % MID_XS) * XB;
 #pragma unroll
         for (int ii = 0; ii < TMW; ++ii)
 #pragma unroll
-            for (int j = 0; j < TNW; ++j) part[ii][j] = float4_t{0, 0, 0, 0};
-        uint32_t D[TNW][2][4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            if ((kk & 1) == 0) {
-#pragma unroll
-                for (int j = 0; j < TNW; ++j)
-                    dequant_pair<BF16>(kk == 0 ? st.w[j].x : st.w[j].z, kk == 0 ? st.w[j].y : st.w[j].w, D[j][0],
-                                       D[j][1]);
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint4 v = *reinterpret_cast<const uint4*>(xb + ii * 4096 + (sw0 ^ (kk << 4)));
+                xf[ii][kk][0] = v.x;
+                xf[ii][kk][1] = v.y;
+                xf[ii][kk][2] = v.z;
+                xf[ii][kk][3] = v.w;
             }
+        // every read of this buffer is issued: the group after next may now be copied
+        asm volatile("" ::: "memory");
+        x_issue(i + 2);
+        asm volatile("" ::: "memory");
+
+        // Sx of each row of the wave's bands: ones x fragment^T
+        float4_t sxa[TMW];
 #pragma unroll
-            for (int ii = 0; ii < TMW; ++ii) {
-                // lane (l16, q): row rw0 + 16 ii + l16, k = 32 q + 8 kk .. + 7 of the group
-                const uint4 av =
-                    *reinterpret_cast<const uint4*>(xb + (rw0 + 16 * ii + l16) * XPITCH + q * 32 + kk * 8);
-                const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+        for (int ii = 0; ii < TMW; ++ii) {
+            sxa[ii] = float4_t{0, 0, 0, 0};
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) part[ii][j] = mfma16<BF16>(a, D[j][kk & 1], part[ii][j]);
-            }
+            for (int kk = 0; kk < 4; ++kk) sxa[ii] = mfma16<BF16>(ones, xf[ii][kk], sxa[ii]);
         }
-        if constexpr (BF16) {
-            // - (MV + z) * Sx on the matrix cores: K slots 0..2 of lane quarter 0
-            uint32_t cb[TNW][4];
+        // lane q of the four-group window takes group 4t + q; the window's
+        // first group clears the other lanes (a last window of fewer than four
+        // groups leaves them at zero)
+        const bool mine = (i & 3) == q, first = (i & 3) == 0;
 #pragma unroll
-            for (int j = 0; j < TNW; ++j) {
-                const uint32_t zz = has_z ? (st.z[j] >> (4 * (g & 1))) & 0xFu : 8u;
-                const uint32_t cc = q == 0 ? ((zz | (zz << 16)) | 0xC300C300u) : 0u;   // -(128 + z), twice
-                cb[j][0] = cc;
-                cb[j][1] = cc;
-                cb[j][2] = 0u;
-                cb[j][3] = 0u;
-            }
-            const uint2* sp = sxpart + (i & 1) * BM;
+        for (int ii = 0; ii < TMW; ++ii) sel[ii] = mine ? sxa[ii][0] : (first ? 0.0f : sel[ii]);
+
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) {
+            uint32_t D[4][4];
+            dequant_tile<BF16>(st.w[j], D);
+            float4_t part[TMW];
 #pragma unroll
             for (int ii = 0; ii < TMW; ++ii) {
-                const uint2 v = sp[rw0 + 16 * ii + l16];
-                const uint32_t a[4] = {q == 0 ? v.x : 0u, q == 0 ? v.y : 0u, 0u, 0u};
+                part[ii] = float4_t{0, 0, 0, 0};
 #pragma unroll
-                for (int j = 0; j < TNW; ++j) part[ii][j] = mfma16<BF16>(a, cb[j], part[ii][j]);
+                for (int kk = 0; kk < 4; ++kk) part[ii] = mfma16<BF16>(xf[ii][kk], D[kk], part[ii]);
             }
+            const float s = f16_to_f32(st.s[j] & 0xFFFFu);
+#pragma unroll
+            for (int ii = 0; ii < TMW; ++ii)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[ii][j][e] += s * part[ii][e];
+            const float zv = (float)(has_z ? (st.z[j] >> (4 * (g & 1))) & 0xFu : 8u);
+            bsel[j] = mine ? -s * (MV + zv) : (first ? 0.0f : bsel[j]);
+        }
+        if ((i & 3) == 3 || i == ng - 1) {
 #pragma unroll
             for (int ii = 0; ii < TMW; ++ii)
 #pragma unroll
                 for (int j = 0; j < TNW; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[ii][j][e] += scale[j] * part[ii][j][e];
-        } else {
-#pragma unroll
-            for (int ii = 0; ii < TMW; ++ii) {
-                // output rows rw0 + 16 ii + 4 q + e of this lane
-                const float4 sx = *reinterpret_cast<const float4*>(sxb + rw0 + 16 * ii + 4 * q);
-                const float sxv[4] = {sx.x, sx.y, sx.z, sx.w};
-#pragma unroll
-                for (int j = 0; j < TNW; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[ii][j][e] += scale[j] * (part[ii][j][e] - corr[j] * sxv[e]);
-            }
+                    acc[ii][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(sel[ii], bsel[j], acc[ii][j], 0, 0, 0);
         }
     };
 
-    // group i: consume it from buffer i & 1, stage group i + 1 into the other
-    // buffer (its last readers finished before the previous barrier), request
-    // group i + 2, refill the weight stage, barrier.  Staging, requests and
-    // barriers run for every step of the unrolled loop (past the slice's end
-    // they move clamped copies nobody reads), so the loads in flight are the
-    // same at every wait.
-    for (int i = 0; i < ng; i += MID_STAGES) {
-#pragma unroll
-        for (int s = 0; s < MID_STAGES; ++s) {
-            if (i + s < ng) consume(stage[s], i + s);
-            x_store((i + s + 1) & 1);
-            x_load(i + s + 2);
-            issue(stage[s], i + s + MID_STAGES);
-            __syncthreads();
-        }
+    // group i: its copies have landed (own: the wait; everyone's: the
+    // barrier) once at most its weight loads, the next group's copies and
+    // the next group's weight loads are in flight; then the fragments are
+    // read, the group after next is copied (ring slot of group i - 1, whose
+    // reads all finished before this barrier), the group is consumed and its
+    // weight stage refilled with the group after next
+    MidStage<TNW> stage[MID_WST];
+    x_issue(0);
+    asm volatile("" ::: "memory");
+    w_issue(stage[0], 0);
+    asm volatile("" ::: "memory");
+    x_issue(1);
+    asm volatile("" ::: "memory");
+    w_issue(stage[1], 1);
+    auto step = [&](MidStage<TNW>& st, int i) {
+        wait_vmcnt<LX + 2 * LW>();
+        block_barrier();
+        consume(st, i);
+        asm volatile("" ::: "memory");
+        w_issue(st, i + MID_WST);
+    };
+    static_assert(MID_WST == 2, "two stages: the loop body takes two groups");
+    int i = 0;
+    for (; i + 1 < ng; i += 2) {                                       // no branch inside: exact load counts
+        step(stage[0], i);
+        step(stage[1], i + 1);
     }
+    if (i < ng) step(stage[0], i);
+    wait_vmcnt<0>();                                                   // no copy into LDS outlives the block
 
     // ---- output: BF16/FP16 rows < M, or FP32 partials of the slice ----
     if (my_tiles == 0) return;
@@ -302,18 +270,17 @@ __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __re
 // ---- configuration (shared by the workspace query and the launch) ----
 namespace {
 struct MidCfg {
-    int TMW, WM, S, gs;
+    int TMW, WM, WN, S, gs;
     int64_t ws_bytes, lds_bytes;
     unsigned nblocks, bands;
 };
-constexpr int MID_TNW = 4;
+constexpr int MID_WAVES = 8;            // waves per block
 
 // Row bands of up to 96 rows; a band of R row tiles (16 rows) is split over
 // WM = 2 waves from R = 4 (WM = 1 below), each with TMW = ceil(R / WM) <= 3
-// row tiles (the accumulators of 3 x 4 tiles, twice, fill the 256 registers
-// a lane has at two waves per SIMD); 8 waves in all, 4 tiles each (256
-// columns per block with WM = 2, 512 with WM = 1).  K is split while one slice's blocks fill less than one
-// round of 256 CUs, at least 3 groups per slice.
+// row tiles; MID_WAVES waves in all, 4 tiles each.  K is split while one
+// slice's blocks fill less than one round of 256 CUs, at least 3 groups per
+// slice.
 MidCfg mid_cfg(int64_t M, int64_t N, int64_t K, bool with_ws) {
     MidCfg c{};
     const int64_t bands = (M + 95) / 96;
@@ -321,9 +288,9 @@ MidCfg mid_cfg(int64_t M, int64_t N, int64_t K, bool with_ws) {
     const int64_t R = (band_rows + 15) / 16;
     c.WM = R >= 4 ? 2 : 1;
     c.TMW = (int)((R + c.WM - 1) / c.WM);
-    const int WN = 8 / c.WM;
+    c.WN = MID_WAVES / c.WM;
     const int64_t ntiles = N >> 4, ngroups = K >> 7;
-    const int64_t nb = (ntiles + WN * MID_TNW - 1) / (WN * MID_TNW);
+    const int64_t nb = (ntiles + c.WN * MID_TNW - 1) / (c.WN * MID_TNW);
     int64_t S = 1;
     if (with_ws) {
         S = 256 / (nb * bands);
@@ -337,16 +304,14 @@ MidCfg mid_cfg(int64_t M, int64_t N, int64_t K, bool with_ws) {
     c.nblocks = (unsigned)nb;
     c.bands = (unsigned)bands;
     c.ws_bytes = S > 1 ? S * M * N * 4 : 0;
-    const int64_t BM = 16 * c.TMW * c.WM;
-    c.lds_bytes = 2 * BM * XPITCH * 2 + 2 * BM * 8;
+    c.lds_bytes = MID_XS * 16 * c.TMW * c.WM * 256;
     return c;
 }
 
-template <bool BF16, int TMW, int WM>
+template <bool BF16, int TMW, int WM, int WN>
 const char* mid_launch(const MidCfg& c, const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
                        const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s) {
-    constexpr int WN = 8 / WM;
-    auto kern = k_w4a16_mid<BF16, TMW, MID_TNW, WM, WN>;
+    auto kern = k_w4a16_mid<BF16, TMW, WM, WN>;
     if (c.lds_bytes > 64 * 1024)
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)c.lds_bytes);
@@ -357,16 +322,16 @@ const char* mid_launch(const MidCfg& c, const void* x, int64_t M, int64_t K, con
     return kname("k_w4a16_mid", BF16, TMW, MID_TNW, WM, WN);
 }
 
-template <bool BF16>
-const char* mid_dt(const MidCfg& c, const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
-                   const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s) {
+template <bool BF16, int NWV>
+const char* mid_shape(const MidCfg& c, const void* x, int64_t M, int64_t K, const uint32_t* qw, const uint16_t* sc,
+                      const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s) {
     if (c.WM == 1) {
-        if (c.TMW == 1) return mid_launch<BF16, 1, 1>(c, x, M, K, qw, sc, zr, N, y, ws, s);
-        if (c.TMW == 2) return mid_launch<BF16, 2, 1>(c, x, M, K, qw, sc, zr, N, y, ws, s);
-        return mid_launch<BF16, 3, 1>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+        if (c.TMW == 1) return mid_launch<BF16, 1, 1, NWV>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+        if (c.TMW == 2) return mid_launch<BF16, 2, 1, NWV>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+        return mid_launch<BF16, 3, 1, NWV>(c, x, M, K, qw, sc, zr, N, y, ws, s);
     }
-    if (c.TMW == 2) return mid_launch<BF16, 2, 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
-    return mid_launch<BF16, 3, 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    if (c.TMW == 2) return mid_launch<BF16, 2, 2, NWV / 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    return mid_launch<BF16, 3, 2, NWV / 2>(c, x, M, K, qw, sc, zr, N, y, ws, s);
 }
 }  // namespace
 
@@ -375,8 +340,8 @@ int64_t w4a16_mid_workspace(int64_t M, int64_t N, int64_t K) { return mid_cfg(M,
 const char* launch_w4a16_mid(const void* x, bool x_bf16, int64_t M, int64_t K, const uint32_t* qw,
                              const uint16_t* sc, const uint8_t* zr, int64_t N, void* y, void* ws, hipStream_t s) {
     const MidCfg c = mid_cfg(M, N, K, ws != nullptr);
-    if (x_bf16) return mid_dt<true>(c, x, M, K, qw, sc, zr, N, y, ws, s);
-    return mid_dt<false>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    if (x_bf16) return mid_shape<true, MID_WAVES>(c, x, M, K, qw, sc, zr, N, y, ws, s);
+    return mid_shape<false, MID_WAVES>(c, x, M, K, qw, sc, zr, N, y, ws, s);
 }
 
 }  // namespace bg
