@@ -1,0 +1,115 @@
+"""Device-rate microbenchmarks (MI355X, gfx950) behind the kernels' ceilings.
+
+    python3 -m bit_gemm_w4_amd.probes
+
+prints a markdown table of: dense MFMA throughput per instruction shape
+(independent accumulator chains, two waves per SIMD on all 1,024 SIMDs),
+LDS read bandwidth per CU (ds_read_b128), and streaming throughput into
+registers and by buffer_load ... lds from an L2-resident buffer (2 MiB) and
+from one that fits the 256 MB last-level cache but not L2 (128 MiB).
+
+Not part of the library path: the kernels live in csrc_probes/probes.hip and
+build into their own shared object (libprobes.so beside this file).
+"""
+import ctypes
+import os
+import subprocess
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_PKG, "csrc_probes", "probes.hip")
+LIB = os.path.join(_PKG, "libprobes.so")
+CLOCK_GHZ = 2.4          # the spec clock, used only to express rates per cycle
+SIMDS = 1024             # 256 CUs x 4
+
+MFMA_KINDS = [           # (kind id, name, operations per instruction)
+    (0, "v_mfma_f32_16x16x32_bf16", 16 * 16 * 32 * 2),
+    (1, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16 * 2),
+    (2, "v_mfma_i32_16x16x64_i8", 16 * 16 * 64 * 2),
+    (3, "v_mfma_i32_32x32x32_i8", 32 * 32 * 32 * 2),
+    (4, "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)", 16 * 16 * 128 * 2),
+    (5, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 32 * 32 * 64 * 2),
+    (6, "v_mfma_f32_16x16x4_f32", 16 * 16 * 4 * 2),
+]
+
+
+def build() -> str:
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        raise RuntimeError(f"hipcc failed for {SRC}:\n{r.stderr}")
+    return LIB
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is not built: call bit_gemm_w4_amd.probes.build()")
+    L = ctypes.CDLL(LIB)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    L.probe_mfma.argtypes = [i32, i32, vp, i32, i32, vp]
+    L.probe_lds.argtypes = [vp, i32, i32, vp]
+    L.probe_stream.argtypes = [i32, vp, i64, vp, i32, i32, vp]
+    return L
+
+
+def _time(torch, launch, reps=3):
+    launch(4)                                            # warm: clocks, code load
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        launch(None)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None or t < best else best
+    return best
+
+
+def run():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("the probes need a GPU")
+    L = _lib()
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks = 512                                         # two blocks of 4 waves per CU: two waves per SIMD
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    po = ctypes.c_void_p(out.data_ptr())
+    rows = []
+    for kind, name, ops in MFMA_KINDS:
+        iters = 2000
+        t = _time(torch, lambda it: L.probe_mfma(kind, 8, po, blocks, it or iters, s))
+        n = blocks * 4 * iters * 8                       # instructions
+        rows.append((name, f"{n * ops / t / 1e12:,.0f} TOP/s",
+                     f"{t * CLOCK_GHZ * 1e9 / (n / SIMDS):.1f} cycles per instruction per SIMD at {CLOCK_GHZ} GHz"))
+    iters = 4000
+    t = _time(torch, lambda it: L.probe_lds(po, blocks, it or iters, s))
+    b = blocks * 256 * 16 * 8 * iters
+    rows.append(("LDS ds_read_b128, 2 blocks per CU", f"{b / t / 1e12:.1f} TB/s", f"{b / t / 256 / (CLOCK_GHZ * 1e9):.0f} B per clock per CU"))
+    for mib in (2, 128):
+        src = torch.randint(0, 255, (mib << 20,), dtype=torch.uint8, device="cuda")
+        for to_lds, how in ((0, "into registers"), (1, "by buffer_load ... lds")):
+            iters = 400 if mib == 2 else 100
+            t = _time(torch, lambda it: L.probe_stream(to_lds, ctypes.c_void_p(src.data_ptr()), src.numel(), po,
+                                                       blocks, it or iters, s))
+            b = blocks * 4 * 16 * 1024 * iters
+            rows.append((f"stream {mib} MiB buffer {how}", f"{b / t / 1e12:.1f} TB/s",
+                         f"{b / t / 256 / (CLOCK_GHZ * 1e9):.0f} B per clock per CU"))
+        del src
+    return rows
+
+
+def main():
+    if not os.path.exists(LIB):
+        build()
+    rows = run()
+    print("| probe | rate | per unit |")
+    print("|---|---|---|")
+    for r in rows:
+        print(f"| {r[0]} | {r[1]} | {r[2]} |")
+
+
+if __name__ == "__main__":
+    main()
