@@ -284,18 +284,26 @@ static const char* decode_cfg(const W8A8Args& g, hipStream_t s) {
 
 // Activation rows staged in LDS (M <= 16) while they take at most 144 KB
 // (K <= 9200 at M = 16, K <= 14336 through M = 10): measured on the
-// projection shapes, one tile per
-// block with 8 waves unless the grid would not fill the device evenly -- two
-// tiles with 4 waves for 256 < N/16 < 1024 (qkv: 192 blocks beat 384), four
-// tiles with 4 waves on wide layers from M = 5 on (the staged rows are then
-// shared by four tiles).
+// projection shapes (graph-replayed, weights rotated past the MALL), one tile
+// per block with 8 waves unless the grid would not fill the device evenly --
+// two tiles for 256 < N/16 < 1024 (qkv: 192 blocks beat 384), with 8 waves
+// from M = 5 (qkv at B = 16: 9.6 against 10.3 us with 4); on wide layers
+// four tiles with 4 waves from M = 5 on (the staged rows are then shared by
+// four tiles), below that one tile with 4 waves (gate_up at B = 4: 25.6
+// against 26.3 us with 8).
 bool w8_decode_xl(int64_t M, int64_t K) { return M <= 16 && (M < 16 ? M : 16) * (K + 16) <= 144 * 1024; }
 
 template <bool FP8, bool BLOCK>
 static const char* decode_xl(const W8A8Args& g, hipStream_t s) {
     const int64_t tiles = (g.N + 15) / 16;
-    if (tiles >= 1024 && g.M > 4) return decode_cfg<FP8, BLOCK, 1, 4, 4, true>(g, s);
-    if (tiles > 256 && tiles < 1024) return decode_cfg<FP8, BLOCK, 1, 2, 4, true>(g, s);
+    if (tiles >= 1024) {
+        if (g.M > 4) return decode_cfg<FP8, BLOCK, 1, 4, 4, true>(g, s);
+        return decode_cfg<FP8, BLOCK, 1, 1, 4, true>(g, s);
+    }
+    if (tiles > 256) {
+        if (g.M > 4) return decode_cfg<FP8, BLOCK, 1, 2, 8, true>(g, s);
+        return decode_cfg<FP8, BLOCK, 1, 2, 4, true>(g, s);
+    }
     return decode_cfg<FP8, BLOCK, 1, 1, 8, true>(g, s);
 }
 

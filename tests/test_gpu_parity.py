@@ -369,8 +369,9 @@ def test_w8a8_small(ops, orc, algo, M, fp8, a_gran, w_gran, out):
 
 
 # The small-M kernel with the activation rows in LDS deals 1, 2 or 4 weight
-# tiles to a block (2 for 256 < N/16 < 1024, 4 from N/16 = 1024 at M > 4); N
-# here leaves the last block with fewer tiles.  K = 14336 puts M = 10 inside
+# tiles to a block (2 for 256 < N/16 < 1024, with 4 or 8 waves; 4 from
+# N/16 = 1024 at M > 4, one tile with 4 waves below); N here leaves the last
+# block with fewer tiles.  K = 14336 puts M = 10 inside
 # and M = 11 outside the LDS limit of the staged rows.
 @pytest.mark.parametrize("M", [1, 5, 16])
 @pytest.mark.parametrize("N", [6416, 16480])
