@@ -152,6 +152,19 @@ def test_w4a16_mid(ops, orc, x_dtype, asym, M, ws):
     _w4a16_case(ops, orc, M, 1040, 2048, x_dtype, asym, ops.ALGO_MID, seed=M + 7, ws=ws)
 
 
+@pytest.mark.parametrize("ws", [None, False], ids=["split", "nosplit"])
+@pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
+@pytest.mark.parametrize("M", [33, 74])
+def test_w4a16_mid_odd_groups(ops, orc, x_dtype, asym, M, ws):
+    """Mid-batch kernel with 18 groups: split into slices of 3 (an odd count:
+    the pipeline's one-group tail, a zero-point window of fewer than four
+    groups), or unsplit (a last window of two)."""
+    N, K = 1040, 2304
+    if ws is None:
+        assert ops.gemm_w4a16_workspace_bytes(M, N, K, ops.ALGO_MID) == 6 * M * N * 4
+    _w4a16_case(ops, orc, M, N, K, x_dtype, asym, ops.ALGO_MID, seed=M + 11, ws=ws)
+
+
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
 @pytest.mark.parametrize("B", [24, 74, 128])
 def test_w4a16_mid_llama_shapes(ops, orc, name, B):
