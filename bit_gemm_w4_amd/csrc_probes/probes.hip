@@ -108,11 +108,14 @@ __global__ __launch_bounds__(256) void k_stream(const uint8_t* src, int64_t nbyt
 }
 
 extern "C" {
-// out: blocks * 256 floats.  Returns 0, or 1 for an unknown kind.
+// out: blocks * 256 floats; nacc: 1, 2, 4 or 8 independent accumulator chains
+// per wave (other values: 4).  Returns 0, or 1 for an unknown kind.
 int probe_mfma(int kind, int nacc, float* out, int blocks, int iters, hipStream_t s) {
 #define PM(K)                                                                                           \
     if (kind == K) {                                                                                    \
         if (nacc == 8) hipLaunchKernelGGL((k_mfma<K, 8>), dim3(blocks), dim3(256), 0, s, out, iters, 1); \
+        else if (nacc == 2) hipLaunchKernelGGL((k_mfma<K, 2>), dim3(blocks), dim3(256), 0, s, out, iters, 1); \
+        else if (nacc == 1) hipLaunchKernelGGL((k_mfma<K, 1>), dim3(blocks), dim3(256), 0, s, out, iters, 1); \
         else hipLaunchKernelGGL((k_mfma<K, 4>), dim3(blocks), dim3(256), 0, s, out, iters, 1);         \
         return 0;                                                                                       \
     }

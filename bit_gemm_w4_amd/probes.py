@@ -34,8 +34,13 @@ MFMA_KINDS = [           # (kind id, name, operations per instruction)
 
 def build() -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    # MFMA results in VGPRs: in the accumulator-register form the compiler
+    # rotates the 16x16 probes' four-register accumulators through
+    # v_accvgpr moves between the MFMAs, and the loop then times those moves
+    # (about half the 16x16 shapes' real rate) instead of the matrix cores.
     cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", SRC, "-o", LIB]
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-mllvm", "-amdgpu-mfma-vgpr-form", SRC, "-o", LIB]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed for {SRC}:\n{r.stderr}")
@@ -84,6 +89,16 @@ def run():
         n = blocks * 4 * iters * 8                       # instructions
         rows.append((name, f"{n * ops / t / 1e12:,.0f} TOP/s",
                      f"{t * CLOCK_GHZ * 1e9 / (n / SIMDS):.1f} cycles per instruction per SIMD at {CLOCK_GHZ} GHz"))
+    # dependent chains: one wave per SIMD, each MFMA accumulating into the
+    # result of the MFMA nacc instructions before it
+    for kind, name, ops in MFMA_KINDS[:4]:
+        for nacc in (1, 2, 4):
+            iters = 16000 // nacc
+            t = _time(torch, lambda it: L.probe_mfma(kind, nacc, po, blocks // 2, it or iters, s))
+            n = blocks // 2 * 4 * iters * nacc
+            rows.append((f"{name}, {nacc} chain{'s' if nacc > 1 else ''}, one wave per SIMD",
+                         f"{n * ops / t / 1e12:,.0f} TOP/s",
+                         f"{t * CLOCK_GHZ * 1e9 / (n / SIMDS):.1f} cycles per instruction per SIMD at {CLOCK_GHZ} GHz"))
     iters = 4000
     t = _time(torch, lambda it: L.probe_lds(po, blocks, it or iters, s))
     b = blocks * 256 * 16 * 8 * iters
