@@ -109,10 +109,10 @@ int64_t w4_ws_need(int algo, int64_t M, int64_t N, int64_t K) {
 // tiles do not fill the device.
 int w4_auto_algo_ws(int64_t M, int64_t N, int64_t K) {
     // mid-batch kernel: measured faster than the split small-M and the tiled
-    // kernels on the projection shapes from M = 32 on the 28672-wide layer
-    // and from M = 64 on the others, through M = 128 (the tiled kernel wins
-    // again at M = 256)
-    if (M <= 128 && (M >= 64 || (M >= 32 && N >= 16384))) return BG_ALGO_MID;
+    // kernels on the projection shapes past M = 16 on the 28672-wide layer
+    // (24.7 against 27.3 us at M = 24) and from M = 64 on the others, through
+    // M = 128 (the tiled kernel wins again at M = 256)
+    if (M <= 128 && (M >= 64 || (M > 16 && N >= 16384))) return BG_ALGO_MID;
     if (M > kW4SkinnyMax) return bg::w4a16_gemm_split(M, N, K).S > 1 ? BG_ALGO_SPLITK : BG_ALGO_TILED;
     // (measured: down, K = 14336, is faster split at every M >= 8; gate_up,
     // N = 28672, is faster unsplit through M = 16 -- 19.2-19.8 us against

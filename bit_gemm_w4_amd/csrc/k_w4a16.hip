@@ -698,9 +698,11 @@ static const char* decode_dt(const void* x, int64_t M, int64_t K, const uint32_t
                 if (per > 1) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
                 return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             }
-            // (four tiles per block on the widest layers through M = 4: gate_up
-            // 14.7 / 15.0 us at B = 1 / 4 against 15.5 / 15.6 with two)
-            if (N >= 16384 && M <= 4) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
+            // (four tiles per block on the widest layers through M = 8: gate_up
+            // 14.8 / 15.2 / 16.3 / 16.3 us at B = 1 / 4 / 6 / 8 against
+            // 15.0 / 16.2 / 17.5 / 19.0 with two and 15.2 / 17.3 / 20.5 / 23.9
+            // with one)
+            if (N >= 16384 && M <= 8) return decode_nw<BF16, 1, 4, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             if (wide) return decode_nw<BF16, 1, 2, true, 0>(x, M, K, qw, sc, zr, N, y, s);
             return decode_nw<BF16, 1, 1, true, 0>(x, M, K, qw, sc, zr, N, y, s);
         }

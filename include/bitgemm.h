@@ -137,7 +137,11 @@ bg_status gemm_w4a16_ex(const void* x, int x_dtype, int64_t M, int64_t K,
  *            while its 256 x 128 output tiles do not fill one round of the
  *            device (S = min(256 / tiles, groups / 4); S = 1 is the plain
  *            kernel and needs no workspace).  BG_ALGO_AUTO picks it whenever
- *            S > 1.
+ *            S > 1 outside the mid-batch range below.
+ * and the mid-batch kernel (BG_ALGO_MID) with K split so that its blocks
+ * fill one round of the device; BG_ALGO_AUTO picks it where it measured
+ * faster than both of the above: 17 <= M <= 128 on layers with N >= 16384,
+ * 64 <= M <= 128 on the others.
  * The FP32 partials go to the workspace and a second kernel, enqueued on the
  * same stream, sums them in a fixed order, so results are deterministic.
  *   workspace        16-byte aligned device memory of at least

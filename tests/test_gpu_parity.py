@@ -126,10 +126,12 @@ def test_w4a16_small(ops, orc, algo, x_dtype, asym, M):
     _w4a16_case(ops, orc, M, 272, 768, x_dtype, asym, algo, seed=M)
 
 
-@pytest.mark.parametrize("M,N", [(9, 16400), (16, 16400), (12, 4112), (16, 4112), (8, 4112)])
+@pytest.mark.parametrize("M,N", [(6, 16400), (8, 16400), (9, 16400), (16, 16400), (12, 4112), (16, 4112),
+                                 (8, 4112)])
 def test_w4a16_small_m_tile_widths(ops, orc, M, N):
-    """Small-M kernel blocks of four weight tiles (N >= 16384, M > 8), two
-    (N > 4096, M > 8) and one, each with a ragged last block (1025 or 257 tiles)."""
+    """Small-M kernel blocks of four weight tiles (N >= 16384, M <= 8), two
+    (N >= 16384 from M = 9, N > 4096 from M = 9) and one, each with a ragged
+    last block (1025 or 257 tiles)."""
     _w4a16_case(ops, orc, M, N, 512, "bf16", True, 2, seed=M + N, ws=False)
 
 
