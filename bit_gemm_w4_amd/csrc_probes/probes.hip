@@ -107,6 +107,33 @@ __global__ __launch_bounds__(256) void k_stream(const uint8_t* src, int64_t nbyt
     out[blockIdx.x * 256 + threadIdx.x] = (float)(acc.x + acc.y);
 }
 
+// An empty kernel: what a launch costs by itself (replayed in a graph).
+__global__ void k_empty() {}
+
+// Reads nbytes once and nothing else: thread t of T takes the 16-byte chunks
+// t, t + T, t + 2T, ..., eight of them in flight; chunks past the end read
+// zeros through the buffer resource (no memory access).  TAG only gives the
+// layers their own kernel names in a trace.
+template <int TAG>
+__global__ __launch_bounds__(256) void k_read_once(const uint8_t* src, int64_t nbytes, float* out) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, (int)nbytes, 0x00020000);
+    const int64_t nchunk = nbytes >> 4, T = (int64_t)gridDim.x * 256;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint4 acc = make_uint4(0, 0, 0, 0);
+    for (int64_t c = t; c < nchunk; c += 8 * T) {
+        uint4 r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t cc = c + u * T;
+            r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rs, cc < nchunk ? (int)(cc << 4) : (int)0x80000000u, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc.x ^= r[u].x, acc.y += r[u].y, acc.z ^= r[u].z, acc.w += r[u].w;
+    }
+    out[t] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
+}
+
 extern "C" {
 // out: blocks * 256 floats; nacc: 1, 2, 4 or 8 independent accumulator chains
 // per wave (other values: 4).  Returns 0, or 1 for an unknown kind.
@@ -125,6 +152,20 @@ int probe_mfma(int kind, int nacc, float* out, int blocks, int iters, hipStream_
 }
 int probe_lds(float* out, int blocks, int iters, hipStream_t s) {
     hipLaunchKernelGGL(k_lds, dim3(blocks), dim3(256), 0, s, out, iters);
+    return 0;
+}
+int probe_empty(hipStream_t s) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
+    return 0;
+}
+// nbytes: a multiple of 16, below 2^31; out: blocks * 256 floats; tag 0..3.
+int probe_read_once(int tag, const void* src, int64_t nbytes, float* out, int blocks, hipStream_t s) {
+    if (nbytes < 16 || nbytes >= ((int64_t)1 << 31) || (nbytes & 15) || tag < 0 || tag > 3) return 1;
+    const uint8_t* p = static_cast<const uint8_t*>(src);
+    if (tag == 0) hipLaunchKernelGGL((k_read_once<0>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
+    if (tag == 1) hipLaunchKernelGGL((k_read_once<1>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
+    if (tag == 2) hipLaunchKernelGGL((k_read_once<2>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
+    if (tag == 3) hipLaunchKernelGGL((k_read_once<3>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
     return 0;
 }
 // nbytes: a multiple of 1024, below 2^31.

@@ -3,10 +3,14 @@
     python3 -m bit_gemm_w4_amd.probes
 
 prints a markdown table of: dense MFMA throughput per instruction shape
-(independent accumulator chains, two waves per SIMD on all 1,024 SIMDs),
-LDS read bandwidth per CU (ds_read_b128), and streaming throughput into
-registers and by buffer_load ... lds from an L2-resident buffer (2 MiB) and
-from one that fits the 256 MB last-level cache but not L2 (128 MiB).
+(independent accumulator chains, two waves per SIMD on all 1,024 SIMDs, and
+dependent chains), LDS read bandwidth per CU (ds_read_b128), and streaming
+throughput into registers and by buffer_load ... lds from an L2-resident
+buffer (2 MiB) and from one that fits the 256 MB last-level cache but not
+L2 (128 MiB); then the floors of the decode step's calls, timed the way the
+step is (HIP graph replay, weights rotated over copies larger than the
+last-level cache): an empty kernel per launch, and a plain read of exactly
+each Llama-3-8B layer's packed W4 bytes.  `--floors` prints only those.
 
 Not part of the library path: the kernels live in csrc_probes/probes.hip and
 build into their own shared object (libprobes.so beside this file).
@@ -55,6 +59,8 @@ def _lib():
     L.probe_mfma.argtypes = [i32, i32, vp, i32, i32, vp]
     L.probe_lds.argtypes = [vp, i32, i32, vp]
     L.probe_stream.argtypes = [i32, vp, i64, vp, i32, i32, vp]
+    L.probe_empty.argtypes = [vp]
+    L.probe_read_once.argtypes = [i32, vp, i64, vp, i32, vp]
     return L
 
 
@@ -116,13 +122,83 @@ def run():
     return rows
 
 
+def _graph_us(torch, launches, replays=40):
+    """Microseconds per launch of `launches` (callables taking a stream
+    handle) captured together in one HIP graph: warm replays first (clocks
+    ramp up from idle), then the median of five timed batches."""
+    s = torch.cuda.Stream()
+    h = ctypes.c_void_p(s.cuda_stream)
+    with torch.cuda.stream(s):
+        for f in launches:
+            f(h)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for f in launches:
+            f(h)
+    torch.cuda.synchronize()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(s):
+            e0.record(s)
+            for _ in range(replays):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / replays / len(launches))
+    return sorted(ts)[2]
+
+
+def floors():
+    """Rows (what, us per launch, rate) of the launch and streaming floors."""
+    import torch
+    from . import synth
+    if not torch.cuda.is_available():
+        raise RuntimeError("the probes need a GPU")
+    L = _lib()
+    rows = []
+    t = _graph_us(torch, [lambda h: L.probe_empty(h)] * 100)
+    rows.append(("empty kernel (1 block), per launch in a graph of 100", f"{t:.2f} us", "-"))
+    grids = (256, 512, 1024, 2048, 4096)                             # blocks of 256 threads; the best counts
+    out = torch.empty(max(grids) * 256, dtype=torch.float32, device="cuda")
+    po = ctypes.c_void_p(out.data_ptr())
+    for tag, name in enumerate(("qkv", "o", "gate_up", "down")):
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        nbytes = N * K // 2 + N * K // 128 * 2 + N * K // 256      # packed codes, FP16 scales, 4-bit zeros
+        nbytes = (nbytes + 15) // 16 * 16
+        copies = max(2, (512 << 20) // nbytes + 1)                   # rotated past the last-level cache
+        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        best = None
+        for blocks in grids:
+            t = _graph_us(torch, [lambda h, b=b, n=blocks: L.probe_read_once(tag, ctypes.c_void_p(b.data_ptr()), nbytes,
+                                                                              po, n, h) for b in bufs])
+            best = (t, blocks) if best is None or t < best[0] else best
+        t, blocks = best
+        rows.append((f"read once: {name}'s packed W4 bytes ({nbytes / 1e6:.2f} MB), {copies} copies rotated, "
+                     f"best of {len(grids)} grids ({blocks} blocks)", f"{t:.2f} us", f"{nbytes / t / 1e3:,.0f} GB/s"))
+        del bufs
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
+    import sys
     if not os.path.exists(LIB):
         build()
-    rows = run()
-    print("| probe | rate | per unit |")
+    if "--floors" not in sys.argv:
+        rows = run()
+        print("| probe | rate | per unit |")
+        print("|---|---|---|")
+        for r in rows:
+            print(f"| {r[0]} | {r[1]} | {r[2]} |")
+        print()
+    print("| floor | time | rate |")
     print("|---|---|---|")
-    for r in rows:
+    for r in floors():
         print(f"| {r[0]} | {r[1]} | {r[2]} |")
 
 

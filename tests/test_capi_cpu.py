@@ -238,14 +238,14 @@ def test_noalloc_rejects_before_touching_the_device(L):
 
 def test_probe_library_exports():
     """The device-rate probes build into their own object (not the library)
-    and export their three entry points; nothing is launched here."""
+    and export their entry points; nothing is launched here."""
     import ctypes
     import os
     from bit_gemm_w4_amd import probes
     if not os.path.exists(probes.LIB):
         probes.build()
     L = ctypes.CDLL(probes.LIB)
-    for name in ("probe_mfma", "probe_lds", "probe_stream"):
+    for name in ("probe_mfma", "probe_lds", "probe_stream", "probe_empty", "probe_read_once"):
         assert hasattr(L, name), name
     main = ctypes.CDLL(os.path.join(os.path.dirname(probes.__file__), "libbitgemm.so"))
     assert not hasattr(main, "probe_mfma")

@@ -263,6 +263,8 @@ def test_act_quant_bitexact(ops, orc, fp8, gran, dtype):
     (True, "row_g128", 2048, 4096, "bf16"),
     (True, "block128", 4096, 14336, "f32"),  # 128x128 FP8 weight blocks
     (False, "row", 3, 20480, "bf16"),        # rows longer than the register-resident kernel
+    (False, "row", 2500, 4224, "bf16"),      # looping blocks: 1024 of them, 2 or 3 rows each
+    (True, "row", 1025, 2048, "f16"),        # one block with a second row, the others one
 ])
 def test_act_quant_full_shapes(ops, orc, fp8, gran, rows, cols, dtype):
     if dtype == "f32":
