@@ -207,6 +207,10 @@ def main():
             "frac": round(achieved / roofline.HBM_GBPS, 4),
             "traffic": None if traffic is None else round(traffic)}
     calibration_copy(torch, dev)
+    ceilings = measured_ceilings(torch, calls, ms_per_step)
+    if ceilings is not None:
+        roof["achievable"] = ceilings["hbm_read_gbps"]
+        roof["frac_of_achievable"] = round(achieved / ceilings["hbm_read_gbps"], 4)
 
     out = {
         "metric": "W4A16/W8A8 linear: HBM GB/s at B=1..16, TFLOPS at M=2048; % of roofline",
@@ -219,6 +223,7 @@ def main():
                    "calls_per_step": len(calls), "bytes_per_step": step_bytes,
                    "weight_copies_rotated": R_COPIES, "timing": "HIP graph replay"},
         "roofline": roof,
+        "measured_ceilings": ceilings,
         "per_call_gbps": {f"{n}@B{B}": round(call_bytes[(n, B)] / per_call[(n, B)] / 1e6, 1) for n, B in calls},
     }
 
@@ -236,6 +241,28 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w_host, xs, calls, args.cpu_seconds, np, synth, roofline)
 
     print(json.dumps(out), flush=True)
+
+
+def measured_ceilings(torch, calls, ms_per_step):
+    """What this device reaches, measured in the same run with the probe
+    kernels (bit_gemm_w4_amd/csrc_probes): a plain read of a 1 GiB buffer,
+    the MFMA-only rates of the 32x32 BF16 / INT8 / FP8 shapes, and the
+    step's streaming floor -- the sum over its calls of a plain read of the
+    call's packed weight bytes, graph-replayed past the last-level cache.
+    None when the probe library is not built."""
+    from bit_gemm_w4_amd import probes
+    if not os.path.exists(probes.LIB):
+        log("probe library not built: no measured ceilings")
+        return None
+    peaks = probes.measured_peaks(torch)
+    floors = probes.layer_floors_us(torch)
+    floor_us = sum(floors[name] for name, _ in calls)
+    step_us = ms_per_step * 1e3
+    res = dict(peaks, layer_read_floor_us=floors, step_read_floor_us=round(floor_us, 2),
+               step_frac_of_read_floor=round(floor_us / step_us, 4))
+    log(f"measured ceilings: read {peaks['hbm_read_gbps']:.0f} GB/s, MFMA {peaks['mfma_tflops']}; "
+        f"step read floor {floor_us:.1f} us ({floor_us / step_us:.1%} of the step)")
+    return res
 
 
 CALIB_BYTES = 512 << 20

@@ -111,25 +111,25 @@ __global__ __launch_bounds__(256) void k_stream(const uint8_t* src, int64_t nbyt
 __global__ void k_empty() {}
 
 // Reads nbytes once and nothing else: thread t of T takes the 16-byte chunks
-// t, t + T, t + 2T, ..., eight of them in flight; chunks past the end read
+// t, t + T, t + 2T, ..., RD of them in flight; chunks past the end read
 // zeros through the buffer resource (no memory access).  TAG only gives the
 // layers their own kernel names in a trace.
-template <int TAG>
+template <int TAG, int RD>
 __global__ __launch_bounds__(256) void k_read_once(const uint8_t* src, int64_t nbytes, float* out) {
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, (int)nbytes, 0x00020000);
     const int64_t nchunk = nbytes >> 4, T = (int64_t)gridDim.x * 256;
     const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
     uint4 acc = make_uint4(0, 0, 0, 0);
-    for (int64_t c = t; c < nchunk; c += 8 * T) {
-        uint4 r[8];
+    for (int64_t c = t; c < nchunk; c += RD * T) {
+        uint4 r[RD];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < RD; ++u) {
             const int64_t cc = c + u * T;
             r[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rs, cc < nchunk ? (int)(cc << 4) : (int)0x80000000u, 0, 0));
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc.x ^= r[u].x, acc.y += r[u].y, acc.z ^= r[u].z, acc.w += r[u].w;
+        for (int u = 0; u < RD; ++u) acc.x ^= r[u].x, acc.y += r[u].y, acc.z ^= r[u].z, acc.w += r[u].w;
     }
     out[t] = (float)(acc.x ^ acc.y ^ acc.z ^ acc.w);
 }
@@ -158,14 +158,18 @@ int probe_empty(hipStream_t s) {
     hipLaunchKernelGGL(k_empty, dim3(1), dim3(64), 0, s);
     return 0;
 }
-// nbytes: a multiple of 16, below 2^31; out: blocks * 256 floats; tag 0..3.
-int probe_read_once(int tag, const void* src, int64_t nbytes, float* out, int blocks, hipStream_t s) {
+// nbytes: a multiple of 16, below 2^31; out: blocks * 256 floats; tag 0..3;
+// depth (loads in flight per thread) 4, 8, 16 or 32.
+int probe_read_once(int tag, int depth, const void* src, int64_t nbytes, float* out, int blocks, hipStream_t s) {
     if (nbytes < 16 || nbytes >= ((int64_t)1 << 31) || (nbytes & 15) || tag < 0 || tag > 3) return 1;
+    if (depth != 4 && depth != 8 && depth != 16 && depth != 32) return 1;
     const uint8_t* p = static_cast<const uint8_t*>(src);
-    if (tag == 0) hipLaunchKernelGGL((k_read_once<0>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
-    if (tag == 1) hipLaunchKernelGGL((k_read_once<1>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
-    if (tag == 2) hipLaunchKernelGGL((k_read_once<2>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
-    if (tag == 3) hipLaunchKernelGGL((k_read_once<3>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
+#define PR(T, D)                                                                                        \
+    if (tag == T && depth == D) hipLaunchKernelGGL((k_read_once<T, D>), dim3(blocks), dim3(256), 0, s, p, nbytes, out);
+#define PRT(T) PR(T, 4) PR(T, 8) PR(T, 16) PR(T, 32)
+    PRT(0) PRT(1) PRT(2) PRT(3)
+#undef PRT
+#undef PR
     return 0;
 }
 // nbytes: a multiple of 1024, below 2^31.

@@ -60,7 +60,7 @@ def _lib():
     L.probe_lds.argtypes = [vp, i32, i32, vp]
     L.probe_stream.argtypes = [i32, vp, i64, vp, i32, i32, vp]
     L.probe_empty.argtypes = [vp]
-    L.probe_read_once.argtypes = [i32, vp, i64, vp, i32, vp]
+    L.probe_read_once.argtypes = [i32, i32, vp, i64, vp, i32, vp]
     return L
 
 
@@ -153,6 +153,78 @@ def _graph_us(torch, launches, replays=40):
     return sorted(ts)[2]
 
 
+def _read_once_us(torch, L, nbytes, tag, grids=(256, 512, 1024, 2048, 4096), depths=(4, 8, 16, 32)):
+    """Best (us per launch, blocks, depth, copies) of a plain read of nbytes,
+    graph-replayed over copies rotated past the last-level cache, over a few
+    grids and load depths (16-byte loads in flight per thread)."""
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = max(2, (512 << 20) // nbytes + 1)
+    out = torch.empty(max(grids) * 256, dtype=torch.float32, device="cuda")
+    po = ctypes.c_void_p(out.data_ptr())
+    bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    best = None
+    for depth in depths:
+        for blocks in grids:
+            t = _graph_us(torch, [lambda h, b=b, n=blocks, d=depth: L.probe_read_once(
+                tag, d, ctypes.c_void_p(b.data_ptr()), nbytes, po, n, h) for b in bufs])
+            best = (t, blocks, depth, copies) if best is None or t < best[0] else best
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
+def hbm_read_tbps(torch, L):
+    """Best read rate from HBM: a 1 GiB buffer (past the 256 MB last-level
+    cache) streamed by the read-once kernel (best grid and depth) and by the
+    long-running strided stream kernel (16 pieces of 1 KB in flight per wave,
+    about 4 GiB read per launch)."""
+    t, _, _, _ = _read_once_us(torch, L, 1 << 30, 0, grids=(1024, 2048, 4096, 8192))
+    best = (1 << 30) / t / 1e6
+    n = 1 << 30
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for blocks in (1024, 2048, 4096):
+        out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+        po = ctypes.c_void_p(out.data_ptr())
+        iters = 4 * n // (blocks * 4 * 16 * 1024)
+        tk = _time(torch, lambda it: L.probe_stream(0, ctypes.c_void_p(src.data_ptr()), n, po, blocks, it or iters, s))
+        best = max(best, blocks * 4 * 16 * 1024 * iters / tk / 1e12)
+    del src
+    torch.cuda.empty_cache()
+    return best
+
+
+def measured_peaks(torch):
+    """Live ceilings of this device: the best HBM read rate (hbm_read_tbps)
+    and the MFMA rates of the 32x32 BF16, INT8 and FP8 shapes (eight
+    independent chains per wave, two waves per SIMD)."""
+    L = _lib()
+    hbm = hbm_read_tbps(torch, L)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks = 512
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    po = ctypes.c_void_p(out.data_ptr())
+    mfma = {}
+    for kind, key in ((1, "bf16"), (3, "i8"), (5, "fp8")):
+        ops = next(o for k, _, o in MFMA_KINDS if k == kind)
+        iters = 2000
+        tk = _time(torch, lambda it: L.probe_mfma(kind, 8, po, blocks, it or iters, s))
+        mfma[key] = round(blocks * 4 * iters * 8 * ops / tk / 1e12, 1)
+    return {"hbm_read_gbps": round(hbm * 1e3, 1), "mfma_tflops": mfma}
+
+
+def layer_floors_us(torch):
+    """Per Llama-3-8B layer: microseconds of a plain read of its packed W4
+    bytes (best grid), graph-replayed past the last-level cache."""
+    from . import synth
+    L = _lib()
+    res = {}
+    for tag, name in enumerate(("qkv", "o", "gate_up", "down")):
+        K, N = synth.LLAMA3_8B_SHAPES[name]
+        res[name] = round(_read_once_us(torch, L, N * K // 2 + N * K // 128 * 2 + N * K // 256, tag)[0], 3)
+    return res
+
+
 def floors():
     """Rows (what, us per launch, rate) of the launch and streaming floors."""
     import torch
@@ -163,25 +235,15 @@ def floors():
     rows = []
     t = _graph_us(torch, [lambda h: L.probe_empty(h)] * 100)
     rows.append(("empty kernel (1 block), per launch in a graph of 100", f"{t:.2f} us", "-"))
-    grids = (256, 512, 1024, 2048, 4096)                             # blocks of 256 threads; the best counts
-    out = torch.empty(max(grids) * 256, dtype=torch.float32, device="cuda")
-    po = ctypes.c_void_p(out.data_ptr())
     for tag, name in enumerate(("qkv", "o", "gate_up", "down")):
         K, N = synth.LLAMA3_8B_SHAPES[name]
         nbytes = N * K // 2 + N * K // 128 * 2 + N * K // 256      # packed codes, FP16 scales, 4-bit zeros
-        nbytes = (nbytes + 15) // 16 * 16
-        copies = max(2, (512 << 20) // nbytes + 1)                   # rotated past the last-level cache
-        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
-        best = None
-        for blocks in grids:
-            t = _graph_us(torch, [lambda h, b=b, n=blocks: L.probe_read_once(tag, ctypes.c_void_p(b.data_ptr()), nbytes,
-                                                                              po, n, h) for b in bufs])
-            best = (t, blocks) if best is None or t < best[0] else best
-        t, blocks = best
+        t, blocks, depth, copies = _read_once_us(torch, L, nbytes, tag)
         rows.append((f"read once: {name}'s packed W4 bytes ({nbytes / 1e6:.2f} MB), {copies} copies rotated, "
-                     f"best of {len(grids)} grids ({blocks} blocks)", f"{t:.2f} us", f"{nbytes / t / 1e3:,.0f} GB/s"))
-        del bufs
-        torch.cuda.empty_cache()
+                     f"best of 5 grids x 4 depths ({blocks} blocks, {depth} loads in flight)", f"{t:.2f} us",
+                     f"{nbytes / t / 1e3:,.0f} GB/s"))
+    rows.append(("HBM read rate: 1 GiB buffer, best of the read-once and the strided stream kernel", "-",
+                 f"{hbm_read_tbps(torch, L) * 1e3:,.0f} GB/s"))
     return rows
 
 
