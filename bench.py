@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the live device ceilings (thousands of probe launches: leave them out of profiled runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--large-m-once", action="store_true",
                     help="run each large-M GEMM three times untimed (for counter collection) and exit")
@@ -207,7 +209,7 @@ def main():
             "frac": round(achieved / roofline.HBM_GBPS, 4),
             "traffic": None if traffic is None else round(traffic)}
     calibration_copy(torch, dev)
-    ceilings = measured_ceilings(torch, calls, ms_per_step)
+    ceilings = None if args.no_ceilings else measured_ceilings(torch, calls, ms_per_step)
     if ceilings is not None:
         roof["achievable"] = ceilings["hbm_read_gbps"]
         roof["frac_of_achievable"] = round(achieved / ceilings["hbm_read_gbps"], 4)

@@ -101,6 +101,7 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // MX: the scale area is copied 256 bytes per wave-copy, MXC copies per
     // wave and stage
     static_assert(!MX || (FP8 && !BLOCK), "MX scaling is an FP8-family variant");
+    static_assert(!BLOCK || FP8, "128 x 128 block scales are an FP8 variant (one MFMA per tile and stage)");
     constexpr int MX_AREA = RUNS * ROWS;
     constexpr int MXC = MX ? (MX_AREA + 256 * NW - 1) / (256 * NW) : 0;
     constexpr int LOADS_T = LOADS + MXC;
@@ -328,7 +329,6 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                 for (int j = 0; j < TN; ++j) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) facc[i][j][e] += acc[i][j][e] * sc;
-                    acc[i][j] = acc_t{};
                 }
             }
 #pragma unroll
@@ -349,7 +349,9 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     constexpr int NREAD = NFRAG + (MX ? MXR * (TM + TN) : 0);
     constexpr int NMFMA = FP8 && !F4 ? TM * TN : 2 * TM * TN;
     constexpr int NSLOT = NMFMA - NMFMA / 4;
-    auto step = [&](FragsT& cur, FragsT& nxt, int kb) {
+    // first: kb opens a 128-wide K block (even kb); with block scales its
+    // MFMAs start from zero instead of the closed block's partial sums
+    auto step = [&](FragsT& cur, FragsT& nxt, int kb, bool first) {
         settle_frags(cur);
         // this wave's copies of stage kb+1 landed: younger than them are the
         // copies of the NB-2 later stages and, with block scales, the scale
@@ -398,7 +400,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         bv, av, acc[i][j], 0, 0, 0, (int)(pkb[0] >> (8 * j)), 0, (int)(pka[0] >> (8 * i)));
                 else
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 0, 0, 0, 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bv, av, (BLOCK && first) ? acc_t{} : acc[i][j], 0, 0, 0, 0, 0, 0);
             } else {
                 const int half = t / (TM * TN);
                 i = (t % (TM * TN)) / TN, j = t % TN;
@@ -466,8 +469,8 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
     for (int r = 0; r < NREAD; ++r) read_one(f0, stage_base(kb0), mx_base(kb0), r);
     for (int kb = kb0; kb < kb1; kb += 2) {                      // slices hold whole 128-byte K blocks
-        step(f0, f1, kb);
-        step(f1, f0, kb + 1);
+        step(f0, f1, kb, true);
+        step(f1, f0, kb + 1, false);
     }
     wait_vmcnt<0>();                                             // no copy may land after the block exits
     // the last step read the (unused) stage after the slice into f0: those

@@ -166,7 +166,7 @@ def _read_once_us(torch, L, nbytes, tag, grids=(256, 512, 1024, 2048, 4096), dep
     for depth in depths:
         for blocks in grids:
             t = _graph_us(torch, [lambda h, b=b, n=blocks, d=depth: L.probe_read_once(
-                tag, d, ctypes.c_void_p(b.data_ptr()), nbytes, po, n, h) for b in bufs])
+                tag, d, ctypes.c_void_p(b.data_ptr()), nbytes, po, n, h) for b in bufs], replays=10)
             best = (t, blocks, depth, copies) if best is None or t < best[0] else best
     del bufs
     torch.cuda.empty_cache()
