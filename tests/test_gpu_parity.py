@@ -135,6 +135,17 @@ def test_w4a16_small_m_tile_widths(ops, orc, M, N):
     _w4a16_case(ops, orc, M, N, 512, "bf16", True, 2, seed=M + N, ws=False)
 
 
+@pytest.mark.parametrize("M,N,kern", [(16, 16400, "k_w4a16_decode<"), (17, 16400, "k_w4a16_mid<"),
+                                      (31, 16400, "k_w4a16_mid<"), (24, 4112, "k_w4a16_splitk<"),
+                                      (64, 4112, "k_w4a16_mid<")])
+def test_w4a16_auto_workspace_dispatch(ops, orc, M, N, kern):
+    """AUTO with a workspace on both sides of the mid-batch threshold: from
+    M = 17 on layers with N >= 16384, from M = 64 on the others (K = 512:
+    four groups, ragged last weight tiles)."""
+    _w4a16_case(ops, orc, M, N, 512, "bf16", True, 0, seed=M + 3 * N)
+    assert ops.last_kernel().startswith(kern), ops.last_kernel()
+
+
 @pytest.mark.parametrize("x_dtype,asym", [("bf16", True), ("f16", False)])
 @pytest.mark.parametrize("M", [65, 130, 300])
 def test_w4a16_splitk_large_m(ops, orc, x_dtype, asym, M):
