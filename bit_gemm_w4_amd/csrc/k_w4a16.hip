@@ -576,37 +576,35 @@ __global__ __launch_bounds__(SPK_NW * 64) void k_w4a16_splitk(const uint16_t* __
 }
 
 // Sum of the S partial tiles of the split-K kernel, in slice order.  One
-// thread per (tile, 16-row band, lane): the lane's four rows of one column.
+// thread per output value -- (tile, 16-row band, lane, row e of the lane's
+// four), i.e. one float of a slice's partial tile -- so the grid has as many
+// threads as a slice has floats and spreads its loads over the device.
 template <bool BF16, int TM>
 __global__ __launch_bounds__(256) void k_w4a16_splitk_reduce(const float* __restrict__ ws, int S, int64_t tiles_pad,
                                                              int64_t M, int64_t N, uint16_t* __restrict__ y) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (tile, i, lane)
-    const int lane = (int)(t & 63);
-    const int64_t ti = t >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;     // float index within a slice
+    const int lane = (int)((t >> 2) & 63), e = (int)(t & 3);
+    const int64_t ti = t >> 8;
     const int i = (int)(ti % TM);
     const int64_t tile = ti / TM;
     const int q = lane >> 4, l16 = lane & 15;
-    if (tile * 16 >= N || 16 * i + 4 * q >= M) return;
+    const int64_t m = 16 * i + 4 * q + e;
+    if (tile * 16 >= N || m >= M) return;
     const int64_t slice = tiles_pad * TM * 256;
-    const float* p = ws + (tile * TM + i) * 256 + lane * 4;
+    const float* p = ws + t;
     // all loads of a batch of up to 16 slices are in flight together; the sum
     // still runs in slice order
     constexpr int RB = 16;
-    float4_t v = float4_t{0, 0, 0, 0};
+    float v = 0.0f;
     for (int b0 = 0; b0 < S; b0 += RB) {
-        float4_t part[RB];
+        float part[RB];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
-            part[r] = b0 + r < S ? *reinterpret_cast<const float4_t*>(p + (b0 + r) * slice) : float4_t{0, 0, 0, 0};
+        for (int r = 0; r < RB; ++r) part[r] = b0 + r < S ? p[(b0 + r) * slice] : 0.0f;
 #pragma unroll
         for (int r = 0; r < RB; ++r)
             if (b0 + r < S) v = b0 + r == 0 ? part[r] : v + part[r];
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int64_t m = 16 * i + 4 * q + e;
-        if (m < M) y[m * N + tile * 16 + l16] = to_out<BF16>(v[e]);
-    }
+    y[m * N + tile * 16 + l16] = to_out<BF16>(v);
 }
 
 constexpr int64_t kLdsMax = 160 * 1024;
@@ -790,7 +788,7 @@ static const char* splitk_launch(const SplitCfg& c, const void* x, int64_t M, in
                        static_cast<float*>(ws), c.S, c.gs);
     if (c.S > 1) {
         const int64_t tiles_pad = (int64_t)c.colgroups * SPK_NW;
-        const int64_t threads = tiles_pad * TM * 64;
+        const int64_t threads = tiles_pad * TM * 256;
         hipLaunchKernelGGL((k_w4a16_splitk_reduce<BF16, TM>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
                            static_cast<const float*>(ws), c.S, tiles_pad, M, N, static_cast<uint16_t*>(y));
     }
