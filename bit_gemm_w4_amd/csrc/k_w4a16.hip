@@ -82,10 +82,17 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
                                                           uint16_t* __restrict__ y, uint64_t rcp) {
     constexpr bool VALU = VROWS > 0;
     static_assert(!VALU || (XLDS && TM == 1), "the VALU product reads activations from LDS");
-    // groups in flight per wave: 4 for two-tile blocks; 3 for one-tile blocks,
-    // whose fewer registers per wave keep more waves resident (o / down /
-    // qkv at B = 1..4: 4-7 % faster per call than with 4)
-    constexpr int STAGES = XLDS ? (TN == 1 ? 3 : TN <= 2 ? 4 : 2) : 3;
+    // groups in flight per wave, chosen so that a CU keeps roughly 24-64 KB of
+    // weights in flight: more requests than that compete at the memory side
+    // (gate_up with two groups per wave of its four- and seven-tile blocks is
+    // 0.3-0.6 us slower per call than with one, qkv at B = 16 0.3 us slower
+    // with four groups of its two-tile blocks than with two); fewer leave
+    // HBM idle (qkv and down at B = 1, with 4-8 one-tile waves per CU: 0.4-
+    // 1 us slower with two groups than with three).  One-tile blocks of 16
+    // waves: two.  (The VALU product keeps 3 / 4 groups for one / two tiles.)
+    constexpr int STAGES = VALU   ? (TN == 1 ? 3 : 4)
+                           : XLDS ? (TN == 1 ? (NW == 16 ? 2 : 3) : TN == 2 ? 2 : 1)
+                                  : 3;
     // X staging batch: 16 chunks per thread for blocks of seven or more
     // tiles (the 16-row, one-round configuration: all of a block's rows in
     // one batch, issued before the weight stages; gate_up at B = 16 19.4 ->
