@@ -53,7 +53,12 @@ __global__ __launch_bounds__(NW * 64) void k_w4a8_decode(const int8_t* __restric
                                                          const uint16_t* __restrict__ sc,
                                                          const uint8_t* __restrict__ zr, int64_t N,
                                                          void* __restrict__ y, int out_dt, uint64_t rcp) {
-    constexpr int STAGES = TN == 1 ? 4 : TN == 2 ? 3 : 2;
+    // two groups in flight per wave: deeper pipelines keep more requests in
+    // flight than the memory side serves well (the twelve Llama-3-8B decode
+    // calls at B = 1, 4, 16: 111.1 us in all against 115.8 with the earlier
+    // 4 / 3 / 2 groups for one / two / more tiles; gate_up at B = 16 18.3
+    // against 19.6; three groups only helped down at B = 1 and 4, by 0.15 us)
+    constexpr int STAGES = 2;
     static_assert(XL || TN <= 2, "activation fragments in the stages: at most two tiles");
     static_assert(TM == 1 || TN <= 4, "two bands: at most four tiles");
     constexpr int XB = 4;                                              // activation chunks per batch
