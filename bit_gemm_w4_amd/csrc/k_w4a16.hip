@@ -433,7 +433,9 @@ __global__ __launch_bounds__(NW * 64) void k_w4a16_decode(const uint16_t* __rest
 // table the block builds next to the staged activations.
 // ============================================================================
 constexpr int SPK_NW = 16;
-constexpr int SPK_STAGES = 4;
+// two groups in flight per wave (16 waves, about one block per CU): down at
+// B = 16 12.37 us against 12.71 with four and 12.78 with three
+constexpr int SPK_STAGES = 2;
 
 struct SpkStage {
     uint4 w;

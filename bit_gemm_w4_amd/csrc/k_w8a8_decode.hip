@@ -50,13 +50,15 @@ enum { DG_T = 0, DG_R = 1, DG_R128 = 2, DG_B128 = 3 };
 // except for four-tile blocks, whose 8 KB stages keep more requests in
 // flight than the memory side serves well (gate_up at B = 16: 27.7 us with
 // two stages, 29.4 with three, 29.5 with four; the one- and two-tile
-// configurations measured best or within 1 % at four).
+// configurations measured best or within 1 % at four).  Without staged rows
+// a stage also carries the activation fragments; 16-wave blocks of one band
+// keep two (down at B = 16: 18.2 us against 19.4 with four, 20.8 with three).
 template <int NW, int TM, int TN, bool XL>
 struct DecCfg {
     static constexpr int STAGES = XL        ? (TN == 4 ? 2 : 4)
                                   : NW == 4 ? (TM == 4 ? 4 : 8)
                                   : NW == 8 ? (TM == 4 ? 3 : 4)
-                                            : (TM == 1 ? 4 : 2);
+                                            : 2;
 };
 }  // namespace
 
