@@ -118,12 +118,14 @@ __device__ __forceinline__ void settle(T& v) {
 // Tile of block b for a grid of tiles_m x tiles_n tiles.  Blocks are dealt
 // round-robin to the 8 XCDs, so b is first remapped to (b % 8) * (nt / 8) +
 // b / 8 (when nt % 8 == 0), giving each XCD a contiguous run of tiles; runs
-// are ordered in bands of 8 row tiles, so the blocks resident on one XCD
-// share row tiles and column tiles in its L2.
+// are ordered in bands of GROUP_M row tiles, so the blocks resident on one
+// XCD share row tiles and column tiles in its L2.  GROUP_M = 1 (row-major
+// runs: an XCD's resident blocks share one row tile) suits kernels whose
+// activation tile is many times their weight tile.
+template <int GROUP_M = 8>
 __device__ __forceinline__ void grouped_tile(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int nt = tiles_m * tiles_n;
     if (nt % 8 == 0) b = (b % 8) * (nt / 8) + b / 8;
-    constexpr int GROUP_M = 8;
     const int band = b / (GROUP_M * tiles_n);
     const int local = b - band * GROUP_M * tiles_n;
     const int first_m = band * GROUP_M;
