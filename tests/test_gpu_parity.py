@@ -376,6 +376,10 @@ def _w8a8_case(ops, orc, M, N, K, fp8, a_gran, w_gran, algo, out_dtype=torch.bfl
     wo, wso = oquant(w, w_gran)
     assert np.array_equal(a.cpu().numpy().view(np.uint8), ao.view(np.uint8))
     assert np.array_equal(wq.cpu().numpy().view(np.uint8), wo.view(np.uint8))
+    # the scales the GEMM reads, bit for bit (same layout on both sides; for a
+    # whole tensor [scale, amax])
+    assert np.array_equal(a_s.cpu().numpy().view(np.uint32), aso.view(np.uint32)), "activation scales"
+    assert np.array_equal(w_s.cpu().numpy().view(np.uint32), wso.view(np.uint32)), "weight scales"
     sel = np.arange(M) if rows is None else np.asarray(rows)
     aso_sel = aso if a_gran == 0 else aso[sel]
     if out_dtype == torch.int32:
