@@ -302,8 +302,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // The scales of K block c are loaded at the close of block c - SCP (a ring
     // of SCP blocks in registers, rotated at every close), so most of their
     // latency is hidden.  The loads are unconditional (rows past M read row
-    // M - 1, blocks past the end of K the last one): every wave issues exactly
-    // TM vector loads per close, which the stage waits below count.
+    // M - 1, blocks past the end of K the last one).  The stage waits below
+    // do not count them: they read through restrict pointers that no inline
+    // assembly names, so the compiler may move them across the waits (it
+    // sank the first ring's loads below the prologue wait, which then let the
+    // first stage's fragment reads race its copies).
     constexpr int SCP = 4;
     const int64_t nkb128 = K >> 7;
     const int64_t nbw = (n0 + wn * WTN) >> 7;                    // this wave's 128-column weight block
@@ -356,10 +359,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
     // MFMAs start from zero instead of the closed block's partial sums
     auto step = [&](FragsT& cur, FragsT& nxt, int kb, bool first) {
         settle_frags(cur);
-        // this wave's copies of stage kb+1 landed: younger than them are the
-        // copies of the NB-2 later stages and, with block scales, the scale
-        // loads of the two closes among the last four steps (NB = 5)
-        wait_vmcnt<(NB - 2) * LOADS_T + (BLOCK ? 2 * TM : 0)>();
+        // this wave's copies of stage kb+1 landed: younger than them are at
+        // least the copies of the NB-2 later stages (block-scale loads, which
+        // the compiler may place anywhere, are not counted: a wait can only
+        // end later for them)
+        wait_vmcnt<(NB - 2) * LOADS_T>();
         block_barrier();
         const uint32_t nb_base = stage_base(kb + 1), nb_mx = mx_base(kb + 1);
         // MX: this stage's E8M0 bytes of the fragment rows for MFMA step c,
@@ -460,13 +464,11 @@ __global__ __launch_bounds__(128 * WN, 1) void k_w8a8_gemm(const uint8_t* __rest
 #pragma unroll
     for (int t = 0; t < NB; ++t) issue(kb0 + t);
     if constexpr (BLOCK) {
-        // ring for the first SCP blocks, issued after the copies (so at least
-        // 2 TM scale loads are younger than every stage's copies, as the step
-        // waits assume)
+        // ring for the first SCP blocks (not counted by the wait below)
 #pragma unroll
         for (int r = 0; r < SCP; ++r) load_scales(sa_ring[r], sw_ring[r], kb0 / 2 + r);
     }
-    wait_vmcnt<(NB - 1) * LOADS_T + (BLOCK ? SCP * TM : 0)>();
+    wait_vmcnt<(NB - 1) * LOADS_T>();
     block_barrier();
     FragsT f0, f1;
 #pragma unroll

@@ -52,12 +52,14 @@ enum { DG_T = 0, DG_R = 1, DG_R128 = 2, DG_B128 = 3 };
 // two stages, 29.4 with three, 29.5 with four; the one- and two-tile
 // configurations measured best or within 1 % at four).  Without staged rows
 // a stage also carries the activation fragments; 16-wave blocks of one band
-// keep two (down at B = 16: 18.2 us against 19.4 with four, 20.8 with three).
+// keep two (down at B = 16: 18.2 us against 19.4 with four, 20.8 with three),
+// and so do 8-wave blocks of two bands (o at B = 24 / 32: 8.8 / 9.4 us
+// against 9.7 / 10.4 with four).
 template <int NW, int TM, int TN, bool XL>
 struct DecCfg {
     static constexpr int STAGES = XL        ? (TN == 4 ? 2 : 4)
                                   : NW == 4 ? (TM == 4 ? 4 : 8)
-                                  : NW == 8 ? (TM == 4 ? 3 : 4)
+                                  : NW == 8 ? (TM == 4 ? 3 : TM == 2 ? 2 : 4)
                                             : 2;
 };
 }  // namespace
