@@ -95,6 +95,12 @@ __global__ __launch_bounds__(WM * WN * 64) void k_w4a16_mid(const uint16_t* __re
     // wave's tiles (ragged N) return 0
     const bool has_z = zr != nullptr;
     const int tt = my_tiles > 0 ? t0 : 0;
+    // The group waits below count this wave's weight, scale and zero loads.
+    // Loads through restrict arguments that no inline assembly names may be
+    // moved across those waits (a "memory" clobber does not cover them), so
+    // the three pointers pass through an empty asm first: loads through them
+    // then stay where the source puts them.
+    asm volatile("" : "+s"(qw), "+s"(sc), "+s"(zr));
     const auto rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw + (int64_t)tt * ngroups * 256), (short)0,
                                                       my_tiles * ngroups * 1024, 0x00020000);
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(sc + (int64_t)tt * ngroups * 16), (short)0,
